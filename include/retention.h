@@ -1,0 +1,123 @@
+/* Multi-scale retention (RetNet) for AMD MI355X (gfx950): C ABI.
+ *
+ * The method: "Retentive Network: A Successor to Transformer for Large
+ * Language Models" (Elamur Research summary). Section "Summary": retention
+ * replaces attention; it comes from a linear recurrence with exponential
+ * decay; positions are encoded like xPos; there are parallel, recurrent and
+ * chunkwise forms; every head has its own decay; a swish gate and GroupNorm
+ * follow. Section "Key points", fifth item: head i decays with
+ * g_i = 1 - 2^(-5-i), and the chunkwise form costs O(dn(b+h)).
+ *
+ * Per head with decay g, token n of a sequence (0-based) gets
+ *     o_n = sum_{m<=n} g^(n-m) (q_n . k_m) v_m + g^(n+1) q_n S0
+ * (S0: a carried-in state, zero unless given), equivalently the recurrence
+ *     S_n = g S_{n-1} + k_n^T v_n,   o_n = q_n S_n.
+ * q and k are first rotated by position: adjacent pairs (2j, 2j+1) turn by
+ * (pos_offset + n) * base^(-2j/dk) radians. When a gate G is given the output
+ * is GroupNorm(o) (one group per head over its dv values, biased variance, no
+ * affine) times swish(G) = G * sigmoid(G).
+ *
+ * Memory layouts (all row-major, contiguous, caller-owned DEVICE memory):
+ *     q, k          [batch, seqlen, heads, dk]     dtype of the descriptor
+ *     v, g, o       [batch, seqlen, heads, dv]     dtype of the descriptor
+ *     state         [batch, heads, dk, dv]         fp32, always
+ * Every pointer must be 16-byte aligned. `o` must not overlap q, k, v or g.
+ *
+ * Every call validates its arguments on the host first and returns an error
+ * status without touching the device when they are invalid. On success it
+ * enqueues its kernels on `stream` and returns at once; faults inside the
+ * kernels surface at the caller's next synchronisation. The library keeps no
+ * pointer after a call returns, allocates no device memory and holds no
+ * global mutable state, so calls on different streams may run concurrently
+ * when their buffers (workspace included) are distinct. Results are bitwise
+ * deterministic for a given build, shape and input.
+ *
+ * Supported: dk == dv in {64, 128, 256}; dtype fp32 or bf16; heads <= 128.
+ * Arithmetic: bf16 inputs are multiplied on the matrix cores with fp32
+ * accumulation; fp32 inputs use fp32 matrix-core products. The state, decay
+ * factors, GroupNorm and gate run in fp32.
+ */
+#ifndef RETENTION_H
+#define RETENTION_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  RET_OK = 0,
+  RET_ERR_NULL = 1,        /* a required pointer is NULL                        */
+  RET_ERR_SHAPE = 2,       /* batch, seqlen, heads or chunk out of range        */
+  RET_ERR_UNSUPPORTED = 3, /* dk/dv/dtype combination not built                 */
+  RET_ERR_GAMMA = 4,       /* a decay outside (0, 1], or not finite             */
+  RET_ERR_ALIGN = 5,       /* a pointer is not 16-byte aligned                  */
+  RET_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than required          */
+  RET_ERR_HIP = 7,         /* the HIP runtime rejected a kernel launch          */
+  RET_ERR_ALIAS = 8,       /* the output overlaps an input                      */
+  RET_ERR_ARG = 9          /* another scalar argument is invalid (eps, base...) */
+} ret_status_t;
+
+typedef enum { RET_F32 = 0, RET_BF16 = 1 } ret_dtype_t;
+
+typedef struct {
+  int32_t batch;       /* >= 1                                                 */
+  int32_t seqlen;      /* >= 1 (exactly 1 for retention_recurrent_step)        */
+  int32_t heads;       /* 1 .. 128                                             */
+  int32_t dk;          /* query/key head dimension                             */
+  int32_t dv;          /* value head dimension (== dk)                         */
+  int32_t dtype;       /* ret_dtype_t of q, k, v, g and o                      */
+  const double *gamma; /* HOST array [heads] of decays in (0, 1]; NULL selects
+                          the per-head default g_i = 1 - 2^(-5-i)               */
+  double rotary_base;  /* 0: no rotation; else theta_j = base^(-2j/dk), > 0   */
+  int64_t pos_offset;  /* absolute position of token 0 (rotation only), >= 0  */
+  float gn_eps;        /* GroupNorm epsilon, > 0; used only when g != NULL    */
+} ret_desc_t;
+
+/* Parallel form: O = (Q K^T (.) D) V over each whole sequence, D[n, m] =
+ * g^(n-m) for n >= m, else 0 ("Summary": the parallel form is the training
+ * form). `g` NULL: o receives the raw retention output. Workspace: at least
+ * retention_parallel_workspace_bytes(desc) bytes (0 when there is no
+ * rotation; then `workspace` may be NULL). */
+size_t retention_parallel_workspace_bytes(const ret_desc_t *desc);
+ret_status_t retention_parallel_fwd(const ret_desc_t *desc, const void *q, const void *k, const void *v,
+                                    const void *g, void *o, void *workspace, size_t workspace_bytes,
+                                    hipStream_t stream);
+
+/* Chunkwise recurrent form ("Summary": parallel inside a chunk, the recurrent
+ * state passed between chunks). For chunk i of length b (the last may be
+ * shorter than `chunk`):
+ *     O_i = (Q_i K_i^T (.) D) V_i + (Q_i R_{i-1}) (.) xi,   xi_r = g^(r+1)
+ *     R_i = K_i^T (V_i (.) zeta) + g^b R_{i-1},            zeta_r = g^(b-1-r)
+ * R_{-1} = state_in (NULL: zeros). state_out (NULL: not written) receives the
+ * state after the last token; state_out == state_in is allowed. chunk >= 1.
+ * Workspace: at least retention_chunkwise_workspace_bytes(desc, chunk) bytes,
+ * never NULL (it holds the per-chunk states). */
+size_t retention_chunkwise_workspace_bytes(const ret_desc_t *desc, int32_t chunk);
+ret_status_t retention_chunkwise_fwd(const ret_desc_t *desc, int32_t chunk, const void *q, const void *k,
+                                     const void *v, const void *g, void *o, const float *state_in,
+                                     float *state_out, void *workspace, size_t workspace_bytes,
+                                     hipStream_t stream);
+
+/* Recurrent form, one decode step for a batch of single tokens (desc->seqlen
+ * must be 1): state <- g * state + k^T v, then o = q state ("Summary": O(1)
+ * per token, no KV cache). `state` is read and written in place. The rotation
+ * uses position desc->pos_offset for every sequence of the batch. */
+ret_status_t retention_recurrent_step(const ret_desc_t *desc, const void *q, const void *k, const void *v,
+                                      const void *g, void *o, float *state, hipStream_t stream);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *retention_status_string(ret_status_t status);
+
+/* Version of this ABI (incremented on incompatible change). */
+int32_t retention_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RETENTION_H */

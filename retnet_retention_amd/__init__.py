@@ -1,0 +1,16 @@
+"""Multi-scale retention (RetNet) for AMD MI355X: hand-written HIP kernels for
+gfx950 behind a C ABI (include/retention.h), with a thin ctypes binding.
+
+    parallel_fwd     parallel form (training)
+    chunkwise_fwd    chunkwise recurrent form (long sequences, prefill)
+    recurrent_step   recurrent form, one decode step, state in place
+"""
+
+from .binding import (  # noqa: F401
+    RetentionError,
+    chunkwise_fwd,
+    chunkwise_workspace_bytes,
+    lib,
+    parallel_fwd,
+    recurrent_step,
+)

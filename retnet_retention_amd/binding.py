@@ -1,0 +1,218 @@
+"""ctypes binding of libretention.so: torch tensors in, C-ABI calls out.
+
+This layer only marshals arguments (shapes, dtypes, device pointers and the
+current HIP stream); every step of the computation runs in the library's
+kernels. It raises when the library has not been built: there is no fallback.
+"""
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libretention.so")
+
+RET_F32 = 0
+RET_BF16 = 1
+
+STATUS = {
+    0: "RET_OK",
+    1: "RET_ERR_NULL",
+    2: "RET_ERR_SHAPE",
+    3: "RET_ERR_UNSUPPORTED",
+    4: "RET_ERR_GAMMA",
+    5: "RET_ERR_ALIGN",
+    6: "RET_ERR_WORKSPACE",
+    7: "RET_ERR_HIP",
+    8: "RET_ERR_ALIAS",
+    9: "RET_ERR_ARG",
+}
+
+# names declared in include/retention.h
+EXPORTS = (
+    "retention_parallel_workspace_bytes",
+    "retention_parallel_fwd",
+    "retention_chunkwise_workspace_bytes",
+    "retention_chunkwise_fwd",
+    "retention_recurrent_step",
+    "retention_status_string",
+    "retention_abi_version",
+)
+
+
+class RetDesc(ctypes.Structure):
+    """Mirror of ret_desc_t."""
+
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("seqlen", ctypes.c_int32),
+        ("heads", ctypes.c_int32),
+        ("dk", ctypes.c_int32),
+        ("dv", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("gamma", ctypes.POINTER(ctypes.c_double)),
+        ("rotary_base", ctypes.c_double),
+        ("pos_offset", ctypes.c_int64),
+        ("gn_eps", ctypes.c_float),
+    ]
+
+
+class RetentionError(RuntimeError):
+    def __init__(self, status, text):
+        super().__init__(f"{STATUS.get(status, status)}: {text}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library (loads it on first use; raises if it is missing)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is missing: build it first (python -m retnet_retention_amd.build); "
+                "there is no fallback implementation"
+            )
+        h = ctypes.CDLL(LIB_PATH)
+        vp, sz, st, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int32
+        pd = ctypes.POINTER(RetDesc)
+        h.retention_parallel_workspace_bytes.argtypes = [pd]
+        h.retention_parallel_workspace_bytes.restype = sz
+        h.retention_parallel_fwd.argtypes = [pd, vp, vp, vp, vp, vp, vp, sz, vp]
+        h.retention_parallel_fwd.restype = st
+        h.retention_chunkwise_workspace_bytes.argtypes = [pd, i32]
+        h.retention_chunkwise_workspace_bytes.restype = sz
+        h.retention_chunkwise_fwd.argtypes = [pd, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        h.retention_chunkwise_fwd.restype = st
+        h.retention_recurrent_step.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp]
+        h.retention_recurrent_step.restype = st
+        h.retention_status_string.argtypes = [st]
+        h.retention_status_string.restype = ctypes.c_char_p
+        h.retention_abi_version.argtypes = []
+        h.retention_abi_version.restype = i32
+        _lib = h
+    return _lib
+
+
+def _check(status):
+    if status != 0:
+        raise RetentionError(status, lib().retention_status_string(status).decode())
+
+
+def make_desc(batch, seqlen, heads, dk, dv, dtype, gammas=None, rotary_base=0.0, pos_offset=0, eps=1e-5):
+    """Build a RetDesc; returns (desc, keepalive) -- keep the second alive
+    while the descriptor is in use (it owns the gamma array)."""
+    gam = None
+    if gammas is not None:
+        gam = (ctypes.c_double * heads)(*[float(x) for x in gammas])
+    d = RetDesc(batch, seqlen, heads, dk, dv, dtype,
+                ctypes.cast(gam, ctypes.POINTER(ctypes.c_double)) if gam is not None else None,
+                float(rotary_base), int(pos_offset), float(eps))
+    return d, gam
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return RET_BF16
+    if t.dtype == torch.float32:
+        return RET_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bf16 or fp32)")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _validate(q, k, v, g, out):
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("out", out)):
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.dtype != q.dtype:
+            raise ValueError(f"{name} has dtype {t.dtype}, expected {q.dtype}")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be [batch, seqlen, heads, d]")
+    if k.shape != q.shape:
+        raise ValueError("k must have the shape of q")
+    if v.shape[:3] != q.shape[:3]:
+        raise ValueError("v must agree with q on [batch, seqlen, heads]")
+    for name, t in (("g", g), ("out", out)):
+        if t is not None and t.shape != v.shape:
+            raise ValueError(f"{name} must have the shape of v")
+
+
+def _desc_for(q, v, gammas, rotary_base, pos_offset, eps):
+    b, n, h, dk = q.shape
+    return make_desc(b, n, h, dk, v.shape[-1], _dtype_code(q), gammas, rotary_base, pos_offset, eps)
+
+
+def parallel_fwd(q, k, v, g=None, *, gammas=None, rotary_base=0.0, pos_offset=0, eps=1e-5, out=None,
+                 workspace=None):
+    """Parallel form over whole sequences; returns the output tensor."""
+    out = torch.empty_like(v) if out is None else out
+    _validate(q, k, v, g, out)
+    desc, keep = _desc_for(q, v, gammas, rotary_base, pos_offset, eps)
+    L = lib()
+    need = L.retention_parallel_workspace_bytes(ctypes.byref(desc))
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(L.retention_parallel_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(out),
+                                    _ptr(workspace), ws_bytes, _stream(q)))
+    del keep
+    return out
+
+
+def chunkwise_workspace_bytes(q, v, chunk, rotary_base=0.0):
+    desc, keep = _desc_for(q, v, None, rotary_base, 0, 1e-5)
+    return lib().retention_chunkwise_workspace_bytes(ctypes.byref(desc), int(chunk))
+
+
+def chunkwise_fwd(q, k, v, g=None, *, chunk=512, state_in=None, state_out=None, gammas=None, rotary_base=0.0,
+                  pos_offset=0, eps=1e-5, out=None, workspace=None):
+    """Chunkwise form; returns the output tensor (state_out, if given, is
+    filled with the state after the last token)."""
+    out = torch.empty_like(v) if out is None else out
+    _validate(q, k, v, g, out)
+    for name, s in (("state_in", state_in), ("state_out", state_out)):
+        if s is not None:
+            b, _, h, dk = q.shape
+            if s.dtype != torch.float32 or not s.is_contiguous() or tuple(s.shape) != (b, h, dk, v.shape[-1]):
+                raise ValueError(f"{name} must be a contiguous fp32 [batch, heads, dk, dv] tensor")
+    desc, keep = _desc_for(q, v, gammas, rotary_base, pos_offset, eps)
+    L = lib()
+    need = L.retention_chunkwise_workspace_bytes(ctypes.byref(desc), int(chunk))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(L.retention_chunkwise_fwd(ctypes.byref(desc), int(chunk), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                     _ptr(out), _ptr(state_in), _ptr(state_out), _ptr(workspace), ws_bytes,
+                                     _stream(q)))
+    del keep
+    return out
+
+
+def recurrent_step(q, k, v, state, g=None, *, gammas=None, rotary_base=0.0, pos=0, eps=1e-5, out=None):
+    """One decode step (q, k: [batch, 1, heads, dk]); updates `state` in place
+    and returns the output [batch, 1, heads, dv]."""
+    out = torch.empty_like(v) if out is None else out
+    _validate(q, k, v, g, out)
+    if q.shape[1] != 1:
+        raise ValueError("recurrent_step takes one token per sequence (seqlen 1)")
+    b, _, h, dk = q.shape
+    if state.dtype != torch.float32 or not state.is_contiguous() or tuple(state.shape) != (b, h, dk, v.shape[-1]):
+        raise ValueError("state must be a contiguous fp32 [batch, heads, dk, dv] tensor")
+    desc, keep = _desc_for(q, v, gammas, rotary_base, pos, eps)
+    _check(lib().retention_recurrent_step(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(out),
+                                          _ptr(state), _stream(q)))
+    del keep
+    return out

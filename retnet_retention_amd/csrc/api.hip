@@ -1,0 +1,196 @@
+// C-ABI host layer: argument validation (before any HIP call), per-head decay
+// table, workspace carving and kernel launches on the caller's stream.
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "launch.hpp"
+#include "retention.h"
+
+namespace {
+
+using ret::Shape;
+
+constexpr size_t kWsAlign = 256;
+size_t align_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+size_t elem_size(int32_t dtype) { return dtype == RET_BF16 ? 2 : 4; }
+
+// Decay of head h: the caller's value, or g_h = 1 - 2^(-5-h) (per-head decay
+// of "Retentive Network: A Successor to Transformer...", Elamur summary,
+// Key points, fifth item).
+double head_gamma(const ret_desc_t* d, int h) { return d->gamma ? d->gamma[h] : 1.0 - std::ldexp(1.0, -5 - h); }
+
+ret_status_t check_desc(const ret_desc_t* d) {
+  if (!d) return RET_ERR_NULL;
+  if (d->batch < 1 || d->seqlen < 1 || d->heads < 1 || d->heads > ret::kMaxHeadsHost) return RET_ERR_SHAPE;
+  // every launch grid is bounded by batch * heads * seqlen workgroups
+  if ((int64_t)d->batch * d->heads * d->seqlen > INT32_MAX) return RET_ERR_SHAPE;
+  if (d->dtype != RET_F32 && d->dtype != RET_BF16) return RET_ERR_UNSUPPORTED;
+  if (d->dk != d->dv || (d->dk != 64 && d->dk != 128 && d->dk != 256)) return RET_ERR_UNSUPPORTED;
+  if (d->gamma) {
+    for (int h = 0; h < d->heads; ++h) {
+      const double g = d->gamma[h];
+      if (!(std::isfinite(g) && g > 0.0 && g <= 1.0)) return RET_ERR_GAMMA;
+    }
+  }
+  if (!(std::isfinite(d->rotary_base) && d->rotary_base >= 0.0)) return RET_ERR_ARG;
+  if (d->pos_offset < 0 || d->pos_offset > (int64_t(1) << 52)) return RET_ERR_ARG;
+  return RET_OK;
+}
+
+ret_status_t check_eps(const ret_desc_t* d, const void* g) {
+  if (g && !(std::isfinite(d->gn_eps) && d->gn_eps > 0.0f)) return RET_ERR_ARG;
+  return RET_OK;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+ret_status_t check_tensors(const ret_desc_t* d, const void* q, const void* k, const void* v, const void* g,
+                           const void* o) {
+  if (!q || !k || !v || !o) return RET_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (g && !aligned16(g)))
+    return RET_ERR_ALIGN;
+  const size_t n = (size_t)d->batch * d->seqlen * d->heads * d->dk * elem_size(d->dtype);
+  if (overlaps(o, n, q, n) || overlaps(o, n, k, n) || overlaps(o, n, v, n) || overlaps(o, n, g, n))
+    return RET_ERR_ALIAS;
+  return RET_OK;
+}
+
+Shape make_shape(const ret_desc_t* d) {
+  Shape s;
+  std::memset(&s, 0, sizeof(s));
+  s.batch = d->batch;
+  s.seqlen = d->seqlen;
+  s.heads = d->heads;
+  s.d = d->dk;
+  s.dtype = d->dtype;
+  for (int h = 0; h < d->heads; ++h) {
+    const double g = head_gamma(d, h);
+    s.log2g[h] = (float)(std::log1p(g - 1.0) / std::log(2.0));
+    s.gam[h] = (float)g;
+  }
+  return s;
+}
+
+size_t rot_bytes(const ret_desc_t* d) {
+  return d->rotary_base != 0.0 ? align_up((size_t)d->seqlen * (d->dk / 2) * sizeof(float2)) : 0;
+}
+
+int32_t eff_chunk(const ret_desc_t* d, int32_t chunk) { return chunk < d->seqlen ? chunk : d->seqlen; }
+
+size_t snap_bytes(const ret_desc_t* d, int32_t chunk) {
+  const int32_t c = eff_chunk(d, chunk);
+  const size_t nchunks = ((size_t)d->seqlen + c - 1) / c;
+  return align_up((size_t)d->batch * d->heads * nchunks * d->dk * d->dv * elem_size(d->dtype));
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t retention_abi_version(void) { return 1; }
+
+const char* retention_status_string(ret_status_t s) {
+  switch (s) {
+    case RET_OK: return "ok";
+    case RET_ERR_NULL: return "a required pointer is NULL";
+    case RET_ERR_SHAPE: return "batch, seqlen, heads or chunk out of range";
+    case RET_ERR_UNSUPPORTED: return "unsupported dk/dv/dtype (need dk == dv in {64,128,256}, fp32 or bf16)";
+    case RET_ERR_GAMMA: return "decay outside (0, 1]";
+    case RET_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case RET_ERR_WORKSPACE: return "workspace NULL or too small";
+    case RET_ERR_HIP: return "HIP runtime error at kernel launch";
+    case RET_ERR_ALIAS: return "output overlaps an input";
+    case RET_ERR_ARG: return "invalid scalar argument (gn_eps, rotary_base or pos_offset)";
+  }
+  return "unknown status";
+}
+
+size_t retention_parallel_workspace_bytes(const ret_desc_t* desc) {
+  if (check_desc(desc) != RET_OK) return 0;
+  return rot_bytes(desc);
+}
+
+ret_status_t retention_parallel_fwd(const ret_desc_t* desc, const void* q, const void* k, const void* v,
+                                    const void* g, void* o, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream) {
+  ret_status_t st = check_desc(desc);
+  if (st != RET_OK) return st;
+  if ((st = check_tensors(desc, q, k, v, g, o)) != RET_OK) return st;
+  if ((st = check_eps(desc, g)) != RET_OK) return st;
+  const size_t need = rot_bytes(desc);
+  if (need && (!workspace || workspace_bytes < need)) return RET_ERR_WORKSPACE;
+  if (workspace && !aligned16(workspace)) return RET_ERR_ALIGN;
+
+  const Shape s = make_shape(desc);
+  float2* rot = nullptr;
+  if (need) {
+    rot = reinterpret_cast<float2*>(workspace);
+    if (ret::launch_rotary_table(rot, desc->seqlen, desc->dk, desc->rotary_base, desc->pos_offset, stream) !=
+        hipSuccess)
+      return RET_ERR_HIP;
+  }
+  if (ret::launch_retention_out(s, desc->seqlen, q, k, v, g, o, rot, nullptr, 0, desc->gn_eps, stream) !=
+      hipSuccess)
+    return RET_ERR_HIP;
+  return RET_OK;
+}
+
+size_t retention_chunkwise_workspace_bytes(const ret_desc_t* desc, int32_t chunk) {
+  if (check_desc(desc) != RET_OK || chunk < 1) return 0;
+  return rot_bytes(desc) + snap_bytes(desc, chunk);
+}
+
+ret_status_t retention_chunkwise_fwd(const ret_desc_t* desc, int32_t chunk, const void* q, const void* k,
+                                     const void* v, const void* g, void* o, const float* state_in,
+                                     float* state_out, void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream) {
+  ret_status_t st = check_desc(desc);
+  if (st != RET_OK) return st;
+  if (chunk < 1) return RET_ERR_SHAPE;
+  if ((st = check_tensors(desc, q, k, v, g, o)) != RET_OK) return st;
+  if ((st = check_eps(desc, g)) != RET_OK) return st;
+  if ((state_in && !aligned16(state_in)) || (state_out && !aligned16(state_out))) return RET_ERR_ALIGN;
+  const size_t rb = rot_bytes(desc), need = rb + snap_bytes(desc, chunk);
+  if (!workspace || workspace_bytes < need) return RET_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return RET_ERR_ALIGN;
+
+  const Shape s = make_shape(desc);
+  const int32_t c = eff_chunk(desc, chunk);
+  float2* rot = nullptr;
+  if (rb) {
+    rot = reinterpret_cast<float2*>(workspace);
+    if (ret::launch_rotary_table(rot, desc->seqlen, desc->dk, desc->rotary_base, desc->pos_offset, stream) !=
+        hipSuccess)
+      return RET_ERR_HIP;
+  }
+  void* snap = static_cast<char*>(workspace) + rb;
+  if (ret::launch_chunk_state(s, c, k, v, rot, state_in, state_out, snap, stream) != hipSuccess) return RET_ERR_HIP;
+  if (ret::launch_retention_out(s, c, q, k, v, g, o, rot, snap, state_in != nullptr, desc->gn_eps, stream) !=
+      hipSuccess)
+    return RET_ERR_HIP;
+  return RET_OK;
+}
+
+ret_status_t retention_recurrent_step(const ret_desc_t* desc, const void* q, const void* k, const void* v,
+                                      const void* g, void* o, float* state, hipStream_t stream) {
+  ret_status_t st = check_desc(desc);
+  if (st != RET_OK) return st;
+  if (desc->seqlen != 1) return RET_ERR_SHAPE;
+  if ((st = check_tensors(desc, q, k, v, g, o)) != RET_OK) return st;
+  if ((st = check_eps(desc, g)) != RET_OK) return st;
+  if (!state) return RET_ERR_NULL;
+  if (!aligned16(state)) return RET_ERR_ALIGN;
+  const Shape s = make_shape(desc);
+  if (ret::launch_recurrent_step(s, q, k, v, g, o, state, desc->rotary_base, desc->pos_offset, desc->gn_eps,
+                                 stream) != hipSuccess)
+    return RET_ERR_HIP;
+  return RET_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,219 @@
+// Device helpers shared by the retention kernels (gfx950 / CDNA4 only).
+//
+// Matrix-core convention used everywhere (checked on gfx950 hardware):
+//   one 16x16 output block, contraction step of 32 ("k-step"):
+//   lane l, g = l/16, c = l%16
+//     A fragment: A[c][k0 + 8g + j]   j = 0..7
+//     B fragment: B[k0 + 8g + j][c]
+//     C/D accum:  C[4g + i][c]        i = 0..3
+//   bf16 runs one v_mfma_f32_16x16x32_bf16; fp32 runs eight
+//   v_mfma_f32_16x16x4_f32, instruction s feeding logical k = 8g + s, which
+//   keeps the per-lane data layout identical for both element types.
+//
+// A contraction is blind to the order of its k index as long as A and B use
+// the same order. Fragments whose k runs down a column of a row-major LDS
+// tile ("column fragments") use the order
+//   j = 0..3 -> row k0 + 4g + j,   j = 4..7 -> row k0 + 16 + 4g + (j - 4)
+// which is exactly the row order of two stacked 16x16 accumulator blocks, so
+// an accumulator tile can feed the next contraction straight from registers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ret {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kMaxHeads = 128;
+
+template <typename T> struct FragOf;
+template <> struct FragOf<bf16> { using type = bf16x8; };
+template <> struct FragOf<float> { using type = f32x8; };
+template <typename T> using frag_t = typename FragOf<T>::type;
+
+__device__ __forceinline__ f32x4 mma(const bf16x8& a, const bf16x8& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mma(const f32x8& a, const f32x8& b, f32x4 c) {
+#pragma unroll
+  for (int s = 0; s < 8; ++s) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], c, 0, 0, 0);
+  return c;
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// ---------------------------------------------------------------------------
+// 8-element vectors in registers, as fp32, loaded from / stored to T memory.
+// ---------------------------------------------------------------------------
+struct F8 { float x[8]; };
+
+__device__ __forceinline__ F8 load8(const bf16* p) {
+  const uint4 w = *reinterpret_cast<const uint4*>(p);
+  F8 r;
+  const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    r.x[2 * i] = __uint_as_float(u[i] << 16);
+    r.x[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+  }
+  return r;
+}
+
+__device__ __forceinline__ F8 load8(const float* p) {
+  const float4 a = reinterpret_cast<const float4*>(p)[0];
+  const float4 b = reinterpret_cast<const float4*>(p)[1];
+  return F8{{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w}};
+}
+
+__device__ __forceinline__ void store8(bf16* p, const F8& v) {
+  bf16x8 o;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = (bf16)v.x[i];
+  *reinterpret_cast<bf16x8*>(p) = o;
+}
+
+__device__ __forceinline__ void store8(float* p, const F8& v) {
+  reinterpret_cast<float4*>(p)[0] = make_float4(v.x[0], v.x[1], v.x[2], v.x[3]);
+  reinterpret_cast<float4*>(p)[1] = make_float4(v.x[4], v.x[5], v.x[6], v.x[7]);
+}
+
+__device__ __forceinline__ void store8_zero(bf16* p) { *reinterpret_cast<uint4*>(p) = make_uint4(0, 0, 0, 0); }
+__device__ __forceinline__ void store8_zero(float* p) {
+  reinterpret_cast<float4*>(p)[0] = make_float4(0.f, 0.f, 0.f, 0.f);
+  reinterpret_cast<float4*>(p)[1] = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+// raw 8-element copy (no conversion)
+__device__ __forceinline__ void copy8(bf16* dst, const bf16* src) {
+  *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+}
+__device__ __forceinline__ void copy8(float* dst, const float* src) {
+  reinterpret_cast<float4*>(dst)[0] = reinterpret_cast<const float4*>(src)[0];
+  reinterpret_cast<float4*>(dst)[1] = reinterpret_cast<const float4*>(src)[1];
+}
+
+// Rotate 4 adjacent pairs (x[2j], x[2j+1]) by the angles whose (cos, sin) are cs[0..3].
+__device__ __forceinline__ void rotate4(F8& v, const float2* cs) {
+  const float4 a = reinterpret_cast<const float4*>(cs)[0];
+  const float4 b = reinterpret_cast<const float4*>(cs)[1];
+  const float c[4] = {a.x, a.z, b.x, b.z};
+  const float s[4] = {a.y, a.w, b.y, b.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float e = v.x[2 * j], o = v.x[2 * j + 1];
+    v.x[2 * j] = e * c[j] - o * s[j];
+    v.x[2 * j + 1] = e * s[j] + o * c[j];
+  }
+}
+
+__device__ __forceinline__ bf16x8 to_frag(const F8& v, bf16*) {
+  bf16x8 o;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = (bf16)v.x[i];
+  return o;
+}
+__device__ __forceinline__ f32x8 to_frag(const F8& v, float*) {
+  f32x8 o;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = v.x[i];
+  return o;
+}
+
+template <typename T> __device__ __forceinline__ frag_t<T> zero_frag() {
+  frag_t<T> f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f[i] = (T)0.f;
+  return f;
+}
+
+// ---------------------------------------------------------------------------
+// LDS fragment loads.
+// ---------------------------------------------------------------------------
+// Row fragment: 8 consecutive elements of one row (k contiguous).
+__device__ __forceinline__ bf16x8 lds_row8(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+__device__ __forceinline__ f32x8 lds_row8(const float* p) {
+  const float4 a = reinterpret_cast<const float4*>(p)[0];
+  const float4 b = reinterpret_cast<const float4*>(p)[1];
+  return f32x8{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+}
+
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// Column fragment of a row-major tile whose element [k0][n0] is at `base`
+// (row stride `stride` elements): lane (g, i) receives rows
+// k0 + {4g..4g+3, 16+4g..16+4g+3} of column n0 + i.
+// bf16 uses the gfx950 transpose read ds_read_b64_tr_b16: inside each group of
+// 16 lanes, lane m fetches 4 elements of row (m/4) at column 4(m%4), and lane
+// i ends up with column i of those four rows.
+__device__ __forceinline__ bf16x8 lds_col8(const bf16* base, int stride, int lane) {
+  const int g = (lane >> 4) & 3, i = lane & 15;
+  const bf16* p = base + (4 * g + (i >> 2)) * stride + 4 * (i & 3);
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 16 * stride));
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  const i16x8 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+__device__ __forceinline__ f32x8 lds_col8(const float* base, int stride, int lane) {
+  const int g = (lane >> 4) & 3, i = lane & 15;
+  const float* p = base + 4 * g * stride + i;
+  f32x8 f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    f[j] = p[j * stride];
+    f[4 + j] = p[(16 + j) * stride];
+  }
+  return f;
+}
+
+// Two stacked 16x16 accumulator blocks (rows k0..k0+15 and k0+16..k0+31 of a
+// 32-deep contraction) become one A fragment in the column-fragment k order.
+__device__ __forceinline__ bf16x8 acc_to_frag(const f32x4& lo, const f32x4& hi, bf16*) {
+  bf16x8 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o[i] = (bf16)lo[i];
+    o[4 + i] = (bf16)hi[i];
+  }
+  return o;
+}
+__device__ __forceinline__ f32x8 acc_to_frag(const f32x4& lo, const f32x4& hi, float*) {
+  return f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// ---------------------------------------------------------------------------
+// Reductions.
+// ---------------------------------------------------------------------------
+// Sum over the 16 lanes that share g (lanes 16g .. 16g+15).
+__device__ __forceinline__ float sum16(float x) {
+  x += __shfl_xor(x, 1, 64);
+  x += __shfl_xor(x, 2, 64);
+  x += __shfl_xor(x, 4, 64);
+  x += __shfl_xor(x, 8, 64);
+  return x;
+}
+
+__device__ __forceinline__ float sum64(float x) {
+  x += __shfl_xor(x, 1, 64);
+  x += __shfl_xor(x, 2, 64);
+  x += __shfl_xor(x, 4, 64);
+  x += __shfl_xor(x, 8, 64);
+  x += __shfl_xor(x, 16, 64);
+  x += __shfl_xor(x, 32, 64);
+  return x;
+}
+
+__device__ __forceinline__ float swish(float x) { return x / (1.0f + expf(-x)); }
+
+// g^e for a decay g given as log2(g): exp2(e * log2 g).
+__device__ __forceinline__ float gpow(float e, float log2g) { return exp2f(e * log2g); }
+
+}  // namespace ret

@@ -1,0 +1,165 @@
+// Recurrent form, one decode step ("Retentive Network: A Successor to
+// Transformer...", Elamur summary, Summary: the recurrent form costs O(1) per
+// token and needs no KV cache):
+//     S <- g S + k^T v,   o = q S,   then GroupNorm + swish gate.
+// The step is a pure stream over the fp32 state: 4 * dk * dv bytes read and
+// written per (sequence, head) against ~5 * dk * dv flops, so it is bound by
+// HBM bandwidth. One workgroup owns one (sequence, head); each wave sweeps
+// whole state rows with 16-byte accesses (a 256-wide row is one wave-wide
+// 1 KiB access) and the row loop is unrolled so that many loads are in flight.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace ret {
+
+struct StepParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* g;
+  void* o;
+  float* state;
+  int heads;
+  int rotary;
+  double base;
+  int64_t pos;
+  float eps;
+  float gam[kMaxHeads];
+};
+
+template <typename T> __device__ __forceinline__ float ld1(const T* p, int i) { return (float)p[i]; }
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void recurrent_step_kernel(StepParams p) {
+  constexpr int CT = D / 4;       // threads across one state row (float4 each)
+  constexpr int RPI = 256 / CT;   // rows per sweep iteration
+  __shared__ __attribute__((aligned(16))) float sq[D], sk[D], sv[D];
+  __shared__ __attribute__((aligned(16))) float part[RPI][D];
+  __shared__ float so[D];
+
+  const int tid = threadIdx.x;
+  const int bh = blockIdx.x;
+  const int h = bh % p.heads;
+  const float gam = p.gam[h];
+  const int64_t vec = (int64_t)bh * D;  // token row of this (sequence, head): seqlen is 1
+  const T* q = reinterpret_cast<const T*>(p.q) + vec;
+  const T* k = reinterpret_cast<const T*>(p.k) + vec;
+  const T* v = reinterpret_cast<const T*>(p.v) + vec;
+
+  for (int i = tid; i < D; i += 256) {
+    sq[i] = ld1(q, i);
+    sk[i] = ld1(k, i);
+    sv[i] = ld1(v, i);
+  }
+  __syncthreads();
+  if (p.rotary) {
+    for (int j = tid; j < D / 2; j += 256) {
+      const double theta = pow(p.base, -2.0 * j / D);
+      double s, c;
+      sincos((double)p.pos * theta, &s, &c);
+      const float cf = (float)c, sf = (float)s;
+      const float q0 = sq[2 * j], q1 = sq[2 * j + 1], k0 = sk[2 * j], k1 = sk[2 * j + 1];
+      sq[2 * j] = q0 * cf - q1 * sf;
+      sq[2 * j + 1] = q0 * sf + q1 * cf;
+      sk[2 * j] = k0 * cf - k1 * sf;
+      sk[2 * j + 1] = k0 * sf + k1 * cf;
+    }
+    __syncthreads();
+  }
+
+  const int c4 = tid % CT, r0 = tid / CT;
+  const float4 vv = *reinterpret_cast<const float4*>(&sv[c4 * 4]);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float* S = p.state + (int64_t)bh * D * D + c4 * 4;
+#pragma unroll 8
+  for (int r = r0; r < D; r += RPI) {
+    float4 s = *reinterpret_cast<const float4*>(S + (int64_t)r * D);
+    const float kr = sk[r], qr = sq[r];
+    s.x = gam * s.x + kr * vv.x;
+    s.y = gam * s.y + kr * vv.y;
+    s.z = gam * s.z + kr * vv.z;
+    s.w = gam * s.w + kr * vv.w;
+    *reinterpret_cast<float4*>(S + (int64_t)r * D) = s;
+    acc.x += qr * s.x;
+    acc.y += qr * s.y;
+    acc.z += qr * s.z;
+    acc.w += qr * s.w;
+  }
+  *reinterpret_cast<float4*>(&part[r0][c4 * 4]) = acc;
+  __syncthreads();
+  for (int j = tid; j < D; j += 256) {
+    float s = 0.f;
+#pragma unroll
+    for (int r = 0; r < RPI; ++r) s += part[r][j];
+    so[j] = s;
+  }
+  __syncthreads();
+
+  if (tid < 64) {
+    constexpr int PER = D / 64;
+    float x[PER];
+#pragma unroll
+    for (int m = 0; m < PER; ++m) x[m] = so[tid + 64 * m];
+    T* o = reinterpret_cast<T*>(p.o) + vec;
+    if (p.g) {
+      const T* gp = reinterpret_cast<const T*>(p.g) + vec;
+      float sum = 0.f;
+#pragma unroll
+      for (int m = 0; m < PER; ++m) sum += x[m];
+      const float mean = sum64(sum) * (1.0f / D);
+      float sq2 = 0.f;
+#pragma unroll
+      for (int m = 0; m < PER; ++m) sq2 += (x[m] - mean) * (x[m] - mean);
+      const float rstd = rsqrtf(sum64(sq2) * (1.0f / D) + p.eps);
+#pragma unroll
+      for (int m = 0; m < PER; ++m) {
+        const float gv = ld1(gp, tid + 64 * m);
+        o[tid + 64 * m] = (T)((x[m] - mean) * rstd * swish(gv));
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < PER; ++m) o[tid + 64 * m] = (T)x[m];
+    }
+  }
+}
+
+template <typename T, int D>
+static hipError_t launch_step_t(const Shape& s, const StepParams& p, hipStream_t stream) {
+  const unsigned blocks = (unsigned)s.batch * (unsigned)s.heads;
+  hipLaunchKernelGGL((recurrent_step_kernel<T, D>), dim3(blocks), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_recurrent_step(const Shape& s, const void* q, const void* k, const void* v, const void* g,
+                                 void* o, float* state, double rotary_base, int64_t pos, float eps,
+                                 hipStream_t stream) {
+  StepParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.g = g;
+  p.o = o;
+  p.state = state;
+  p.heads = s.heads;
+  p.rotary = rotary_base != 0.0;
+  p.base = rotary_base;
+  p.pos = pos;
+  p.eps = eps;
+  for (int h = 0; h < kMaxHeads; ++h) p.gam[h] = h < s.heads ? s.gam[h] : 0.f;
+  if (s.dtype == 1) {
+    switch (s.d) {
+      case 64: return launch_step_t<bf16, 64>(s, p, stream);
+      case 128: return launch_step_t<bf16, 128>(s, p, stream);
+      case 256: return launch_step_t<bf16, 256>(s, p, stream);
+    }
+  } else {
+    switch (s.d) {
+      case 64: return launch_step_t<float, 64>(s, p, stream);
+      case 128: return launch_step_t<float, 128>(s, p, stream);
+      case 256: return launch_step_t<float, 256>(s, p, stream);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ret

@@ -1,0 +1,88 @@
+"""Shared helpers for the GPU parity tests: run the HIP library through its
+binding on synthetic inputs and compare with the fp64 oracle."""
+
+import numpy as np
+import torch
+
+import oracle
+import retnet_retention_amd as rr
+from synth import draw
+
+DEV = "cuda:0"
+
+# Bars: fp32 inputs max-abs 1e-4; bf16 inputs relative Frobenius 2e-2 (fp32 accumulation).
+F32_MAX_ABS = 1e-4
+BF16_REL_FROB = 2e-2
+
+
+def to64(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def rel_frob(got, ref):
+    den = np.linalg.norm(ref.ravel())
+    return float(np.linalg.norm((got - ref).ravel()) / (den if den > 0 else 1.0))
+
+
+def assert_close(got, ref, dtype, what=""):
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    if dtype == "f32":
+        err = float(np.max(np.abs(got - ref)))
+        assert err <= F32_MAX_ABS, f"{what}: max-abs {err:.3e} > {F32_MAX_ABS}"
+    else:
+        err = rel_frob(got, ref)
+        assert err <= BF16_REL_FROB, f"{what}: rel-Frobenius {err:.3e} > {BF16_REL_FROB}"
+    return err
+
+
+def make_inputs(seed, b, n, h, d, dtype, scale, gate_scale=None, state=False):
+    specs = [((b, n, h, d), scale)] * 3
+    if gate_scale is not None:
+        specs.append(((b, n, h, d), gate_scale))
+    ts = draw(seed, specs, dtype)
+    q, k, v = ts[:3]
+    g = ts[3] if gate_scale is not None else None
+    s0 = None
+    if state:
+        rng = np.random.default_rng(seed + 1000)
+        s0 = rng.standard_normal((b, h, d, d)) * 0.05
+        s0 = s0.astype(np.float32).astype(np.float64)
+    return q, k, v, g, s0
+
+
+def gpu_run(form, q, k, v, g, *, chunk=64, rotary_base=0.0, pos_offset=0, state_in=None, gammas=None, eps=1e-5):
+    """Run one form on the GPU; returns (out fp64, final state fp64 or None)."""
+    tq, tk, tv = q.torch(DEV), k.torch(DEV), v.torch(DEV)
+    tg = g.torch(DEV) if g is not None else None
+    b, n, h, dk = tq.shape
+    dv = tv.shape[-1]
+    s_in = torch.from_numpy(state_in.astype(np.float32)).to(DEV) if state_in is not None else None
+    state = None
+    if form == "parallel":
+        out = rr.parallel_fwd(tq, tk, tv, tg, gammas=gammas, rotary_base=rotary_base, pos_offset=pos_offset, eps=eps)
+    elif form == "chunkwise":
+        s_out = torch.full((b, h, dk, dv), float("nan"), device=DEV)
+        out = rr.chunkwise_fwd(tq, tk, tv, tg, chunk=chunk, state_in=s_in, state_out=s_out, gammas=gammas,
+                               rotary_base=rotary_base, pos_offset=pos_offset, eps=eps)
+        state = s_out
+    elif form == "recurrent":
+        st = s_in.clone() if s_in is not None else torch.zeros((b, h, dk, dv), device=DEV)
+        out = torch.empty_like(tv)
+        for t in range(n):
+            sl = slice(t, t + 1)
+            o_t = rr.recurrent_step(tq[:, sl].contiguous(), tk[:, sl].contiguous(), tv[:, sl].contiguous(), st,
+                                    tg[:, sl].contiguous() if tg is not None else None, gammas=gammas,
+                                    rotary_base=rotary_base, pos=pos_offset + t, eps=eps)
+            out[:, sl] = o_t
+        state = st
+    else:
+        raise ValueError(form)
+    torch.cuda.synchronize()
+    return to64(out), (to64(state) if state is not None else None)
+
+
+def oracle_run(form, q, k, v, g, *, chunk=64, rotary_base=0.0, pos_offset=0, state_in=None, gammas=None, eps=1e-5):
+    """The fp64 oracle on the same bits; returns (out, final state or None)."""
+    return oracle.retention(form, q.f64, k.f64, v.f64, g=None if g is None else g.f64, gammas=gammas,
+                            rotary_base=rotary_base, pos_offset=pos_offset, eps=eps, chunk=chunk,
+                            state_in=state_in)

@@ -1,0 +1,137 @@
+"""The C-ABI library on the host: it loads without a GPU, exports every entry
+point include/retention.h declares, sizes workspaces, and rejects invalid
+arguments with the documented status before any HIP call. Only calls that
+fail validation are made here, so no kernel is ever launched."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from retnet_retention_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "retention.h")
+
+ALIGNED = 1 << 32  # fake, never dereferenced: every call below fails validation first
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(binding.LIB_PATH):
+        pytest.skip("libretention.so not built (run __graft_entry__.build())")
+    return binding.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(retention_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_functions() == sorted(binding.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    assert L.retention_abi_version() == 1
+
+
+def _desc(**kw):
+    args = dict(batch=2, seqlen=100, heads=4, dk=256, dv=256, dtype=binding.RET_BF16)
+    args.update(kw)
+    gam = args.pop("gammas", None)
+    rot = args.pop("rotary_base", 0.0)
+    eps = args.pop("eps", 1e-5)
+    d, keep = binding.make_desc(gammas=gam, rotary_base=rot, eps=eps, **args)
+    return d, keep
+
+
+def _par(L, d, q=ALIGNED, k=ALIGNED * 2, v=ALIGNED * 3, g=None, o=ALIGNED * 4, ws=None, wsb=0):
+    return L.retention_parallel_fwd(ctypes.byref(d), q, k, v, g, o, ws, wsb, None)
+
+
+def _chk(L, d, chunk=64, q=ALIGNED, k=ALIGNED * 2, v=ALIGNED * 3, g=None, o=ALIGNED * 4, si=None, so=None,
+         ws=None, wsb=0):
+    return L.retention_chunkwise_fwd(ctypes.byref(d), chunk, q, k, v, g, o, si, so, ws, wsb, None)
+
+
+def _step(L, d, q=ALIGNED, k=ALIGNED * 2, v=ALIGNED * 3, g=None, o=ALIGNED * 4, s=ALIGNED * 5):
+    return L.retention_recurrent_step(ctypes.byref(d), q, k, v, g, o, s, None)
+
+
+def test_status_strings(L):
+    for code in range(10):
+        assert L.retention_status_string(code)
+    assert L.retention_status_string(0) == b"ok"
+
+
+def test_workspace_sizes(L):
+    d, _ = _desc(batch=2, seqlen=1000, heads=3, dk=128, dv=128)
+    assert L.retention_parallel_workspace_bytes(ctypes.byref(d)) == 0
+    # snapshots: batch * heads * ceil(1000/64) chunks * 128 * 128 * 2 bytes, rounded up to 256
+    assert L.retention_chunkwise_workspace_bytes(ctypes.byref(d), 64) == 2 * 3 * 16 * 128 * 128 * 2
+    d, _ = _desc(batch=1, seqlen=10, heads=1, dk=64, dv=64, dtype=binding.RET_F32, rotary_base=10000.0)
+    rot = (10 * 32 * 8 + 255) // 256 * 256
+    assert L.retention_parallel_workspace_bytes(ctypes.byref(d)) == rot
+    # chunk larger than the sequence counts as one chunk
+    assert L.retention_chunkwise_workspace_bytes(ctypes.byref(d), 4096) == rot + 256 * ((64 * 64 * 4 + 255) // 256)
+    assert L.retention_chunkwise_workspace_bytes(ctypes.byref(d), 0) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=0), 2), (dict(seqlen=0), 2), (dict(heads=0), 2), (dict(heads=129), 2),
+    (dict(dk=32, dv=32), 3), (dict(dk=128, dv=256), 3), (dict(dtype=7), 3),
+    (dict(gammas=[0.9, 0.0, 0.5, 0.5]), 4), (dict(gammas=[0.9, 1.5, 0.5, 0.5]), 4),
+    (dict(gammas=[0.9, float("nan"), 0.5, 0.5]), 4), (dict(rotary_base=-1.0), 9),
+    (dict(rotary_base=float("inf")), 9),
+])
+def test_descriptor_validation(L, kw, status):
+    d, _ = _desc(**kw)
+    assert _par(L, d) == status
+    assert _chk(L, d) == status
+
+
+def test_pointer_validation(L):
+    d, _ = _desc()
+    assert _par(L, d, q=None) == 1
+    assert _par(L, d, o=None) == 1
+    assert _par(L, d, k=ALIGNED + 8) == 5
+    assert _par(L, d, g=ALIGNED * 6 + 4) == 5
+    # the output overlaps q
+    assert _par(L, d, o=ALIGNED + 256) == 8
+    # gate given but eps invalid
+    d2, _ = _desc(eps=0.0)
+    assert _par(L, d2, g=ALIGNED * 6) == 9
+    # rotation needs a workspace
+    d3, _ = _desc(rotary_base=10000.0)
+    assert _par(L, d3) == 6
+    # chunkwise: chunk < 1, no workspace, workspace too small, misaligned state
+    assert _chk(L, d, chunk=0) == 2
+    assert _chk(L, d) == 6
+    need = L.retention_chunkwise_workspace_bytes(ctypes.byref(d), 64)
+    assert _chk(L, d, ws=ALIGNED * 8, wsb=need - 1) == 6
+    assert _chk(L, d, ws=ALIGNED * 8, wsb=need, si=ALIGNED * 7 + 4) == 5
+    assert _chk(L, d, ws=ALIGNED * 8 + 8, wsb=need) == 5
+
+
+def test_step_validation(L):
+    d, _ = _desc()  # seqlen 100: a step takes exactly one token
+    assert _step(L, d) == 2
+    d, _ = _desc(seqlen=1)
+    assert _step(L, d, s=None) == 1
+    assert _step(L, d, s=ALIGNED * 5 + 8) == 5
+    assert _step(L, d, v=None) == 1
+
+
+def test_product_path_never_touches_the_oracle():
+    """No file of the package (Python or HIP/C++) imports or names the oracle."""
+    pkg = os.path.join(ROOT, "retnet_retention_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text, f
+                assert "retention_oracle" not in text, f

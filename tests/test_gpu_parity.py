@@ -1,0 +1,181 @@
+"""GPU parity of the HIP library against the fp64 oracle, at sizes the oracle
+finishes in seconds that still span several tiles and ragged tails, plus the
+edge cases: a single token, chunk sizes that do not divide the sequence, a
+carried state, custom decays (1, 1/2, vanishing), aliased state in/out,
+decode after prefill, and bitwise run-to-run determinism."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import retnet_retention_amd as rr
+from synth import get
+from tests.gpu_helpers import DEV, assert_close, gpu_run, make_inputs, oracle_run, to64
+
+pytestmark = pytest.mark.gpu
+
+
+def _announce(**kw):
+    print("case:", " ".join(f"{k}={v}" for k, v in kw.items()), flush=True)
+
+
+# --- the tiny fp32 workload: all three forms, max-abs 1e-4 -----------------
+@pytest.mark.parametrize("form", ["parallel", "chunkwise", "recurrent"])
+def test_tiny_fp32_workload(form):
+    w = get("tiny_fp32")
+    _announce(workload=w.name, form=form)
+    q, k, v, g = w.inputs()
+    ref, ref_s = oracle_run(form, q, k, v, g, chunk=w.chunk, rotary_base=w.rotary_base)
+    out, st = gpu_run(form, q, k, v, g, chunk=w.chunk, rotary_base=w.rotary_base)
+    assert_close(out, ref, "f32", f"{form} out")
+    if ref_s is not None:
+        assert_close(st, ref_s, "f32", f"{form} state")
+
+
+# --- bf16 shapes: tiles, ragged tails, gate, rotation, carried state -------
+BF16_CASES = [
+    # (batch, seqlen, heads, d, chunk, gate, rotary, state)
+    (1, 1, 1, 64, 64, True, True, False),
+    (2, 63, 3, 64, 64, False, False, False),
+    (1, 64, 1, 128, 64, True, False, True),
+    (2, 65, 3, 256, 64, True, True, False),
+    (1, 250, 2, 256, 64, True, True, True),
+    (1, 250, 1, 128, 100, False, True, True),
+    (2, 300, 2, 64, 7, True, False, True),
+    (1, 700, 2, 256, 512, True, True, False),
+    (1, 520, 1, 256, 128, False, False, False),
+]
+
+
+@pytest.mark.parametrize("b,n,h,d,chunk,gate,rot,state", BF16_CASES)
+def test_bf16_chunkwise(b, n, h, d, chunk, gate, rot, state):
+    _announce(form="chunkwise", b=b, n=n, h=h, d=d, chunk=chunk, gate=gate, rot=rot, state=state)
+    q, k, v, g, s0 = make_inputs(11 + n + d, b, n, h, d, "bf16", 1 / 16, 1.0 if gate else None, state)
+    base = 10000.0 if rot else 0.0
+    ref, ref_s = oracle_run("chunkwise", q, k, v, g, chunk=chunk, rotary_base=base, pos_offset=3, state_in=s0)
+    out, st = gpu_run("chunkwise", q, k, v, g, chunk=chunk, rotary_base=base, pos_offset=3, state_in=s0)
+    assert_close(out, ref, "bf16", "out")
+    assert_close(st, ref_s, "bf16", "state")
+
+
+@pytest.mark.parametrize("b,n,h,d,gate,rot", [(1, 1, 1, 256, True, False), (2, 63, 3, 64, True, True),
+                                              (1, 200, 2, 128, False, True), (1, 700, 2, 256, True, True)])
+def test_bf16_parallel(b, n, h, d, gate, rot):
+    _announce(form="parallel", b=b, n=n, h=h, d=d, gate=gate, rot=rot)
+    q, k, v, g, _ = make_inputs(23 + n, b, n, h, d, "bf16", 1 / 16, 1 / 16 if gate else None)
+    base = 10000.0 if rot else 0.0
+    ref, _ = oracle_run("parallel", q, k, v, g, rotary_base=base)
+    out, _ = gpu_run("parallel", q, k, v, g, rotary_base=base)
+    assert_close(out, ref, "bf16", "out")
+
+
+@pytest.mark.parametrize("b,n,h,d,gate,state", [(2, 20, 3, 256, True, True), (3, 9, 2, 64, False, False),
+                                                (1, 12, 1, 128, True, True)])
+def test_bf16_recurrent(b, n, h, d, gate, state):
+    _announce(form="recurrent", b=b, n=n, h=h, d=d, gate=gate, state=state)
+    q, k, v, g, s0 = make_inputs(31 + n, b, n, h, d, "bf16", 1 / 16, 1.0 if gate else None, state)
+    ref, ref_s = oracle_run("recurrent", q, k, v, g, rotary_base=10000.0, pos_offset=100, state_in=s0)
+    out, st = gpu_run("recurrent", q, k, v, g, rotary_base=10000.0, pos_offset=100, state_in=s0)
+    assert_close(out, ref, "bf16", "out")
+    assert_close(st, ref_s, "bf16", "state")
+
+
+# --- fp32 at larger head dims ----------------------------------------------
+@pytest.mark.parametrize("form", ["parallel", "chunkwise"])
+@pytest.mark.parametrize("d", [128, 256])
+def test_f32_larger_heads(form, d):
+    _announce(form=form, dtype="f32", d=d)
+    q, k, v, g, s0 = make_inputs(41 + d, 1, 130, 2, d, "f32", d ** -0.5, None, form == "chunkwise")
+    ref, ref_s = oracle_run(form, q, k, v, g, chunk=64, rotary_base=10000.0, state_in=s0)
+    out, st = gpu_run(form, q, k, v, g, chunk=64, rotary_base=10000.0, state_in=s0)
+    assert_close(out, ref, "f32", "out")
+    if ref_s is not None:
+        assert_close(st, ref_s, "f32", "state")
+
+
+# --- decays: 1 (linear attention), 1/2, vanishing ---------------------------
+def test_custom_gammas():
+    _announce(case="custom gammas")
+    gam = [1.0, 0.5, 2.0 ** -40, 0.999]
+    q, k, v, g, _ = make_inputs(53, 1, 150, 4, 64, "f32", 1 / 8)
+    for form in ("parallel", "chunkwise"):
+        ref, _ = oracle_run(form, q, k, v, g, chunk=64, gammas=gam)
+        out, _ = gpu_run(form, q, k, v, g, chunk=64, gammas=gam)
+        assert_close(out, ref, "f32", form)
+
+
+# --- state in == state out (in place) ---------------------------------------
+def test_state_in_out_alias():
+    _announce(case="state alias")
+    q, k, v, g, s0 = make_inputs(61, 2, 200, 2, 256, "bf16", 1 / 16, 1.0, True)
+    ref_out, ref_s = oracle_run("chunkwise", q, k, v, g, chunk=64, state_in=s0)
+    st = torch.from_numpy(s0.astype(np.float32)).to(DEV)
+    out = rr.chunkwise_fwd(q.torch(DEV), k.torch(DEV), v.torch(DEV), g.torch(DEV), chunk=64, state_in=st,
+                           state_out=st)
+    torch.cuda.synchronize()
+    assert_close(to64(out), ref_out, "bf16", "out")
+    assert_close(to64(st), ref_s, "bf16", "state")
+
+
+# --- prefill, then decode steps: the state is the checkpoint ---------------
+def test_decode_after_prefill_matches_longer_prefill():
+    _announce(case="prefill+decode")
+    b, n0, t, h, d = 2, 300, 12, 2, 256
+    q, k, v, g, _ = make_inputs(71, b, n0 + t, h, d, "bf16", 1 / 16, 1 / 16)
+    ref, _ = oracle_run("chunkwise", q, k, v, g, chunk=128, rotary_base=10000.0)
+    tq, tk, tv, tg = q.torch(DEV), k.torch(DEV), v.torch(DEV), g.torch(DEV)
+    st = torch.empty((b, h, d, d), device=DEV)
+    rr.chunkwise_fwd(tq[:, :n0].contiguous(), tk[:, :n0].contiguous(), tv[:, :n0].contiguous(),
+                     tg[:, :n0].contiguous(), chunk=128, state_out=st, rotary_base=10000.0)
+    outs = []
+    for i in range(t):
+        sl = slice(n0 + i, n0 + i + 1)
+        outs.append(rr.recurrent_step(tq[:, sl].contiguous(), tk[:, sl].contiguous(), tv[:, sl].contiguous(), st,
+                                      tg[:, sl].contiguous(), rotary_base=10000.0, pos=n0 + i))
+    torch.cuda.synchronize()
+    got = np.concatenate([to64(o) for o in outs], axis=1)
+    assert_close(got, ref[:, n0:], "bf16", "decode tail")
+    # a split prefill with pos_offset continues the rotation and the state
+    st2 = torch.empty_like(st)
+    rr.chunkwise_fwd(tq[:, :n0].contiguous(), tk[:, :n0].contiguous(), tv[:, :n0].contiguous(),
+                     tg[:, :n0].contiguous(), chunk=128, state_out=st2, rotary_base=10000.0)
+    tail = rr.chunkwise_fwd(tq[:, n0:].contiguous(), tk[:, n0:].contiguous(), tv[:, n0:].contiguous(),
+                            tg[:, n0:].contiguous(), chunk=128, state_in=st2, rotary_base=10000.0, pos_offset=n0)
+    torch.cuda.synchronize()
+    assert_close(to64(tail), ref[:, n0:], "bf16", "split prefill tail")
+
+
+# --- determinism --------------------------------------------------------------
+def test_bitwise_determinism():
+    _announce(case="determinism")
+    q, k, v, g, s0 = make_inputs(81, 2, 1100, 4, 256, "bf16", 1 / 16, 1.0, True)
+    args = [x.torch(DEV) for x in (q, k, v, g)]
+    s_in = torch.from_numpy(s0.astype(np.float32)).to(DEV)
+    runs = []
+    for _ in range(3):
+        so = torch.empty_like(s_in)
+        o = rr.chunkwise_fwd(*args, chunk=512, state_in=s_in, state_out=so)
+        p = rr.parallel_fwd(*args, rotary_base=10000.0)
+        torch.cuda.synchronize()
+        runs.append((o.clone(), so.clone(), p.clone()))
+    for r in runs[1:]:
+        for a, b in zip(r, runs[0]):
+            assert torch.equal(a, b)
+
+
+# --- NaN in the input propagates instead of hanging or vanishing -------------
+def test_nan_propagates_forward_only():
+    """A NaN in v at the first token of a chunk reaches that column of every
+    later output and no earlier one (inside a chunk 0 * NaN is NaN in IEEE
+    arithmetic, for the oracle's matrix product as well)."""
+    _announce(case="nan")
+    q, k, v, g, _ = make_inputs(91, 1, 150, 1, 64, "f32", 1 / 8)
+    tq, tk, tv = q.torch(DEV), k.torch(DEV), v.torch(DEV)
+    tv[0, 64, 0, 5] = float("nan")
+    out = rr.chunkwise_fwd(tq, tk, tv, chunk=64)
+    torch.cuda.synchronize()
+    o = out.cpu()
+    assert torch.isfinite(o[0, :64]).all()
+    assert torch.isnan(o[0, 64:, 0, 5]).all()
+    assert torch.isfinite(o[0, 64:, 0, :5]).all()
