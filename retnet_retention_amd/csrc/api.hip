@@ -26,6 +26,8 @@ ret_status_t check_desc(const ret_desc_t* d) {
   if (d->batch < 1 || d->seqlen < 1 || d->heads < 1 || d->heads > ret::kMaxHeadsHost) return RET_ERR_SHAPE;
   // every launch grid is bounded by batch * heads * seqlen workgroups
   if ((int64_t)d->batch * d->heads * d->seqlen > INT32_MAX) return RET_ERR_SHAPE;
+  // kernels address within one sequence with 32-bit element offsets
+  if ((int64_t)d->seqlen * d->heads * (d->dk > d->dv ? d->dk : d->dv) >= INT32_MAX) return RET_ERR_SHAPE;
   if (d->dtype != RET_F32 && d->dtype != RET_BF16) return RET_ERR_UNSUPPORTED;
   if (d->dk != d->dv || (d->dk != 64 && d->dk != 128 && d->dk != 256)) return RET_ERR_UNSUPPORTED;
   if (d->gamma) {
@@ -77,8 +79,30 @@ Shape make_shape(const ret_desc_t* d) {
   return s;
 }
 
+// Rotation needs the angle table and rotated copies of q and k.
 size_t rot_bytes(const ret_desc_t* d) {
-  return d->rotary_base != 0.0 ? align_up((size_t)d->seqlen * (d->dk / 2) * sizeof(float2)) : 0;
+  if (d->rotary_base == 0.0) return 0;
+  const size_t qk = (size_t)d->batch * d->seqlen * d->heads * d->dk * elem_size(d->dtype);
+  return align_up((size_t)d->seqlen * (d->dk / 2) * sizeof(float2)) + 2 * align_up(qk);
+}
+
+// Launch the table and rotation passes when rotation is on; q and k are
+// replaced by their rotated copies in the workspace.
+bool rotate_inputs(const ret_desc_t* d, const void*& q, const void*& k, void* workspace, hipStream_t stream) {
+  if (d->rotary_base == 0.0) return true;
+  const size_t qk = (size_t)d->batch * d->seqlen * d->heads * d->dk * elem_size(d->dtype);
+  char* ws = static_cast<char*>(workspace);
+  float2* table = reinterpret_cast<float2*>(ws);
+  char* qr = ws + align_up((size_t)d->seqlen * (d->dk / 2) * sizeof(float2));
+  char* kr = qr + align_up(qk);
+  if (ret::launch_rotary_table(table, d->seqlen, d->dk, d->rotary_base, d->pos_offset, stream) != hipSuccess)
+    return false;
+  if (ret::launch_rotate_qk(q, k, qr, kr, table, d->batch, d->seqlen, d->heads, d->dk, d->dtype, stream) !=
+      hipSuccess)
+    return false;
+  q = qr;
+  k = kr;
+  return true;
 }
 
 int32_t eff_chunk(const ret_desc_t* d, int32_t chunk) { return chunk < d->seqlen ? chunk : d->seqlen; }
@@ -128,15 +152,8 @@ ret_status_t retention_parallel_fwd(const ret_desc_t* desc, const void* q, const
   if (workspace && !aligned16(workspace)) return RET_ERR_ALIGN;
 
   const Shape s = make_shape(desc);
-  float2* rot = nullptr;
-  if (need) {
-    rot = reinterpret_cast<float2*>(workspace);
-    if (ret::launch_rotary_table(rot, desc->seqlen, desc->dk, desc->rotary_base, desc->pos_offset, stream) !=
-        hipSuccess)
-      return RET_ERR_HIP;
-  }
-  if (ret::launch_retention_out(s, desc->seqlen, q, k, v, g, o, rot, nullptr, 0, desc->gn_eps, stream) !=
-      hipSuccess)
+  if (!rotate_inputs(desc, q, k, workspace, stream)) return RET_ERR_HIP;
+  if (ret::launch_retention_out(s, desc->seqlen, q, k, v, g, o, nullptr, 0, desc->gn_eps, stream) != hipSuccess)
     return RET_ERR_HIP;
   return RET_OK;
 }
@@ -162,16 +179,10 @@ ret_status_t retention_chunkwise_fwd(const ret_desc_t* desc, int32_t chunk, cons
 
   const Shape s = make_shape(desc);
   const int32_t c = eff_chunk(desc, chunk);
-  float2* rot = nullptr;
-  if (rb) {
-    rot = reinterpret_cast<float2*>(workspace);
-    if (ret::launch_rotary_table(rot, desc->seqlen, desc->dk, desc->rotary_base, desc->pos_offset, stream) !=
-        hipSuccess)
-      return RET_ERR_HIP;
-  }
+  if (!rotate_inputs(desc, q, k, workspace, stream)) return RET_ERR_HIP;
   void* snap = static_cast<char*>(workspace) + rb;
-  if (ret::launch_chunk_state(s, c, k, v, rot, state_in, state_out, snap, stream) != hipSuccess) return RET_ERR_HIP;
-  if (ret::launch_retention_out(s, c, q, k, v, g, o, rot, snap, state_in != nullptr, desc->gn_eps, stream) !=
+  if (ret::launch_chunk_state(s, c, k, v, state_in, state_out, snap, stream) != hipSuccess) return RET_ERR_HIP;
+  if (ret::launch_retention_out(s, c, q, k, v, g, o, snap, state_in != nullptr, desc->gn_eps, stream) !=
       hipSuccess)
     return RET_ERR_HIP;
   return RET_OK;

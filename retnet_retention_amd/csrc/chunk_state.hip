@@ -33,7 +33,6 @@ struct StTile {
 struct StateParams {
   const void* k;
   const void* v;
-  const float2* rot;
   const float* state_in;
   float* state_out;
   void* snap;
@@ -109,37 +108,44 @@ __global__ __launch_bounds__((StTile<T, D>::THREADS)) void chunk_state_kernel(St
       for (int nb = 0; nb < C::NBV; ++nb) racc[rr][nb] *= dec;
 
     for (int kb0 = cs; kb0 < cend; kb0 += C::BK) {
-      __syncthreads();
-      for (int idx = tid; idx < C::BK * (C::TK / 8); idx += C::THREADS) {
+      // all global loads of the stage first (rows clamped in range), then the
+      // LDS writes; keys past the chunk are zeroed (K) and dropped (V * 0).
+      constexpr int KI = C::BK * (C::TK / 8) / C::THREADS;
+      constexpr int VI = C::BK * (C::TV / 8) / C::THREADS;
+      Raw8<T> kr[KI], vr[VI];
+#pragma unroll
+      for (int it = 0; it < KI; ++it) {
+        const int idx = tid + C::THREADS * it;
         const int r = idx / (C::TK / 8), c8 = idx % (C::TK / 8);
-        const int key = kb0 + r;
-        T* kd = ks + r * C::KSTR + c8 * 8;
-        if (key < cend) {
-          const T* src = K + key * tstride + tk0 + c8 * 8;
-          if (p.rot) {
-            F8 x = load8(src);
-            rotate4(x, p.rot + (int64_t)key * (D / 2) + (tk0 + c8 * 8) / 2);
-            store8(kd, x);
-          } else {
-            copy8(kd, src);
-          }
-        } else {
-          store8_zero(kd);
-        }
+        const int key = min(kb0 + r, cend - 1);
+        kr[it] = ld_raw8(K + key * tstride + tk0 + c8 * 8);
       }
-      for (int idx = tid; idx < C::BK * (C::TV / 8); idx += C::THREADS) {
+#pragma unroll
+      for (int it = 0; it < VI; ++it) {
+        const int idx = tid + C::THREADS * it;
+        const int r = idx / (C::TV / 8), c8 = idx % (C::TV / 8);
+        const int key = min(kb0 + r, cend - 1);
+        vr[it] = ld_raw8(V + key * tstride + tv0 + c8 * 8);
+      }
+      __syncthreads();  // previous stage's LDS reads are done
+#pragma unroll
+      for (int it = 0; it < KI; ++it) {
+        const int idx = tid + C::THREADS * it;
+        const int r = idx / (C::TK / 8), c8 = idx % (C::TK / 8);
+        const bool keep = kb0 + r < cend;
+        st_raw8(ks + r * C::KSTR + c8 * 8, kr[it], keep);
+      }
+#pragma unroll
+      for (int it = 0; it < VI; ++it) {
+        const int idx = tid + C::THREADS * it;
         const int r = idx / (C::TV / 8), c8 = idx % (C::TV / 8);
         const int key = kb0 + r;
-        T* vd = vs + r * C::VSTR + c8 * 8;
-        if (key < cend) {
-          F8 x = load8(V + key * tstride + tv0 + c8 * 8);
-          const float z = gpow((float)(cend - 1 - key), lg);
+        F8 x = unpack8(vr[it]);
+        const float z = gpow((float)(cend - 1 - key), lg);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) x.x[e] *= z;
-          store8(vd, x);
-        } else {
-          store8_zero(vd);
-        }
+        for (int e = 0; e < 8; ++e) x.x[e] *= z;
+        zero_unless(x, key < cend);
+        store8(vs + r * C::VSTR + c8 * 8, x);
       }
       __syncthreads();
 #pragma unroll
@@ -180,12 +186,11 @@ static hipError_t launch_state_t(const Shape& s, const StateParams& p0, hipStrea
   return hipGetLastError();
 }
 
-hipError_t launch_chunk_state(const Shape& s, int chunk, const void* k, const void* v, const float2* rot,
-                              const float* state_in, float* state_out, void* snap, hipStream_t stream) {
+hipError_t launch_chunk_state(const Shape& s, int chunk, const void* k, const void* v, const float* state_in,
+                              float* state_out, void* snap, hipStream_t stream) {
   StateParams p;
   p.k = k;
   p.v = v;
-  p.rot = rot;
   p.state_in = state_in;
   p.state_out = state_out;
   p.snap = snap;

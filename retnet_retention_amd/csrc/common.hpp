@@ -99,6 +99,60 @@ __device__ __forceinline__ void copy8(float* dst, const float* src) {
   reinterpret_cast<float4*>(dst)[1] = reinterpret_cast<const float4*>(src)[1];
 }
 
+// Raw 8-element chunk as loaded (no conversion), so that a batch of global
+// loads can be issued back to back before any of them is consumed.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+template <typename T> struct Raw8;
+template <> struct Raw8<bf16> { u32x4 w; };
+template <> struct Raw8<float> { f32x4 a, b; };
+
+__device__ __forceinline__ Raw8<bf16> ld_raw8(const bf16* p) { return Raw8<bf16>{*reinterpret_cast<const u32x4*>(p)}; }
+__device__ __forceinline__ Raw8<float> ld_raw8(const float* p) {
+  return Raw8<float>{reinterpret_cast<const f32x4*>(p)[0], reinterpret_cast<const f32x4*>(p)[1]};
+}
+// store, or zeros when !keep (a select: no branch around the store)
+__device__ __forceinline__ void st_raw8(bf16* p, const Raw8<bf16>& r, bool keep) {
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  *reinterpret_cast<u32x4*>(p) = keep ? r.w : z;
+}
+__device__ __forceinline__ void st_raw8(float* p, const Raw8<float>& r, bool keep) {
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  reinterpret_cast<f32x4*>(p)[0] = keep ? r.a : z;
+  reinterpret_cast<f32x4*>(p)[1] = keep ? r.b : z;
+}
+__device__ __forceinline__ F8 unpack8(const Raw8<bf16>& r) {
+  F8 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o.x[2 * i] = __uint_as_float(r.w[i] << 16);
+    o.x[2 * i + 1] = __uint_as_float(r.w[i] & 0xffff0000u);
+  }
+  return o;
+}
+__device__ __forceinline__ F8 unpack8(const Raw8<float>& r) {
+  return F8{{r.a[0], r.a[1], r.a[2], r.a[3], r.b[0], r.b[1], r.b[2], r.b[3]}};
+}
+__device__ __forceinline__ void zero_unless(F8& v, bool keep) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v.x[i] = keep ? v.x[i] : 0.f;
+}
+
+// (cos, sin) of 4 consecutive pairs, as two 16-byte loads
+struct CS4 { f32x4 a, b; };
+__device__ __forceinline__ CS4 ld_cs4(const float2* p) {
+  return CS4{reinterpret_cast<const f32x4*>(p)[0], reinterpret_cast<const f32x4*>(p)[1]};
+}
+__device__ __forceinline__ void rotate4(F8& v, const CS4& t) {
+  const float c[4] = {t.a[0], t.a[2], t.b[0], t.b[2]};
+  const float s[4] = {t.a[1], t.a[3], t.b[1], t.b[3]};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float e = v.x[2 * j], o = v.x[2 * j + 1];
+    v.x[2 * j] = e * c[j] - o * s[j];
+    v.x[2 * j + 1] = e * s[j] + o * c[j];
+  }
+}
+
 // Rotate 4 adjacent pairs (x[2j], x[2j+1]) by the angles whose (cos, sin) are cs[0..3].
 __device__ __forceinline__ void rotate4(F8& v, const float2* cs) {
   const float4 a = reinterpret_cast<const float4*>(cs)[0];
@@ -190,6 +244,97 @@ __device__ __forceinline__ f32x8 acc_to_frag(const f32x4& lo, const f32x4& hi, f
 }
 
 // ---------------------------------------------------------------------------
+// Padded LDS tiles filled by direct global->LDS loads.
+//
+// A tile holds ROWS rows of COLS elements; each row is followed by PADB
+// bytes of padding so that the fragment reads of one instruction fall in
+// different banks: PADB = 16 for row-fragment reads (16 lanes read 16 rows
+// at the same column; row stride = 16 mod 256 bytes) and PADB = 32 for
+// column (transpose) reads (32 lanes read 8 rows x 32 bytes; row stride =
+// 32 * odd bytes). Every fragment address is then a per-lane base plus an
+// immediate offset.
+//
+// global_load_lds_dwordx4 writes lane i's 16 bytes to LDS base + 16 i (M0
+// holds the base), so a wave instruction fills 64 consecutive 16-byte slots.
+// The tile is treated as a flat run of slots: a slot inside a row's data
+// loads its chunk, a padding slot (or a slot past the tile, inside the tile's
+// rounded-up allocation) loads a harmless in-range chunk that is never read.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <typename T, int ROWS, int COLS, int PADB>
+struct PTile {
+  static constexpr int DATAB = COLS * (int)sizeof(T);  // data bytes per row
+  static constexpr int ROWB = DATAB + PADB;            // row stride in LDS
+  static constexpr int CPR = DATAB / 16;               // data chunks per row
+  static constexpr int SPR = ROWB / 16;                // slots per row
+  static constexpr int SLOTS = ROWS * SPR;
+  static constexpr int NINST = (SLOTS + 63) / 64;      // wave-wide loads
+  static constexpr int BYTES = NINST * 1024;           // allocation
+  static_assert(DATAB % 16 == 0 && PADB % 16 == 0, "16-byte chunks");
+  __device__ static __forceinline__ int off(int r, int col) { return r * ROWB + col * (int)sizeof(T); }
+};
+
+// Issue the async loads of tile TL from rows row0 .. row0+ROWS-1 of a
+// row-major global matrix (`gstride` elements between rows, rows clamped to
+// rmax), spread over NW waves. Completion: s_waitcnt vmcnt + barrier.
+template <typename T, typename TL, int NW>
+__device__ __forceinline__ void async_tile(char* lds, const T* g, int64_t gstride, int row0, int rmax, int wave,
+                                           int lane) {
+#pragma unroll
+  for (int m = 0; m < (TL::NINST + NW - 1) / NW; ++m) {
+    const int n = wave + m * NW;  // wave-uniform
+    if (TL::NINST % NW != 0 && n >= TL::NINST) break;
+    const int slot = n * 64 + lane;
+    int r = slot / TL::SPR, ch = slot % TL::SPR;
+    if (ch >= TL::CPR) ch = 0;  // padding slot: any in-range chunk
+    if (slot >= TL::SLOTS) r = 0;                                  // slack past the tile
+    const int gr = min(row0 + r, rmax);
+    // 32-bit element offset from a wave-uniform base (the host bounds every
+    // per-sequence offset below 2^31 elements)
+    const T* src = g + (uint32_t)(gr * (int)gstride + ch * (16 / (int)sizeof(T)));
+    __builtin_amdgcn_global_load_lds(src, (lds_void*)(lds + n * 1024), 16, 0, 0);
+  }
+}
+
+// Row fragment: elements (r, col .. col+7).
+template <typename TL>
+__device__ __forceinline__ bf16x8 tile_row8(const char* t, int r, int col, bf16*) {
+  return *reinterpret_cast<const bf16x8*>(t + TL::off(r, col));
+}
+template <typename TL>
+__device__ __forceinline__ f32x8 tile_row8(const char* t, int r, int col, float*) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(t + TL::off(r, col));
+  const f32x4 b = *reinterpret_cast<const f32x4*>(t + TL::off(r, col + 4));
+  return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+// Column fragment: lane (g, i) receives rows k0 + {4g..4g+3, 16+4g..16+4g+3}
+// of column n0 + i (see lds_col8).
+template <typename TL>
+__device__ __forceinline__ bf16x8 tile_col8(const char* t, int k0, int n0, int lane, bf16*) {
+  const int g = (lane >> 4) & 3, i = lane & 15;
+  const char* p = t + TL::off(k0 + 4 * g + (i >> 2), n0 + 4 * (i & 3));
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 16 * TL::ROWB));
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  const i16x8 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, w);
+}
+template <typename TL>
+__device__ __forceinline__ f32x8 tile_col8(const char* t, int k0, int n0, int lane, float*) {
+  const int g = (lane >> 4) & 3, i = lane & 15;
+  const char* p = t + TL::off(k0 + 4 * g, n0 + i);
+  f32x8 f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    f[j] = *reinterpret_cast<const float*>(p + j * TL::ROWB);
+    f[4 + j] = *reinterpret_cast<const float*>(p + (16 + j) * TL::ROWB);
+  }
+  return f;
+}
+
+// ---------------------------------------------------------------------------
 // Reductions.
 // ---------------------------------------------------------------------------
 // Sum over the 16 lanes that share g (lanes 16g .. 16g+15).
@@ -211,9 +356,15 @@ __device__ __forceinline__ float sum64(float x) {
   return x;
 }
 
-__device__ __forceinline__ float swish(float x) { return x / (1.0f + expf(-x)); }
+// swish(x) = x * sigmoid(x) with the hardware exp2 and reciprocal (about 1 ulp
+// each): exp2(-x log2 e) saturates to +inf for very negative x, giving -0.
+__device__ __forceinline__ float swish(float x) {
+  return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * x));
+}
 
 // g^e for a decay g given as log2(g): exp2(e * log2 g).
-__device__ __forceinline__ float gpow(float e, float log2g) { return exp2f(e * log2g); }
+// The hardware exp2 flushes results below the normal range to zero, which is
+// the right answer for a decay factor that small.
+__device__ __forceinline__ float gpow(float e, float log2g) { return __builtin_amdgcn_exp2f(e * log2g); }
 
 }  // namespace ret
