@@ -96,7 +96,12 @@ ret_status_t retention_parallel_fwd(const ret_desc_t *desc, const void *q, const
  * R_{-1} = state_in (NULL: zeros). state_out (NULL: not written) receives the
  * state after the last token; state_out == state_in is allowed. chunk >= 1.
  * Workspace: at least retention_chunkwise_workspace_bytes(desc, chunk) bytes,
- * never NULL (it holds the per-chunk states). */
+ * never NULL (it holds the per-chunk states and the hand-off between the
+ * workgroups that carry the state from chunk to chunk). Its first two int32
+ * words form a control block that the call resets: after the call has
+ * completed, word 0 counts the workgroups that ran and word 1 is nonzero only
+ * if a cross-workgroup wait gave up after its bound (an internal error; the
+ * output is then not valid). */
 size_t retention_chunkwise_workspace_bytes(const ret_desc_t *desc, int32_t chunk);
 ret_status_t retention_chunkwise_fwd(const ret_desc_t *desc, int32_t chunk, const void *q, const void *k,
                                      const void *v, const void *g, void *o, const float *state_in,

@@ -107,10 +107,19 @@ bool rotate_inputs(const ret_desc_t* d, const void*& q, const void*& k, void* wo
 
 int32_t eff_chunk(const ret_desc_t* d, int32_t chunk) { return chunk < d->seqlen ? chunk : d->seqlen; }
 
-size_t snap_bytes(const ret_desc_t* d, int32_t chunk) {
+size_t nchunks_of(const ret_desc_t* d, int32_t chunk) {
   const int32_t c = eff_chunk(d, chunk);
-  const size_t nchunks = ((size_t)d->seqlen + c - 1) / c;
-  return align_up((size_t)d->batch * d->heads * nchunks * d->dk * d->dv * elem_size(d->dtype));
+  return ((size_t)d->seqlen + c - 1) / c;
+}
+
+// Chunkwise workspace: control block | rotation (optional) | fp32 state chain
+// (two slots per sequence and head) | per-chunk states R_{i-1}^T.
+size_t ctrl_bytes(const ret_desc_t* d, int32_t chunk) {
+  return align_up(ret::chunkwise_ctrl_bytes(d->batch, d->heads, (int)nchunks_of(d, chunk)));
+}
+size_t chain_bytes(const ret_desc_t* d) { return align_up((size_t)d->batch * d->heads * 2 * d->dk * d->dv * 4); }
+size_t snap_bytes(const ret_desc_t* d, int32_t chunk) {
+  return align_up((size_t)d->batch * d->heads * nchunks_of(d, chunk) * d->dk * d->dv * elem_size(d->dtype));
 }
 
 }  // namespace
@@ -153,14 +162,15 @@ ret_status_t retention_parallel_fwd(const ret_desc_t* desc, const void* q, const
 
   const Shape s = make_shape(desc);
   if (!rotate_inputs(desc, q, k, workspace, stream)) return RET_ERR_HIP;
-  if (ret::launch_retention_out(s, desc->seqlen, q, k, v, g, o, nullptr, 0, desc->gn_eps, stream) != hipSuccess)
+  if (ret::launch_retention_fwd(s, desc->seqlen, false, q, k, v, g, o, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                desc->gn_eps, stream) != hipSuccess)
     return RET_ERR_HIP;
   return RET_OK;
 }
 
 size_t retention_chunkwise_workspace_bytes(const ret_desc_t* desc, int32_t chunk) {
   if (check_desc(desc) != RET_OK || chunk < 1) return 0;
-  return rot_bytes(desc) + snap_bytes(desc, chunk);
+  return ctrl_bytes(desc, chunk) + rot_bytes(desc) + chain_bytes(desc) + snap_bytes(desc, chunk);
 }
 
 ret_status_t retention_chunkwise_fwd(const ret_desc_t* desc, int32_t chunk, const void* q, const void* k,
@@ -173,17 +183,20 @@ ret_status_t retention_chunkwise_fwd(const ret_desc_t* desc, int32_t chunk, cons
   if ((st = check_tensors(desc, q, k, v, g, o)) != RET_OK) return st;
   if ((st = check_eps(desc, g)) != RET_OK) return st;
   if ((state_in && !aligned16(state_in)) || (state_out && !aligned16(state_out))) return RET_ERR_ALIGN;
-  const size_t rb = rot_bytes(desc), need = rb + snap_bytes(desc, chunk);
+  const size_t cb = ctrl_bytes(desc, chunk), rb = rot_bytes(desc), hb = chain_bytes(desc);
+  const size_t need = cb + rb + hb + snap_bytes(desc, chunk);
   if (!workspace || workspace_bytes < need) return RET_ERR_WORKSPACE;
   if (!aligned16(workspace)) return RET_ERR_ALIGN;
 
   const Shape s = make_shape(desc);
   const int32_t c = eff_chunk(desc, chunk);
-  if (!rotate_inputs(desc, q, k, workspace, stream)) return RET_ERR_HIP;
-  void* snap = static_cast<char*>(workspace) + rb;
-  if (ret::launch_chunk_state(s, c, k, v, state_in, state_out, snap, stream) != hipSuccess) return RET_ERR_HIP;
-  if (ret::launch_retention_out(s, c, q, k, v, g, o, snap, state_in != nullptr, desc->gn_eps, stream) !=
-      hipSuccess)
+  char* ws = static_cast<char*>(workspace);
+  int* ctrl = reinterpret_cast<int*>(ws);
+  if (!rotate_inputs(desc, q, k, ws + cb, stream)) return RET_ERR_HIP;
+  float* chain = reinterpret_cast<float*>(ws + cb + rb);
+  void* snap = ws + cb + rb + hb;
+  if (ret::launch_retention_fwd(s, c, true, q, k, v, g, o, state_in, state_out, snap, chain, ctrl, desc->gn_eps,
+                                stream) != hipSuccess)
     return RET_ERR_HIP;
   return RET_OK;
 }

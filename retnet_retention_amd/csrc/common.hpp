@@ -278,7 +278,9 @@ struct PTile {
 // Issue the async loads of tile TL from rows row0 .. row0+ROWS-1 of a
 // row-major global matrix (`gstride` elements between rows, rows clamped to
 // rmax), spread over NW waves. Completion: s_waitcnt vmcnt + barrier.
-template <typename T, typename TL, int NW>
+// CPOL: cache policy of the loads (0: default; 17 = sc0|sc1: read coherently
+// data that another XCD wrote with sc1 stores, bypassing stale cache lines).
+template <typename T, typename TL, int NW, int CPOL = 0>
 __device__ __forceinline__ void async_tile(char* lds, const T* g, int64_t gstride, int row0, int rmax, int wave,
                                            int lane) {
 #pragma unroll
@@ -293,7 +295,7 @@ __device__ __forceinline__ void async_tile(char* lds, const T* g, int64_t gstrid
     // 32-bit element offset from a wave-uniform base (the host bounds every
     // per-sequence offset below 2^31 elements)
     const T* src = g + (uint32_t)(gr * (int)gstride + ch * (16 / (int)sizeof(T)));
-    __builtin_amdgcn_global_load_lds(src, (lds_void*)(lds + n * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(src, (lds_void*)(lds + n * 1024), 16, 0, CPOL);
   }
 }
 

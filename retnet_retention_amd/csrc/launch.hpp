@@ -25,16 +25,14 @@ hipError_t launch_rotary_table(float2* table, int seqlen, int d, double base, in
 hipError_t launch_rotate_qk(const void* q, const void* k, void* qr, void* kr, const float2* table, int batch,
                             int seqlen, int heads, int d, int dtype, hipStream_t stream);
 
-// Per-chunk states: snap[b][h][i] = R_{i-1} transposed ([dv][dk], element
-// type = dtype), state_out = R_last (fp32 [dk][dv]) when non-null.
-hipError_t launch_chunk_state(const Shape& s, int chunk, const void* k, const void* v, const float* state_in,
-                              float* state_out, void* snap, hipStream_t stream);
-
-// Output of the parallel form (snap == nullptr, chunk == seqlen) or of the
-// chunkwise form (snap from launch_chunk_state).
-hipError_t launch_retention_out(const Shape& s, int chunk, const void* q, const void* k, const void* v,
-                                const void* g, void* o, const void* snap, int has_state0, float eps,
-                                hipStream_t stream);
+// Parallel form (chunked == false: chunk == seqlen, no state) or chunkwise
+// form (chunked == true) in one launch. Chunkwise needs: snap [BH][nchunks]
+// [d][d] of the input dtype, chain [BH][2][d][d] fp32 and a control block of
+// chunkwise_ctrl_bytes() ints, all device memory owned by the caller.
+size_t chunkwise_ctrl_bytes(int batch, int heads, int nchunks);
+hipError_t launch_retention_fwd(const Shape& s, int chunk, bool chunked, const void* q, const void* k, const void* v,
+                                const void* g, void* o, const float* state_in, float* state_out, void* snap,
+                                float* chain, int* ctrl, float eps, hipStream_t stream);
 
 // One decode step, in place on `state`.
 hipError_t launch_recurrent_step(const Shape& s, const void* q, const void* k, const void* v, const void* g,

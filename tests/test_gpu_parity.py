@@ -179,3 +179,24 @@ def test_nan_propagates_forward_only():
     assert torch.isfinite(o[0, :64]).all()
     assert torch.isnan(o[0, 64:, 0, 5]).all()
     assert torch.isfinite(o[0, 64:, 0, :5]).all()
+
+
+# --- the chunk-to-chunk hand-off completes: every workgroup ran, no wait expired
+def test_chunkwise_handoff_completes():
+    _announce(case="handoff control block")
+    b, n, h, d, chunk = 2, 1100, 4, 256, 128
+    q, k, v, g, s0 = make_inputs(97, b, n, h, d, "bf16", 1 / 16, 1.0, True)
+    tq, tk, tv, tg = (x.torch(DEV) for x in (q, k, v, g))
+    ws = torch.zeros(rr.chunkwise_workspace_bytes(tq, tv, chunk), dtype=torch.uint8, device=DEV)
+    s_in = torch.from_numpy(s0.astype(np.float32)).to(DEV)
+    s_out = torch.empty_like(s_in)
+    out = rr.chunkwise_fwd(tq, tk, tv, tg, chunk=chunk, state_in=s_in, state_out=s_out, workspace=ws)
+    torch.cuda.synchronize()
+    ctrl = ws[:8].view(torch.int32).cpu()
+    nchunks = -(-n // chunk)
+    # two state workgroups and one 128-row output workgroup per (sequence, head, chunk)
+    assert int(ctrl[0]) == nchunks * b * h * (2 + 1)
+    assert int(ctrl[1]) == 0
+    ref, ref_s = oracle_run("chunkwise", q, k, v, g, chunk=chunk, state_in=s0)
+    assert_close(to64(out), ref, "bf16", "out")
+    assert_close(to64(s_out), ref_s, "bf16", "state")
