@@ -19,8 +19,12 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only chunkwise|dec
 """
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -32,6 +36,39 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak (published)
 PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E (published)
+
+CSRC = os.path.join(ROOT, "retnet_retention_amd", "csrc")
+# sources that define the chunkwise kernel: counters taken on another version
+# of them no longer describe the kernel that runs
+CHUNKWISE_SOURCES = ("retention_fwd.hip", "common.hpp", "launch.hpp")
+CHUNKWISE_KERNEL = "retention_chunkwise_kernel"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "chunkwise_7b_8k_traffic.txt")
+COPY_PROBE_BYTES = 512 << 20  # plain device-to-device copy of known size (counter calibration)
+
+
+def source_hash(names=CHUNKWISE_SOURCES):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(CSRC, n), "rb") as f:
+            h.update(n.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic():
+    """HBM bytes per chunkwise launch from the committed counter summary, or
+    None when that summary is missing or was taken on other kernel sources."""
+    try:
+        fields = dict(ln.split(":", 1) for ln in open(TRAFFIC_FILE) if ":" in ln and not ln.startswith(" "))
+    except OSError:
+        return None
+    fields = {k.strip(): v.strip() for k, v in fields.items()}
+    if fields.get("source_hash") != source_hash():
+        return None
+    try:
+        return {"bytes": int(fields["traffic_bytes_per_launch"]), "fetch": int(fields["fetch_bytes_per_launch"]),
+                "write": int(fields["write_bytes_per_launch"])}
+    except (KeyError, ValueError):
+        return None
 
 
 # ---------------------------------------------------------------------------
@@ -89,6 +126,19 @@ def time_calls(fn, steps, warmup):
     return start.elapsed_time(stop) / steps, wall
 
 
+def copy_probe():
+    """Two plain copies of COPY_PROBE_BYTES: counter runs scale FETCH_SIZE and
+    WRITE_SIZE by what they read for this kernel of known traffic."""
+    import torch
+
+    src = torch.ones(COPY_PROBE_BYTES // 4, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def bench_chunkwise(steps, warmup):
     import torch
 
@@ -137,7 +187,7 @@ def bench_parallel(steps, warmup):
     return {"workload": w, "ms": ms, "tflops": flops / (ms * 1e-3) / 1e12}
 
 
-def bench_decode(n_steps=256, warmup=16):
+def bench_decode(n_steps=256, warmup=16, batches=None):
     """Prefill 8 distinct sequences of 8192 tokens (chunkwise, seeded GPU
     normals / 16 in bf16), tile the states to the batch, then time decode."""
     import torch
@@ -161,7 +211,7 @@ def bench_decode(n_steps=256, warmup=16):
     torch.cuda.synchronize()
     del pq, pk, pv, pg
     results = {}
-    for bsz in w.decode_batches:
+    for bsz in batches or w.decode_batches:
         reps = (bsz + distinct - 1) // distinct
         state = base_state.repeat(reps, 1, 1, 1)[:bsz].contiguous()
         sshape = (bsz, 1, w.heads, w.dk)
@@ -216,6 +266,184 @@ def cpu_baseline(sample_seqs=2):
     }
 
 
+# ---------------------------------------------------------------------------
+# rocprofv3 runs (children of this process, which never touches the GPU in
+# this mode) and their text summaries
+# ---------------------------------------------------------------------------
+LEG_ARGS = {
+    "chunkwise": ["--only", "chunkwise", "--steps", "10", "--warmup", "2"],
+    "decode": ["--only", "decode", "--decode-batches", "64", "--decode-steps", "64"],
+    "parallel": ["--only", "parallel", "--steps", "10", "--warmup", "2"],
+}
+SQ_COUNTERS = ["SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "SQ_INSTS_LDS",
+               "SQ_LDS_BANK_CONFLICT", "SQ_WAIT_INST_LDS", "SQ_INSTS_VALU", "GRBM_GUI_ACTIVE"]
+# where the waves of the chunkwise kernel spend their cycles (one pass each)
+SQ_STALL_SETS = [
+    ["SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_LDS",
+     "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_VMEM", "SQ_IFETCH"],
+    ["SQ_LDS_DATA_FIFO_FULL", "SQ_LDS_CMD_FIFO_FULL", "SQ_INST_LEVEL_LDS", "SQ_INSTS_MFMA", "SQ_INSTS_SALU",
+     "SQ_ACTIVE_INST_MISC", "SQ_ACTIVE_INST_SCA", "SQ_INSTS_VMEM"],
+]
+
+
+def _run_profiler(args, log, limit):
+    print("$ " + " ".join(args), file=sys.stderr, flush=True)
+    with open(log, "w") as f:
+        r = subprocess.run(args, stdout=f, stderr=subprocess.STDOUT, timeout=limit, cwd="/tmp",
+                           env={**os.environ, "TMPDIR": "/tmp"})
+    if r.returncode != 0:
+        tail = open(log).read()[-3000:]
+        raise SystemExit(f"profiler run failed ({r.returncode}):\n{tail}")
+
+
+def _bench_cmd(leg_args):
+    return ["python3", os.path.join(ROOT, "bench.py"), *leg_args, "--no-cpu-baseline"]
+
+
+def _rel(cmd):
+    return " ".join(c.replace(ROOT + "/", "").replace(ROOT, ".") for c in cmd)
+
+
+def _counter_rows(d):
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    rows = []
+    for f in files:
+        rows.extend(csv.DictReader(open(f)))
+    return rows
+
+
+def _per_dispatch(rows, counter, match):
+    vals = {}
+    for r in rows:
+        if r["Counter_Name"] == counter and match(r["Kernel_Name"]):
+            key = (r.get("Dispatch_Id"), r.get("Agent_Id"))
+            vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+    return list(vals.values())
+
+
+def profile_stats(out, raw):
+    for leg, leg_args in LEG_ARGS.items():
+        d = os.path.join(raw, f"stats_{leg}")
+        cmd = ["rocprofv3", "--kernel-trace", "--stats", "-d", d, "-o", "run", "--output-format", "csv", "--",
+               *_bench_cmd(leg_args)]
+        _run_profiler(cmd, d + ".log", 600)
+        line = [ln for ln in open(d + ".log") if ln.startswith("{")]
+        stats = list(csv.DictReader(open(glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)[0])))
+        name = {"chunkwise": "chunkwise_7b_8k", "decode": "decode_step_7b_b64", "parallel": "parallel_3b"}[leg]
+        with open(os.path.join(out, f"{name}_kernel_stats.txt"), "w") as f:
+            f.write(f"rocprofv3 kernel statistics, {leg} leg of the benchmark\n")
+            f.write(f"command: {_rel(cmd)}\n")
+            f.write(f"kernel sources: {source_hash()} (chunkwise/parallel kernel), host {os.uname().nodename}\n\n")
+            f.write(f"{'kernel':70s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'share%':>7s}\n")
+            for r in stats[:12]:
+                f.write(f"{r['Name'][:70]:70s} {r['Calls']:>6s} {float(r['AverageNs']) / 1e3:10.2f} "
+                        f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f} "
+                        f"{float(r['Percentage']):7.2f}\n")
+            if line:
+                f.write("\nbenchmark line of the same (profiled) run, HIP-event timed:\n" + line[-1])
+        print(f"wrote {name}_kernel_stats.txt", file=sys.stderr, flush=True)
+
+
+def profile_traffic(out, raw):
+    """Two counter passes (FETCH_SIZE, then WRITE_SIZE) over the chunkwise leg
+    plus a plain copy of known size; each counter is scaled by what it reads
+    for the copy."""
+    leg = ["--only", "chunkwise", "--steps", "2", "--warmup", "1", "--copy-probe"]
+    res, cmds = {}, []
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        d = os.path.join(raw, f"pmc_{counter.lower()}")
+        cmd = ["rocprofv3", "--pmc", counter, "-d", d, "-o", "run", "--output-format", "csv", "--",
+               *_bench_cmd(leg)]
+        _run_profiler(cmd, d + ".log", 180)
+        cmds.append(cmd)
+        rows = _counter_rows(d)
+        kern = _per_dispatch(rows, counter, lambda n: CHUNKWISE_KERNEL in n)
+        copy = _per_dispatch(rows, counter, lambda n: "copy" in n.lower() and "retention" not in n)
+        if not kern or not copy:
+            raise SystemExit(f"{counter}: kernel dispatches {len(kern)}, copy dispatches {len(copy)}")
+        kib = sum(kern) / len(kern)
+        copy_kib = max(copy)  # the copies are the largest non-retention dispatches
+        scale = COPY_PROBE_BYTES / (copy_kib * 1024.0)
+        res[counter] = (kib, copy_kib, scale, kib * 1024.0 * scale, len(kern))
+    fetch, write = res["FETCH_SIZE"][3], res["WRITE_SIZE"][3]
+    from synth import get
+
+    w = get("retention_7b_8k")
+    alg = chunkwise_bytes(w.batch, w.seqlen, w.heads, w.dk, w.dv)
+    with open(os.path.join(out, "chunkwise_7b_8k_traffic.txt"), "w") as f:
+        f.write("HBM traffic of the chunkwise kernel on the 7B long-context workload (batch 2, 8192 tokens,\n"
+                "16 heads x 256, chunk 512, bf16, gate, state out), from two rocprofv3 counter passes\n")
+        for c in cmds:
+            f.write(f"command: {_rel(c)}\n")
+        f.write(f"kernel: {CHUNKWISE_KERNEL}<bf16, 256>\n")
+        f.write(f"source_hash: {source_hash()}\n")
+        for c, (kib, copy_kib, scale, b, n) in res.items():
+            f.write(f"  {c}: {kib:.0f} KiB per dispatch (mean of {n}); copy of {COPY_PROBE_BYTES >> 20} MiB reads "
+                    f"{copy_kib:.0f} KiB -> scale {scale:.4f} -> {b / 1e6:.1f} MB\n")
+        f.write(f"fetch_bytes_per_launch: {int(fetch)}\n")
+        f.write(f"write_bytes_per_launch: {int(write)}\n")
+        f.write(f"traffic_bytes_per_launch: {int(fetch + write)}\n")
+        f.write(f"algorithmic_bytes_per_launch: {alg}\n")
+        f.write(f"  ratio measured/algorithmic: {(fetch + write) / alg:.3f}\n")
+    print("wrote chunkwise_7b_8k_traffic.txt", file=sys.stderr, flush=True)
+
+
+def profile_counters(out, raw):
+    """SQ counter passes per leg: matrix-core activity and LDS behaviour, and
+    for the chunkwise leg where its waves spend their cycles."""
+    for leg in ("chunkwise", "parallel", "decode"):
+        leg_args = [*LEG_ARGS[leg]]
+        if leg != "decode":
+            leg_args[leg_args.index("--steps") + 1] = "2"
+        match = {"chunkwise": lambda n: CHUNKWISE_KERNEL in n, "parallel": lambda n: "retention_parallel" in n,
+                 "decode": lambda n: "recurrent_step" in n}[leg]
+        name = {"chunkwise": "chunkwise_7b_8k", "decode": "decode_step_7b_b64", "parallel": "parallel_3b"}[leg]
+        sets = [SQ_COUNTERS] + (SQ_STALL_SETS if leg == "chunkwise" else [])
+        lines, vals = [], {}
+        for k, counters in enumerate(sets):
+            d = os.path.join(raw, f"pmc_sq_{leg}_{k}")
+            cmd = ["rocprofv3", "--pmc", *counters, "-d", d, "-o", "run", "--output-format", "csv", "--",
+                   *_bench_cmd(leg_args)]
+            _run_profiler(cmd, d + ".log", 180)
+            rows = _counter_rows(d)
+            lines.append(f"command: {_rel(cmd)}\n")
+            for c in counters:
+                v = _per_dispatch(rows, c, match)
+                vals[c] = sum(v) / len(v) if v else float("nan")
+                lines.append(f"  {c:32s} {vals[c]:.6g}  (dispatches {len(v)})\n")
+        with open(os.path.join(out, f"{name}_sq_counters.txt"), "w") as f:
+            f.write(f"rocprofv3 SQ counters, {leg} leg, mean per dispatch of the retention kernel\n")
+            f.write(f"kernel sources: {source_hash()}\n")
+            f.writelines(lines)
+            xcds, cus, simds = 8, 256, 4
+            gui = vals["GRBM_GUI_ACTIVE"] / xcds  # GRBM_GUI_ACTIVE sums the 8 XCDs
+            f.write(f"derived: kernel cycles (GRBM_GUI_ACTIVE / {xcds} XCDs) = {gui:.4g}\n")
+            f.write(f"derived: MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (cycles x {cus} CUs x {simds} SIMDs) = "
+                    f"{vals['SQ_VALU_MFMA_BUSY_CYCLES'] / (gui * cus * simds):.4f}\n")
+            f.write(f"derived: bf16 matrix flops executed = 512 x SQ_INSTS_VALU_MFMA_MOPS_BF16 = "
+                    f"{512 * vals['SQ_INSTS_VALU_MFMA_MOPS_BF16'] / 1e9:.2f} GFLOP per dispatch\n")
+            if "SQ_WAVE_CYCLES" in vals:
+                wc = vals["SQ_WAVE_CYCLES"]
+                for c in ("SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_LDS",
+                          "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_VMEM", "SQ_ACTIVE_INST_MISC", "SQ_ACTIVE_INST_SCA"):
+                    f.write(f"derived: {c} / SQ_WAVE_CYCLES = {vals[c] / wc:.4f}\n")
+        print(f"wrote {name}_sq_counters.txt", file=sys.stderr, flush=True)
+
+
+def profile(kinds, out):
+    os.makedirs(out, exist_ok=True)
+    raw = os.path.join(out, "raw")
+    os.makedirs(raw, exist_ok=True)
+    if "stats" in kinds:
+        profile_stats(out, raw)
+    if "traffic" in kinds:
+        profile_traffic(out, raw)
+    if "counters" in kinds:
+        profile_counters(out, raw)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -223,11 +451,20 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", choices=["chunkwise", "decode", "parallel"], default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode-batches", type=int, nargs="*", default=None)
+    ap.add_argument("--decode-steps", type=int, default=256)
+    ap.add_argument("--copy-probe", action="store_true", help="also run a plain copy of known size")
+    ap.add_argument("--profile", nargs="+", choices=["stats", "traffic", "counters"], default=None,
+                    help="run the named rocprofv3 passes over this benchmark and write text summaries")
+    ap.add_argument("--profile-out", default=os.path.join(ROOT, "profiles"))
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
         sys.exit(2)
+    if args.profile:
+        profile(args.profile, os.path.abspath(args.profile_out))
+        return
 
     import torch
 
@@ -243,6 +480,8 @@ def main():
         cw = bench_chunkwise(args.steps, args.warmup)
         w = cw["workload"]
         print(f"chunkwise {w.name}: {cw['ms']:.3f} ms/step, {cw['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
+        alg_gbps = cw["bytes"] / (cw["ms"] * 1e-3) / 1e9
+        traffic = recorded_traffic()
         line.update({
             "metric": "chunkwise retention TFLOP/s (+% MFMA peak); decode-step tokens/s and HBM GB/s",
             "value": round(cw["tflops"], 2),
@@ -259,25 +498,31 @@ def main():
             "config": {"workload": w.name, "form": "chunkwise", "batch": w.batch, "seq_len": w.seqlen,
                        "heads": w.heads, "head_dim": w.dk, "chunk": w.chunk, "gate": True, "rotary": False,
                        "state_out": True, "parallelism": "single GPU"},
-            "mfma_frac_step": round(cw["tflops"] / PEAK_BF16_TFLOPS, 4),
-            "hbm_gbps_step": round(cw["bytes"] / (cw["ms"] * 1e-3) / 1e9, 1),
-            # The chunkwise call runs two kernels (per-chunk states, then the
-            # fused output); the whole call is timed on its stream.
-            "roofline": {"bound": "mfma", "kernel": "chunkwise call (state + output kernels)",
+            # One chunkwise call = a control-block reset (a few microseconds)
+            # and the fused chunkwise kernel, both on the timed stream; the
+            # whole call's event time is charged to the kernel.
+            "roofline": {"bound": "mfma", "kernel": f"{CHUNKWISE_KERNEL}<bf16,256>",
                          "achieved": round(cw["tflops"], 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(cw["tflops"] / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                         "frac": round(cw["tflops"] / PEAK_BF16_TFLOPS, 4),
+                         "traffic": traffic["bytes"] if traffic else None,
+                         "flops_per_launch": cw["flops"],
+                         "hbm": {"algorithmic_bytes": cw["bytes"], "achieved": round(alg_gbps, 1),
+                                 "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(alg_gbps / PEAK_HBM_GBPS, 4),
+                                 "measured_gbps": (round(traffic["bytes"] / (cw["ms"] * 1e-3) / 1e9, 1)
+                                                   if traffic else None)}},
         })
     if args.only in (None, "decode"):
-        wd, dec = bench_decode()
+        wd, dec = bench_decode(args.decode_steps, batches=args.decode_batches)
         for b, r in dec.items():
             print(f"decode batch {b}: {r['us_per_step']:.2f} us/step, {r['tokens_per_s']:.0f} tok/s, "
                   f"{r['gbps']:.0f} GB/s", file=sys.stderr, flush=True)
+        ref_b = 64 if 64 in dec else max(dec)
         line["decode"] = {
             "workload": f"{wd.name}: 16 heads x 256, fp32 state from an 8192-token chunkwise prefill, bf16 steps",
             "per_batch": {str(b): {k: round(v, 2) for k, v in r.items()} for b, r in dec.items()},
-            "tokens_per_s_b64": round(dec[64]["tokens_per_s"], 1),
-            "hbm_gbps_b64": round(dec[64]["gbps"], 1),
-            "hbm_frac_b64": round(dec[64]["gbps"] / PEAK_HBM_GBPS, 4),
+            f"tokens_per_s_b{ref_b}": round(dec[ref_b]["tokens_per_s"], 1),
+            f"hbm_gbps_b{ref_b}": round(dec[ref_b]["gbps"], 1),
+            f"hbm_frac_b{ref_b}": round(dec[ref_b]["gbps"] / PEAK_HBM_GBPS, 4),
         }
     if args.only in (None, "parallel"):
         par = bench_parallel(max(args.steps // 2, 3), args.warmup)
@@ -286,6 +531,8 @@ def main():
         line["parallel"] = {"workload": f"{par['workload'].name}: batch 4, 2048 tokens, 10 x 256, rotation, gate",
                             "ms": round(par["ms"], 4), "tflops": round(par["tflops"], 2),
                             "mfma_frac": round(par["tflops"] / PEAK_BF16_TFLOPS, 4)}
+    if args.copy_probe:
+        copy_probe()
     if args.only is None and not args.no_cpu_baseline:
         cb = cpu_baseline()
         print(f"cpu baseline: {cb['value'] * 1e3:.2f} GFLOP/s ({cb['seconds']:.1f} s)", file=sys.stderr, flush=True)

@@ -21,6 +21,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 namespace ret {
 
 typedef __bf16 bf16;
@@ -31,6 +33,16 @@ typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMaxHeads = 128;
+
+// f(integral_constant<int, 0>), ..., f(integral_constant<int, N-1>), inlined
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 template <typename T> struct FragOf;
 template <> struct FragOf<bf16> { using type = bf16x8; };
@@ -242,6 +254,26 @@ __device__ __forceinline__ bf16x8 acc_to_frag(const f32x4& lo, const f32x4& hi, 
 __device__ __forceinline__ f32x8 acc_to_frag(const f32x4& lo, const f32x4& hi, float*) {
   return f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
+// Multiply every element of a fragment by x (bf16 fragments round back).
+__device__ __forceinline__ void scale_frag(bf16x8& f, float x) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f[i] = (bf16)((float)f[i] * x);
+}
+__device__ __forceinline__ void scale_frag(f32x8& f, float x) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f[i] *= x;
+}
+// One half (H = 0: rows k0..k0+15, H = 1: k0+16..k0+31) of such a fragment.
+template <int H>
+__device__ __forceinline__ void set_half(bf16x8& f, const f32x4& x, std::integral_constant<int, H>) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) f[4 * H + i] = (bf16)x[i];
+}
+template <int H>
+__device__ __forceinline__ void set_half(f32x8& f, const f32x4& x, std::integral_constant<int, H>) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) f[4 * H + i] = x[i];
+}
 
 // ---------------------------------------------------------------------------
 // Padded LDS tiles filled by direct global->LDS loads.
@@ -287,7 +319,11 @@ __device__ __forceinline__ void async_tile(char* lds, const T* g, int64_t gstrid
   for (int m = 0; m < (TL::NINST + NW - 1) / NW; ++m) {
     const int n = wave + m * NW;  // wave-uniform
     if (TL::NINST % NW != 0 && n >= TL::NINST) break;
-    const int slot = n * 64 + lane;
+    // the lane's offsets are recomputed for every load rather than kept live
+    // across the caller's loop
+    int ln = lane;
+    __asm__ volatile("" : "+v"(ln));
+    const int slot = n * 64 + ln;
     int r = slot / TL::SPR, ch = slot % TL::SPR;
     if (ch >= TL::CPR) ch = 0;  // padding slot: any in-range chunk
     if (slot >= TL::SLOTS) r = 0;                                  // slack past the tile
@@ -339,12 +375,18 @@ __device__ __forceinline__ f32x8 tile_col8(const char* t, int k0, int n0, int la
 // ---------------------------------------------------------------------------
 // Reductions.
 // ---------------------------------------------------------------------------
-// Sum over the 16 lanes that share g (lanes 16g .. 16g+15).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+// Sum over the 16 lanes that share g (lanes 16g .. 16g+15): butterflies
+// within the row of 16 lanes (quad xor 1, quad xor 2, mirror in 8, mirror in
+// 16); every lane ends with the full sum.
 __device__ __forceinline__ float sum16(float x) {
-  x += __shfl_xor(x, 1, 64);
-  x += __shfl_xor(x, 2, 64);
-  x += __shfl_xor(x, 4, 64);
-  x += __shfl_xor(x, 8, 64);
+  x += dpp<0xB1>(x);
+  x += dpp<0x4E>(x);
+  x += dpp<0x141>(x);
+  x += dpp<0x140>(x);
   return x;
 }
 

@@ -21,9 +21,11 @@
 //     R_i = g^b R_{i-1} + dR_i and publishes it: fp32 for the next state
 //     workgroup, transposed in the input dtype for the next chunk's output
 //     workgroups, and as the state output after the last chunk.
-// Workgroups take their role from an atomic ticket in chunk-major order, so
-// a workgroup only ever waits for workgroups that hold smaller tickets and
-// are therefore already running: the waits always end. Every wait is also
+// Workgroups take their role from an atomic ticket in chunk-major order (one
+// ticket counter per class of workgroups when the classes can own disjoint
+// (sequence, head) pairs), so a workgroup only ever waits for workgroups of
+// its class that hold smaller tickets and are therefore already running or
+// done: the waits always end. Every wait is also
 // bounded; on expiry it sets an error word in the control block and goes on.
 #include <type_traits>
 
@@ -32,18 +34,28 @@
 
 namespace ret {
 
-template <typename T, int D>
+// FAST: every head's decay over the span that one workgroup's decay factors
+// cover stays within 2^64 (see kFastSpanLog2); the scores then take one factor
+// per key and the rows one factor at the end.
+template <typename T, int D, bool FAST = true>
 struct OutTile {
   static constexpr int E = sizeof(T);
   static constexpr int WAVES = 4;
-  static constexpr int QW = 32;  // query rows per wave
+  // Query rows per wave, in groups of 16: 48 rows for bf16 on the fast path
+  // (the wave's fp32 output tile, 48 x D, and its query fragments stay in
+  // registers with room for the fragment pipeline), 32 otherwise (fp32
+  // fragments take twice the registers). Every K and V fragment read from
+  // LDS feeds QG products. Group i of wave w holds rows 16 (w + WAVES i) ..
+  // +15 of the block: every wave spans the whole block, so the causal work is
+  // shared evenly.
+  static constexpr int QG = E == 2 && FAST ? 3 : 2;
+  static constexpr int QW = 16 * QG;
   static constexpr int BM = WAVES * QW;
   static constexpr int BN = E == 2 ? 64 : 32;  // keys per block
-  static constexpr int KK = BN / 16;           // 16-key score blocks per key block
-  static constexpr int K2 = BN / 32;           // P V contraction steps per key block
+  static constexpr int K2 = BN / 32;           // 32-key steps per key block
   static constexpr int KS = D / 32;            // contraction steps over dk
   static constexpr int NB = D / 16;            // 16-wide output column blocks
-  // dk columns per R^T slice; slices are loaded two at a time
+  // dk columns per R^T slice; the slices stream through the two stages
   static constexpr int RS = D / 2 < 256 / E ? D / 2 : 256 / E;
   static constexpr int NRS = D / RS;
   using KT = PTile<T, BN, D, 16>;   // K block, row fragments
@@ -51,8 +63,17 @@ struct OutTile {
   using RT = PTile<T, D, RS, 16>;   // R^T slice (dv rows x RS dk), row fragments
   static constexpr int KVB = KT::BYTES + VT::BYTES;
   static constexpr int YSTR = D + 4;  // epilogue rows (fp32), two waves per stage buffer
-  static_assert(NRS % 2 == 0, "slices come in pairs");
 };
+
+// Fast path: with a reference row r0 (the row before the chunk, or before the
+// parallel form's query block) the decay factors split as
+//     g^(q-k) = g^(q - r0) * g^(r0 - k):
+// the products P' = S g^(r0 - k) accumulate O' = P' V (+ Q R_{i-1}, whose row
+// scale xi_q = g^(q - r0) is then the same row factor), and O = g^(q - r0) O'.
+// Keys reach at most kFastSpan rows past r0, so |log2 g| * span <= 64 keeps
+// every factor within 2^+-64 (factors of far keys underflow towards zero,
+// which is what they are worth).
+constexpr double kFastSpanLog2 = 64.0;
 
 template <typename T, int D>
 struct StTile {
@@ -83,8 +104,8 @@ struct FwdParams {
   const float* state_in;
   float* state_out;
   void* snap;    // [BH][nchunks][dv][dk] of T: R_{i-1}^T for chunk i
-  float* chain;  // [BH][2][dk][dv] fp32: R_i handed to the next state workgroup
-  int* ctrl;     // [0] ticket, [1] error, [2 + (bh*(nchunks+1) + i)*2 + half]: "half of R_{i-1} ready"
+  float* chain;  // [BH][2][D*D] fp32: R_i handed to the next state workgroup (fragment order)
+  int* ctrl;     // [0] count, [1] error, [8..15] tickets, [16 + (bh*(nchunks+1) + i)*2 + half]: R_{i-1} ready
   int batch, seqlen, heads, chunk, nchunks, qblocks;
   int has_state0, xcd_order;
   float eps;
@@ -103,7 +124,9 @@ struct FwdParams {
 // loads, then a barrier orders every wave's reads after it.
 // ---------------------------------------------------------------------------
 constexpr int kSpinLimit = 1 << 22;  // ~2^22 x 512 cycles: about a second
-constexpr int kCoherent = 17;        // sc0 | sc1 cache policy for direct loads
+[[maybe_unused]] constexpr int kCoherent = 17;        // sc0 | sc1 cache policy for direct loads
+[[maybe_unused]] constexpr int kTicketWord = 8;       // control block: ticket counters at words 8..15
+constexpr int kCtrlHead = 16;        // ... and the ready flags from word 16 on
 
 __device__ __forceinline__ void wait_flag(const int* flag, int* err) {
   if (threadIdx.x == 0) {
@@ -141,20 +164,22 @@ __device__ __forceinline__ void store4_coherent(float* p, const f32x4& x) {
   __hip_atomic_store(reinterpret_cast<uint64_t*>(p + 2), __builtin_bit_cast(uint64_t, b), __ATOMIC_RELAXED,
                      __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void store1_coherent(float* p, float x) {
-  __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float load1_coherent(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ f32x4 load4_coherent(const float* p) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  uint64_t* q = reinterpret_cast<uint64_t*>(const_cast<float*>(p));
+  const f32x2 a = __builtin_bit_cast(f32x2, __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  const f32x2 b = __builtin_bit_cast(f32x2, __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  return f32x4{a[0], a[1], b[0], b[1]};
 }
 
 // ---------------------------------------------------------------------------
 // Output role.
 // ---------------------------------------------------------------------------
-template <typename T, int D>
+template <typename T, int D, bool FAST>
 __device__ __forceinline__ void out_role(const FwdParams& p, int bh, int ci, int qb, bool chunked, char* stage0,
                                          char* stage1) {
-  using C = OutTile<T, D>;
+  using C = OutTile<T, D, FAST>;
+  constexpr int QG = C::QG;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, c = lane & 15;
@@ -166,6 +191,7 @@ __device__ __forceinline__ void out_role(const FwdParams& p, int bh, int ci, int
   if (q0 >= cend) return;  // uniform for the whole workgroup
 
   const float lg = p.log2g[h];
+  const int ref = chunked ? c0 - 1 : q0 - 1;  // reference row of the fast path
   const int64_t tstride = (int64_t)p.heads * D;  // elements between tokens
   const int64_t head0 = ((int64_t)b * p.seqlen * p.heads + h) * D;
   const T* Q = reinterpret_cast<const T*>(p.q) + head0;
@@ -174,7 +200,8 @@ __device__ __forceinline__ void out_role(const FwdParams& p, int bh, int ci, int
   const T* G = p.g ? reinterpret_cast<const T*>(p.g) + head0 : nullptr;
   T* O = reinterpret_cast<T*>(p.o) + head0;
 
-  const int qw0 = q0 + wave * C::QW;
+  // first row of this wave's group i
+  auto grow = [&](int i) __attribute__((always_inline)) { return q0 + 16 * (wave + C::WAVES * i); };
   const int kend = min(q0 + C::BM, cend);
   const int nkb = (kend - c0 + C::BN - 1) / C::BN;
 
@@ -183,127 +210,183 @@ __device__ __forceinline__ void out_role(const FwdParams& p, int bh, int ci, int
     async_tile<T, typename C::KT, C::WAVES>(buf, K, tstride, kb0, cend - 1, wave, lane);
     async_tile<T, typename C::VT, C::WAVES>(buf + C::KT::BYTES, V, tstride, kb0, cend - 1, wave, lane);
   };
+  const bool cross = chunked && (ci > 0 || p.has_state0);
+  const T* R = cross ? reinterpret_cast<const T*>(p.snap) + ((int64_t)bh * p.nchunks + ci) * D * D : nullptr;
+  // R^T slice s ([dv][RS dk columns]) into an LDS stage; waits (once) for
+  // both halves of R_{i-1} to be published
+  auto issue_slice = [&](int sl, char* buf) __attribute__((always_inline)) {
+    if (sl == 0) {
+      int* flags = p.ctrl + kCtrlHead + (bh * (p.nchunks + 1) + ci) * 2;
+      wait_flag(flags + 0, p.ctrl + 1);
+      wait_flag(flags + 1, p.ctrl + 1);
+    }
+    async_tile<T, typename C::RT, C::WAVES, kCoherent>(buf, R + sl * C::RS, D, 0, D - 1, wave, lane);
+  };
   issue_kv(0, stage0);
 
   // Query fragments, kept in registers for the whole workgroup life. Rows
   // past the chunk load a clamped in-range row: their outputs are never
   // stored.
-  frag_t<T> qf[2][C::KS];
+  frag_t<T> qf[QG][C::KS];
 #pragma unroll
-  for (int qq = 0; qq < 2; ++qq) {
-    const int row = min(qw0 + qq * 16 + c, cend - 1);
+  for (int i = 0; i < QG; ++i) {
+    const int row = min(grow(i) + c, cend - 1);
 #pragma unroll
     for (int s = 0; s < C::KS; ++s)
-      qf[qq][s] = to_frag(unpack8(ld_raw8(Q + row * tstride + s * 32 + 8 * g)), (T*)nullptr);
+      qf[i][s] = to_frag(unpack8(ld_raw8(Q + row * tstride + s * 32 + 8 * g)), (T*)nullptr);
   }
 
-  f32x4 oacc[2][C::NB];
+  f32x4 oacc[QG][C::NB];
 #pragma unroll
-  for (int qq = 0; qq < 2; ++qq)
+  for (int i = 0; i < QG; ++i)
 #pragma unroll
-    for (int nb = 0; nb < C::NB; ++nb) oacc[qq][nb] = zero4();
+    for (int nb = 0; nb < C::NB; ++nb) oacc[i][nb] = zero4();
 
-  // Intra-chunk term (Q K^T (.) D) V over key blocks up to the diagonal; the
-  // decay g^(q-k) = exp2((q-k) log2 g) is formed per score (exact integer
-  // distance, one multiply, one exp2) and masked above the diagonal.
-  auto key_block = [&](int kb0, const char* kt) __attribute__((always_inline)) {
-    if (kb0 > qw0 + C::QW - 1 || qw0 >= cend) return;  // block above this wave's diagonal
+  // Intra-chunk term (Q K^T (.) D) V over key blocks up to the diagonal, 32
+  // keys at a time: S^T = K Q^T for 16 keys per group, decay and causal
+  // mask, then O += P V. Only groups 0 .. HI-1 hold rows of the chunk. The K
+  // and V fragments of a 32-key step form one sequence of LDS reads with a
+  // two-deep prefetch ring.
+  constexpr int U = 2 * C::KS + C::NB;  // fragment reads per 32-key step
+  auto key_block = [&](auto hi_c, int kb0, const char* kt) __attribute__((always_inline)) {
+    constexpr int HI = decltype(hi_c)::value;
     const char* vt = kt + C::KT::BYTES;
-    f32x4 st[2][C::KK];
+    auto load = [&](auto t_c) __attribute__((always_inline)) {
+      constexpr int t = decltype(t_c)::value, kh = t / U, u = t % U;
+      if constexpr (u < 2 * C::KS)  // key group 2 kh + u % 2, contraction step u / 2
+        return tile_row8<typename C::KT>(kt, (2 * kh + u % 2) * 16 + c, (u / 2) * 32 + 8 * g, (T*)nullptr);
+      else
+        return tile_col8<typename C::VT>(vt, kh * 32, (u - 2 * C::KS) * 16, lane, (T*)nullptr);
+    };
+    frag_t<T> ring[3];
+    ring[0] = load(std::integral_constant<int, 0>{});
+    ring[1] = load(std::integral_constant<int, 1>{});
+    f32x4 st[QG][2];
+    frag_t<T> pf[QG];
+    static_for<C::K2 * U>([&](auto t_c) __attribute__((always_inline)) {
+      constexpr int t = decltype(t_c)::value, kh = t / U, u = t % U;
+      if constexpr (t + 2 < C::K2 * U) ring[(t + 2) % 3] = load(std::integral_constant<int, t + 2>{});
+      if constexpr (u < 2 * C::KS) {
+        // the two 16-key groups of the step alternate, so that consecutive
+        // products go to different accumulators
+        constexpr int k2 = u % 2, s = u / 2;
+        if constexpr (s == 0) {
 #pragma unroll
-    for (int qq = 0; qq < 2; ++qq)
-#pragma unroll
-      for (int kk = 0; kk < C::KK; ++kk) st[qq][kk] = zero4();
-    {  // K fragments prefetched two steps ahead of their products
-      constexpr int NT = C::KS * C::KK;
-      auto kload = [&](int t) __attribute__((always_inline)) {
-        return tile_row8<typename C::KT>(kt, (t % C::KK) * 16 + c, (t / C::KK) * 32 + 8 * g, (T*)nullptr);
-      };
-      frag_t<T> kb[3];
-      kb[0] = kload(0);
-      kb[1] = kload(1);
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        if (t + 2 < NT) kb[(t + 2) % 3] = kload(t + 2);
-#pragma unroll
-        for (int qq = 0; qq < 2; ++qq) st[qq][t % C::KK] = mma(kb[t % 3], qf[qq][t / C::KK], st[qq][t % C::KK]);
-      }
-    }
-    frag_t<T> pf[2][C::K2];
-#pragma unroll
-    for (int qq = 0; qq < 2; ++qq) {
-      const int qrow = qw0 + qq * 16 + c;
-#pragma unroll
-      for (int kk = 0; kk < C::KK; ++kk) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int dist = qrow - (kb0 + kk * 16 + 4 * g + i);
-          const float val = st[qq][kk][i] * gpow((float)dist, lg);
-          st[qq][kk][i] = dist < 0 ? 0.f : val;
+          for (int i = 0; i < HI; ++i) st[i][k2] = zero4();
         }
+#pragma unroll
+        for (int i = 0; i < HI; ++i) st[i][k2] = mma(ring[t % 3], qf[i][s], st[i][k2]);
+        if constexpr (u == 2 * C::KS - 1) {
+          // decay g^(q-k) and causal mask over the 32 keys, which become P
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            const int k0 = 32 * kh + 16 * h2 + 4 * g;  // key - kb0 of element 0
+            if constexpr (FAST) {
+              float bk[4];  // g^(r0 - k)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) bk[e] = gpow((float)(ref - kb0 - k0 - e), lg);
+#pragma unroll
+              for (int i = 0; i < HI; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  const float val = st[i][h2][e] * bk[e];
+                  st[i][h2][e] = grow(i) + c - kb0 < k0 + e ? 0.f : val;
+                }
+            } else {
+#pragma unroll
+              for (int i = 0; i < HI; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  const int dist = grow(i) + c - kb0 - k0 - e;
+                  const float val = st[i][h2][e] * gpow((float)dist, lg);
+                  st[i][h2][e] = dist < 0 ? 0.f : val;
+                }
+            }
+          }
+#pragma unroll
+          for (int i = 0; i < HI; ++i) pf[i] = acc_to_frag(st[i][0], st[i][1], (T*)nullptr);
+        }
+      } else {
+        constexpr int nb = u - 2 * C::KS;
+#pragma unroll
+        for (int i = 0; i < HI; ++i) oacc[i][nb] = mma(pf[i], ring[t % 3], oacc[i][nb]);
       }
-#pragma unroll
-      for (int k2 = 0; k2 < C::K2; ++k2) pf[qq][k2] = acc_to_frag(st[qq][2 * k2], st[qq][2 * k2 + 1], (T*)nullptr);
-    }
-    {  // V fragments prefetched two steps ahead of their products
-      constexpr int NT = C::K2 * C::NB;
-      auto vload = [&](int t) __attribute__((always_inline)) {
-        return tile_col8<typename C::VT>(vt, (t / C::NB) * 32, (t % C::NB) * 16, lane, (T*)nullptr);
-      };
-      frag_t<T> vb[3];
-      vb[0] = vload(0);
-      vb[1] = vload(1);
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        if (t + 2 < NT) vb[(t + 2) % 3] = vload(t + 2);
-#pragma unroll
-        for (int qq = 0; qq < 2; ++qq)
-          oacc[qq][t % C::NB] = mma(pf[qq][t / C::NB], vb[t % 3], oacc[qq][t % C::NB]);
-      }
-    }
+    });
   };
 
   // One pipeline step: wait for block j, release the other stage, prefetch
-  // block j+1 into it. The stages are distinct LDS objects and the loop is
-  // unrolled by two, so the compiler can tell the reads of one stage from
-  // the in-flight loads into the other.
+  // block j+1 into it -- or, after the last key block, the first R^T slice.
+  // The stages are distinct LDS objects and the loop is unrolled by two, so
+  // the compiler can tell the reads of one stage from the in-flight loads
+  // into the other.
   auto sync_and_prefetch = [&](int j, char* nxt) __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (j + 1 < nkb) issue_kv(j + 1, nxt);
+    if (j + 1 < nkb)
+      issue_kv(j + 1, nxt);
+    else if (cross)
+      issue_slice(0, nxt);
   };
-  for (int j = 0; j < nkb; j += 2) {
-    sync_and_prefetch(j, stage1);
-    key_block(c0 + j * C::BN, stage0);
-    if (j + 1 < nkb) {
-      sync_and_prefetch(j + 1, stage0);
-      key_block(c0 + (j + 1) * C::BN, stage1);
-    }
-  }
-
-  // Cross-chunk term, added last: O = xi (.) (O_intra / xi + Q R_{i-1}).
-  // Rows whose xi is below 2^-100 skip it (their Q fragment is zeroed and
-  // their scale is 1): the term is then far below fp32 resolution.
-  if (chunked && (ci > 0 || p.has_state0)) {
-    int* flags = p.ctrl + 2 + (bh * (p.nchunks + 1) + ci) * 2;
-    __syncthreads();  // both stages are free
-    wait_flag(flags + 0, p.ctrl + 1);
-    wait_flag(flags + 1, p.ctrl + 1);
-    const T* R = reinterpret_cast<const T*>(p.snap) + ((int64_t)bh * p.nchunks + ci) * D * D;  // [dv][dk]
-    float inv[2][4];
-#pragma unroll
-    for (int qq = 0; qq < 2; ++qq) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float xi = gpow((float)(qw0 + qq * 16 + 4 * g + i - c0 + 1), lg);
-        inv[qq][i] = xi >= 7.888609e-31f ? __builtin_amdgcn_rcpf(xi) : 1.f;
-#pragma unroll
-        for (int nb = 0; nb < C::NB; ++nb) oacc[qq][nb][i] *= inv[qq][i];
+  auto key_loop = [&](auto hi_c) __attribute__((always_inline)) {
+    for (int j = 0; j < nkb; j += 2) {
+      sync_and_prefetch(j, stage1);
+      key_block(hi_c, c0 + j * C::BN, stage0);
+      if (j + 1 < nkb) {
+        sync_and_prefetch(j + 1, stage0);
+        key_block(hi_c, c0 + (j + 1) * C::BN, stage1);
       }
-      const float xq = gpow((float)(qw0 + qq * 16 + c - c0 + 1), lg);
-      if (!(xq >= 7.888609e-31f)) {
+    }
+  };
+  // groups that hold rows of the chunk (group i starts at row 64 i of the block)
+  const int hi = min(QG, (cend - q0 + 16 * C::WAVES - 1) / (16 * C::WAVES));
+  static_assert(QG == 2 || QG == 3, "two or three row groups per wave");
+  if (hi == QG)
+    key_loop(std::integral_constant<int, QG>{});
+  else if (hi == QG - 1)
+    key_loop(std::integral_constant<int, QG - 1>{});
+  else
+    key_loop(std::integral_constant<int, 1>{});
+
+  // Gate values, one group at a time. bf16 gates of the first group are
+  // loaded now, so that their latency hides behind the cross-chunk term, and
+  // each next group's while the current one is stored; fp32 gates (twice the
+  // registers) are loaded when needed.
+  constexpr int EI = 16 * (D / 8) / 64;  // 8-value groups per lane per 16 rows
+  constexpr bool kEarlyGate = false;
+  auto load_gate = [&](int i, Raw8<T> (&dst)[EI]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int s = 0; s < C::KS; ++s) qf[qq][s] = zero_frag<T>();
+    for (int e = 0; e < EI; ++e) {
+      const int idx = lane + 64 * e;
+      const int r = idx / (D / 8), c8 = idx % (D / 8);
+      const int tok = min(grow(i) + r, cend - 1);
+      dst[e] = ld_raw8(G + tok * tstride + c8 * 8);
+    }
+  };
+  Raw8<T> gbuf[kEarlyGate ? 2 : 1][EI];
+  if (kEarlyGate && G) load_gate(0, gbuf[0]);
+
+  // Cross-chunk term, added last. Fast path: O' += Q R_{i-1} (its row scale
+  // xi is the final row factor). Otherwise O = xi (.) (O_intra / xi + Q R):
+  // rows whose xi is below 2^-100 skip it (their Q fragment is zeroed, their
+  // scale is 1), the term being far below fp32 resolution there. The R^T
+  // slices stream through the two stages, the first one already in flight.
+  if (cross) {
+    float inv[QG][4];
+    if constexpr (!FAST) {
+#pragma unroll
+      for (int i = 0; i < QG; ++i) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float xi = gpow((float)(grow(i) + 4 * g + e - c0 + 1), lg);
+          inv[i][e] = xi >= 7.888609e-31f ? __builtin_amdgcn_rcpf(xi) : 1.f;
+#pragma unroll
+          for (int nb = 0; nb < C::NB; ++nb) oacc[i][nb][e] *= inv[i][e];
+        }
+        const float xq = gpow((float)(grow(i) + c - c0 + 1), lg);
+        if (!(xq >= 7.888609e-31f)) {
+#pragma unroll
+          for (int s = 0; s < C::KS; ++s) qf[i][s] = zero_frag<T>();
+        }
       }
     }
     auto cross_slice = [&](auto sl_c, const char* buf) __attribute__((always_inline)) {
@@ -319,93 +402,108 @@ __device__ __forceinline__ void out_role(const FwdParams& p, int bh, int ci, int
       for (int t = 0; t < NT; ++t) {
         if (t + 2 < NT) rb[(t + 2) % 3] = rload(t + 2);
 #pragma unroll
-        for (int qq = 0; qq < 2; ++qq)
-          oacc[qq][t % C::NB] = mma(qf[qq][SL * (C::RS / 32) + t / C::NB], rb[t % 3], oacc[qq][t % C::NB]);
+        for (int i = 0; i < QG; ++i)
+          oacc[i][t % C::NB] = mma(qf[i][SL * (C::RS / 32) + t / C::NB], rb[t % 3], oacc[i][t % C::NB]);
       }
     };
-    auto slice_pair = [&](auto sl_c) __attribute__((always_inline)) {
-      constexpr int SL = decltype(sl_c)::value;
-      async_tile<T, typename C::RT, C::WAVES, kCoherent>(stage0, R + SL * C::RS, D, 0, D - 1, wave, lane);
-      async_tile<T, typename C::RT, C::WAVES, kCoherent>(stage1, R + (SL + 1) * C::RS, D, 0, D - 1, wave, lane);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      cross_slice(std::integral_constant<int, SL>{}, stage0);
-      cross_slice(std::integral_constant<int, SL + 1>{}, stage1);
-      __syncthreads();
-    };
-    slice_pair(std::integral_constant<int, 0>{});
-    if constexpr (C::NRS > 2) slice_pair(std::integral_constant<int, 2>{});
-    static_assert(C::NRS <= 4, "at most four R^T slices");
-#pragma unroll
-    for (int qq = 0; qq < 2; ++qq)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float xi = inv[qq][i] == 1.f ? 1.f : gpow((float)(qw0 + qq * 16 + 4 * g + i - c0 + 1), lg);
-#pragma unroll
-        for (int nb = 0; nb < C::NB; ++nb) oacc[qq][nb][i] *= xi;
+    // slice SL sits in stage `sa`; slice SL+1 goes into stage `sb` meanwhile
+    auto slices = [&](char* sa, char* sb) __attribute__((always_inline)) {
+      auto step = [&](auto sl_c, char* cur, char* nxt) __attribute__((always_inline)) {
+        constexpr int SL = decltype(sl_c)::value;
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if constexpr (SL + 1 < C::NRS) issue_slice(SL + 1, nxt);
+        cross_slice(sl_c, cur);
+      };
+      step(std::integral_constant<int, 0>{}, sa, sb);
+      step(std::integral_constant<int, 1>{}, sb, sa);
+      if constexpr (C::NRS > 2) {
+        step(std::integral_constant<int, 2>{}, sa, sb);
+        step(std::integral_constant<int, 3>{}, sb, sa);
       }
+    };
+    static_assert(C::NRS == 2 || C::NRS == 4, "two or four R^T slices");
+    // the last key block used stage0 when nkb is odd, so slice 0 is in stage1
+    if (nkb & 1)
+      slices(stage1, stage0);
+    else
+      slices(stage0, stage1);
+    if constexpr (!FAST) {
+#pragma unroll
+      for (int i = 0; i < QG; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float xi = inv[i][e] == 1.f ? 1.f : gpow((float)(grow(i) + 4 * g + e - c0 + 1), lg);
+#pragma unroll
+          for (int nb = 0; nb < C::NB; ++nb) oacc[i][nb][e] *= xi;
+        }
+    }
   }
 
-  // Epilogue: GroupNorm over dv per (token, head), swish gate, store.
-  __syncthreads();
+  // Epilogue: GroupNorm over dv per (token, head), swish gate, store. Each
+  // wave stages one 16-row group at a time through its own LDS area to turn
+  // the accumulator layout into row-contiguous stores.
+  __syncthreads();  // every wave is done with the stages
   float* yw = reinterpret_cast<float*>(wave < 2 ? stage0 : stage1) + (wave & 1) * 16 * C::YSTR;
 #pragma unroll
-  for (int qq = 0; qq < 2; ++qq) {
-    constexpr int EI = 16 * (D / 8) / 64;
-    Raw8<T> gr[EI];
+  for (int i = 0; i < QG; ++i) {
+    Raw8<T>(&gq)[EI] = gbuf[kEarlyGate ? (i & 1) : 0];
     if (G) {
-#pragma unroll
-      for (int e = 0; e < EI; ++e) {
-        const int idx = lane + 64 * e;
-        const int r = idx / (D / 8), c8 = idx % (D / 8);
-        const int tok = min(qw0 + qq * 16 + r, cend - 1);
-        gr[e] = ld_raw8(G + tok * tstride + c8 * 8);
+      if constexpr (kEarlyGate) {
+        if (i + 1 < QG) load_gate(i + 1, gbuf[(i + 1) & 1]);
+      } else {
+        load_gate(i, gq);
       }
     }
+    // row factor of the fast path (1 otherwise): o = f o'. GroupNorm of f o'
+    // is (o' - mean') f / sqrt(f^2 var' + eps), so the statistics are taken
+    // on o' and the factor joins the scale.
     float mean[4], rstd[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      mean[i] = 0.f;
-      rstd[i] = 1.f;
-    }
-    if (G) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
+    for (int e = 0; e < 4; ++e) {
+      const float f = FAST ? gpow((float)(grow(i) + 4 * g + e - ref), lg) : 1.f;
+      mean[e] = 0.f;
+      rstd[e] = f;
+      if (G) {
         float s = 0.f;
 #pragma unroll
-        for (int nb = 0; nb < C::NB; ++nb) s += oacc[qq][nb][i];
-        mean[i] = sum16(s) * (1.0f / D);
+        for (int nb = 0; nb < C::NB; ++nb) s += oacc[i][nb][e];
+        mean[e] = sum16(s) * (1.0f / D);
         float s2 = 0.f;
 #pragma unroll
         for (int nb = 0; nb < C::NB; ++nb) {
-          const float d = oacc[qq][nb][i] - mean[i];
+          const float d = oacc[i][nb][e] - mean[e];
           s2 += d * d;
         }
-        rstd[i] = rsqrtf(sum16(s2) * (1.0f / D) + p.eps);
+        rstd[e] = f * rsqrtf(f * f * (sum16(s2) * (1.0f / D)) + p.eps);
       }
     }
 #pragma unroll
     for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) yw[(4 * g + i) * C::YSTR + nb * 16 + c] = (oacc[qq][nb][i] - mean[i]) * rstd[i];
-    __syncthreads();
+      for (int e = 0; e < 4; ++e) yw[(4 * g + e) * C::YSTR + nb * 16 + c] = (oacc[i][nb][e] - mean[e]) * rstd[e];
+    // the slab is private to this wave: its own LDS writes are done before
+    // it reads them back
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int e = 0; e < EI; ++e) {
       const int idx = lane + 64 * e;
       const int r = idx / (D / 8), c8 = idx % (D / 8);
-      const int tok = qw0 + qq * 16 + r;
+      const int tok = grow(i) + r;
       const float* yp = yw + r * C::YSTR + c8 * 8;
       const f32x4 ya = reinterpret_cast<const f32x4*>(yp)[0];
       const f32x4 yb = reinterpret_cast<const f32x4*>(yp)[1];
       F8 y{{ya[0], ya[1], ya[2], ya[3], yb[0], yb[1], yb[2], yb[3]}};
       if (G) {
-        const F8 gv = unpack8(gr[e]);
+        const F8 gv = unpack8(gq[e]);
 #pragma unroll
         for (int k = 0; k < 8; ++k) y.x[k] *= swish(gv.x[k]);
       }
       if (tok < cend) store8(O + tok * tstride + c8 * 8, y);
     }
-    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // the slab's reads are done before it is rewritten
+    __builtin_amdgcn_wave_barrier();
   }
 }
 
@@ -449,7 +547,7 @@ __device__ __forceinline__ void state_role(const FwdParams& p, int bh, int ci, i
   const T* K = reinterpret_cast<const T*>(p.k) + head0;
   const T* V = reinterpret_cast<const T*>(p.v) + head0;
   // flag of (chunk index j, this half)
-  auto flag_of = [&](int j) __attribute__((always_inline)) { return p.ctrl + 2 + (bh * (p.nchunks + 1) + j) * 2 + half; };
+  auto flag_of = [&](int j) __attribute__((always_inline)) { return p.ctrl + kCtrlHead + (bh * (p.nchunks + 1) + j) * 2 + half; };
 
   // accumulator element (a, nb, j) of lane (g, c) is R[dk][dv] with
   const int dkw = wave * (D / 4) + 4 * g;  // + 16 a + j
@@ -534,33 +632,39 @@ __device__ __forceinline__ void state_role(const FwdParams& p, int bh, int ci, i
     }
   }
 
-  // R_i = g^b R_{i-1} + dR_i
-  const float* Rprev = nullptr;
+  // R_i = g^b R_{i-1} + dR_i. The fp32 chain keeps R in this role's
+  // accumulator layout (four contiguous floats per lane and fragment), so
+  // the next chunk's workgroup of the same half reads it back coalesced.
+  auto chain_frag = [&](int slot, int a, int nb) __attribute__((always_inline)) {
+    return p.chain + ((int64_t)bh * 2 + slot) * D * D +
+           ((((half * 4 + wave) * SC::RB + a) * SC::NB + nb) * 64 + lane) * 4;
+  };
+  const float dec = gpow((float)(cend - c0), lg);
   if (ci > 0) {
     wait_flag(flag_of(ci), p.ctrl + 1);
-    Rprev = p.chain + ((int64_t)bh * 2 + ((ci - 1) & 1)) * D * D;
+    const int slot = (ci - 1) & 1;
+#pragma unroll
+    for (int a = 0; a < SC::RB; ++a)
+#pragma unroll
+      for (int nb = 0; nb < SC::NB; ++nb) {
+        const f32x4 r = load4_coherent(chain_frag(slot, a, nb));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) racc[a][nb][j] += dec * r[j];
+      }
   } else if (p.state_in) {
-    Rprev = p.state_in + (int64_t)bh * D * D;
-  }
-  if (Rprev) {
-    const float dec = gpow((float)(cend - c0), lg);
+    const float* S0 = p.state_in + (int64_t)bh * D * D;
 #pragma unroll
     for (int a = 0; a < SC::RB; ++a)
 #pragma unroll
       for (int nb = 0; nb < SC::NB; ++nb)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          racc[a][nb][j] += dec * (ci > 0 ? load1_coherent(Rprev + (int64_t)(dkw + 16 * a + j) * D + dv0 + nb * 16)
-                                          : Rprev[(int64_t)(dkw + 16 * a + j) * D + dv0 + nb * 16]);
+        for (int j = 0; j < 4; ++j) racc[a][nb][j] += dec * S0[(int64_t)(dkw + 16 * a + j) * D + dv0 + nb * 16];
   }
   if (ci + 1 < p.nchunks) {
-    float* Rn = p.chain + ((int64_t)bh * 2 + (ci & 1)) * D * D;
 #pragma unroll
     for (int a = 0; a < SC::RB; ++a)
 #pragma unroll
-      for (int nb = 0; nb < SC::NB; ++nb)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) store1_coherent(Rn + (int64_t)(dkw + 16 * a + j) * D + dv0 + nb * 16, racc[a][nb][j]);
+      for (int nb = 0; nb < SC::NB; ++nb) store4_coherent(chain_frag(ci & 1, a, nb), racc[a][nb]);
     write_snapshot(snap_next, racc);
     release_flag(flag_of(ci + 1));
   } else if (p.state_out) {
@@ -577,7 +681,7 @@ __device__ __forceinline__ void state_role(const FwdParams& p, int bh, int ci, i
 // ---------------------------------------------------------------------------
 // Kernels.
 // ---------------------------------------------------------------------------
-template <typename T, int D>
+template <typename T, int D, bool FAST>
 __global__ __launch_bounds__(256, 1) void retention_parallel_kernel(FwdParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the kernel's signature
   __shared__ __attribute__((aligned(1024))) char stage0[Stage<T, D>::BYTES];
@@ -593,33 +697,42 @@ __global__ __launch_bounds__(256, 1) void retention_parallel_kernel(FwdParams p)
     bh = bid / p.qblocks;
     qb = p.qblocks - 1 - bid % p.qblocks;
   }
-  out_role<T, D>(p, bh, 0, qb, false, stage0, stage1);
+  out_role<T, D, FAST>(p, bh, 0, qb, false, stage0, stage1);
 #endif
 }
 
-template <typename T, int D>
+template <typename T, int D, bool FAST>
 __global__ __launch_bounds__(256, 1) void retention_chunkwise_kernel(FwdParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the kernel's signature
   __shared__ __attribute__((aligned(1024))) char stage0[Stage<T, D>::BYTES];
   __shared__ __attribute__((aligned(1024))) char stage1[Stage<T, D>::BYTES];
   __shared__ int s_ticket;
-  if (threadIdx.x == 0) s_ticket = atomicAdd(p.ctrl, 1);
+  constexpr int SPLIT = StTile<T, D>::SPLIT;
+  const int bhs = p.batch * p.heads;
+  const int roles = SPLIT + p.qblocks;  // workgroups per (sequence, head, chunk)
+  // class of this workgroup: blockIdx mod 8, which is also the XCD it runs on
+  // when workgroups are dealt round-robin over the 8 XCDs
+  const int cls = p.xcd_order ? (int)(blockIdx.x & 7) : 0;
+  if (threadIdx.x == 0) {
+    atomicAdd(p.ctrl, 1);  // workgroups that ran
+    s_ticket = p.xcd_order ? atomicAdd(p.ctrl + kTicketWord + cls, 1) : atomicAdd(p.ctrl + kTicketWord, 1);
+  }
   __syncthreads();
   const int t = s_ticket;
-  const int bhs = p.batch * p.heads;
-  constexpr int SPLIT = StTile<T, D>::SPLIT;
-  const int roles = SPLIT + p.qblocks;  // workgroups per (sequence, head, chunk)
-  const int ci = t / (bhs * roles);
-  int r = t % (bhs * roles);
-  int bh, role;  // role < SPLIT: state half; else query block qblocks-1-(role-SPLIT)
+  int ci, bh, role;  // role < SPLIT: state half; else query block qblocks-1-(role-SPLIT)
   if (p.xcd_order) {
-    // blocks of 8 (sequence, head) pairs: slot r -> lane of 8 = likely XCD
-    // (workgroups are dispatched round-robin over the 8 XCDs), so the state
-    // and output workgroups of one pair tend to share an XCD and its L2
-    const int blk = r / (8 * roles), sidx = r % (8 * roles);
-    bh = blk * 8 + (sidx & 7);
-    role = sidx >> 3;
+    // Class c owns the (sequence, head) pairs bh = 8j + c and takes them
+    // chunk-major, role-major: every dependency stays inside the class, and
+    // the workgroups of one chunk share an XCD and its L2 when the class is
+    // the XCD. Each class has exactly total/8 workgroups and items.
+    const int nbl = bhs / 8;
+    ci = t / (nbl * roles);
+    const int r = t % (nbl * roles);
+    role = r / nbl;
+    bh = (r % nbl) * 8 + cls;
   } else {
+    ci = t / (bhs * roles);
+    const int r = t % (bhs * roles);
     bh = r / roles;
     role = r % roles;
   }
@@ -627,7 +740,7 @@ __global__ __launch_bounds__(256, 1) void retention_chunkwise_kernel(FwdParams p
   if (qb < 0)
     state_role<T, D>(p, bh, ci, role, stage0, stage1);
   else
-    out_role<T, D>(p, bh, ci, qb, true, stage0, stage1);
+    out_role<T, D, FAST>(p, bh, ci, qb, true, stage0, stage1);
 #endif
 }
 
@@ -635,29 +748,41 @@ __global__ void reset_ctrl_kernel(int* ctrl, int n) {
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) ctrl[i] = 0;
 }
 
-template <typename T, int D>
-static hipError_t launch_fwd_t(const Shape& s, int chunk, FwdParams p, bool chunked, hipStream_t stream) {
-  using C = OutTile<T, D>;
+template <typename T, int D, bool FAST>
+static hipError_t launch_fwd_impl(const Shape& s, int chunk, FwdParams p, bool chunked, hipStream_t stream) {
+  using C = OutTile<T, D, FAST>;
   p.qblocks = (chunk + C::BM - 1) / C::BM;
   const int bhs = s.batch * s.heads;
   if (!chunked) {
     const int64_t blocks = (int64_t)bhs * p.qblocks;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((retention_parallel_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((retention_parallel_kernel<T, D, FAST>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
     return hipGetLastError();
   }
-  const int64_t nctrl = 2 + (int64_t)bhs * (p.nchunks + 1) * 2;
+  const int64_t nctrl = kCtrlHead + (int64_t)bhs * (p.nchunks + 1) * 2;
   hipLaunchKernelGGL(reset_ctrl_kernel, dim3((unsigned)((nctrl + 255) / 256 < 1024 ? (nctrl + 255) / 256 : 1024)),
                      dim3(256), 0, stream, p.ctrl, (int)nctrl);
   p.xcd_order = bhs % 8 == 0;
   const int64_t blocks = (int64_t)p.nchunks * bhs * (StTile<T, D>::SPLIT + p.qblocks);
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((retention_chunkwise_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((retention_chunkwise_kernel<T, D, FAST>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
+// The fast path applies when every head's decay over the span of one
+// workgroup's factors (the chunk, or the parallel form's query block) stays
+// within 2^64.
+template <typename T, int D>
+static hipError_t launch_fwd_t(const Shape& s, int chunk, FwdParams p, bool chunked, hipStream_t stream) {
+  const double span = chunked ? chunk : OutTile<T, D, true>::BM;
+  bool fast = true;
+  for (int h = 0; h < s.heads; ++h) fast = fast && -(double)s.log2g[h] * span <= kFastSpanLog2;
+  return fast ? launch_fwd_impl<T, D, true>(s, chunk, p, chunked, stream)
+              : launch_fwd_impl<T, D, false>(s, chunk, p, chunked, stream);
+}
+
 size_t chunkwise_ctrl_bytes(int batch, int heads, int nchunks) {
-  return ((size_t)2 + (size_t)batch * heads * (nchunks + 1) * 2) * sizeof(int);
+  return ((size_t)kCtrlHead + (size_t)batch * heads * (nchunks + 1) * 2) * sizeof(int);
 }
 
 hipError_t launch_retention_fwd(const Shape& s, int chunk, bool chunked, const void* q, const void* k, const void* v,

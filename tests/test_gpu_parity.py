@@ -181,10 +181,13 @@ def test_nan_propagates_forward_only():
     assert torch.isfinite(o[0, 64:, 0, :5]).all()
 
 
-# --- the chunk-to-chunk hand-off completes: every workgroup ran, no wait expired
-def test_chunkwise_handoff_completes():
-    _announce(case="handoff control block")
-    b, n, h, d, chunk = 2, 1100, 4, 256, 128
+# --- the chunk-to-chunk hand-off completes: every workgroup ran, no wait
+# expired; with 8 | batch*heads the workgroups split into 8 classes (one ticket
+# counter each), otherwise they share one counter
+@pytest.mark.parametrize("b,h", [(2, 4), (1, 3)])
+def test_chunkwise_handoff_completes(b, h):
+    _announce(case=f"handoff control block b={b} h={h}")
+    n, d, chunk = 1100, 256, 128
     q, k, v, g, s0 = make_inputs(97, b, n, h, d, "bf16", 1 / 16, 1.0, True)
     tq, tk, tv, tg = (x.torch(DEV) for x in (q, k, v, g))
     ws = torch.zeros(rr.chunkwise_workspace_bytes(tq, tv, chunk), dtype=torch.uint8, device=DEV)
@@ -192,11 +195,16 @@ def test_chunkwise_handoff_completes():
     s_out = torch.empty_like(s_in)
     out = rr.chunkwise_fwd(tq, tk, tv, tg, chunk=chunk, state_in=s_in, state_out=s_out, workspace=ws)
     torch.cuda.synchronize()
-    ctrl = ws[:8].view(torch.int32).cpu()
+    ctrl = ws[:64].view(torch.int32).cpu()
     nchunks = -(-n // chunk)
     # two state workgroups and one 128-row output workgroup per (sequence, head, chunk)
-    assert int(ctrl[0]) == nchunks * b * h * (2 + 1)
+    total = nchunks * b * h * (2 + 1)
+    assert int(ctrl[0]) == total
     assert int(ctrl[1]) == 0
+    if (b * h) % 8 == 0:
+        assert [int(x) for x in ctrl[8:16]] == [total // 8] * 8
+    else:
+        assert int(ctrl[8]) == total
     ref, ref_s = oracle_run("chunkwise", q, k, v, g, chunk=chunk, state_in=s0)
     assert_close(to64(out), ref, "bf16", "out")
     assert_close(to64(s_out), ref_s, "bf16", "state")
