@@ -254,6 +254,15 @@ __device__ __forceinline__ bf16x8 acc_to_frag(const f32x4& lo, const f32x4& hi, 
 __device__ __forceinline__ f32x8 acc_to_frag(const f32x4& lo, const f32x4& hi, float*) {
   return f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
+// Multiply element j of a fragment by z[j] (bf16 fragments round back).
+__device__ __forceinline__ void scale_frag(bf16x8& f, const float* z) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f[i] = (bf16)((float)f[i] * z[i]);
+}
+__device__ __forceinline__ void scale_frag(f32x8& f, const float* z) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f[i] *= z[i];
+}
 // Multiply every element of a fragment by x (bf16 fragments round back).
 __device__ __forceinline__ void scale_frag(bf16x8& f, float x) {
 #pragma unroll

@@ -248,9 +248,13 @@ __device__ __forceinline__ void out_role(const FwdParams& p, int bh, int ci, int
   // and V fragments of a 32-key step form one sequence of LDS reads with a
   // two-deep prefetch ring.
   constexpr int U = 2 * C::KS + C::NB;  // fragment reads per 32-key step
+  float bkl[4];  // g^-(4 g + e): this lane's part of the per-key factors
+#pragma unroll
+  for (int e = 0; e < 4; ++e) bkl[e] = FAST ? gpow(-(float)(4 * g + e), lg) : 0.f;
   auto key_block = [&](auto hi_c, int kb0, const char* kt) __attribute__((always_inline)) {
     constexpr int HI = decltype(hi_c)::value;
     const char* vt = kt + C::KT::BYTES;
+    const bool diag = kb0 + C::BN - 1 > q0;  // some key may follow some row (uniform)
     auto load = [&](auto t_c) __attribute__((always_inline)) {
       constexpr int t = decltype(t_c)::value, kh = t / U, u = t % U;
       if constexpr (u < 2 * C::KS)  // key group 2 kh + u % 2, contraction step u / 2
@@ -277,21 +281,31 @@ __device__ __forceinline__ void out_role(const FwdParams& p, int bh, int ci, int
 #pragma unroll
         for (int i = 0; i < HI; ++i) st[i][k2] = mma(ring[t % 3], qf[i][s], st[i][k2]);
         if constexpr (u == 2 * C::KS - 1) {
-          // decay g^(q-k) and causal mask over the 32 keys, which become P
+          // decay g^(q-k) and causal mask over the 32 keys, which become P;
+          // only the diagonal blocks need the mask
 #pragma unroll
           for (int h2 = 0; h2 < 2; ++h2) {
             const int k0 = 32 * kh + 16 * h2 + 4 * g;  // key - kb0 of element 0
             if constexpr (FAST) {
-              float bk[4];  // g^(r0 - k)
+              // g^(r0 - k) = g^(r0 - kb0 - 32 kh - 16 h2) * g^-(4 g + e)
+              const float sb = gpow((float)(ref - kb0 - 32 * kh - 16 * h2), lg);
+              float bk[4];
 #pragma unroll
-              for (int e = 0; e < 4; ++e) bk[e] = gpow((float)(ref - kb0 - k0 - e), lg);
+              for (int e = 0; e < 4; ++e) bk[e] = sb * bkl[e];
+              if (diag) {
 #pragma unroll
-              for (int i = 0; i < HI; ++i)
+                for (int i = 0; i < HI; ++i)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                  const float val = st[i][h2][e] * bk[e];
-                  st[i][h2][e] = grow(i) + c - kb0 < k0 + e ? 0.f : val;
-                }
+                  for (int e = 0; e < 4; ++e) {
+                    const float val = st[i][h2][e] * bk[e];
+                    st[i][h2][e] = grow(i) + c - kb0 < k0 + e ? 0.f : val;
+                  }
+              } else {
+#pragma unroll
+                for (int i = 0; i < HI; ++i)
+#pragma unroll
+                  for (int e = 0; e < 4; ++e) st[i][h2][e] *= bk[e];
+              }
             } else {
 #pragma unroll
               for (int i = 0; i < HI; ++i)
@@ -597,10 +611,14 @@ __device__ __forceinline__ void state_role(const FwdParams& p, int bh, int ci, i
         z[j] = gpow((float)(cend - 1 - key), lg);
       }
       frag_t<T> af[SC::RB];
+      const bool ragged = kb0 + SC::BK > cend;  // keys past the chunk in this block (uniform)
 #pragma unroll
       for (int a = 0; a < SC::RB; ++a) {
         af[a] = tile_col8<typename SC::KT>(kt, ks * 32, wave * (D / 4) + 16 * a, lane, (T*)nullptr);
-        scale_frag(af[a], z, keep);
+        if (ragged)
+          scale_frag(af[a], z, keep);
+        else
+          scale_frag(af[a], z);
       }
       constexpr int NT = SC::NB;
       auto vload = [&](int t) __attribute__((always_inline)) {
