@@ -28,9 +28,11 @@ def assert_close(got, ref, dtype, what=""):
     assert np.all(np.isfinite(got)), f"{what}: non-finite output"
     if dtype == "f32":
         err = float(np.max(np.abs(got - ref)))
+        print(f"  {what}: max-abs {err:.3e}", flush=True)
         assert err <= F32_MAX_ABS, f"{what}: max-abs {err:.3e} > {F32_MAX_ABS}"
     else:
         err = rel_frob(got, ref)
+        print(f"  {what}: rel-Frobenius {err:.3e}", flush=True)
         assert err <= BF16_REL_FROB, f"{what}: rel-Frobenius {err:.3e} > {BF16_REL_FROB}"
     return err
 
