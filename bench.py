@@ -234,9 +234,10 @@ def bench_decode(n_steps=256, warmup=16, batches=None):
     return w, results
 
 
-def cpu_baseline(sample_seqs=2):
-    """The fp64 oracle's chunkwise form on a bounded sample of the headline
-    workload: `sample_seqs` of its 2 sequences, all 16 heads, all 8192 tokens."""
+def cpu_baseline(sample_seqs=2, min_seconds=10.0, max_runs=20):
+    """The fp64 oracle's chunkwise form on the headline workload (`sample_seqs`
+    of its 2 sequences, all 16 heads, all 8192 tokens), repeated until at
+    least `min_seconds` of CPU work; the rate is that of the mean run."""
     import oracle
     from synth import get
 
@@ -250,9 +251,11 @@ def cpu_baseline(sample_seqs=2):
     except Exception:
         pass
     cores = len(os.sched_getaffinity(0))
-    t0 = time.perf_counter()
-    oracle.retention("chunkwise", q.f64, k.f64, v.f64, g=g.f64, chunk=w.chunk)
-    dt = time.perf_counter() - t0
+    runs, t0 = 0, time.perf_counter()
+    while runs < max_runs and (runs == 0 or time.perf_counter() - t0 < min_seconds):
+        oracle.retention("chunkwise", q.f64, k.f64, v.f64, g=g.f64, chunk=w.chunk)
+        runs += 1
+    dt = (time.perf_counter() - t0) / runs
     flops = chunkwise_flops(sample_seqs, w.seqlen, w.heads, w.dk, w.dv, w.chunk)
     return {
         "value": flops / dt / 1e12,
@@ -260,9 +263,9 @@ def cpu_baseline(sample_seqs=2):
         "cores": threads or cores,
         "kind": "oracle",
         "sample": f"chunkwise fp64 oracle on {sample_seqs} of 2 sequences of retention_7b_8k "
-                  f"(8192 tokens, 16 heads x 256, chunk 512, gate): {dt:.2f} s on {threads or cores} BLAS threads "
-                  f"({cores} cores in affinity mask)",
-        "seconds": dt,
+                  f"(8192 tokens, 16 heads x 256, chunk 512, gate), {runs} runs of {dt:.2f} s each on "
+                  f"{threads or cores} BLAS threads ({cores} cores in the affinity mask)",
+        "seconds": dt * runs,
     }
 
 
@@ -300,8 +303,14 @@ def _bench_cmd(leg_args):
     return ["python3", os.path.join(ROOT, "bench.py"), *leg_args, "--no-cpu-baseline"]
 
 
+PROFILE_OUT = [None]  # the --profile-out directory, shown as <out> in the recorded commands
+
+
 def _rel(cmd):
-    return " ".join(c.replace(ROOT + "/", "").replace(ROOT, ".") for c in cmd)
+    out = " ".join(cmd)
+    if PROFILE_OUT[0]:
+        out = out.replace(PROFILE_OUT[0], "<out>")
+    return out.replace(ROOT + "/", "").replace(ROOT, ".")
 
 
 def _counter_rows(d):
@@ -334,6 +343,7 @@ def profile_stats(out, raw):
         name = {"chunkwise": "chunkwise_7b_8k", "decode": "decode_step_7b_b64", "parallel": "parallel_3b"}[leg]
         with open(os.path.join(out, f"{name}_kernel_stats.txt"), "w") as f:
             f.write(f"rocprofv3 kernel statistics, {leg} leg of the benchmark\n")
+            f.write("made by: python bench.py --profile stats --profile-out <out>\n")
             f.write(f"command: {_rel(cmd)}\n")
             f.write(f"kernel sources: {source_hash()} (chunkwise/parallel kernel), host {os.uname().nodename}\n\n")
             f.write(f"{'kernel':70s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'share%':>7s}\n")
@@ -375,6 +385,7 @@ def profile_traffic(out, raw):
     with open(os.path.join(out, "chunkwise_7b_8k_traffic.txt"), "w") as f:
         f.write("HBM traffic of the chunkwise kernel on the 7B long-context workload (batch 2, 8192 tokens,\n"
                 "16 heads x 256, chunk 512, bf16, gate, state out), from two rocprofv3 counter passes\n")
+        f.write("made by: python bench.py --profile traffic --profile-out <out>\n")
         for c in cmds:
             f.write(f"command: {_rel(c)}\n")
         f.write(f"kernel: {CHUNKWISE_KERNEL}<bf16, 256>\n")
@@ -415,6 +426,7 @@ def profile_counters(out, raw):
                 lines.append(f"  {c:32s} {vals[c]:.6g}  (dispatches {len(v)})\n")
         with open(os.path.join(out, f"{name}_sq_counters.txt"), "w") as f:
             f.write(f"rocprofv3 SQ counters, {leg} leg, mean per dispatch of the retention kernel\n")
+            f.write("made by: python bench.py --profile counters --profile-out <out>\n")
             f.write(f"kernel sources: {source_hash()}\n")
             f.writelines(lines)
             xcds, cus, simds = 8, 256, 4
@@ -433,6 +445,7 @@ def profile_counters(out, raw):
 
 
 def profile(kinds, out):
+    PROFILE_OUT[0] = out
     os.makedirs(out, exist_ok=True)
     raw = os.path.join(out, "raw")
     os.makedirs(raw, exist_ok=True)
@@ -535,7 +548,8 @@ def main():
         copy_probe()
     if args.only is None and not args.no_cpu_baseline:
         cb = cpu_baseline()
-        print(f"cpu baseline: {cb['value'] * 1e3:.2f} GFLOP/s ({cb['seconds']:.1f} s)", file=sys.stderr, flush=True)
+        print(f"cpu baseline: {cb['value'] * 1e3:.2f} GFLOP/s ({cb['seconds']:.1f} s in all)", file=sys.stderr,
+              flush=True)
         cb.pop("seconds")
         line["cpu_baseline"] = cb
     print(json.dumps(line), flush=True)
