@@ -29,7 +29,9 @@ struct StepParams {
 
 template <typename T> __device__ __forceinline__ float ld1(const T* p, int i) { return (float)p[i]; }
 
-template <typename T, int D>
+// STREAM: non-temporal state accesses, for states too large to stay in the
+// caches from one step to the next.
+template <typename T, int D, bool STREAM>
 __global__ __launch_bounds__(256) void recurrent_step_kernel(StepParams p) {
   constexpr int CT = D / 4;       // threads across one state row (float4 each)
   constexpr int RPI = 256 / CT;   // rows per sweep iteration
@@ -71,19 +73,24 @@ __global__ __launch_bounds__(256) void recurrent_step_kernel(StepParams p) {
   const float4 vv = *reinterpret_cast<const float4*>(&sv[c4 * 4]);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   float* S = p.state + (int64_t)bh * D * D + c4 * 4;
-#pragma unroll 8
+  constexpr int kUnroll = STREAM ? 16 : 8;  // loads in flight per thread
+#pragma unroll kUnroll
   for (int r = r0; r < D; r += RPI) {
-    float4 s = *reinterpret_cast<const float4*>(S + (int64_t)r * D);
+    f32x4* sp = reinterpret_cast<f32x4*>(S + (int64_t)r * D);
+    f32x4 s = STREAM ? __builtin_nontemporal_load(sp) : *sp;
     const float kr = sk[r], qr = sq[r];
-    s.x = gam * s.x + kr * vv.x;
-    s.y = gam * s.y + kr * vv.y;
-    s.z = gam * s.z + kr * vv.z;
-    s.w = gam * s.w + kr * vv.w;
-    *reinterpret_cast<float4*>(S + (int64_t)r * D) = s;
-    acc.x += qr * s.x;
-    acc.y += qr * s.y;
-    acc.z += qr * s.z;
-    acc.w += qr * s.w;
+    s[0] = gam * s[0] + kr * vv.x;
+    s[1] = gam * s[1] + kr * vv.y;
+    s[2] = gam * s[2] + kr * vv.z;
+    s[3] = gam * s[3] + kr * vv.w;
+    if constexpr (STREAM)
+      __builtin_nontemporal_store(s, sp);
+    else
+      *sp = s;
+    acc.x += qr * s[0];
+    acc.y += qr * s[1];
+    acc.z += qr * s[2];
+    acc.w += qr * s[3];
   }
   *reinterpret_cast<float4*>(&part[r0][c4 * 4]) = acc;
   __syncthreads();
@@ -123,10 +130,16 @@ __global__ __launch_bounds__(256) void recurrent_step_kernel(StepParams p) {
   }
 }
 
+// States above this size do not stay in the caches between steps.
+constexpr size_t kStreamStateBytes = size_t(512) << 20;
+
 template <typename T, int D>
 static hipError_t launch_step_t(const Shape& s, const StepParams& p, hipStream_t stream) {
   const unsigned blocks = (unsigned)s.batch * (unsigned)s.heads;
-  hipLaunchKernelGGL((recurrent_step_kernel<T, D>), dim3(blocks), dim3(256), 0, stream, p);
+  if ((size_t)blocks * D * D * sizeof(float) > kStreamStateBytes)
+    hipLaunchKernelGGL((recurrent_step_kernel<T, D, true>), dim3(blocks), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((recurrent_step_kernel<T, D, false>), dim3(blocks), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

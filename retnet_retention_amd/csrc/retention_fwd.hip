@@ -77,14 +77,24 @@ constexpr double kFastSpanLog2 = 64.0;
 
 template <typename T, int D>
 struct StTile {
-  static constexpr int SPLIT = 2;               // state workgroups per chunk, one per dv half
+  // State workgroups per chunk: one per 128 dk rows of R (one for D <= 128).
+  // The four waves split the workgroup's rows; each holds its rows x D of R
+  // in fp32 registers. Fewer rows per workgroup shorten the serial chunk-to-
+  // chunk hand-off; more rows cost fewer K reads per chunk.
+  static constexpr int SPLIT = D > 128 ? D / 128 : 1;
+  static constexpr int ROWS = D / SPLIT;        // dk rows per workgroup
   static constexpr int BK = OutTile<T, D>::BN;  // keys per block
-  static constexpr int RB = D / 64;             // 16-row dk blocks per wave (wave owns D/4 dk rows)
-  static constexpr int NB = D / 16 / SPLIT;     // 16-wide dv blocks of this half
-  using KT = PTile<T, BK, D, 32>;               // K block, column fragments (K^T operand)
+  static constexpr int RB = ROWS / 64;          // 16-row dk blocks per wave
+  static constexpr int NB = D / 16;             // 16-wide dv blocks
+  using KT = PTile<T, BK, ROWS, 32>;            // this workgroup's dk columns of K (K^T operand)
   using VT = PTile<T, BK, D, 32>;               // V block, column fragments
   static constexpr int KVB = KT::BYTES + VT::BYTES;
 };
+// per (sequence, head, chunk j) and state part q two ready flags: rows of
+// R_{j-1} in the fp32 chain (for chunk j's state workgroup of part q) and in
+// the snapshot (for chunk j's output workgroups)
+constexpr int kMaxSplit = 2;
+constexpr int kFlagsPerChunk = 2 * kMaxSplit;
 
 template <typename T, int D>
 struct Stage {
@@ -105,7 +115,7 @@ struct FwdParams {
   float* state_out;
   void* snap;    // [BH][nchunks][dv][dk] of T: R_{i-1}^T for chunk i
   float* chain;  // [BH][2][D*D] fp32: R_i handed to the next state workgroup (fragment order)
-  int* ctrl;     // [0] count, [1] error, [8..15] tickets, [16 + (bh*(nchunks+1) + i)*2 + half]: R_{i-1} ready
+  int* ctrl;     // [0] count, [1] error, [8..15] tickets, [16 + (bh*(nchunks+1) + i)*4 + kind*2 + part]: R_{i-1} ready
   int batch, seqlen, heads, chunk, nchunks, qblocks;
   int has_state0, xcd_order;
   float eps;
@@ -213,12 +223,12 @@ __device__ __forceinline__ void out_role(const FwdParams& p, int bh, int ci, int
   const bool cross = chunked && (ci > 0 || p.has_state0);
   const T* R = cross ? reinterpret_cast<const T*>(p.snap) + ((int64_t)bh * p.nchunks + ci) * D * D : nullptr;
   // R^T slice s ([dv][RS dk columns]) into an LDS stage; waits (once) for
-  // both halves of R_{i-1} to be published
+  // the snapshot of R_{i-1} to be published
   auto issue_slice = [&](int sl, char* buf) __attribute__((always_inline)) {
     if (sl == 0) {
-      int* flags = p.ctrl + kCtrlHead + (bh * (p.nchunks + 1) + ci) * 2;
-      wait_flag(flags + 0, p.ctrl + 1);
-      wait_flag(flags + 1, p.ctrl + 1);
+      const int* flags = p.ctrl + kCtrlHead + (bh * (p.nchunks + 1) + ci) * kFlagsPerChunk + kMaxSplit;
+#pragma unroll
+      for (int q = 0; q < StTile<T, D>::SPLIT; ++q) wait_flag(flags + q, p.ctrl + 1);
     }
     async_tile<T, typename C::RT, C::WAVES, kCoherent>(buf, R + sl * C::RS, D, 0, D - 1, wave, lane);
   };
@@ -325,6 +335,8 @@ __device__ __forceinline__ void out_role(const FwdParams& p, int bh, int ci, int
 #pragma unroll
         for (int i = 0; i < HI; ++i) oacc[i][nb] = mma(pf[i], ring[t % 3], oacc[i][nb]);
       }
+      // keep each step's prefetch where it is: two steps ahead of its use
+      __builtin_amdgcn_sched_barrier(0);
     });
   };
 
@@ -361,12 +373,8 @@ __device__ __forceinline__ void out_role(const FwdParams& p, int bh, int ci, int
   else
     key_loop(std::integral_constant<int, 1>{});
 
-  // Gate values, one group at a time. bf16 gates of the first group are
-  // loaded now, so that their latency hides behind the cross-chunk term, and
-  // each next group's while the current one is stored; fp32 gates (twice the
-  // registers) are loaded when needed.
-  constexpr int EI = 16 * (D / 8) / 64;  // 8-value groups per lane per 16 rows
-  constexpr bool kEarlyGate = false;
+  // Gate values, one 16-row group at a time (8-value groups per lane).
+  constexpr int EI = 16 * (D / 8) / 64;
   auto load_gate = [&](int i, Raw8<T> (&dst)[EI]) __attribute__((always_inline)) {
 #pragma unroll
     for (int e = 0; e < EI; ++e) {
@@ -376,8 +384,6 @@ __device__ __forceinline__ void out_role(const FwdParams& p, int bh, int ci, int
       dst[e] = ld_raw8(G + tok * tstride + c8 * 8);
     }
   };
-  Raw8<T> gbuf[kEarlyGate ? 2 : 1][EI];
-  if (kEarlyGate && G) load_gate(0, gbuf[0]);
 
   // Cross-chunk term, added last. Fast path: O' += Q R_{i-1} (its row scale
   // xi is the final row factor). Otherwise O = xi (.) (O_intra / xi + Q R):
@@ -418,6 +424,7 @@ __device__ __forceinline__ void out_role(const FwdParams& p, int bh, int ci, int
 #pragma unroll
         for (int i = 0; i < QG; ++i)
           oacc[i][t % C::NB] = mma(qf[i][SL * (C::RS / 32) + t / C::NB], rb[t % 3], oacc[i][t % C::NB]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     };
     // slice SL sits in stage `sa`; slice SL+1 goes into stage `sb` meanwhile
@@ -456,14 +463,19 @@ __device__ __forceinline__ void out_role(const FwdParams& p, int bh, int ci, int
 
   // Epilogue: GroupNorm over dv per (token, head), swish gate, store. Each
   // wave stages one 16-row group at a time through its own LDS area to turn
-  // the accumulator layout into row-contiguous stores.
+  // the accumulator layout into row-contiguous stores. The gate of the next
+  // group loads while the current one is processed (bf16; fp32 gates take
+  // twice the registers and load per group).
+  constexpr bool kGatePipe = sizeof(T) == 2;
+  Raw8<T> gbuf[kGatePipe ? 2 : 1][EI];
+  if (kGatePipe && G) load_gate(0, gbuf[0]);
   __syncthreads();  // every wave is done with the stages
   float* yw = reinterpret_cast<float*>(wave < 2 ? stage0 : stage1) + (wave & 1) * 16 * C::YSTR;
 #pragma unroll
   for (int i = 0; i < QG; ++i) {
-    Raw8<T>(&gq)[EI] = gbuf[kEarlyGate ? (i & 1) : 0];
+    Raw8<T>(&gq)[EI] = gbuf[kGatePipe ? (i & 1) : 0];
     if (G) {
-      if constexpr (kEarlyGate) {
+      if constexpr (kGatePipe) {
         if (i + 1 < QG) load_gate(i + 1, gbuf[(i + 1) & 1]);
       } else {
         load_gate(i, gq);
@@ -544,8 +556,14 @@ __device__ __forceinline__ void state_issue(char* buf, const T* K, const T* V, i
   async_tile<T, VT, 4>(buf + KT::BYTES, V, tstride, kb0, rmax, wave, lane);
 }
 
+// State role: rows dk0 .. dk0+ROWS-1 (dk0 = ROWS part) of R_i for one chunk
+// of one (sequence, head). Accumulates
+// dR = K^T (V (.) zeta) over the chunk's keys, waits for R_{i-1} in the fp32
+// chain from the previous chunk's workgroup, forms R_i = g^b R_{i-1} + dR,
+// hands it on in the chain and then publishes its snapshot R_i^T for the next
+// chunk's output workgroups.
 template <typename T, int D>
-__device__ __forceinline__ void state_role(const FwdParams& p, int bh, int ci, int half, char* stage0,
+__device__ __forceinline__ void state_role(const FwdParams& p, int bh, int ci, int part, char* stage0,
                                            char* stage1) {
   using SC = StTile<T, D>;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -558,21 +576,24 @@ __device__ __forceinline__ void state_role(const FwdParams& p, int bh, int ci, i
   const int nkb = (cend - c0 + SC::BK - 1) / SC::BK;
   const int64_t tstride = (int64_t)p.heads * D;
   const int64_t head0 = ((int64_t)b * p.seqlen * p.heads + h) * D;
-  const T* K = reinterpret_cast<const T*>(p.k) + head0;
+  const int dk0 = part * SC::ROWS;
+  const T* K = reinterpret_cast<const T*>(p.k) + head0 + dk0;
   const T* V = reinterpret_cast<const T*>(p.v) + head0;
-  // flag of (chunk index j, this half)
-  auto flag_of = [&](int j) __attribute__((always_inline)) { return p.ctrl + kCtrlHead + (bh * (p.nchunks + 1) + j) * 2 + half; };
+  // flags of chunk index j for this part: kind 0 = chain, 1 = snapshot
+  auto flag_of = [&](int j, int kind) __attribute__((always_inline)) {
+    return p.ctrl + kCtrlHead + (bh * (p.nchunks + 1) + j) * kFlagsPerChunk + kind * kMaxSplit + part;
+  };
 
   // accumulator element (a, nb, j) of lane (g, c) is R[dk][dv] with
-  const int dkw = wave * (D / 4) + 4 * g;  // + 16 a + j
-  const int dv0 = half * (D / SC::SPLIT) + c;  // + 16 nb
+  const int dkl = dk0 + wave * (SC::ROWS / 4) + 4 * g;  // + 16 a + j
+  const int dvl = c;                        // + 16 nb
   T* snap_next = reinterpret_cast<T*>(p.snap) + ((int64_t)bh * p.nchunks + ci + 1) * D * D;
   auto write_snapshot = [&](T* sn, const f32x4 (&acc)[SC::RB][SC::NB]) __attribute__((always_inline)) {
 #pragma unroll
     for (int a = 0; a < SC::RB; ++a)
 #pragma unroll
       for (int nb = 0; nb < SC::NB; ++nb)
-        store4_coherent(sn + (int64_t)(dv0 + nb * 16) * D + dkw + 16 * a, acc[a][nb]);
+        store4_coherent(sn + (int64_t)(dvl + nb * 16) * D + dkl + 16 * a, acc[a][nb]);
   };
 
   f32x4 racc[SC::RB][SC::NB];
@@ -584,9 +605,9 @@ __device__ __forceinline__ void state_role(const FwdParams& p, int bh, int ci, i
 #pragma unroll
       for (int nb = 0; nb < SC::NB; ++nb)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) racc[a][nb][j] = S0[(int64_t)(dkw + 16 * a + j) * D + dv0 + nb * 16];
+        for (int j = 0; j < 4; ++j) racc[a][nb][j] = S0[(int64_t)(dkl + 16 * a + j) * D + dvl + nb * 16];
     write_snapshot(reinterpret_cast<T*>(p.snap) + (int64_t)bh * p.nchunks * D * D, racc);
-    release_flag(flag_of(0));
+    release_flag(flag_of(0, 1));
   }
 #pragma unroll
   for (int a = 0; a < SC::RB; ++a)
@@ -596,42 +617,56 @@ __device__ __forceinline__ void state_role(const FwdParams& p, int bh, int ci, i
   auto issue_kv = [&](int j, char* buf) __attribute__((always_inline)) {
     state_issue<T, D>(buf, K, V, tstride, c0 + j * SC::BK, cend - 1, wave, lane);
   };
+  // zeta_k = g^(cend-1-k) for key k = kb0 + 32 ks + koff(j), with koff(j) the
+  // column-fragment key order {4g..4g+3, 16+4g..16+4g+3}
+  float zl[8];  // this lane's part: g^-koff(j)
+#pragma unroll
+  for (int j = 0; j < 8; ++j) zl[j] = gpow(-(float)(j < 4 ? 4 * g + j : 16 + 4 * g + j - 4), lg);
   // dR += K_blk^T (V_blk (.) zeta): zeta is applied to the K^T fragments (one
   // factor per key), keys past the chunk get zero.
   auto block = [&](int kb0, const char* kt) __attribute__((always_inline)) {
     const char* vt = kt + SC::KT::BYTES;
+    const bool ragged = kb0 + SC::BK > cend;  // keys past the chunk in this block (uniform)
 #pragma unroll
     for (int ks = 0; ks < SC::BK / 32; ++ks) {
       float z[8];
       bool keep[8];
+      if (ragged || lg < -1.5f) {  // exact per key (vanishing decays, ragged block)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int key = kb0 + ks * 32 + (j < 4 ? 4 * g + j : 16 + 4 * g + j - 4);
-        keep[j] = key < cend;
-        z[j] = gpow((float)(cend - 1 - key), lg);
+        for (int j = 0; j < 8; ++j) {
+          const int key = kb0 + ks * 32 + (j < 4 ? 4 * g + j : 16 + 4 * g + j - 4);
+          keep[j] = key < cend;
+          z[j] = gpow((float)(cend - 1 - key), lg);
+        }
+      } else {
+        const float zs = gpow((float)(cend - 1 - kb0 - ks * 32), lg);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          keep[j] = true;
+          z[j] = zs * zl[j];
+        }
       }
       frag_t<T> af[SC::RB];
-      const bool ragged = kb0 + SC::BK > cend;  // keys past the chunk in this block (uniform)
 #pragma unroll
       for (int a = 0; a < SC::RB; ++a) {
-        af[a] = tile_col8<typename SC::KT>(kt, ks * 32, wave * (D / 4) + 16 * a, lane, (T*)nullptr);
+        af[a] = tile_col8<typename SC::KT>(kt, ks * 32, wave * (SC::ROWS / 4) + 16 * a, lane, (T*)nullptr);
         if (ragged)
           scale_frag(af[a], z, keep);
         else
           scale_frag(af[a], z);
       }
-      constexpr int NT = SC::NB;
       auto vload = [&](int t) __attribute__((always_inline)) {
-        return tile_col8<typename SC::VT>(vt, ks * 32, half * (D / SC::SPLIT) + t * 16, lane, (T*)nullptr);
+        return tile_col8<typename SC::VT>(vt, ks * 32, t * 16, lane, (T*)nullptr);
       };
       frag_t<T> vb[3];
       vb[0] = vload(0);
       vb[1] = vload(1);
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        if (t + 2 < NT) vb[(t + 2) % 3] = vload(t + 2);
+      for (int t = 0; t < SC::NB; ++t) {
+        if (t + 2 < SC::NB) vb[(t + 2) % 3] = vload(t + 2);
 #pragma unroll
         for (int a = 0; a < SC::RB; ++a) racc[a][t] = mma(af[a], vb[t % 3], racc[a][t]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
@@ -652,14 +687,14 @@ __device__ __forceinline__ void state_role(const FwdParams& p, int bh, int ci, i
 
   // R_i = g^b R_{i-1} + dR_i. The fp32 chain keeps R in this role's
   // accumulator layout (four contiguous floats per lane and fragment), so
-  // the next chunk's workgroup of the same half reads it back coalesced.
+  // the next chunk's workgroup reads it back coalesced.
   auto chain_frag = [&](int slot, int a, int nb) __attribute__((always_inline)) {
     return p.chain + ((int64_t)bh * 2 + slot) * D * D +
-           ((((half * 4 + wave) * SC::RB + a) * SC::NB + nb) * 64 + lane) * 4;
+           ((((part * 4 + wave) * SC::RB + a) * SC::NB + nb) * 64 + lane) * 4;
   };
   const float dec = gpow((float)(cend - c0), lg);
   if (ci > 0) {
-    wait_flag(flag_of(ci), p.ctrl + 1);
+    wait_flag(flag_of(ci, 0), p.ctrl + 1);
     const int slot = (ci - 1) & 1;
 #pragma unroll
     for (int a = 0; a < SC::RB; ++a)
@@ -676,15 +711,17 @@ __device__ __forceinline__ void state_role(const FwdParams& p, int bh, int ci, i
 #pragma unroll
       for (int nb = 0; nb < SC::NB; ++nb)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) racc[a][nb][j] += dec * S0[(int64_t)(dkw + 16 * a + j) * D + dv0 + nb * 16];
+        for (int j = 0; j < 4; ++j) racc[a][nb][j] += dec * S0[(int64_t)(dkl + 16 * a + j) * D + dvl + nb * 16];
   }
   if (ci + 1 < p.nchunks) {
+    // the next state workgroup needs only the chain: release it first
 #pragma unroll
     for (int a = 0; a < SC::RB; ++a)
 #pragma unroll
       for (int nb = 0; nb < SC::NB; ++nb) store4_coherent(chain_frag(ci & 1, a, nb), racc[a][nb]);
+    release_flag(flag_of(ci + 1, 0));
     write_snapshot(snap_next, racc);
-    release_flag(flag_of(ci + 1));
+    release_flag(flag_of(ci + 1, 1));
   } else if (p.state_out) {
     float* SO = p.state_out + (int64_t)bh * D * D;
 #pragma unroll
@@ -692,7 +729,7 @@ __device__ __forceinline__ void state_role(const FwdParams& p, int bh, int ci, i
 #pragma unroll
       for (int nb = 0; nb < SC::NB; ++nb)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) SO[(int64_t)(dkw + 16 * a + j) * D + dv0 + nb * 16] = racc[a][nb][j];
+        for (int j = 0; j < 4; ++j) SO[(int64_t)(dkl + 16 * a + j) * D + dvl + nb * 16] = racc[a][nb][j];
   }
 }
 
@@ -737,7 +774,7 @@ __global__ __launch_bounds__(256, 1) void retention_chunkwise_kernel(FwdParams p
   }
   __syncthreads();
   const int t = s_ticket;
-  int ci, bh, role;  // role < SPLIT: state half; else query block qblocks-1-(role-SPLIT)
+  int ci, bh, role;  // role < SPLIT: state part; else query block qblocks-1-(role-SPLIT)
   if (p.xcd_order) {
     // Class c owns the (sequence, head) pairs bh = 8j + c and takes them
     // chunk-major, role-major: every dependency stays inside the class, and
@@ -777,7 +814,7 @@ static hipError_t launch_fwd_impl(const Shape& s, int chunk, FwdParams p, bool c
     hipLaunchKernelGGL((retention_parallel_kernel<T, D, FAST>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
     return hipGetLastError();
   }
-  const int64_t nctrl = kCtrlHead + (int64_t)bhs * (p.nchunks + 1) * 2;
+  const int64_t nctrl = kCtrlHead + (int64_t)bhs * (p.nchunks + 1) * kFlagsPerChunk;
   hipLaunchKernelGGL(reset_ctrl_kernel, dim3((unsigned)((nctrl + 255) / 256 < 1024 ? (nctrl + 255) / 256 : 1024)),
                      dim3(256), 0, stream, p.ctrl, (int)nctrl);
   p.xcd_order = bhs % 8 == 0;
@@ -800,7 +837,7 @@ static hipError_t launch_fwd_t(const Shape& s, int chunk, FwdParams p, bool chun
 }
 
 size_t chunkwise_ctrl_bytes(int batch, int heads, int nchunks) {
-  return ((size_t)kCtrlHead + (size_t)batch * heads * (nchunks + 1) * 2) * sizeof(int);
+  return ((size_t)kCtrlHead + (size_t)batch * heads * (nchunks + 1) * kFlagsPerChunk) * sizeof(int);
 }
 
 hipError_t launch_retention_fwd(const Shape& s, int chunk, bool chunked, const void* q, const void* k, const void* v,

@@ -71,10 +71,10 @@ def test_status_strings(L):
 def test_workspace_sizes(L):
     d, _ = _desc(batch=2, seqlen=1000, heads=3, dk=128, dv=128)
     assert L.retention_parallel_workspace_bytes(ctypes.byref(d)) == 0
-    # control block (2 + batch*heads*(chunks+1)*2 ints) + fp32 state chain (2 slots per
+    # control block (16 + batch*heads*(chunks+1)*4 ints) + fp32 state chain (2 slots per
     # sequence and head) + per-chunk states in bf16, each rounded up to 256 bytes
     up = lambda x: (x + 255) // 256 * 256
-    ctrl = up((16 + 2 * 3 * 17 * 2) * 4)
+    ctrl = up((16 + 2 * 3 * 17 * 4) * 4)
     assert L.retention_chunkwise_workspace_bytes(ctypes.byref(d), 64) == (
         ctrl + up(2 * 3 * 2 * 128 * 128 * 4) + up(2 * 3 * 16 * 128 * 128 * 2))
     d, _ = _desc(batch=1, seqlen=10, heads=1, dk=64, dv=64, dtype=binding.RET_F32, rotary_base=10000.0)

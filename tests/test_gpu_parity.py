@@ -197,7 +197,8 @@ def test_chunkwise_handoff_completes(b, h):
     torch.cuda.synchronize()
     ctrl = ws[:64].view(torch.int32).cpu()
     nchunks = -(-n // chunk)
-    # two state workgroups and one 128-row output workgroup per (sequence, head, chunk)
+    # d/128 state workgroups (d = 256) and one output workgroup (up to 192
+    # rows) per (sequence, head, chunk)
     total = nchunks * b * h * (2 + 1)
     assert int(ctrl[0]) == total
     assert int(ctrl[1]) == 0
