@@ -30,6 +30,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMaxHeads = 128;
@@ -60,6 +61,52 @@ __device__ __forceinline__ f32x4 mma(const f32x8& a, const f32x8& b, f32x4 c) {
 }
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// ---------------------------------------------------------------------------
+// 32x32 tiles, contraction step 16 (checked on gfx950 hardware):
+//   lane l, n = l % 32, h = l / 32
+//     A fragment: A[n][k0 + 8h + j]   j = 0..7
+//     B fragment: B[k0 + 8h + j][n]
+//     C/D accum:  C[8(i/4) + 4h + (i%4)][n]   i = 0..15
+//   bf16 runs one v_mfma_f32_32x32x16_bf16, which issues at the full matrix
+//   rate from a single wave (the 16x16x32 form does not); fp32 runs eight
+//   v_mfma_f32_32x32x2_f32, instruction j pairing element j of both halves.
+// Column fragments (k down a column of a row-major tile) use the key order
+//   j = 0..3 -> row k0 + 4h + j,   j = 4..7 -> row k0 + 8 + 4h + (j - 4)
+// which is the row order of accumulator elements 0..7 (and, 16 rows on,
+// 8..15): a 32x32 accumulator feeds the next contraction as two fragments
+// without leaving its lanes.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ f32x16 mma32(const bf16x8& a, const bf16x8& b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mma32(const f32x8& a, const f32x8& b, f32x16 c) {
+#pragma unroll
+  for (int s = 0; s < 8; ++s) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[s], b[s], c, 0, 0, 0);
+  return c;
+}
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+// accumulator elements 8 sl .. 8 sl + 7 as a fragment (rows 16 sl .. 16 sl + 15
+// in the column-fragment order)
+template <int SL>
+__device__ __forceinline__ bf16x8 acc_frag(const f32x16& c, bf16*) {
+  bf16x8 f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) f[j] = (bf16)c[8 * SL + j];
+  return f;
+}
+template <int SL>
+__device__ __forceinline__ f32x8 acc_frag(const f32x16& c, float*) {
+  f32x8 f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) f[j] = c[8 * SL + j];
+  return f;
+}
 
 // ---------------------------------------------------------------------------
 // 8-element vectors in registers, as fp32, loaded from / stored to T memory.
@@ -94,6 +141,27 @@ __device__ __forceinline__ void store8(bf16* p, const F8& v) {
 __device__ __forceinline__ void store8(float* p, const F8& v) {
   reinterpret_cast<float4*>(p)[0] = make_float4(v.x[0], v.x[1], v.x[2], v.x[3]);
   reinterpret_cast<float4*>(p)[1] = make_float4(v.x[4], v.x[5], v.x[6], v.x[7]);
+}
+
+// Four consecutive elements (8 bytes of bf16, 16 of fp32) to and from floats.
+__device__ __forceinline__ void load4(const bf16* p, float* v) {
+  const bf16x4 x = *reinterpret_cast<const bf16x4*>(p);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[e] = (float)x[e];
+}
+__device__ __forceinline__ void load4(const float* p, float* v) {
+  const f32x4 x = *reinterpret_cast<const f32x4*>(p);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[e] = x[e];
+}
+__device__ __forceinline__ void store4(bf16* p, const float* v) {
+  bf16x4 x;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) x[e] = (bf16)v[e];
+  *reinterpret_cast<bf16x4*>(p) = x;
+}
+__device__ __forceinline__ void store4(float* p, const float* v) {
+  *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
 }
 
 __device__ __forceinline__ void store8_zero(bf16* p) { *reinterpret_cast<uint4*>(p) = make_uint4(0, 0, 0, 0); }
@@ -344,6 +412,21 @@ __device__ __forceinline__ void async_tile(char* lds, const T* g, int64_t gstrid
   }
 }
 
+// A contiguous block of BYTES (a multiple of 1 KiB) copied into LDS by NW
+// waves, one 16-byte chunk per lane and load.
+template <typename T, int BYTES, int NW, int CPOL = 0>
+__device__ __forceinline__ void async_flat(char* lds, const T* g, int wave, int lane) {
+  static_assert(BYTES % 1024 == 0, "whole wave-wide loads");
+  constexpr int NINST = BYTES / 1024;
+#pragma unroll
+  for (int m = 0; m < (NINST + NW - 1) / NW; ++m) {
+    const int n = wave + m * NW;  // wave-uniform
+    if (NINST % NW != 0 && n >= NINST) break;
+    const T* src = g + (uint32_t)((n * 64 + lane) * (16 / (int)sizeof(T)));
+    __builtin_amdgcn_global_load_lds(src, (lds_void*)(lds + n * 1024), 16, 0, CPOL);
+  }
+}
+
 // Row fragment: elements (r, col .. col+7).
 template <typename TL>
 __device__ __forceinline__ bf16x8 tile_row8(const char* t, int r, int col, bf16*) {
@@ -381,6 +464,34 @@ __device__ __forceinline__ f32x8 tile_col8(const char* t, int k0, int n0, int la
   return f;
 }
 
+// Column fragment for 32x32 tiles: lane (n = l%32, h = l/32) receives rows
+// k0 + {4h..4h+3, 8+4h..8+4h+3} of column n0 + n. bf16: per 16-lane group
+// (h = group/2, 16 columns from n0 + 16 (group%2)) lane m fetches 4 elements
+// of row k0 + 4h + m/4 at column 4(m%4), and the transpose read hands lane m
+// column m of those four rows; a second read 8 rows on gives the rest.
+template <typename TL>
+__device__ __forceinline__ bf16x8 tile_col8w(const char* t, int k0, int n0, int lane, bf16*) {
+  const int grp = lane >> 4, m = lane & 15, h = grp >> 1;
+  const char* p = t + TL::off(k0 + 4 * h + (m >> 2), n0 + 16 * (grp & 1) + 4 * (m & 3));
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 8 * TL::ROWB));
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  const i16x8 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, w);
+}
+template <typename TL>
+__device__ __forceinline__ f32x8 tile_col8w(const char* t, int k0, int n0, int lane, float*) {
+  const int n = lane & 31, h = lane >> 5;
+  const char* p = t + TL::off(k0 + 4 * h, n0 + n);
+  f32x8 f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    f[j] = *reinterpret_cast<const float*>(p + j * TL::ROWB);
+    f[4 + j] = *reinterpret_cast<const float*>(p + (8 + j) * TL::ROWB);
+  }
+  return f;
+}
+
 // ---------------------------------------------------------------------------
 // Reductions.
 // ---------------------------------------------------------------------------
@@ -398,6 +509,9 @@ __device__ __forceinline__ float sum16(float x) {
   x += dpp<0x140>(x);
   return x;
 }
+
+// Sum of the two lanes l and l ^ 32.
+__device__ __forceinline__ float sum_pair32(float x) { return x + __shfl_xor(x, 32, 64); }
 
 __device__ __forceinline__ float sum64(float x) {
   x += __shfl_xor(x, 1, 64);

@@ -41,28 +41,22 @@ template <typename T, int D, bool FAST = true>
 struct OutTile {
   static constexpr int E = sizeof(T);
   static constexpr int WAVES = 4;
-  // Query rows per wave, in groups of 16: 48 rows for bf16 on the fast path
-  // (the wave's fp32 output tile, 48 x D, and its query fragments stay in
-  // registers with room for the fragment pipeline), 32 otherwise (fp32
-  // fragments take twice the registers). Every K and V fragment read from
-  // LDS feeds QG products. Group i of wave w holds rows 16 (w + WAVES i) ..
-  // +15 of the block: every wave spans the whole block, so the causal work is
-  // shared evenly.
-  static constexpr int QG = E == 2 && FAST ? 3 : 2;
-  static constexpr int QW = 16 * QG;
-  static constexpr int BM = WAVES * QW;
+  static constexpr int QW = 32;                // query rows per wave: one 32-row tile
+  static constexpr int BM = WAVES * QW;        // query rows per workgroup
   static constexpr int BN = E == 2 ? 64 : 32;  // keys per block
-  static constexpr int K2 = BN / 32;           // 32-key steps per key block
-  static constexpr int KS = D / 32;            // contraction steps over dk
-  static constexpr int NB = D / 16;            // 16-wide output column blocks
+  static constexpr int KH = BN / 32;           // 32-key steps per block
+  static constexpr int KS = D / 16;            // contraction steps over dk
+  static constexpr int NT = D / 32;            // 32-wide dv tiles
   // dk columns per R^T slice; the slices stream through the two stages
   static constexpr int RS = D / 2 < 256 / E ? D / 2 : 256 / E;
   static constexpr int NRS = D / RS;
   using KT = PTile<T, BN, D, 16>;   // K block, row fragments
-  using VT = PTile<T, BN, D, 32>;   // V block, column (transpose) fragments
-  using RT = PTile<T, D, RS, 16>;   // R^T slice (dv rows x RS dk), row fragments
+  using VT = PTile<T, BN, D, 64>;   // V block, column (transpose) fragments
+  // R^T slice: RS dk columns x D dv rows, stored (in HBM and LDS alike) in
+  // fragment order: [dk step s][dv tile t][lane][8 elements], lane (n, h)
+  // holding R^T[32 t + n][16 s + 8 h .. +7] -- the A operand of the cross term
+  static constexpr int RT_BYTES = RS * D * E;
   static constexpr int KVB = KT::BYTES + VT::BYTES;
-  static constexpr int YSTR = D + 4;  // epilogue rows (fp32), two waves per stage buffer
 };
 
 // Fast path: with a reference row r0 (the row before the chunk, or before the
@@ -70,25 +64,27 @@ struct OutTile {
 //     g^(q-k) = g^(q - r0) * g^(r0 - k):
 // the products P' = S g^(r0 - k) accumulate O' = P' V (+ Q R_{i-1}, whose row
 // scale xi_q = g^(q - r0) is then the same row factor), and O = g^(q - r0) O'.
-// Keys reach at most kFastSpan rows past r0, so |log2 g| * span <= 64 keeps
-// every factor within 2^+-64 (factors of far keys underflow towards zero,
-// which is what they are worth).
+// Keys reach at most one span past r0, so |log2 g| * span <= 64 keeps every
+// factor within 2^+-64 (factors of far keys underflow towards zero, which is
+// what they are worth).
 constexpr double kFastSpanLog2 = 64.0;
 
 template <typename T, int D>
 struct StTile {
   // State workgroups per chunk: one per 128 dk rows of R (one for D <= 128).
-  // The four waves split the workgroup's rows; each holds its rows x D of R
-  // in fp32 registers. Fewer rows per workgroup shorten the serial chunk-to-
-  // chunk hand-off; more rows cost fewer K reads per chunk.
+  // The four waves split dv; each holds the workgroup's rows x D/4 columns of
+  // R in fp32 registers. Fewer rows per workgroup shorten the serial chunk-
+  // to-chunk hand-off; more rows cost fewer K reads per chunk.
   static constexpr int SPLIT = D > 128 ? D / 128 : 1;
   static constexpr int ROWS = D / SPLIT;        // dk rows per workgroup
   static constexpr int BK = OutTile<T, D>::BN;  // keys per block
-  static constexpr int RB = ROWS / 64;          // 16-row dk blocks per wave
-  static constexpr int NB = D / 16;             // 16-wide dv blocks
-  using KT = PTile<T, BK, ROWS, 32>;            // this workgroup's dk columns of K (K^T operand)
-  using VT = PTile<T, BK, D, 32>;               // V block, column fragments
+  static constexpr int MT = ROWS / 32;          // 32-row dk tiles per wave
+  static constexpr int NTW = D / 128 > 0 ? D / 128 : 1;  // 32-wide dv tiles per wave
+  static constexpr int DVW = 32 * NTW;          // dv columns per wave
+  using KT = PTile<T, BK, ROWS, 64>;            // this workgroup's dk columns of K (K^T operand)
+  using VT = PTile<T, BK, D, 64>;               // V block, column fragments
   static constexpr int KVB = KT::BYTES + VT::BYTES;
+  static_assert(4 * DVW >= D, "the waves cover every dv column");
 };
 // per (sequence, head, chunk j) and state part q two ready flags: rows of
 // R_{j-1} in the fp32 chain (for chunk j's state workgroup of part q) and in
@@ -100,9 +96,8 @@ template <typename T, int D>
 struct Stage {
   using O = OutTile<T, D>;
   using S = StTile<T, D>;
-  static constexpr int A = O::KVB > O::RT::BYTES ? O::KVB : O::RT::BYTES;
+  static constexpr int A = O::KVB > O::RT_BYTES ? O::KVB : O::RT_BYTES;
   static constexpr int BYTES = A > S::KVB ? A : S::KVB;
-  static_assert(2 * 16 * O::YSTR * 4 <= BYTES, "epilogue buffer");
 };
 
 struct FwdParams {
@@ -113,7 +108,7 @@ struct FwdParams {
   void* o;
   const float* state_in;
   float* state_out;
-  void* snap;    // [BH][nchunks][dv][dk] of T: R_{i-1}^T for chunk i
+  void* snap;    // [BH][nchunks][D*D] of T: R_{i-1}^T for chunk i (output fragment order)
   float* chain;  // [BH][2][D*D] fp32: R_i handed to the next state workgroup (fragment order)
   int* ctrl;     // [0] count, [1] error, [8..15] tickets, [16 + (bh*(nchunks+1) + i)*4 + kind*2 + part]: R_{i-1} ready
   int batch, seqlen, heads, chunk, nchunks, qblocks;
@@ -189,10 +184,9 @@ template <typename T, int D, bool FAST>
 __device__ __forceinline__ void out_role(const FwdParams& p, int bh, int ci, int qb, bool chunked, char* stage0,
                                          char* stage1) {
   using C = OutTile<T, D, FAST>;
-  constexpr int QG = C::QG;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g = lane >> 4, c = lane & 15;
+  const int n = lane & 31, hh = lane >> 5;  // column / half of the 32x32 layout
 
   const int h = bh % p.heads, b = bh / p.heads;
   const int c0 = ci * p.chunk;
@@ -210,8 +204,8 @@ __device__ __forceinline__ void out_role(const FwdParams& p, int bh, int ci, int
   const T* G = p.g ? reinterpret_cast<const T*>(p.g) + head0 : nullptr;
   T* O = reinterpret_cast<T*>(p.o) + head0;
 
-  // first row of this wave's group i
-  auto grow = [&](int i) __attribute__((always_inline)) { return q0 + 16 * (wave + C::WAVES * i); };
+  const int qw0 = q0 + wave * C::QW;     // first row of this wave
+  const int qrow = qw0 + n;              // this lane's query row
   const int kend = min(q0 + C::BM, cend);
   const int nkb = (kend - c0 + C::BN - 1) / C::BN;
 
@@ -230,110 +224,89 @@ __device__ __forceinline__ void out_role(const FwdParams& p, int bh, int ci, int
 #pragma unroll
       for (int q = 0; q < StTile<T, D>::SPLIT; ++q) wait_flag(flags + q, p.ctrl + 1);
     }
-    async_tile<T, typename C::RT, C::WAVES, kCoherent>(buf, R + sl * C::RS, D, 0, D - 1, wave, lane);
+    async_flat<T, C::RT_BYTES, C::WAVES, kCoherent>(buf, R + (int64_t)sl * C::RS * D, wave, lane);
   };
   issue_kv(0, stage0);
 
-  // Query fragments, kept in registers for the whole workgroup life. Rows
-  // past the chunk load a clamped in-range row: their outputs are never
-  // stored.
-  frag_t<T> qf[QG][C::KS];
+  // Query fragments of this lane's row, kept in registers for the whole
+  // workgroup life: qf[s] = Q[qrow][16 s + 8 hh .. +7]. Rows past the chunk
+  // load a clamped in-range row: their outputs are never stored.
+  frag_t<T> qf[C::KS];
+  {
+    const T* qr = Q + (int64_t)min(qrow, cend - 1) * tstride + 8 * hh;
 #pragma unroll
-  for (int i = 0; i < QG; ++i) {
-    const int row = min(grow(i) + c, cend - 1);
-#pragma unroll
-    for (int s = 0; s < C::KS; ++s)
-      qf[i][s] = to_frag(unpack8(ld_raw8(Q + row * tstride + s * 32 + 8 * g)), (T*)nullptr);
+    for (int s = 0; s < C::KS; ++s) qf[s] = to_frag(unpack8(ld_raw8(qr + 16 * s)), (T*)nullptr);
   }
 
-  f32x4 oacc[QG][C::NB];
+  // O^T accumulators: oacc[t] element i is O'[qrow][32 t + 8 (i/4) + 4 hh + i%4]
+  f32x16 oacc[C::NT];
 #pragma unroll
-  for (int i = 0; i < QG; ++i)
-#pragma unroll
-    for (int nb = 0; nb < C::NB; ++nb) oacc[i][nb] = zero4();
+  for (int t = 0; t < C::NT; ++t) oacc[t] = zero16();
 
-  // Intra-chunk term (Q K^T (.) D) V over key blocks up to the diagonal, 32
-  // keys at a time: S^T = K Q^T for 16 keys per group, decay and causal
-  // mask, then O += P V. Only groups 0 .. HI-1 hold rows of the chunk. The K
-  // and V fragments of a 32-key step form one sequence of LDS reads with a
-  // two-deep prefetch ring.
-  constexpr int U = 2 * C::KS + C::NB;  // fragment reads per 32-key step
-  float bkl[4];  // g^-(4 g + e): this lane's part of the per-key factors
+  // per-key decay factors of the fast path, this lane's part:
+  // g^-(8 (i/4) + 4 hh + i%4) for accumulator element i
+  float bkl[16];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) bkl[e] = FAST ? gpow(-(float)(4 * g + e), lg) : 0.f;
-  auto key_block = [&](auto hi_c, int kb0, const char* kt) __attribute__((always_inline)) {
-    constexpr int HI = decltype(hi_c)::value;
+  for (int i = 0; i < 16; ++i) bkl[i] = FAST ? gpow(-(float)(8 * (i / 4) + 4 * hh + (i % 4)), lg) : 0.f;
+
+  // Intra-chunk term over key blocks up to the diagonal, 32 keys at a time:
+  // S^T = K Q^T (16 products), decay and causal mask, then O^T += V^T P^T
+  // (NT x 2 products). The K and V fragments of a step form one sequence of
+  // LDS reads with a two-deep prefetch ring.
+  constexpr int U = C::KS + 2 * C::NT;  // fragment reads per 32-key step
+  auto key_block = [&](int kb0, const char* kt) __attribute__((always_inline)) {
+    if (kb0 > qw0 + C::QW - 1) return;  // block above this wave's rows (uniform)
     const char* vt = kt + C::KT::BYTES;
-    const bool diag = kb0 + C::BN - 1 > q0;  // some key may follow some row (uniform)
+    const bool diag = kb0 + C::BN - 1 > qw0;  // some key may follow some row (uniform)
     auto load = [&](auto t_c) __attribute__((always_inline)) {
       constexpr int t = decltype(t_c)::value, kh = t / U, u = t % U;
-      if constexpr (u < 2 * C::KS)  // key group 2 kh + u % 2, contraction step u / 2
-        return tile_row8<typename C::KT>(kt, (2 * kh + u % 2) * 16 + c, (u / 2) * 32 + 8 * g, (T*)nullptr);
-      else
-        return tile_col8<typename C::VT>(vt, kh * 32, (u - 2 * C::KS) * 16, lane, (T*)nullptr);
+      if constexpr (u < C::KS)  // K rows 32 kh + n, dk 16 u + 8 hh
+        return tile_row8<typename C::KT>(kt, 32 * kh + n, 16 * u + 8 * hh, (T*)nullptr);
+      else  // V keys 32 kh + 16 (u' % 2) + {..}, dv 32 (u' / 2) + n
+        return tile_col8w<typename C::VT>(vt, 32 * kh + 16 * ((u - C::KS) % 2), 32 * ((u - C::KS) / 2), lane,
+                                          (T*)nullptr);
     };
     frag_t<T> ring[3];
     ring[0] = load(std::integral_constant<int, 0>{});
     ring[1] = load(std::integral_constant<int, 1>{});
-    f32x4 st[QG][2];
-    frag_t<T> pf[QG];
-    static_for<C::K2 * U>([&](auto t_c) __attribute__((always_inline)) {
+    f32x16 st;
+    frag_t<T> pf[2];
+    static_for<C::KH * U>([&](auto t_c) __attribute__((always_inline)) {
       constexpr int t = decltype(t_c)::value, kh = t / U, u = t % U;
-      if constexpr (t + 2 < C::K2 * U) ring[(t + 2) % 3] = load(std::integral_constant<int, t + 2>{});
-      if constexpr (u < 2 * C::KS) {
-        // the two 16-key groups of the step alternate, so that consecutive
-        // products go to different accumulators
-        constexpr int k2 = u % 2, s = u / 2;
-        if constexpr (s == 0) {
+      if constexpr (t + 2 < C::KH * U) ring[(t + 2) % 3] = load(std::integral_constant<int, t + 2>{});
+      if constexpr (u < C::KS) {
+        if constexpr (u == 0) st = zero16();
+        st = mma32(ring[t % 3], qf[u], st);
+        if constexpr (u == C::KS - 1) {
+          // decay g^(q-k) and causal mask; element i is key kb0 + 32 kh + k_i
+          const int kk0 = kb0 + 32 * kh;
+          if constexpr (FAST) {
+            const float sb = gpow((float)(ref - kk0), lg);  // g^(r0 - kk0), uniform
+            if (diag) {
 #pragma unroll
-          for (int i = 0; i < HI; ++i) st[i][k2] = zero4();
-        }
-#pragma unroll
-        for (int i = 0; i < HI; ++i) st[i][k2] = mma(ring[t % 3], qf[i][s], st[i][k2]);
-        if constexpr (u == 2 * C::KS - 1) {
-          // decay g^(q-k) and causal mask over the 32 keys, which become P;
-          // only the diagonal blocks need the mask
-#pragma unroll
-          for (int h2 = 0; h2 < 2; ++h2) {
-            const int k0 = 32 * kh + 16 * h2 + 4 * g;  // key - kb0 of element 0
-            if constexpr (FAST) {
-              // g^(r0 - k) = g^(r0 - kb0 - 32 kh - 16 h2) * g^-(4 g + e)
-              const float sb = gpow((float)(ref - kb0 - 32 * kh - 16 * h2), lg);
-              float bk[4];
-#pragma unroll
-              for (int e = 0; e < 4; ++e) bk[e] = sb * bkl[e];
-              if (diag) {
-#pragma unroll
-                for (int i = 0; i < HI; ++i)
-#pragma unroll
-                  for (int e = 0; e < 4; ++e) {
-                    const float val = st[i][h2][e] * bk[e];
-                    st[i][h2][e] = grow(i) + c - kb0 < k0 + e ? 0.f : val;
-                  }
-              } else {
-#pragma unroll
-                for (int i = 0; i < HI; ++i)
-#pragma unroll
-                  for (int e = 0; e < 4; ++e) st[i][h2][e] *= bk[e];
+              for (int i = 0; i < 16; ++i) {
+                const int key = kk0 + 8 * (i / 4) + 4 * hh + (i % 4);
+                const float val = st[i] * (sb * bkl[i]);
+                st[i] = qrow < key ? 0.f : val;
               }
             } else {
 #pragma unroll
-              for (int i = 0; i < HI; ++i)
+              for (int i = 0; i < 16; ++i) st[i] *= sb * bkl[i];
+            }
+          } else {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                  const int dist = grow(i) + c - kb0 - k0 - e;
-                  const float val = st[i][h2][e] * gpow((float)dist, lg);
-                  st[i][h2][e] = dist < 0 ? 0.f : val;
-                }
+            for (int i = 0; i < 16; ++i) {
+              const int dist = qrow - (kk0 + 8 * (i / 4) + 4 * hh + (i % 4));
+              const float val = st[i] * gpow((float)dist, lg);
+              st[i] = dist < 0 ? 0.f : val;
             }
           }
-#pragma unroll
-          for (int i = 0; i < HI; ++i) pf[i] = acc_to_frag(st[i][0], st[i][1], (T*)nullptr);
+          pf[0] = acc_frag<0>(st, (T*)nullptr);
+          pf[1] = acc_frag<1>(st, (T*)nullptr);
         }
       } else {
-        constexpr int nb = u - 2 * C::KS;
-#pragma unroll
-        for (int i = 0; i < HI; ++i) oacc[i][nb] = mma(pf[i], ring[t % 3], oacc[i][nb]);
+        constexpr int v = u - C::KS, tt = v / 2, sl = v % 2;
+        oacc[tt] = mma32(ring[t % 3], pf[sl], oacc[tt]);
       }
       // keep each step's prefetch where it is: two steps ahead of its use
       __builtin_amdgcn_sched_barrier(0);
@@ -353,77 +326,49 @@ __device__ __forceinline__ void out_role(const FwdParams& p, int bh, int ci, int
     else if (cross)
       issue_slice(0, nxt);
   };
-  auto key_loop = [&](auto hi_c) __attribute__((always_inline)) {
-    for (int j = 0; j < nkb; j += 2) {
-      sync_and_prefetch(j, stage1);
-      key_block(hi_c, c0 + j * C::BN, stage0);
-      if (j + 1 < nkb) {
-        sync_and_prefetch(j + 1, stage0);
-        key_block(hi_c, c0 + (j + 1) * C::BN, stage1);
-      }
+  for (int j = 0; j < nkb; j += 2) {
+    sync_and_prefetch(j, stage1);
+    key_block(c0 + j * C::BN, stage0);
+    if (j + 1 < nkb) {
+      sync_and_prefetch(j + 1, stage0);
+      key_block(c0 + (j + 1) * C::BN, stage1);
     }
-  };
-  // groups that hold rows of the chunk (group i starts at row 64 i of the block)
-  const int hi = min(QG, (cend - q0 + 16 * C::WAVES - 1) / (16 * C::WAVES));
-  static_assert(QG == 2 || QG == 3, "two or three row groups per wave");
-  if (hi == QG)
-    key_loop(std::integral_constant<int, QG>{});
-  else if (hi == QG - 1)
-    key_loop(std::integral_constant<int, QG - 1>{});
-  else
-    key_loop(std::integral_constant<int, 1>{});
+  }
 
-  // Gate values, one 16-row group at a time (8-value groups per lane).
-  constexpr int EI = 16 * (D / 8) / 64;
-  auto load_gate = [&](int i, Raw8<T> (&dst)[EI]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int e = 0; e < EI; ++e) {
-      const int idx = lane + 64 * e;
-      const int r = idx / (D / 8), c8 = idx % (D / 8);
-      const int tok = min(grow(i) + r, cend - 1);
-      dst[e] = ld_raw8(G + tok * tstride + c8 * 8);
-    }
-  };
-
-  // Cross-chunk term, added last. Fast path: O' += Q R_{i-1} (its row scale
+  // Cross-chunk term, added last. Fast path: O'^T += R^T Q^T (its row scale
   // xi is the final row factor). Otherwise O = xi (.) (O_intra / xi + Q R):
-  // rows whose xi is below 2^-100 skip it (their Q fragment is zeroed, their
-  // scale is 1), the term being far below fp32 resolution there. The R^T
+  // a row whose xi is below 2^-100 skips it (its Q fragments are zeroed and
+  // its scale is 1), the term being far below fp32 resolution there. The R^T
   // slices stream through the two stages, the first one already in flight.
   if (cross) {
-    float inv[QG][4];
+    float inv = 1.f;
     if constexpr (!FAST) {
+      const float xi = gpow((float)(qrow - c0 + 1), lg);
+      if (xi >= 7.888609e-31f) {
+        inv = __builtin_amdgcn_rcpf(xi);
+      } else {
 #pragma unroll
-      for (int i = 0; i < QG; ++i) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float xi = gpow((float)(grow(i) + 4 * g + e - c0 + 1), lg);
-          inv[i][e] = xi >= 7.888609e-31f ? __builtin_amdgcn_rcpf(xi) : 1.f;
-#pragma unroll
-          for (int nb = 0; nb < C::NB; ++nb) oacc[i][nb][e] *= inv[i][e];
-        }
-        const float xq = gpow((float)(grow(i) + c - c0 + 1), lg);
-        if (!(xq >= 7.888609e-31f)) {
-#pragma unroll
-          for (int s = 0; s < C::KS; ++s) qf[i][s] = zero_frag<T>();
-        }
+        for (int s = 0; s < C::KS; ++s) qf[s] = zero_frag<T>();
       }
+#pragma unroll
+      for (int t = 0; t < C::NT; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[t][i] *= inv;
     }
     auto cross_slice = [&](auto sl_c, const char* buf) __attribute__((always_inline)) {
       constexpr int SL = decltype(sl_c)::value;
-      constexpr int NT = (C::RS / 32) * C::NB;
-      auto rload = [&](int t) __attribute__((always_inline)) {
-        return tile_row8<typename C::RT>(buf, (t % C::NB) * 16 + c, (t / C::NB) * 32 + 8 * g, (T*)nullptr);
+      constexpr int SS = C::RS / 16;  // dk steps per slice
+      constexpr int NTT = SS * C::NT;
+      auto rload = [&](int t) __attribute__((always_inline)) {  // step t / NT, dv tile t % NT
+        return *reinterpret_cast<const frag_t<T>*>(buf + (t * 64 + lane) * (int)sizeof(frag_t<T>));
       };
       frag_t<T> rb[3];
       rb[0] = rload(0);
       rb[1] = rload(1);
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        if (t + 2 < NT) rb[(t + 2) % 3] = rload(t + 2);
-#pragma unroll
-        for (int i = 0; i < QG; ++i)
-          oacc[i][t % C::NB] = mma(qf[i][SL * (C::RS / 32) + t / C::NB], rb[t % 3], oacc[i][t % C::NB]);
+      for (int t = 0; t < NTT; ++t) {
+        if (t + 2 < NTT) rb[(t + 2) % 3] = rload(t + 2);
+        oacc[t % C::NT] = mma32(rb[t % 3], qf[SL * SS + t / C::NT], oacc[t % C::NT]);
         __builtin_amdgcn_sched_barrier(0);
       }
     };
@@ -450,86 +395,56 @@ __device__ __forceinline__ void out_role(const FwdParams& p, int bh, int ci, int
     else
       slices(stage0, stage1);
     if constexpr (!FAST) {
+      const float xi = inv == 1.f ? 1.f : gpow((float)(qrow - c0 + 1), lg);
 #pragma unroll
-      for (int i = 0; i < QG; ++i)
+      for (int t = 0; t < C::NT; ++t)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float xi = inv[i][e] == 1.f ? 1.f : gpow((float)(grow(i) + 4 * g + e - c0 + 1), lg);
-#pragma unroll
-          for (int nb = 0; nb < C::NB; ++nb) oacc[i][nb][e] *= xi;
-        }
+        for (int i = 0; i < 16; ++i) oacc[t][i] *= xi;
     }
   }
 
-  // Epilogue: GroupNorm over dv per (token, head), swish gate, store. Each
-  // wave stages one 16-row group at a time through its own LDS area to turn
-  // the accumulator layout into row-contiguous stores. The gate of the next
-  // group loads while the current one is processed (bf16; fp32 gates take
-  // twice the registers and load per group).
-  constexpr bool kGatePipe = sizeof(T) == 2;
-  Raw8<T> gbuf[kGatePipe ? 2 : 1][EI];
-  if (kGatePipe && G) load_gate(0, gbuf[0]);
-  __syncthreads();  // every wave is done with the stages
-  float* yw = reinterpret_cast<float*>(wave < 2 ? stage0 : stage1) + (wave & 1) * 16 * C::YSTR;
+  // Epilogue, in registers: each lane holds half of one query row (the other
+  // half is in lane ^ 32). GroupNorm over dv per (token, head) -- with the
+  // fast path's row factor f: GN(f o') = (o' - mean') f / sqrt(f^2 var' + eps)
+  // -- then the swish gate and 4-element stores.
+  const float f = FAST ? gpow((float)(qrow - ref), lg) : 1.f;
+  float mean = 0.f, scale = f;
+  if (G) {
+    float s1 = 0.f;
 #pragma unroll
-  for (int i = 0; i < QG; ++i) {
-    Raw8<T>(&gq)[EI] = gbuf[kGatePipe ? (i & 1) : 0];
-    if (G) {
-      if constexpr (kGatePipe) {
-        if (i + 1 < QG) load_gate(i + 1, gbuf[(i + 1) & 1]);
-      } else {
-        load_gate(i, gq);
+    for (int t = 0; t < C::NT; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s1 += oacc[t][i];
+    mean = sum_pair32(s1) * (1.0f / D);
+    float s2 = 0.f;
+#pragma unroll
+    for (int t = 0; t < C::NT; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float d = oacc[t][i] - mean;
+        s2 += d * d;
       }
-    }
-    // row factor of the fast path (1 otherwise): o = f o'. GroupNorm of f o'
-    // is (o' - mean') f / sqrt(f^2 var' + eps), so the statistics are taken
-    // on o' and the factor joins the scale.
-    float mean[4], rstd[4];
+    scale = f * rsqrtf(f * f * (sum_pair32(s2) * (1.0f / D)) + p.eps);
+  }
+  if (qrow < cend) {
+    T* orow = O + (int64_t)qrow * tstride + 4 * hh;
+    const T* grow_ = G ? G + (int64_t)qrow * tstride + 4 * hh : nullptr;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float f = FAST ? gpow((float)(grow(i) + 4 * g + e - ref), lg) : 1.f;
-      mean[e] = 0.f;
-      rstd[e] = f;
-      if (G) {
-        float s = 0.f;
+    for (int t = 0; t < C::NT; ++t)
 #pragma unroll
-        for (int nb = 0; nb < C::NB; ++nb) s += oacc[i][nb][e];
-        mean[e] = sum16(s) * (1.0f / D);
-        float s2 = 0.f;
+      for (int a = 0; a < 4; ++a) {
+        const int col = 32 * t + 8 * a;  // + 4 hh + e
+        float y[4];
 #pragma unroll
-        for (int nb = 0; nb < C::NB; ++nb) {
-          const float d = oacc[i][nb][e] - mean[e];
-          s2 += d * d;
+        for (int e = 0; e < 4; ++e) y[e] = (oacc[t][4 * a + e] - mean) * scale;
+        if (G) {
+          float gv[4];
+          load4(grow_ + col, gv);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) y[e] *= swish(gv[e]);
         }
-        rstd[e] = f * rsqrtf(f * f * (sum16(s2) * (1.0f / D)) + p.eps);
+        store4(orow + col, y);
       }
-    }
-#pragma unroll
-    for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) yw[(4 * g + e) * C::YSTR + nb * 16 + c] = (oacc[i][nb][e] - mean[e]) * rstd[e];
-    // the slab is private to this wave: its own LDS writes are done before
-    // it reads them back
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int e = 0; e < EI; ++e) {
-      const int idx = lane + 64 * e;
-      const int r = idx / (D / 8), c8 = idx % (D / 8);
-      const int tok = grow(i) + r;
-      const float* yp = yw + r * C::YSTR + c8 * 8;
-      const f32x4 ya = reinterpret_cast<const f32x4*>(yp)[0];
-      const f32x4 yb = reinterpret_cast<const f32x4*>(yp)[1];
-      F8 y{{ya[0], ya[1], ya[2], ya[3], yb[0], yb[1], yb[2], yb[3]}};
-      if (G) {
-        const F8 gv = unpack8(gq[e]);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) y.x[k] *= swish(gv.x[k]);
-      }
-      if (tok < cend) store8(O + tok * tstride + c8 * 8, y);
-    }
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // the slab's reads are done before it is rewritten
-    __builtin_amdgcn_wave_barrier();
   }
 }
 
@@ -557,18 +472,18 @@ __device__ __forceinline__ void state_issue(char* buf, const T* K, const T* V, i
 }
 
 // State role: rows dk0 .. dk0+ROWS-1 (dk0 = ROWS part) of R_i for one chunk
-// of one (sequence, head). Accumulates
-// dR = K^T (V (.) zeta) over the chunk's keys, waits for R_{i-1} in the fp32
-// chain from the previous chunk's workgroup, forms R_i = g^b R_{i-1} + dR,
-// hands it on in the chain and then publishes its snapshot R_i^T for the next
-// chunk's output workgroups.
+// of one (sequence, head). Accumulates dR = K^T (V (.) zeta) over the chunk's
+// keys, waits for those rows of R_{i-1} in the fp32 chain from the previous
+// chunk's workgroup, forms R_i = g^b R_{i-1} + dR, hands it on in the chain
+// and then publishes its snapshot R_i^T for the next chunk's output
+// workgroups. Wave w owns dv columns w DVW .. +DVW-1 of the rows.
 template <typename T, int D>
 __device__ __forceinline__ void state_role(const FwdParams& p, int bh, int ci, int part, char* stage0,
                                            char* stage1) {
   using SC = StTile<T, D>;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g = lane >> 4, c = lane & 15;
+  const int n = lane & 31, hh = lane >> 5;
   const int h = bh % p.heads, b = bh / p.heads;
   const float lg = p.log2g[h];
   const int c0 = ci * p.chunk;
@@ -583,91 +498,103 @@ __device__ __forceinline__ void state_role(const FwdParams& p, int bh, int ci, i
   auto flag_of = [&](int j, int kind) __attribute__((always_inline)) {
     return p.ctrl + kCtrlHead + (bh * (p.nchunks + 1) + j) * kFlagsPerChunk + kind * kMaxSplit + part;
   };
-
-  // accumulator element (a, nb, j) of lane (g, c) is R[dk][dv] with
-  const int dkl = dk0 + wave * (SC::ROWS / 4) + 4 * g;  // + 16 a + j
-  const int dvl = c;                        // + 16 nb
+  // rows 4 hh + {0..3} + 8 a (a = 0..3) of dk tile mt hold accumulator elements
+  // 4a .. 4a+3; the columns are dv = dvw + 32 nt + n
+  const int dvw = wave * SC::DVW;
+  const bool active = dvw < D;  // every wave has columns when 4 DVW == D (uniform)
+  auto dk_of = [&](int mt, int a) __attribute__((always_inline)) { return dk0 + 32 * mt + 8 * a + 4 * hh; };
   T* snap_next = reinterpret_cast<T*>(p.snap) + ((int64_t)bh * p.nchunks + ci + 1) * D * D;
-  auto write_snapshot = [&](T* sn, const f32x4 (&acc)[SC::RB][SC::NB]) __attribute__((always_inline)) {
+  // Snapshot R^T in the output role's fragment order (see OutTile): the 4
+  // values of (tile mt, nt, row group a) of lane (n, hh) are rows
+  // dk = 16 S + 8 (a%2) + 4 hh + e of column dv = 32 t + n, i.e. half hh of
+  // the fragment of lane (n, a%2) at step S, tile t. One store per lane writes
+  // 8 bytes; a wave writes 512 contiguous bytes.
+  using OT = OutTile<T, D>;
+  auto write_snapshot = [&](T* sn, const f32x16 (&acc)[SC::MT][SC::NTW]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int a = 0; a < SC::RB; ++a)
+    for (int mt = 0; mt < SC::MT; ++mt)
 #pragma unroll
-      for (int nb = 0; nb < SC::NB; ++nb)
-        store4_coherent(sn + (int64_t)(dvl + nb * 16) * D + dkl + 16 * a, acc[a][nb]);
+      for (int nt = 0; nt < SC::NTW; ++nt)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const int S = (dk0 + 32 * mt) / 16 + a / 2;  // dk step
+          const int t = (dvw + 32 * nt) / 32;           // dv tile
+          const int64_t off = (int64_t)(S / (OT::RS / 16)) * OT::RS * D +
+                              ((int64_t)((S % (OT::RS / 16)) * OT::NT + t) * 64 + 32 * (a % 2) + n) * 8 + 4 * hh;
+          store4_coherent(sn + off, f32x4{acc[mt][nt][4 * a], acc[mt][nt][4 * a + 1], acc[mt][nt][4 * a + 2],
+                                          acc[mt][nt][4 * a + 3]});
+        }
   };
 
-  f32x4 racc[SC::RB][SC::NB];
-  if (ci == 0 && p.state_in) {
+  f32x16 racc[SC::MT][SC::NTW];
+  if (ci == 0 && p.state_in && active) {
     // R_{-1} = state_in: publish it for the output workgroups of chunk 0
     const float* S0 = p.state_in + (int64_t)bh * D * D;
 #pragma unroll
-    for (int a = 0; a < SC::RB; ++a)
+    for (int mt = 0; mt < SC::MT; ++mt)
 #pragma unroll
-      for (int nb = 0; nb < SC::NB; ++nb)
+      for (int nt = 0; nt < SC::NTW; ++nt)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) racc[a][nb][j] = S0[(int64_t)(dkl + 16 * a + j) * D + dvl + nb * 16];
+        for (int i = 0; i < 16; ++i)
+          racc[mt][nt][i] = S0[(int64_t)(dk_of(mt, i / 4) + i % 4) * D + dvw + 32 * nt + n];
     write_snapshot(reinterpret_cast<T*>(p.snap) + (int64_t)bh * p.nchunks * D * D, racc);
-    release_flag(flag_of(0, 1));
   }
+  if (ci == 0 && p.state_in) release_flag(flag_of(0, 1));
 #pragma unroll
-  for (int a = 0; a < SC::RB; ++a)
+  for (int mt = 0; mt < SC::MT; ++mt)
 #pragma unroll
-    for (int nb = 0; nb < SC::NB; ++nb) racc[a][nb] = zero4();
+    for (int nt = 0; nt < SC::NTW; ++nt) racc[mt][nt] = zero16();
 
   auto issue_kv = [&](int j, char* buf) __attribute__((always_inline)) {
     state_issue<T, D>(buf, K, V, tstride, c0 + j * SC::BK, cend - 1, wave, lane);
   };
-  // zeta_k = g^(cend-1-k) for key k = kb0 + 32 ks + koff(j), with koff(j) the
-  // column-fragment key order {4g..4g+3, 16+4g..16+4g+3}
-  float zl[8];  // this lane's part: g^-koff(j)
+  // zeta_k = g^(cend-1-k); fragment element j is key k0 + kj(j) with
+  // kj(j) = 4 hh + j (j < 4), 8 + 4 hh + j - 4 (j >= 4)
+  float zl[8];  // this lane's part: g^-kj(j)
 #pragma unroll
-  for (int j = 0; j < 8; ++j) zl[j] = gpow(-(float)(j < 4 ? 4 * g + j : 16 + 4 * g + j - 4), lg);
-  // dR += K_blk^T (V_blk (.) zeta): zeta is applied to the K^T fragments (one
-  // factor per key), keys past the chunk get zero.
+  for (int j = 0; j < 8; ++j) zl[j] = gpow(-(float)(j < 4 ? 4 * hh + j : 8 + 4 * hh + j - 4), lg);
+  // dR += K_blk^T (V_blk (.) zeta): zeta scales the V fragments (one factor
+  // per key); keys past the chunk get zero.
   auto block = [&](int kb0, const char* kt) __attribute__((always_inline)) {
+    if (!active) return;
     const char* vt = kt + SC::KT::BYTES;
     const bool ragged = kb0 + SC::BK > cend;  // keys past the chunk in this block (uniform)
 #pragma unroll
-    for (int ks = 0; ks < SC::BK / 32; ++ks) {
+    for (int ks = 0; ks < SC::BK / 16; ++ks) {
+      const int k0 = kb0 + 16 * ks;
       float z[8];
       bool keep[8];
       if (ragged || lg < -1.5f) {  // exact per key (vanishing decays, ragged block)
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const int key = kb0 + ks * 32 + (j < 4 ? 4 * g + j : 16 + 4 * g + j - 4);
+          const int key = k0 + (j < 4 ? 4 * hh + j : 8 + 4 * hh + j - 4);
           keep[j] = key < cend;
           z[j] = gpow((float)(cend - 1 - key), lg);
         }
       } else {
-        const float zs = gpow((float)(cend - 1 - kb0 - ks * 32), lg);
+        const float zs = gpow((float)(cend - 1 - k0), lg);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           keep[j] = true;
           z[j] = zs * zl[j];
         }
       }
-      frag_t<T> af[SC::RB];
+      frag_t<T> af[SC::MT];
 #pragma unroll
-      for (int a = 0; a < SC::RB; ++a) {
-        af[a] = tile_col8<typename SC::KT>(kt, ks * 32, wave * (SC::ROWS / 4) + 16 * a, lane, (T*)nullptr);
+      for (int mt = 0; mt < SC::MT; ++mt) af[mt] = tile_col8w<typename SC::KT>(kt, 16 * ks, 32 * mt, lane, (T*)nullptr);
+#pragma unroll
+      for (int nt = 0; nt < SC::NTW; ++nt) {
+        // zeta scales this wave's own V fragments (the K^T fragments are
+        // shared by all four waves)
+        frag_t<T> vb = tile_col8w<typename SC::VT>(vt, 16 * ks, dvw + 32 * nt, lane, (T*)nullptr);
         if (ragged)
-          scale_frag(af[a], z, keep);
+          scale_frag(vb, z, keep);
         else
-          scale_frag(af[a], z);
-      }
-      auto vload = [&](int t) __attribute__((always_inline)) {
-        return tile_col8<typename SC::VT>(vt, ks * 32, t * 16, lane, (T*)nullptr);
-      };
-      frag_t<T> vb[3];
-      vb[0] = vload(0);
-      vb[1] = vload(1);
+          scale_frag(vb, z);
 #pragma unroll
-      for (int t = 0; t < SC::NB; ++t) {
-        if (t + 2 < SC::NB) vb[(t + 2) % 3] = vload(t + 2);
-#pragma unroll
-        for (int a = 0; a < SC::RB; ++a) racc[a][t] = mma(af[a], vb[t % 3], racc[a][t]);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int mt = 0; mt < SC::MT; ++mt) racc[mt][nt] = mma32(af[mt], vb, racc[mt][nt]);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
   issue_kv(0, stage0);
@@ -686,50 +613,67 @@ __device__ __forceinline__ void state_role(const FwdParams& p, int bh, int ci, i
   }
 
   // R_i = g^b R_{i-1} + dR_i. The fp32 chain keeps R in this role's
-  // accumulator layout (four contiguous floats per lane and fragment), so
-  // the next chunk's workgroup reads it back coalesced.
-  auto chain_frag = [&](int slot, int a, int nb) __attribute__((always_inline)) {
-    return p.chain + ((int64_t)bh * 2 + slot) * D * D +
-           ((((part * 4 + wave) * SC::RB + a) * SC::NB + nb) * 64 + lane) * 4;
+  // accumulator layout (16 contiguous floats per lane and tile), so the next
+  // chunk's workgroup of the same part reads it back coalesced.
+  // element pair q of tile (mt, nt): a wave's 8-byte accesses cover 512
+  // contiguous bytes
+  auto chain_pair = [&](int slot, int mt, int nt, int q) __attribute__((always_inline)) {
+    return reinterpret_cast<uint64_t*>(p.chain + ((int64_t)bh * 2 + slot) * D * D) +
+           (((((part * 4 + wave) * SC::MT + mt) * SC::NTW + nt) * 8 + q) * 64 + lane);
   };
   const float dec = gpow((float)(cend - c0), lg);
   if (ci > 0) {
     wait_flag(flag_of(ci, 0), p.ctrl + 1);
-    const int slot = (ci - 1) & 1;
+    if (active) {
+      const int slot = (ci - 1) & 1;
+      typedef float f32x2 __attribute__((ext_vector_type(2)));
 #pragma unroll
-    for (int a = 0; a < SC::RB; ++a)
+      for (int mt = 0; mt < SC::MT; ++mt)
 #pragma unroll
-      for (int nb = 0; nb < SC::NB; ++nb) {
-        const f32x4 r = load4_coherent(chain_frag(slot, a, nb));
+        for (int nt = 0; nt < SC::NTW; ++nt)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) racc[a][nb][j] += dec * r[j];
-      }
-  } else if (p.state_in) {
+          for (int q = 0; q < 8; ++q) {
+            const f32x2 r = __builtin_bit_cast(
+                f32x2, __hip_atomic_load(chain_pair(slot, mt, nt, q), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+            racc[mt][nt][2 * q] += dec * r[0];
+            racc[mt][nt][2 * q + 1] += dec * r[1];
+          }
+    }
+  } else if (p.state_in && active) {
     const float* S0 = p.state_in + (int64_t)bh * D * D;
 #pragma unroll
-    for (int a = 0; a < SC::RB; ++a)
+    for (int mt = 0; mt < SC::MT; ++mt)
 #pragma unroll
-      for (int nb = 0; nb < SC::NB; ++nb)
+      for (int nt = 0; nt < SC::NTW; ++nt)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) racc[a][nb][j] += dec * S0[(int64_t)(dkl + 16 * a + j) * D + dvl + nb * 16];
+        for (int i = 0; i < 16; ++i)
+          racc[mt][nt][i] += dec * S0[(int64_t)(dk_of(mt, i / 4) + i % 4) * D + dvw + 32 * nt + n];
   }
   if (ci + 1 < p.nchunks) {
     // the next state workgroup needs only the chain: release it first
+    if (active) {
+      typedef float f32x2 __attribute__((ext_vector_type(2)));
 #pragma unroll
-    for (int a = 0; a < SC::RB; ++a)
+      for (int mt = 0; mt < SC::MT; ++mt)
 #pragma unroll
-      for (int nb = 0; nb < SC::NB; ++nb) store4_coherent(chain_frag(ci & 1, a, nb), racc[a][nb]);
+        for (int nt = 0; nt < SC::NTW; ++nt)
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+            __hip_atomic_store(chain_pair(ci & 1, mt, nt, q),
+                               __builtin_bit_cast(uint64_t, f32x2{racc[mt][nt][2 * q], racc[mt][nt][2 * q + 1]}),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     release_flag(flag_of(ci + 1, 0));
-    write_snapshot(snap_next, racc);
+    if (active) write_snapshot(snap_next, racc);
     release_flag(flag_of(ci + 1, 1));
-  } else if (p.state_out) {
+  } else if (p.state_out && active) {
     float* SO = p.state_out + (int64_t)bh * D * D;
 #pragma unroll
-    for (int a = 0; a < SC::RB; ++a)
+    for (int mt = 0; mt < SC::MT; ++mt)
 #pragma unroll
-      for (int nb = 0; nb < SC::NB; ++nb)
+      for (int nt = 0; nt < SC::NTW; ++nt)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) SO[(int64_t)(dkl + 16 * a + j) * D + dvl + nb * 16] = racc[a][nb][j];
+        for (int i = 0; i < 16; ++i) SO[(int64_t)(dk_of(mt, i / 4) + i % 4) * D + dvw + 32 * nt + n] = racc[mt][nt][i];
   }
 }
 
