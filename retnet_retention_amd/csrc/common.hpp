@@ -144,6 +144,20 @@ __device__ __forceinline__ void store8(float* p, const F8& v) {
 }
 
 // Four consecutive elements (8 bytes of bf16, 16 of fp32) to and from floats.
+// a wave-uniform int held in a scalar register
+__device__ __forceinline__ int uniform_i(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// a wave-uniform float held in a scalar register
+__device__ __forceinline__ float uniform_f(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
+}
+
+// four consecutive elements, raw
+template <typename T> struct Vec4Of;
+template <> struct Vec4Of<bf16> { using type = bf16x4; };
+template <> struct Vec4Of<float> { using type = f32x4; };
+template <typename T> using vec4_t = typename Vec4Of<T>::type;
+
 __device__ __forceinline__ void load4(const bf16* p, float* v) {
   const bf16x4 x = *reinterpret_cast<const bf16x4*>(p);
 #pragma unroll
@@ -353,77 +367,123 @@ __device__ __forceinline__ void set_half(f32x8& f, const f32x4& x, std::integral
 }
 
 // ---------------------------------------------------------------------------
-// Padded LDS tiles filled by direct global->LDS loads.
+// LDS tiles filled by direct global->LDS loads.
 //
-// A tile holds ROWS rows of COLS elements; each row is followed by PADB
-// bytes of padding so that the fragment reads of one instruction fall in
-// different banks: PADB = 16 for row-fragment reads (16 lanes read 16 rows
-// at the same column; row stride = 16 mod 256 bytes) and PADB = 32 for
-// column (transpose) reads (32 lanes read 8 rows x 32 bytes; row stride =
-// 32 * odd bytes). Every fragment address is then a per-lane base plus an
-// immediate offset.
-//
-// global_load_lds_dwordx4 writes lane i's 16 bytes to LDS base + 16 i (M0
-// holds the base), so a wave instruction fills 64 consecutive 16-byte slots.
-// The tile is treated as a flat run of slots: a slot inside a row's data
-// loads its chunk, a padding slot (or a slot past the tile, inside the tile's
-// rounded-up allocation) loads a harmless in-range chunk that is never read.
+// global_load_lds_dwordx4 / buffer_load ... lds write lane i's 16 bytes to
+// LDS base + 16 i (M0 holds the base): one wave-wide load fills 1 KiB of
+// consecutive LDS. A tile of ROWS rows of COLS elements (row bytes ROWB a
+// power of two, 128 .. 1024) is stored load by load: load n holds rows
+// n RPI .. n RPI + RPI-1 (RPI = 1024 / ROWB) at LDS offset n (1024 + PADL),
+// and inside it the rows' 16-byte chunks are interleaved in groups of G:
+// chunk c of row lr sits at chunk position (c / G) G RPI + lr G + c % G.
+// A lane's global offset is then the same for every load up to a
+// wave-uniform row step, a fragment read is a per-lane base plus an
+// immediate offset (the constant part of its chunk index being a multiple of
+// G), and G and PADL put the reads of one instruction in distinct banks (64
+// banks of 4 bytes):
+//   row tiles (16 lanes read one chunk of 16 consecutive rows);
+//   column tiles (transposed reads: 32 lanes read 4 chunks of 4 aligned rows).
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void lds_void;
 
-template <typename T, int ROWS, int COLS, int PADB>
-struct PTile {
-  static constexpr int DATAB = COLS * (int)sizeof(T);  // data bytes per row
-  static constexpr int ROWB = DATAB + PADB;            // row stride in LDS
-  static constexpr int CPR = DATAB / 16;               // data chunks per row
-  static constexpr int SPR = ROWB / 16;                // slots per row
-  static constexpr int SLOTS = ROWS * SPR;
-  static constexpr int NINST = (SLOTS + 63) / 64;      // wave-wide loads
-  static constexpr int BYTES = NINST * 1024;           // allocation
-  static_assert(DATAB % 16 == 0 && PADB % 16 == 0, "16-byte chunks");
-  __device__ static __forceinline__ int off(int r, int col) { return r * ROWB + col * (int)sizeof(T); }
+enum TileKind { kRowTile, kColTile };
+
+template <typename T, int ROWS, int COLS, TileKind KIND>
+struct LTile {
+  static constexpr int ROWB = COLS * (int)sizeof(T);  // row bytes
+  static constexpr int CPR = ROWB / 16;               // chunks per row
+  static constexpr int RPI = 1024 / ROWB;             // rows per wave-wide load
+  static_assert(ROWB >= 128 && ROWB <= 1024 && (ROWB & (ROWB - 1)) == 0, "power-of-two rows of 128..1024 bytes");
+  static_assert(ROWS % RPI == 0, "whole loads");
+  // (G, PADL) by row bytes 128 / 256 / 512 / 1024
+  static constexpr int G = KIND == kRowTile ? (ROWB == 128 ? 2 : 1) : (ROWB == 128 ? 4 : 1);
+  static constexpr int PADL = KIND == kRowTile ? (ROWB == 128 ? 16 : ROWB == 256 ? 64 : ROWB == 512 ? 32 : 16)
+                                               : (ROWB <= 256 ? 0 : ROWB == 512 ? 128 : 64);
+  static constexpr int LSTRIDE = 1024 + PADL;  // LDS bytes per load
+  static constexpr int NINST = ROWS / RPI;     // wave-wide loads
+  static constexpr int BYTES = NINST * LSTRIDE;
+  __device__ static __forceinline__ int off(int r, int col) {
+    const int byte = col * (int)sizeof(T), c = byte >> 4;
+    return (r / RPI) * LSTRIDE + (((c / G) * G * RPI + (r % RPI) * G + c % G) << 4) + (byte & 15);
+  }
+  // byte step of DR rows (a multiple of RPI): the same chunk positions
+  static constexpr int row_step(int dr) { return (dr / RPI) * LSTRIDE; }
 };
 
-// Issue the async loads of tile TL from rows row0 .. row0+ROWS-1 of a
-// row-major global matrix (`gstride` elements between rows, rows clamped to
-// rmax), spread over NW waves. Completion: s_waitcnt vmcnt + barrier.
-// CPOL: cache policy of the loads (0: default; 17 = sc0|sc1: read coherently
-// data that another XCD wrote with sc1 stores, bypassing stale cache lines).
-template <typename T, typename TL, int NW, int CPOL = 0>
-__device__ __forceinline__ void async_tile(char* lds, const T* g, int64_t gstride, int row0, int rmax, int wave,
-                                           int lane) {
-#pragma unroll
-  for (int m = 0; m < (TL::NINST + NW - 1) / NW; ++m) {
-    const int n = wave + m * NW;  // wave-uniform
-    if (TL::NINST % NW != 0 && n >= TL::NINST) break;
-    // the lane's offsets are recomputed for every load rather than kept live
-    // across the caller's loop
-    int ln = lane;
-    __asm__ volatile("" : "+v"(ln));
-    const int slot = n * 64 + ln;
-    int r = slot / TL::SPR, ch = slot % TL::SPR;
-    if (ch >= TL::CPR) ch = 0;  // padding slot: any in-range chunk
-    if (slot >= TL::SLOTS) r = 0;                                  // slack past the tile
-    const int gr = min(row0 + r, rmax);
-    // 32-bit element offset from a wave-uniform base (the host bounds every
-    // per-sequence offset below 2^31 elements)
-    const T* src = g + (uint32_t)(gr * (int)gstride + ch * (16 / (int)sizeof(T)));
-    __builtin_amdgcn_global_load_lds(src, (lds_void*)(lds + n * 1024), 16, 0, CPOL);
-  }
+// Direct loads of tile TL spread over NW waves (wave w issues loads w, w+NW,
+// ...). The lane's offset is worked out once: loads of rows that all exist
+// take it plus a scalar row step, as buffer loads from a scalar descriptor
+// (no vector arithmetic per load); loads of a tile with rows past rmax clamp
+// each lane's row. Completion: s_waitcnt vmcnt + barrier.
+constexpr int kBufferWord3 = 0x00020000;  // raw 32-bit buffer descriptor, gfx9 family
+
+// buffer descriptor of a wave-uniform base address, in scalar registers
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t scalar_rsrc(const void* base) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(((uint64_t)hi << 32) | lo), (short)0, -1,
+                                           kBufferWord3);
 }
 
+template <typename T, typename TL, int NW>
+struct TileLoads {
+  static constexpr int PER = (TL::NINST + NW - 1) / NW;
+  static constexpr int EPC = 16 / (int)sizeof(T);  // elements per chunk
+  uint32_t off;  // byte offset of this lane's chunk from the load's first row
+  // chunk position `lane` of a load: row (lane / G) % RPI, chunk
+  // (lane / (G RPI)) G + lane % G
+  __device__ static __forceinline__ int lane_row(int lane) { return (lane / TL::G) % TL::RPI; }
+  __device__ static __forceinline__ int lane_chunk(int lane) {
+    return (lane / (TL::G * TL::RPI)) * TL::G + lane % TL::G;
+  }
+  __device__ __forceinline__ void init(int64_t gstride, int lane) {
+    off = (uint32_t)((lane_row(lane) * (int)gstride + lane_chunk(lane) * EPC) * (int)sizeof(T));
+  }
+  // rows row0 .. row0 + ROWS - 1 of g, all in range (g + row0 gstride is
+  // wave-uniform)
+  __device__ __forceinline__ void issue(char* lds, const T* g, int64_t gstride, int row0, int wave) const {
+    const __amdgpu_buffer_rsrc_t rs = scalar_rsrc(g + row0 * gstride);
+    const uint32_t step = (uint32_t)(TL::RPI * gstride * (int64_t)sizeof(T));  // bytes per load
+#pragma unroll
+    for (int m = 0; m < PER; ++m) {
+      const int n = wave + m * NW;  // wave-uniform; below NINST except maybe in the last load
+      if (TL::NINST % NW != 0 && m == PER - 1 && n >= TL::NINST) break;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + n * TL::LSTRIDE), 16, off, n * step, 0, 0);
+    }
+  }
+  // rows row0 .. row0 + ROWS - 1 of g with every row past rmax replaced by
+  // row rmax (rmax >= row0)
+  __device__ __forceinline__ void issue_clamped(char* lds, const T* g, int64_t gstride, int row0, int rmax,
+                                                int wave) const {
+    const __amdgpu_buffer_rsrc_t rs = scalar_rsrc(g + row0 * gstride);
+    const int lane = threadIdx.x & 63, lr = lane_row(lane), lc = lane_chunk(lane);
+#pragma unroll
+    for (int m = 0; m < PER; ++m) {
+      const int n = wave + m * NW;
+      if (TL::NINST % NW != 0 && m == PER - 1 && n >= TL::NINST) break;
+      const int r = min(n * TL::RPI + lr, rmax - row0);  // row relative to row0
+      const uint32_t o = (uint32_t)((r * (int)gstride + lc * EPC) * (int)sizeof(T));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + n * TL::LSTRIDE), 16, o, 0, 0, 0);
+    }
+  }
+};
+
 // A contiguous block of BYTES (a multiple of 1 KiB) copied into LDS by NW
-// waves, one 16-byte chunk per lane and load.
+// waves, one 16-byte chunk per lane and load (g wave-uniform). CPOL: cache
+// policy (0: default; 17 = sc0|sc1: read coherently data that another XCD
+// wrote with sc1 stores).
 template <typename T, int BYTES, int NW, int CPOL = 0>
 __device__ __forceinline__ void async_flat(char* lds, const T* g, int wave, int lane) {
   static_assert(BYTES % 1024 == 0, "whole wave-wide loads");
   constexpr int NINST = BYTES / 1024;
+  const __amdgpu_buffer_rsrc_t rs = scalar_rsrc(g);
 #pragma unroll
   for (int m = 0; m < (NINST + NW - 1) / NW; ++m) {
     const int n = wave + m * NW;  // wave-uniform
     if (NINST % NW != 0 && n >= NINST) break;
-    const T* src = g + (uint32_t)((n * 64 + lane) * (16 / (int)sizeof(T)));
-    __builtin_amdgcn_global_load_lds(src, (lds_void*)(lds + n * 1024), 16, 0, CPOL);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + n * 1024), 16, (uint32_t)lane * 16u,
+                                             (uint32_t)n * 1024u, 0, CPOL);
   }
 }
 
@@ -439,42 +499,18 @@ __device__ __forceinline__ f32x8 tile_row8(const char* t, int r, int col, float*
   return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
-// Column fragment: lane (g, i) receives rows k0 + {4g..4g+3, 16+4g..16+4g+3}
-// of column n0 + i (see lds_col8).
-template <typename TL>
-__device__ __forceinline__ bf16x8 tile_col8(const char* t, int k0, int n0, int lane, bf16*) {
-  const int g = (lane >> 4) & 3, i = lane & 15;
-  const char* p = t + TL::off(k0 + 4 * g + (i >> 2), n0 + 4 * (i & 3));
-  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
-  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 16 * TL::ROWB));
-  typedef short i16x8 __attribute__((ext_vector_type(8)));
-  const i16x8 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  return __builtin_bit_cast(bf16x8, w);
-}
-template <typename TL>
-__device__ __forceinline__ f32x8 tile_col8(const char* t, int k0, int n0, int lane, float*) {
-  const int g = (lane >> 4) & 3, i = lane & 15;
-  const char* p = t + TL::off(k0 + 4 * g, n0 + i);
-  f32x8 f;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    f[j] = *reinterpret_cast<const float*>(p + j * TL::ROWB);
-    f[4 + j] = *reinterpret_cast<const float*>(p + (16 + j) * TL::ROWB);
-  }
-  return f;
-}
-
 // Column fragment for 32x32 tiles: lane (n = l%32, h = l/32) receives rows
-// k0 + {4h..4h+3, 8+4h..8+4h+3} of column n0 + n. bf16: per 16-lane group
-// (h = group/2, 16 columns from n0 + 16 (group%2)) lane m fetches 4 elements
-// of row k0 + 4h + m/4 at column 4(m%4), and the transpose read hands lane m
-// column m of those four rows; a second read 8 rows on gives the rest.
+// k0 + {4h..4h+3, 8+4h..8+4h+3} of column n0 + n (k0 a multiple of 16). bf16:
+// per 16-lane group (h = group/2, 16 columns from n0 + 16 (group%2)) lane m
+// fetches 4 elements of row k0 + 4h + m/4 at column 4(m%4), and the transpose
+// read hands lane m column m of those four rows; a second read 8 rows on
+// gives the rest.
 template <typename TL>
 __device__ __forceinline__ bf16x8 tile_col8w(const char* t, int k0, int n0, int lane, bf16*) {
   const int grp = lane >> 4, m = lane & 15, h = grp >> 1;
   const char* p = t + TL::off(k0 + 4 * h + (m >> 2), n0 + 16 * (grp & 1) + 4 * (m & 3));
   const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
-  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 8 * TL::ROWB));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + TL::row_step(8)));
   typedef short i16x8 __attribute__((ext_vector_type(8)));
   const i16x8 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return __builtin_bit_cast(bf16x8, w);
@@ -482,12 +518,11 @@ __device__ __forceinline__ bf16x8 tile_col8w(const char* t, int k0, int n0, int 
 template <typename TL>
 __device__ __forceinline__ f32x8 tile_col8w(const char* t, int k0, int n0, int lane, float*) {
   const int n = lane & 31, h = lane >> 5;
-  const char* p = t + TL::off(k0 + 4 * h, n0 + n);
   f32x8 f;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    f[j] = *reinterpret_cast<const float*>(p + j * TL::ROWB);
-    f[4 + j] = *reinterpret_cast<const float*>(p + (8 + j) * TL::ROWB);
+    f[j] = *reinterpret_cast<const float*>(t + TL::off(k0 + 4 * h + j, n0 + n));
+    f[4 + j] = *reinterpret_cast<const float*>(t + TL::off(k0 + 8 + 4 * h + j, n0 + n));
   }
   return f;
 }

@@ -37,11 +37,21 @@ namespace ret {
 // FAST: every head's decay over the span that one workgroup's decay factors
 // cover stays within 2^64 (see kFastSpanLog2); the scores then take one factor
 // per key and the rows one factor at the end.
+// Waves per workgroup: eight for bf16 (two per SIMD: the direct loads of a
+// compute unit run faster with more waves issuing them, and one wave's LDS
+// and matrix work overlaps the other's), four for fp32, whose fragments take
+// twice the registers.
+template <typename T> constexpr int kWaves = sizeof(T) == 2 ? 8 : 4;
+
 template <typename T, int D, bool FAST = true>
 struct OutTile {
   static constexpr int E = sizeof(T);
-  static constexpr int WAVES = 4;
-  static constexpr int QW = 32;                // query rows per wave: one 32-row tile
+  static constexpr int WAVES = kWaves<T>;
+  // 32-row query tiles per wave. Every K, V and R^T fragment read from LDS
+  // feeds QT products; two tiles would halve the LDS traffic per product but
+  // need more than a wave's registers at D = 256 (O^T and Q alone take 384).
+  static constexpr int QT = 1;
+  static constexpr int QW = 32 * QT;           // query rows per wave
   static constexpr int BM = WAVES * QW;        // query rows per workgroup
   static constexpr int BN = E == 2 ? 64 : 32;  // keys per block
   static constexpr int KH = BN / 32;           // 32-key steps per block
@@ -50,8 +60,8 @@ struct OutTile {
   // dk columns per R^T slice; the slices stream through the two stages
   static constexpr int RS = D / 2 < 256 / E ? D / 2 : 256 / E;
   static constexpr int NRS = D / RS;
-  using KT = PTile<T, BN, D, 16>;   // K block, row fragments
-  using VT = PTile<T, BN, D, 64>;   // V block, column (transpose) fragments
+  using KT = LTile<T, BN, D, kRowTile>;  // K block, row fragments
+  using VT = LTile<T, BN, D, kColTile>;  // V block, column (transpose) fragments
   // R^T slice: RS dk columns x D dv rows, stored (in HBM and LDS alike) in
   // fragment order: [dk step s][dv tile t][lane][8 elements], lane (n, h)
   // holding R^T[32 t + n][16 s + 8 h .. +7] -- the A operand of the cross term
@@ -71,20 +81,29 @@ constexpr double kFastSpanLog2 = 64.0;
 
 template <typename T, int D>
 struct StTile {
-  // State workgroups per chunk: one per 128 dk rows of R (one for D <= 128).
-  // The four waves split dv; each holds the workgroup's rows x D/4 columns of
-  // R in fp32 registers. Fewer rows per workgroup shorten the serial chunk-
-  // to-chunk hand-off; more rows cost fewer K reads per chunk.
-  static constexpr int SPLIT = D > 128 ? D / 128 : 1;
+  // State workgroups per chunk: one (eight waves), or one per 128 dk rows of
+  // R (four waves, D = 256). Fewer rows per workgroup shorten the serial
+  // chunk-to-chunk hand-off; more rows read V once for more of R and give
+  // each block more work to hide the loads of the next. The waves form a
+  // WR x WC grid over the workgroup's 32 x 32 tiles of R (rows x dv), each
+  // holding MTW x NTW tiles in fp32 registers; waves past the tiles (D = 64)
+  // stay idle.
+  static constexpr int NW = kWaves<T>;
+  static constexpr int SPLIT = NW < 8 && D > 128 ? D / 128 : 1;
   static constexpr int ROWS = D / SPLIT;        // dk rows per workgroup
   static constexpr int BK = OutTile<T, D>::BN;  // keys per block
-  static constexpr int MT = ROWS / 32;          // 32-row dk tiles per wave
-  static constexpr int NTW = D / 128 > 0 ? D / 128 : 1;  // 32-wide dv tiles per wave
-  static constexpr int DVW = 32 * NTW;          // dv columns per wave
-  using KT = PTile<T, BK, ROWS, 64>;            // this workgroup's dk columns of K (K^T operand)
-  using VT = PTile<T, BK, D, 64>;               // V block, column fragments
+  static constexpr int MTA = ROWS / 32, NTA = D / 32;   // tiles of the workgroup
+  // wave columns: with eight waves two wave rows, so that a wave's 4 tiles
+  // take 2 K^T and 2 V fragments per step (4 x 1 tiles would take 5)
+  static constexpr int WC = NW >= 8 && NTA >= NW / 2 && MTA >= 2 ? NW / 2 : (NW < NTA ? NW : NTA);
+  static constexpr int WR = NW / WC;                    // wave rows
+  static constexpr int NTW = NTA / WC;                  // dv tiles per wave
+  static constexpr int MTW = MTA / WR > 0 ? MTA / WR : 1;  // row tiles per wave
+  static constexpr int ACTIVE = (MTA / MTW) * WC;       // waves with tiles
+  using KT = LTile<T, BK, ROWS, kColTile>;      // this workgroup's dk columns of K (K^T operand)
+  using VT = LTile<T, BK, D, kColTile>;         // V block, column fragments
   static constexpr int KVB = KT::BYTES + VT::BYTES;
-  static_assert(4 * DVW >= D, "the waves cover every dv column");
+  static_assert(WC * NTW == NTA && (MTA / MTW) * MTW == MTA, "the waves cover every tile");
 };
 // per (sequence, head, chunk j) and state part q two ready flags: rows of
 // R_{j-1} in the fp32 chain (for chunk j's state workgroup of part q) and in
@@ -153,42 +172,51 @@ __device__ __forceinline__ void release_flag(int* flag) {
   if (threadIdx.x == 0) __hip_atomic_store(flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// coherent (sc1) stores and loads of handed-off values
-__device__ __forceinline__ void store4_coherent(bf16* p, const f32x4& x) {
+// coherent (sc1) stores and loads of handed-off values, as buffer accesses:
+// a scalar descriptor, a per-lane byte offset and a wave-uniform byte offset
+// (no per-lane 64-bit addresses to keep in registers)
+constexpr int kSc1 = 16;  // cache policy bits: sc1
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store4_coherent(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff, bf16*,
+                                                const f32x4& x) {
   bf16x4 o;
 #pragma unroll
   for (int i = 0; i < 4; ++i) o[i] = (bf16)x[i];
-  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), __builtin_bit_cast(uint64_t, o), __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, o), rs, voff, soff, kSc1);
 }
-__device__ __forceinline__ void store4_coherent(float* p, const f32x4& x) {
-  typedef float f32x2 __attribute__((ext_vector_type(2)));
-  const f32x2 a = {x[0], x[1]}, b = {x[2], x[3]};
-  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), __builtin_bit_cast(uint64_t, a), __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
-  __hip_atomic_store(reinterpret_cast<uint64_t*>(p + 2), __builtin_bit_cast(uint64_t, b), __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ void store4_coherent(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff, float*,
+                                                const f32x4& x) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), rs, voff, soff, kSc1);
 }
-__device__ __forceinline__ f32x4 load4_coherent(const float* p) {
+__device__ __forceinline__ void store2_coherent(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff, float x0,
+                                                float x1) {
   typedef float f32x2 __attribute__((ext_vector_type(2)));
-  uint64_t* q = reinterpret_cast<uint64_t*>(const_cast<float*>(p));
-  const f32x2 a = __builtin_bit_cast(f32x2, __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-  const f32x2 b = __builtin_bit_cast(f32x2, __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-  return f32x4{a[0], a[1], b[0], b[1]};
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, f32x2{x0, x1}), rs, voff, soff, kSc1);
+}
+// volatile (bit 31 of the policy word, a compiler-side flag): the loads keep
+// their place relative to scheduling barriers
+__device__ __forceinline__ u32x2 load2_coherent(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b64(rs, voff, soff, kSc1 | (int)0x80000000u);
 }
 
 // ---------------------------------------------------------------------------
 // Output role.
 // ---------------------------------------------------------------------------
-template <typename T, int D, bool FAST>
+// CROSS: the chunk has a previous state R_{i-1} (chunkwise form, chunk > 0
+// or an initial state); the parallel form and chunk 0 without one have none.
+template <typename T, int D, bool FAST, bool CROSS>
 __device__ __forceinline__ void out_role(const FwdParams& p, int bh, int ci, int qb, bool chunked, char* stage0,
                                          char* stage1) {
   using C = OutTile<T, D, FAST>;
+  constexpr int QT = C::QT;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, hh = lane >> 5;  // column / half of the 32x32 layout
 
-  const int h = bh % p.heads, b = bh / p.heads;
+  // integer division runs on the vector unit: bring the uniform results back
+  // to scalar registers
+  const int h = uniform_i(bh % p.heads), b = uniform_i(bh / p.heads);
   const int c0 = ci * p.chunk;
   const int cend = min(c0 + p.chunk, p.seqlen);
   const int q0 = c0 + qb * C::BM;
@@ -204,18 +232,26 @@ __device__ __forceinline__ void out_role(const FwdParams& p, int bh, int ci, int
   const T* G = p.g ? reinterpret_cast<const T*>(p.g) + head0 : nullptr;
   T* O = reinterpret_cast<T*>(p.o) + head0;
 
-  const int qw0 = q0 + wave * C::QW;     // first row of this wave
-  const int qrow = qw0 + n;              // this lane's query row
+  const int qw0 = q0 + wave * C::QW;  // first row of this wave
+  // this lane's query row in the wave's query tile r: qw0 + 32 r + n
   const int kend = min(q0 + C::BM, cend);
   const int nkb = (kend - c0 + C::BN - 1) / C::BN;
 
+  TileLoads<T, typename C::KT, C::WAVES> kload;
+  TileLoads<T, typename C::VT, C::WAVES> vload;
+  kload.init(tstride, lane);
+  vload.init(tstride, lane);
   auto issue_kv = [&](int j, char* buf) __attribute__((always_inline)) {
     const int kb0 = c0 + j * C::BN;
-    async_tile<T, typename C::KT, C::WAVES>(buf, K, tstride, kb0, cend - 1, wave, lane);
-    async_tile<T, typename C::VT, C::WAVES>(buf + C::KT::BYTES, V, tstride, kb0, cend - 1, wave, lane);
+    if (kb0 + C::BN <= cend) {
+      kload.issue(buf, K, tstride, kb0, wave);
+      vload.issue(buf + C::KT::BYTES, V, tstride, kb0, wave);
+    } else {
+      kload.issue_clamped(buf, K, tstride, kb0, cend - 1, wave);
+      vload.issue_clamped(buf + C::KT::BYTES, V, tstride, kb0, cend - 1, wave);
+    }
   };
-  const bool cross = chunked && (ci > 0 || p.has_state0);
-  const T* R = cross ? reinterpret_cast<const T*>(p.snap) + ((int64_t)bh * p.nchunks + ci) * D * D : nullptr;
+  const T* R = CROSS ? reinterpret_cast<const T*>(p.snap) + ((int64_t)bh * p.nchunks + ci) * D * D : nullptr;
   // R^T slice s ([dv][RS dk columns]) into an LDS stage; waits (once) for
   // the snapshot of R_{i-1} to be published
   auto issue_slice = [&](int sl, char* buf) __attribute__((always_inline)) {
@@ -226,33 +262,44 @@ __device__ __forceinline__ void out_role(const FwdParams& p, int bh, int ci, int
     }
     async_flat<T, C::RT_BYTES, C::WAVES, kCoherent>(buf, R + (int64_t)sl * C::RS * D, wave, lane);
   };
-  issue_kv(0, stage0);
+  issue_kv(0, stage1);
 
-  // Query fragments of this lane's row, kept in registers for the whole
-  // workgroup life: qf[s] = Q[qrow][16 s + 8 hh .. +7]. Rows past the chunk
-  // load a clamped in-range row: their outputs are never stored.
-  frag_t<T> qf[C::KS];
-  {
-    const T* qr = Q + (int64_t)min(qrow, cend - 1) * tstride + 8 * hh;
+  // Query fragments of this lane's rows, kept in registers for the whole
+  // workgroup life: qf[r][s] = Q[qw0 + 32 r + n][16 s + 8 hh .. +7]. Rows
+  // past the chunk load a clamped in-range row: their outputs are never
+  // stored.
+  frag_t<T> qf[QT][C::KS];
 #pragma unroll
-    for (int s = 0; s < C::KS; ++s) qf[s] = to_frag(unpack8(ld_raw8(qr + 16 * s)), (T*)nullptr);
+  for (int r = 0; r < QT; ++r) {
+    const T* qr = Q + (int64_t)min(qw0 + 32 * r + n, cend - 1) * tstride + 8 * hh;
+#pragma unroll
+    for (int s = 0; s < C::KS; ++s) qf[r][s] = to_frag(unpack8(ld_raw8(qr + 16 * s)), (T*)nullptr);
   }
 
-  // O^T accumulators: oacc[t] element i is O'[qrow][32 t + 8 (i/4) + 4 hh + i%4]
-  f32x16 oacc[C::NT];
+  // O^T accumulators: oacc[r][t] element i is O'[qw0 + 32 r + n][32 t + 8 (i/4) + 4 hh + i%4]
+  f32x16 oacc[QT][C::NT];
 #pragma unroll
-  for (int t = 0; t < C::NT; ++t) oacc[t] = zero16();
+  for (int r = 0; r < QT; ++r)
+#pragma unroll
+    for (int t = 0; t < C::NT; ++t) oacc[r][t] = zero16();
 
-  // per-key decay factors of the fast path, this lane's part:
-  // g^-(8 (i/4) + 4 hh + i%4) for accumulator element i
-  float bkl[16];
+  // per-key decay factors of the fast path: accumulator element i is key
+  // 8 (i/4) + 4 hh + i%4 of a 32-key step, with factor
+  // g^-(8 (i/4)) g^-(i%4) g^-(4 hh); the first two are wave-uniform (kept in
+  // scalar registers), the last one is this lane's.
+  float g8[4], g1[4];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) bkl[i] = FAST ? gpow(-(float)(8 * (i / 4) + 4 * hh + (i % 4)), lg) : 0.f;
+  for (int a = 0; a < 4; ++a) {
+    g8[a] = uniform_f(FAST ? gpow(-(float)(8 * a), lg) : 0.f);
+    g1[a] = uniform_f(FAST ? gpow(-(float)a, lg) : 0.f);
+  }
+  const float ghh = FAST ? gpow(-(float)(4 * hh), lg) : 0.f;
 
   // Intra-chunk term over key blocks up to the diagonal, 32 keys at a time:
-  // S^T = K Q^T (16 products), decay and causal mask, then O^T += V^T P^T
-  // (NT x 2 products). The K and V fragments of a step form one sequence of
-  // LDS reads with a two-deep prefetch ring.
+  // S^T = K Q^T (16 products per query tile), decay and causal mask, then
+  // O^T += V^T P^T (NT x 2 products per query tile). Every K and V fragment
+  // read from LDS feeds the QT query tiles; the fragments of a step form one
+  // sequence of LDS reads with a two-deep prefetch ring.
   constexpr int U = C::KS + 2 * C::NT;  // fragment reads per 32-key step
   auto key_block = [&](int kb0, const char* kt) __attribute__((always_inline)) {
     if (kb0 > qw0 + C::QW - 1) return;  // block above this wave's rows (uniform)
@@ -269,44 +316,50 @@ __device__ __forceinline__ void out_role(const FwdParams& p, int bh, int ci, int
     frag_t<T> ring[3];
     ring[0] = load(std::integral_constant<int, 0>{});
     ring[1] = load(std::integral_constant<int, 1>{});
-    f32x16 st;
-    frag_t<T> pf[2];
+    f32x16 st[QT];
+    frag_t<T> pf[QT][2];
     static_for<C::KH * U>([&](auto t_c) __attribute__((always_inline)) {
       constexpr int t = decltype(t_c)::value, kh = t / U, u = t % U;
       if constexpr (t + 2 < C::KH * U) ring[(t + 2) % 3] = load(std::integral_constant<int, t + 2>{});
       if constexpr (u < C::KS) {
-        if constexpr (u == 0) st = zero16();
-        st = mma32(ring[t % 3], qf[u], st);
+#pragma unroll
+        for (int r = 0; r < QT; ++r) st[r] = mma32(ring[t % 3], qf[r][u], u == 0 ? zero16() : st[r]);
         if constexpr (u == C::KS - 1) {
           // decay g^(q-k) and causal mask; element i is key kb0 + 32 kh + k_i
           const int kk0 = kb0 + 32 * kh;
-          if constexpr (FAST) {
-            const float sb = gpow((float)(ref - kk0), lg);  // g^(r0 - kk0), uniform
-            if (diag) {
+#pragma unroll
+          for (int r = 0; r < QT; ++r) {
+            const int qrow = qw0 + 32 * r + n;
+            if constexpr (FAST) {
+              const float sb = gpow((float)(ref - kk0), lg) * ghh;  // g^(r0 - kk0 - 4 hh)
 #pragma unroll
               for (int i = 0; i < 16; ++i) {
-                const int key = kk0 + 8 * (i / 4) + 4 * hh + (i % 4);
-                const float val = st[i] * (sb * bkl[i]);
-                st[i] = qrow < key ? 0.f : val;
+                if (i % 4 != 0) st[r][i] *= g1[i % 4];
+                st[r][i] *= (i / 4 == 0 ? sb : sb * g8[i / 4]);
+              }
+              if (diag) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                  const int key = kk0 + 8 * (i / 4) + 4 * hh + (i % 4);
+                  if (qrow < key) st[r][i] = 0.f;
+                }
               }
             } else {
 #pragma unroll
-              for (int i = 0; i < 16; ++i) st[i] *= sb * bkl[i];
+              for (int i = 0; i < 16; ++i) {
+                const int dist = qrow - (kk0 + 8 * (i / 4) + 4 * hh + (i % 4));
+                const float val = st[r][i] * gpow((float)dist, lg);
+                st[r][i] = dist < 0 ? 0.f : val;
+              }
             }
-          } else {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int dist = qrow - (kk0 + 8 * (i / 4) + 4 * hh + (i % 4));
-              const float val = st[i] * gpow((float)dist, lg);
-              st[i] = dist < 0 ? 0.f : val;
-            }
+            pf[r][0] = acc_frag<0>(st[r], (T*)nullptr);
+            pf[r][1] = acc_frag<1>(st[r], (T*)nullptr);
           }
-          pf[0] = acc_frag<0>(st, (T*)nullptr);
-          pf[1] = acc_frag<1>(st, (T*)nullptr);
         }
       } else {
         constexpr int v = u - C::KS, tt = v / 2, sl = v % 2;
-        oacc[tt] = mma32(ring[t % 3], pf[sl], oacc[tt]);
+#pragma unroll
+        for (int r = 0; r < QT; ++r) oacc[r][tt] = mma32(ring[t % 3], pf[r][sl], oacc[r][tt]);
       }
       // keep each step's prefetch where it is: two steps ahead of its use
       __builtin_amdgcn_sched_barrier(0);
@@ -314,46 +367,79 @@ __device__ __forceinline__ void out_role(const FwdParams& p, int bh, int ci, int
   };
 
   // One pipeline step: wait for block j, release the other stage, prefetch
-  // block j+1 into it -- or, after the last key block, the first R^T slice.
-  // The stages are distinct LDS objects and the loop is unrolled by two, so
-  // the compiler can tell the reads of one stage from the in-flight loads
-  // into the other.
-  auto sync_and_prefetch = [&](int j, char* nxt) __attribute__((always_inline)) {
+  // block j+1 into it. Block j sits in stage1 for even j, stage0 for odd j,
+  // so that after an even number of blocks the last step prefetches the first
+  // R^T slice into stage1 (after an odd number the slice is loaded once the
+  // last block is done). The stages are distinct LDS objects and the loop is
+  // unrolled by two, so the compiler can tell the reads of one stage from the
+  // in-flight loads into the other.
+  auto sync_and_prefetch = [&](int j, char* nxt, auto slice_c) __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (j + 1 < nkb)
       issue_kv(j + 1, nxt);
-    else if (cross)
+    else if constexpr (CROSS && decltype(slice_c)::value)
       issue_slice(0, nxt);
   };
   for (int j = 0; j < nkb; j += 2) {
-    sync_and_prefetch(j, stage1);
-    key_block(c0 + j * C::BN, stage0);
+    sync_and_prefetch(j, stage0, std::false_type{});
+    key_block(c0 + j * C::BN, stage1);
     if (j + 1 < nkb) {
-      sync_and_prefetch(j + 1, stage0);
-      key_block(c0 + (j + 1) * C::BN, stage1);
+      sync_and_prefetch(j + 1, stage1, std::true_type{});
+      key_block(c0 + (j + 1) * C::BN, stage0);
     }
   }
+
+  // Gate values of this lane's half-rows, loaded as soon as registers free
+  // up: bf16 all dv tiles (half of them during the last R^T slice, whose
+  // predecessors' query fragments are dead, the rest after the cross term),
+  // fp32 one tile ahead of use in the epilogue.
+  constexpr int GPRE = sizeof(T) == 2 ? C::NT : 1;
+  vec4_t<T> graw[QT][GPRE][4];
+  auto grow = [&](int r) __attribute__((always_inline)) {
+    return G + (int64_t)min(qw0 + 32 * r + n, cend - 1) * tstride + 4 * hh;
+  };
+  auto gload = [&](const T* gr, int t, vec4_t<T>* dst) __attribute__((always_inline)) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a) dst[a] = *reinterpret_cast<const vec4_t<T>*>(gr + 32 * t + 8 * a);
+  };
+  auto gate_prefetch = [&](int r, int t0, int t1) __attribute__((always_inline)) {
+    if (G) {
+#pragma unroll
+      for (int t = t0; t < t1; ++t) gload(grow(r), t, graw[r][t]);
+    }
+  };
+  constexpr int GHALF = GPRE > 1 && QT == 1 ? GPRE / 2 : 0;  // tiles loaded during the last slice
 
   // Cross-chunk term, added last. Fast path: O'^T += R^T Q^T (its row scale
   // xi is the final row factor). Otherwise O = xi (.) (O_intra / xi + Q R):
   // a row whose xi is below 2^-100 skips it (its Q fragments are zeroed and
   // its scale is 1), the term being far below fp32 resolution there. The R^T
-  // slices stream through the two stages, the first one already in flight.
-  if (cross) {
-    float inv = 1.f;
-    if constexpr (!FAST) {
-      const float xi = gpow((float)(qrow - c0 + 1), lg);
-      if (xi >= 7.888609e-31f) {
-        inv = __builtin_amdgcn_rcpf(xi);
-      } else {
+  // slices stream through the two stages, the first one already in flight;
+  // every R^T fragment feeds the QT query tiles.
+  if constexpr (CROSS) {
+    if (nkb & 1) {  // the last key block sat in stage1
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      issue_slice(0, stage1);
+    }
+    float inv[QT];
 #pragma unroll
-        for (int s = 0; s < C::KS; ++s) qf[s] = zero_frag<T>();
+    for (int r = 0; r < QT; ++r) {
+      inv[r] = 1.f;
+      if constexpr (!FAST) {
+        const float xi = gpow((float)(qw0 + 32 * r + n - c0 + 1), lg);
+        if (xi >= 7.888609e-31f) {
+          inv[r] = __builtin_amdgcn_rcpf(xi);
+        } else {
+#pragma unroll
+          for (int s = 0; s < C::KS; ++s) qf[r][s] = zero_frag<T>();
+        }
+#pragma unroll
+        for (int t = 0; t < C::NT; ++t)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[r][t][i] *= inv[r];
       }
-#pragma unroll
-      for (int t = 0; t < C::NT; ++t)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[t][i] *= inv;
     }
     auto cross_slice = [&](auto sl_c, const char* buf) __attribute__((always_inline)) {
       constexpr int SL = decltype(sl_c)::value;
@@ -368,7 +454,9 @@ __device__ __forceinline__ void out_role(const FwdParams& p, int bh, int ci, int
 #pragma unroll
       for (int t = 0; t < NTT; ++t) {
         if (t + 2 < NTT) rb[(t + 2) % 3] = rload(t + 2);
-        oacc[t % C::NT] = mma32(rb[t % 3], qf[SL * SS + t / C::NT], oacc[t % C::NT]);
+#pragma unroll
+        for (int r = 0; r < QT; ++r)
+          oacc[r][t % C::NT] = mma32(rb[t % 3], qf[r][SL * SS + t / C::NT], oacc[r][t % C::NT]);
         __builtin_amdgcn_sched_barrier(0);
       }
     };
@@ -379,6 +467,7 @@ __device__ __forceinline__ void out_role(const FwdParams& p, int bh, int ci, int
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if constexpr (SL + 1 < C::NRS) issue_slice(SL + 1, nxt);
+        if constexpr (SL + 1 == C::NRS) gate_prefetch(0, 0, GHALF);
         cross_slice(sl_c, cur);
       };
       step(std::integral_constant<int, 0>{}, sa, sb);
@@ -389,62 +478,73 @@ __device__ __forceinline__ void out_role(const FwdParams& p, int bh, int ci, int
       }
     };
     static_assert(C::NRS == 2 || C::NRS == 4, "two or four R^T slices");
-    // the last key block used stage0 when nkb is odd, so slice 0 is in stage1
-    if (nkb & 1)
-      slices(stage1, stage0);
-    else
-      slices(stage0, stage1);
+    slices(stage1, stage0);
     if constexpr (!FAST) {
-      const float xi = inv == 1.f ? 1.f : gpow((float)(qrow - c0 + 1), lg);
+#pragma unroll
+      for (int r = 0; r < QT; ++r) {
+        const float xi = inv[r] == 1.f ? 1.f : gpow((float)(qw0 + 32 * r + n - c0 + 1), lg);
+#pragma unroll
+        for (int t = 0; t < C::NT; ++t)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[r][t][i] *= xi;
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < QT; ++r) gate_prefetch(r, CROSS && r == 0 ? GHALF : 0, GPRE);
+
+  // Epilogue, in registers: each lane holds half of one query row per tile
+  // (the other half is in lane ^ 32). GroupNorm over dv per (token, head) --
+  // with the fast path's row factor f: GN(f o') = (o' - mean') f / sqrt(f^2
+  // var' + eps) -- then the swish gate and 4-element stores.
+#pragma unroll
+  for (int r = 0; r < QT; ++r) {
+    const int qrow = qw0 + 32 * r + n;
+    const float f = FAST ? gpow((float)(qrow - ref), lg) : 1.f;
+    float mean = 0.f, scale = f;
+    if (G) {
+      float s1 = 0.f;
 #pragma unroll
       for (int t = 0; t < C::NT; ++t)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[t][i] *= xi;
-    }
-  }
-
-  // Epilogue, in registers: each lane holds half of one query row (the other
-  // half is in lane ^ 32). GroupNorm over dv per (token, head) -- with the
-  // fast path's row factor f: GN(f o') = (o' - mean') f / sqrt(f^2 var' + eps)
-  // -- then the swish gate and 4-element stores.
-  const float f = FAST ? gpow((float)(qrow - ref), lg) : 1.f;
-  float mean = 0.f, scale = f;
-  if (G) {
-    float s1 = 0.f;
+        for (int i = 0; i < 16; ++i) s1 += oacc[r][t][i];
+      mean = sum_pair32(s1) * (1.0f / D);
+      float s2 = 0.f;
 #pragma unroll
-    for (int t = 0; t < C::NT; ++t)
+      for (int t = 0; t < C::NT; ++t)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s1 += oacc[t][i];
-    mean = sum_pair32(s1) * (1.0f / D);
-    float s2 = 0.f;
-#pragma unroll
-    for (int t = 0; t < C::NT; ++t)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float d = oacc[t][i] - mean;
-        s2 += d * d;
-      }
-    scale = f * rsqrtf(f * f * (sum_pair32(s2) * (1.0f / D)) + p.eps);
-  }
-  if (qrow < cend) {
-    T* orow = O + (int64_t)qrow * tstride + 4 * hh;
-    const T* grow_ = G ? G + (int64_t)qrow * tstride + 4 * hh : nullptr;
-#pragma unroll
-    for (int t = 0; t < C::NT; ++t)
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const int col = 32 * t + 8 * a;  // + 4 hh + e
-        float y[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) y[e] = (oacc[t][4 * a + e] - mean) * scale;
-        if (G) {
-          float gv[4];
-          load4(grow_ + col, gv);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) y[e] *= swish(gv[e]);
+        for (int i = 0; i < 16; ++i) {
+          const float d = oacc[r][t][i] - mean;
+          s2 += d * d;
         }
-        store4(orow + col, y);
-      }
+      scale = f * rsqrtf(f * f * (sum_pair32(s2) * (1.0f / D)) + p.eps);
+    }
+    if (qrow < cend) {
+      T* orow = O + (int64_t)qrow * tstride + 4 * hh;
+      auto emit = [&](auto gate_c) __attribute__((always_inline)) {
+        constexpr bool GATE = decltype(gate_c)::value;
+        static_for<C::NT>([&](auto t_c) __attribute__((always_inline)) {
+          constexpr int t = decltype(t_c)::value;
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            const int col = 32 * t + 8 * a;  // + 4 hh + e
+            float y[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) y[e] = (oacc[r][t][4 * a + e] - mean) * scale;
+            if constexpr (GATE) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) y[e] *= swish((float)graw[r][t % GPRE][a][e]);
+            }
+            store4(orow + col, y);
+          }
+          if constexpr (GATE && t + GPRE < C::NT) gload(grow(r), t + GPRE, graw[r][t % GPRE]);
+        });
+      };
+      if (G)
+        emit(std::true_type{});
+      else
+        emit(std::false_type{});
+    }
   }
 }
 
@@ -462,21 +562,13 @@ __device__ __forceinline__ void scale_frag(f32x8& f, const float* z, const bool*
   for (int j = 0; j < 8; ++j) f[j] = keep[j] ? f[j] * z[j] : 0.f;
 }
 
-template <typename T, int D>
-__device__ __forceinline__ void state_issue(char* buf, const T* K, const T* V, int64_t tstride, int kb0, int rmax,
-                                            int wave, int lane) {
-  using KT = typename StTile<T, D>::KT;
-  using VT = typename StTile<T, D>::VT;
-  async_tile<T, KT, 4>(buf, K, tstride, kb0, rmax, wave, lane);
-  async_tile<T, VT, 4>(buf + KT::BYTES, V, tstride, kb0, rmax, wave, lane);
-}
-
 // State role: rows dk0 .. dk0+ROWS-1 (dk0 = ROWS part) of R_i for one chunk
 // of one (sequence, head). Accumulates dR = K^T (V (.) zeta) over the chunk's
 // keys, waits for those rows of R_{i-1} in the fp32 chain from the previous
 // chunk's workgroup, forms R_i = g^b R_{i-1} + dR, hands it on in the chain
 // and then publishes its snapshot R_i^T for the next chunk's output
-// workgroups. Wave w owns dv columns w DVW .. +DVW-1 of the rows.
+// workgroups. Wave (wr, wc) owns row tiles wr MTW .. +MTW-1 and dv tiles
+// wc NTW .. +NTW-1.
 template <typename T, int D>
 __device__ __forceinline__ void state_role(const FwdParams& p, int bh, int ci, int part, char* stage0,
                                            char* stage1) {
@@ -484,7 +576,9 @@ __device__ __forceinline__ void state_role(const FwdParams& p, int bh, int ci, i
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, hh = lane >> 5;
-  const int h = bh % p.heads, b = bh / p.heads;
+  // integer division runs on the vector unit: bring the uniform results back
+  // to scalar registers
+  const int h = uniform_i(bh % p.heads), b = uniform_i(bh / p.heads);
   const float lg = p.log2g[h];
   const int c0 = ci * p.chunk;
   const int cend = min(c0 + p.chunk, p.seqlen);
@@ -498,11 +592,15 @@ __device__ __forceinline__ void state_role(const FwdParams& p, int bh, int ci, i
   auto flag_of = [&](int j, int kind) __attribute__((always_inline)) {
     return p.ctrl + kCtrlHead + (bh * (p.nchunks + 1) + j) * kFlagsPerChunk + kind * kMaxSplit + part;
   };
-  // rows 4 hh + {0..3} + 8 a (a = 0..3) of dk tile mt hold accumulator elements
-  // 4a .. 4a+3; the columns are dv = dvw + 32 nt + n
-  const int dvw = wave * SC::DVW;
-  const bool active = dvw < D;  // every wave has columns when 4 DVW == D (uniform)
-  auto dk_of = [&](int mt, int a) __attribute__((always_inline)) { return dk0 + 32 * mt + 8 * a + 4 * hh; };
+  // rows 4 hh + {0..3} + 8 a (a = 0..3) of the wave's row tile mt hold
+  // accumulator elements 4a .. 4a+3; the columns are dv = dvw + 32 nt + n
+  const int wr = wave / SC::WC, wc = wave % SC::WC;
+  const int dvw = wc * SC::NTW * 32;
+  const int mt0 = wr * SC::MTW;       // first row tile of the wave
+  const bool active = wave < SC::ACTIVE;  // uniform
+  auto dk_of = [&](int mt, int a) __attribute__((always_inline)) {
+    return dk0 + 32 * (mt0 + mt) + 8 * a + 4 * hh;
+  };
   T* snap_next = reinterpret_cast<T*>(p.snap) + ((int64_t)bh * p.nchunks + ci + 1) * D * D;
   // Snapshot R^T in the output role's fragment order (see OutTile): the 4
   // values of (tile mt, nt, row group a) of lane (n, hh) are rows
@@ -510,43 +608,64 @@ __device__ __forceinline__ void state_role(const FwdParams& p, int bh, int ci, i
   // the fragment of lane (n, a%2) at step S, tile t. One store per lane writes
   // 8 bytes; a wave writes 512 contiguous bytes.
   using OT = OutTile<T, D>;
-  auto write_snapshot = [&](T* sn, const f32x16 (&acc)[SC::MT][SC::NTW]) __attribute__((always_inline)) {
+  auto write_snapshot = [&](T* sn, const f32x16 (&acc)[SC::MTW][SC::NTW]) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t rs = scalar_rsrc(sn);
+    const uint32_t voff = (uint32_t)((n * 8 + 4 * hh) * (int)sizeof(T));  // this lane's part
 #pragma unroll
-    for (int mt = 0; mt < SC::MT; ++mt)
+    for (int mt = 0; mt < SC::MTW; ++mt)
 #pragma unroll
       for (int nt = 0; nt < SC::NTW; ++nt)
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
-          const int S = (dk0 + 32 * mt) / 16 + a / 2;  // dk step
-          const int t = (dvw + 32 * nt) / 32;           // dv tile
-          const int64_t off = (int64_t)(S / (OT::RS / 16)) * OT::RS * D +
-                              ((int64_t)((S % (OT::RS / 16)) * OT::NT + t) * 64 + 32 * (a % 2) + n) * 8 + 4 * hh;
-          store4_coherent(sn + off, f32x4{acc[mt][nt][4 * a], acc[mt][nt][4 * a + 1], acc[mt][nt][4 * a + 2],
-                                          acc[mt][nt][4 * a + 3]});
+          const int S = (dk0 + 32 * (mt0 + mt)) / 16 + a / 2;  // dk step (uniform)
+          const int t = (dvw + 32 * nt) / 32;                   // dv tile (uniform)
+          const int soff = (S / (OT::RS / 16)) * OT::RS * D + (((S % (OT::RS / 16)) * OT::NT + t) * 64 + 32 * (a % 2)) * 8;
+          store4_coherent(rs, voff, (uint32_t)(soff * (int)sizeof(T)), (T*)nullptr,
+                          f32x4{acc[mt][nt][4 * a], acc[mt][nt][4 * a + 1], acc[mt][nt][4 * a + 2], acc[mt][nt][4 * a + 3]});
         }
   };
-
-  f32x16 racc[SC::MT][SC::NTW];
+  // R_i accumulates from g^b R_{i-1}: for chunk 0 with an initial state that
+  // term is added here (R_{-1} = state_in, also published for the output
+  // workgroups of chunk 0); for later chunks after the keys, from the chain
+  const float dec = gpow((float)(cend - c0), lg);
+  f32x16 racc[SC::MTW][SC::NTW];
   if (ci == 0 && p.state_in && active) {
-    // R_{-1} = state_in: publish it for the output workgroups of chunk 0
     const float* S0 = p.state_in + (int64_t)bh * D * D;
 #pragma unroll
-    for (int mt = 0; mt < SC::MT; ++mt)
+    for (int mt = 0; mt < SC::MTW; ++mt)
 #pragma unroll
       for (int nt = 0; nt < SC::NTW; ++nt)
 #pragma unroll
         for (int i = 0; i < 16; ++i)
           racc[mt][nt][i] = S0[(int64_t)(dk_of(mt, i / 4) + i % 4) * D + dvw + 32 * nt + n];
     write_snapshot(reinterpret_cast<T*>(p.snap) + (int64_t)bh * p.nchunks * D * D, racc);
+#pragma unroll
+    for (int mt = 0; mt < SC::MTW; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < SC::NTW; ++nt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) racc[mt][nt][i] *= dec;
+  } else {
+#pragma unroll
+    for (int mt = 0; mt < SC::MTW; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < SC::NTW; ++nt) racc[mt][nt] = zero16();
   }
   if (ci == 0 && p.state_in) release_flag(flag_of(0, 1));
-#pragma unroll
-  for (int mt = 0; mt < SC::MT; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < SC::NTW; ++nt) racc[mt][nt] = zero16();
 
+  TileLoads<T, typename SC::KT, SC::NW> kload;
+  TileLoads<T, typename SC::VT, SC::NW> vload;
+  kload.init(tstride, lane);
+  vload.init(tstride, lane);
   auto issue_kv = [&](int j, char* buf) __attribute__((always_inline)) {
-    state_issue<T, D>(buf, K, V, tstride, c0 + j * SC::BK, cend - 1, wave, lane);
+    const int kb0 = c0 + j * SC::BK;
+    if (kb0 + SC::BK <= cend) {
+      kload.issue(buf, K, tstride, kb0, wave);
+      vload.issue(buf + SC::KT::BYTES, V, tstride, kb0, wave);
+    } else {
+      kload.issue_clamped(buf, K, tstride, kb0, cend - 1, wave);
+      vload.issue_clamped(buf + SC::KT::BYTES, V, tstride, kb0, cend - 1, wave);
+    }
   };
   // zeta_k = g^(cend-1-k); fragment element j is key k0 + kj(j) with
   // kj(j) = 4 hh + j (j < 4), 8 + 4 hh + j - 4 (j >= 4)
@@ -579,20 +698,20 @@ __device__ __forceinline__ void state_role(const FwdParams& p, int bh, int ci, i
           z[j] = zs * zl[j];
         }
       }
-      frag_t<T> af[SC::MT];
+      frag_t<T> af[SC::MTW];
 #pragma unroll
-      for (int mt = 0; mt < SC::MT; ++mt) af[mt] = tile_col8w<typename SC::KT>(kt, 16 * ks, 32 * mt, lane, (T*)nullptr);
+      for (int mt = 0; mt < SC::MTW; ++mt)
+        af[mt] = tile_col8w<typename SC::KT>(kt, 16 * ks, 32 * (mt0 + mt), lane, (T*)nullptr);
 #pragma unroll
       for (int nt = 0; nt < SC::NTW; ++nt) {
-        // zeta scales this wave's own V fragments (the K^T fragments are
-        // shared by all four waves)
+        // zeta scales this wave's own V fragments (fewer than its K^T ones)
         frag_t<T> vb = tile_col8w<typename SC::VT>(vt, 16 * ks, dvw + 32 * nt, lane, (T*)nullptr);
         if (ragged)
           scale_frag(vb, z, keep);
         else
           scale_frag(vb, z);
 #pragma unroll
-        for (int mt = 0; mt < SC::MT; ++mt) racc[mt][nt] = mma32(af[mt], vb, racc[mt][nt]);
+        for (int mt = 0; mt < SC::MTW; ++mt) racc[mt][nt] = mma32(af[mt], vb, racc[mt][nt]);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -614,54 +733,55 @@ __device__ __forceinline__ void state_role(const FwdParams& p, int bh, int ci, i
 
   // R_i = g^b R_{i-1} + dR_i. The fp32 chain keeps R in this role's
   // accumulator layout (16 contiguous floats per lane and tile), so the next
-  // chunk's workgroup of the same part reads it back coalesced.
-  // element pair q of tile (mt, nt): a wave's 8-byte accesses cover 512
-  // contiguous bytes
-  auto chain_pair = [&](int slot, int mt, int nt, int q) __attribute__((always_inline)) {
-    return reinterpret_cast<uint64_t*>(p.chain + ((int64_t)bh * 2 + slot) * D * D) +
-           (((((part * 4 + wave) * SC::MT + mt) * SC::NTW + nt) * 8 + q) * 64 + lane);
+  // chunk's workgroup of the same part reads it back coalesced: element pair
+  // q of tile (mt, nt) of a wave sits at a wave-uniform offset, its lanes'
+  // 8-byte accesses covering 512 contiguous bytes.
+  auto chain_rsrc = [&](int slot) __attribute__((always_inline)) {
+    return scalar_rsrc(p.chain + ((int64_t)bh * 2 + slot) * D * D);
   };
-  const float dec = gpow((float)(cend - c0), lg);
+  auto chain_soff = [&](int mt, int nt, int q) __attribute__((always_inline)) {
+    return (uint32_t)((((((part * SC::NW + wave) * SC::MTW + mt) * SC::NTW + nt) * 8 + q) * 64) * 8);
+  };
+  const uint32_t chain_voff = (uint32_t)lane * 8u;
   if (ci > 0) {
     wait_flag(flag_of(ci, 0), p.ctrl + 1);
     if (active) {
-      const int slot = (ci - 1) & 1;
+      const __amdgpu_buffer_rsrc_t rs = chain_rsrc((ci - 1) & 1);
       typedef float f32x2 __attribute__((ext_vector_type(2)));
+      // one 32-row tile at a time, every load of the tile in flight before
+      // the first use (the compiler would otherwise wait on each in turn)
 #pragma unroll
-      for (int mt = 0; mt < SC::MT; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < SC::NTW; ++nt)
-#pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            const f32x2 r = __builtin_bit_cast(
-                f32x2, __hip_atomic_load(chain_pair(slot, mt, nt, q), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-            racc[mt][nt][2 * q] += dec * r[0];
-            racc[mt][nt][2 * q + 1] += dec * r[1];
-          }
-    }
-  } else if (p.state_in && active) {
-    const float* S0 = p.state_in + (int64_t)bh * D * D;
-#pragma unroll
-    for (int mt = 0; mt < SC::MT; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < SC::NTW; ++nt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          racc[mt][nt][i] += dec * S0[(int64_t)(dk_of(mt, i / 4) + i % 4) * D + dvw + 32 * nt + n];
-  }
-  if (ci + 1 < p.nchunks) {
-    // the next state workgroup needs only the chain: release it first
-    if (active) {
-      typedef float f32x2 __attribute__((ext_vector_type(2)));
-#pragma unroll
-      for (int mt = 0; mt < SC::MT; ++mt)
+      for (int mt = 0; mt < SC::MTW; ++mt) {
+        uint64_t r[SC::NTW][8];
 #pragma unroll
         for (int nt = 0; nt < SC::NTW; ++nt)
 #pragma unroll
           for (int q = 0; q < 8; ++q)
-            __hip_atomic_store(chain_pair(ci & 1, mt, nt, q),
-                               __builtin_bit_cast(uint64_t, f32x2{racc[mt][nt][2 * q], racc[mt][nt][2 * q + 1]}),
-                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            r[nt][q] = __builtin_bit_cast(uint64_t, load2_coherent(rs, chain_voff, chain_soff(mt, nt, q)));
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int nt = 0; nt < SC::NTW; ++nt)
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const f32x2 x = __builtin_bit_cast(f32x2, r[nt][q]);
+            racc[mt][nt][2 * q] += dec * x[0];
+            racc[mt][nt][2 * q + 1] += dec * x[1];
+          }
+        __builtin_amdgcn_sched_barrier(0);  // the next tile's loads stay behind this one's uses
+      }
+    }
+  }
+  if (ci + 1 < p.nchunks) {
+    // the next state workgroup needs only the chain: release it first
+    if (active) {
+      const __amdgpu_buffer_rsrc_t rs = chain_rsrc(ci & 1);
+#pragma unroll
+      for (int mt = 0; mt < SC::MTW; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < SC::NTW; ++nt)
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+            store2_coherent(rs, chain_voff, chain_soff(mt, nt, q), racc[mt][nt][2 * q], racc[mt][nt][2 * q + 1]);
     }
     release_flag(flag_of(ci + 1, 0));
     if (active) write_snapshot(snap_next, racc);
@@ -669,7 +789,7 @@ __device__ __forceinline__ void state_role(const FwdParams& p, int bh, int ci, i
   } else if (p.state_out && active) {
     float* SO = p.state_out + (int64_t)bh * D * D;
 #pragma unroll
-    for (int mt = 0; mt < SC::MT; ++mt)
+    for (int mt = 0; mt < SC::MTW; ++mt)
 #pragma unroll
       for (int nt = 0; nt < SC::NTW; ++nt)
 #pragma unroll
@@ -681,7 +801,7 @@ __device__ __forceinline__ void state_role(const FwdParams& p, int bh, int ci, i
 // Kernels.
 // ---------------------------------------------------------------------------
 template <typename T, int D, bool FAST>
-__global__ __launch_bounds__(256, 1) void retention_parallel_kernel(FwdParams p) {
+__global__ __launch_bounds__(kWaves<T> * 64, 1) void retention_parallel_kernel(FwdParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the kernel's signature
   __shared__ __attribute__((aligned(1024))) char stage0[Stage<T, D>::BYTES];
   __shared__ __attribute__((aligned(1024))) char stage1[Stage<T, D>::BYTES];
@@ -696,12 +816,12 @@ __global__ __launch_bounds__(256, 1) void retention_parallel_kernel(FwdParams p)
     bh = bid / p.qblocks;
     qb = p.qblocks - 1 - bid % p.qblocks;
   }
-  out_role<T, D, FAST>(p, bh, 0, qb, false, stage0, stage1);
+  out_role<T, D, FAST, false>(p, bh, 0, qb, false, stage0, stage1);
 #endif
 }
 
 template <typename T, int D, bool FAST>
-__global__ __launch_bounds__(256, 1) void retention_chunkwise_kernel(FwdParams p) {
+__global__ __launch_bounds__(kWaves<T> * 64, 1) void retention_chunkwise_kernel(FwdParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the kernel's signature
   __shared__ __attribute__((aligned(1024))) char stage0[Stage<T, D>::BYTES];
   __shared__ __attribute__((aligned(1024))) char stage1[Stage<T, D>::BYTES];
@@ -717,8 +837,8 @@ __global__ __launch_bounds__(256, 1) void retention_chunkwise_kernel(FwdParams p
     s_ticket = p.xcd_order ? atomicAdd(p.ctrl + kTicketWord + cls, 1) : atomicAdd(p.ctrl + kTicketWord, 1);
   }
   __syncthreads();
-  const int t = s_ticket;
-  int ci, bh, role;  // role < SPLIT: state part; else query block qblocks-1-(role-SPLIT)
+  const int t = __builtin_amdgcn_readfirstlane(s_ticket);  // uniform: scalar registers for all it derives
+  int ci, bh, role;  // role slot inside the chunk (see below)
   if (p.xcd_order) {
     // Class c owns the (sequence, head) pairs bh = 8j + c and takes them
     // chunk-major, role-major: every dependency stays inside the class, and
@@ -735,11 +855,19 @@ __global__ __launch_bounds__(256, 1) void retention_chunkwise_kernel(FwdParams p
     bh = r / roles;
     role = r % roles;
   }
-  const int qb = role < SPLIT ? -1 : p.qblocks - 1 - (role - SPLIT);
+  ci = uniform_i(ci);
+  bh = uniform_i(bh);
+  role = uniform_i(role);
+  // role order inside a chunk: the longest query block first (it pulls the
+  // chunk's K and V from HBM while the state workgroups follow into L2), the
+  // state parts, then the other query blocks
+  const int qb = role == 0 ? p.qblocks - 1 : role <= SPLIT ? -1 : p.qblocks - 1 - (role - SPLIT);
   if (qb < 0)
-    state_role<T, D>(p, bh, ci, role, stage0, stage1);
+    state_role<T, D>(p, bh, ci, role - 1, stage0, stage1);
+  else if (ci > 0 || p.has_state0)
+    out_role<T, D, FAST, true>(p, bh, ci, qb, true, stage0, stage1);
   else
-    out_role<T, D, FAST>(p, bh, ci, qb, true, stage0, stage1);
+    out_role<T, D, FAST, false>(p, bh, ci, qb, true, stage0, stage1);
 #endif
 }
 
@@ -755,7 +883,7 @@ static hipError_t launch_fwd_impl(const Shape& s, int chunk, FwdParams p, bool c
   if (!chunked) {
     const int64_t blocks = (int64_t)bhs * p.qblocks;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((retention_parallel_kernel<T, D, FAST>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((retention_parallel_kernel<T, D, FAST>), dim3((unsigned)blocks), dim3(64 * C::WAVES), 0, stream, p);
     return hipGetLastError();
   }
   const int64_t nctrl = kCtrlHead + (int64_t)bhs * (p.nchunks + 1) * kFlagsPerChunk;
@@ -764,7 +892,7 @@ static hipError_t launch_fwd_impl(const Shape& s, int chunk, FwdParams p, bool c
   p.xcd_order = bhs % 8 == 0;
   const int64_t blocks = (int64_t)p.nchunks * bhs * (StTile<T, D>::SPLIT + p.qblocks);
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((retention_chunkwise_kernel<T, D, FAST>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((retention_chunkwise_kernel<T, D, FAST>), dim3((unsigned)blocks), dim3(64 * C::WAVES), 0, stream, p);
   return hipGetLastError();
 }
 

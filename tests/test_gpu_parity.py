@@ -197,9 +197,9 @@ def test_chunkwise_handoff_completes(b, h):
     torch.cuda.synchronize()
     ctrl = ws[:64].view(torch.int32).cpu()
     nchunks = -(-n // chunk)
-    # d/128 state workgroups (d = 256) and one output workgroup (up to 192
-    # rows) per (sequence, head, chunk)
-    total = nchunks * b * h * (2 + 1)
+    # one state workgroup (bf16 runs eight waves per workgroup) and one output
+    # workgroup (the whole 128-row chunk) per (sequence, head, chunk)
+    total = nchunks * b * h * (1 + 1)
     assert int(ctrl[0]) == total
     assert int(ctrl[1]) == 0
     if (b * h) % 8 == 0:
