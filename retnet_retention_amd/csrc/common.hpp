@@ -131,6 +131,27 @@ __device__ __forceinline__ F8 load8(const float* p) {
   return F8{{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w}};
 }
 
+// 16 bytes of T (8 bf16 or 4 fp32 elements) to and from floats
+__device__ __forceinline__ void load16f(const bf16* p, float* v) {
+  const bf16x8 x = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = (float)x[i];
+}
+__device__ __forceinline__ void load16f(const float* p, float* v) {
+  const f32x4 x = *reinterpret_cast<const f32x4*>(p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = x[i];
+}
+__device__ __forceinline__ void store16f(bf16* p, const float* v) {
+  bf16x8 o;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = (bf16)v[i];
+  *reinterpret_cast<bf16x8*>(p) = o;
+}
+__device__ __forceinline__ void store16f(float* p, const float* v) {
+  *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
+}
+
 __device__ __forceinline__ void store8(bf16* p, const F8& v) {
   bf16x8 o;
 #pragma unroll
@@ -144,6 +165,12 @@ __device__ __forceinline__ void store8(float* p, const F8& v) {
 }
 
 // Four consecutive elements (8 bytes of bf16, 16 of fp32) to and from floats.
+// Bare workgroup barrier: no wait of any kind is attached (a fence would
+// also wait for the direct loads still in flight into other LDS buffers).
+// The caller waits for what the barrier must cover (s_waitcnt); the memory
+// clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void bare_barrier() { __asm__ volatile("s_barrier" ::: "memory"); }
+
 // a wave-uniform int held in a scalar register
 __device__ __forceinline__ int uniform_i(int x) { return __builtin_amdgcn_readfirstlane(x); }
 

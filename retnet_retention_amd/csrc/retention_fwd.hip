@@ -57,8 +57,9 @@ struct OutTile {
   static constexpr int KH = BN / 32;           // 32-key steps per block
   static constexpr int KS = D / 16;            // contraction steps over dk
   static constexpr int NT = D / 32;            // 32-wide dv tiles
-  // dk columns per R^T slice; the slices stream through the two stages
-  static constexpr int RS = D / 2 < 256 / E ? D / 2 : 256 / E;
+  // dk columns per R^T slice (32 KiB at most); the slices stream through
+  // two LDS arrays
+  static constexpr int RS = D / 2 < 128 / E ? D / 2 : 128 / E;
   static constexpr int NRS = D / RS;
   using KT = LTile<T, BN, D, kRowTile>;  // K block, row fragments
   using VT = LTile<T, BN, D, kColTile>;  // V block, column (transpose) fragments
@@ -91,7 +92,7 @@ struct StTile {
   static constexpr int NW = kWaves<T>;
   static constexpr int SPLIT = NW < 8 && D > 128 ? D / 128 : 1;
   static constexpr int ROWS = D / SPLIT;        // dk rows per workgroup
-  static constexpr int BK = OutTile<T, D>::BN;  // keys per block
+  static constexpr int BK = 32 / (int)sizeof(T) * 2;  // keys per block: 32 (bf16), 16 (fp32)
   static constexpr int MTA = ROWS / 32, NTA = D / 32;   // tiles of the workgroup
   // wave columns: with eight waves two wave rows, so that a wave's 4 tiles
   // take 2 K^T and 2 V fragments per step (4 x 1 tiles would take 5)
@@ -113,10 +114,21 @@ constexpr int kFlagsPerChunk = 2 * kMaxSplit;
 
 template <typename T, int D>
 struct Stage {
+  // Four LDS arrays of BYTES each. The output role's two stages are arrays
+  // (0, 1) and (2, 3) (K tile, V tile), its R^T slices alternate between
+  // arrays 2 and 0; the state role keeps four stages, one per array, with
+  // up to three blocks in flight.
   using O = OutTile<T, D>;
   using S = StTile<T, D>;
-  static constexpr int A = O::KVB > O::RT_BYTES ? O::KVB : O::RT_BYTES;
-  static constexpr int BYTES = A > S::KVB ? A : S::KVB;
+  static constexpr int max2(int a, int b) { return a > b ? a : b; }
+  // output epilogue: each wave stages its 32 rows, HALF dv columns at a
+  // time, as fp32 rows of EROW bytes (padded against bank conflicts); two
+  // waves share an array
+  static constexpr int HALF = D < 128 ? D : 128;
+  static constexpr int EROW = HALF * 4 + 16;
+  static constexpr int BYTES =
+      max2(max2(max2(O::KT::BYTES, O::VT::BYTES), max2(O::RT_BYTES, S::KVB)), 2 * 32 * EROW);
+  static_assert(O::WAVES <= 8, "two waves per array");
 };
 
 struct FwdParams {
@@ -206,8 +218,8 @@ __device__ __forceinline__ u32x2 load2_coherent(__amdgpu_buffer_rsrc_t rs, uint3
 // CROSS: the chunk has a previous state R_{i-1} (chunkwise form, chunk > 0
 // or an initial state); the parallel form and chunk 0 without one have none.
 template <typename T, int D, bool FAST, bool CROSS>
-__device__ __forceinline__ void out_role(const FwdParams& p, int bh, int ci, int qb, bool chunked, char* stage0,
-                                         char* stage1) {
+__device__ __forceinline__ void out_role(const FwdParams& p, int bh, int ci, int qb, bool chunked, char* l0, char* l1,
+                                         char* l2, char* l3) {
   using C = OutTile<T, D, FAST>;
   constexpr int QT = C::QT;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -241,14 +253,14 @@ __device__ __forceinline__ void out_role(const FwdParams& p, int bh, int ci, int
   TileLoads<T, typename C::VT, C::WAVES> vload;
   kload.init(tstride, lane);
   vload.init(tstride, lane);
-  auto issue_kv = [&](int j, char* buf) __attribute__((always_inline)) {
+  auto issue_kv = [&](int j, char* kbuf, char* vbuf) __attribute__((always_inline)) {
     const int kb0 = c0 + j * C::BN;
     if (kb0 + C::BN <= cend) {
-      kload.issue(buf, K, tstride, kb0, wave);
-      vload.issue(buf + C::KT::BYTES, V, tstride, kb0, wave);
+      kload.issue(kbuf, K, tstride, kb0, wave);
+      vload.issue(vbuf, V, tstride, kb0, wave);
     } else {
-      kload.issue_clamped(buf, K, tstride, kb0, cend - 1, wave);
-      vload.issue_clamped(buf + C::KT::BYTES, V, tstride, kb0, cend - 1, wave);
+      kload.issue_clamped(kbuf, K, tstride, kb0, cend - 1, wave);
+      vload.issue_clamped(vbuf, V, tstride, kb0, cend - 1, wave);
     }
   };
   const T* R = CROSS ? reinterpret_cast<const T*>(p.snap) + ((int64_t)bh * p.nchunks + ci) * D * D : nullptr;
@@ -262,7 +274,7 @@ __device__ __forceinline__ void out_role(const FwdParams& p, int bh, int ci, int
     }
     async_flat<T, C::RT_BYTES, C::WAVES, kCoherent>(buf, R + (int64_t)sl * C::RS * D, wave, lane);
   };
-  issue_kv(0, stage1);
+  issue_kv(0, l2, l3);
 
   // Query fragments of this lane's rows, kept in registers for the whole
   // workgroup life: qf[r][s] = Q[qw0 + 32 r + n][16 s + 8 hh .. +7]. Rows
@@ -301,9 +313,8 @@ __device__ __forceinline__ void out_role(const FwdParams& p, int bh, int ci, int
   // read from LDS feeds the QT query tiles; the fragments of a step form one
   // sequence of LDS reads with a two-deep prefetch ring.
   constexpr int U = C::KS + 2 * C::NT;  // fragment reads per 32-key step
-  auto key_block = [&](int kb0, const char* kt) __attribute__((always_inline)) {
+  auto key_block = [&](int kb0, const char* kt, const char* vt) __attribute__((always_inline)) {
     if (kb0 > qw0 + C::QW - 1) return;  // block above this wave's rows (uniform)
-    const char* vt = kt + C::KT::BYTES;
     const bool diag = kb0 + C::BN - 1 > qw0;  // some key may follow some row (uniform)
     auto load = [&](auto t_c) __attribute__((always_inline)) {
       constexpr int t = decltype(t_c)::value, kh = t / U, u = t % U;
@@ -367,61 +378,40 @@ __device__ __forceinline__ void out_role(const FwdParams& p, int bh, int ci, int
   };
 
   // One pipeline step: wait for block j, release the other stage, prefetch
-  // block j+1 into it. Block j sits in stage1 for even j, stage0 for odd j,
-  // so that after an even number of blocks the last step prefetches the first
-  // R^T slice into stage1 (after an odd number the slice is loaded once the
-  // last block is done). The stages are distinct LDS objects and the loop is
-  // unrolled by two, so the compiler can tell the reads of one stage from the
-  // in-flight loads into the other.
-  auto sync_and_prefetch = [&](int j, char* nxt, auto slice_c) __attribute__((always_inline)) {
+  // block j+1 into it. Block j sits in stage (2, 3) for even j, (0, 1) for
+  // odd j, so that after an even number of blocks the last step prefetches
+  // the first R^T slice into array 2 (after an odd number the slice is
+  // loaded once the last block is done). The arrays are distinct LDS objects
+  // and the loop is unrolled by two, so the compiler can tell the reads of
+  // one stage from the in-flight loads into the other.
+  auto sync_and_prefetch = [&](int j, char* nk, char* nv, auto slice_c) __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (j + 1 < nkb)
-      issue_kv(j + 1, nxt);
+      issue_kv(j + 1, nk, nv);
     else if constexpr (CROSS && decltype(slice_c)::value)
-      issue_slice(0, nxt);
+      issue_slice(0, nk);
   };
   for (int j = 0; j < nkb; j += 2) {
-    sync_and_prefetch(j, stage0, std::false_type{});
-    key_block(c0 + j * C::BN, stage1);
+    sync_and_prefetch(j, l0, l1, std::false_type{});
+    key_block(c0 + j * C::BN, l2, l3);
     if (j + 1 < nkb) {
-      sync_and_prefetch(j + 1, stage1, std::true_type{});
-      key_block(c0 + (j + 1) * C::BN, stage0);
+      sync_and_prefetch(j + 1, l2, l3, std::true_type{});
+      key_block(c0 + (j + 1) * C::BN, l0, l1);
     }
   }
-
-  // Gate values of this lane's half-rows, loaded as soon as registers free
-  // up: bf16 all dv tiles (half of them during the last R^T slice, whose
-  // predecessors' query fragments are dead, the rest after the cross term),
-  // fp32 one tile ahead of use in the epilogue.
-  constexpr int GPRE = sizeof(T) == 2 ? C::NT : 1;
-  vec4_t<T> graw[QT][GPRE][4];
-  auto grow = [&](int r) __attribute__((always_inline)) {
-    return G + (int64_t)min(qw0 + 32 * r + n, cend - 1) * tstride + 4 * hh;
-  };
-  auto gload = [&](const T* gr, int t, vec4_t<T>* dst) __attribute__((always_inline)) {
-#pragma unroll
-    for (int a = 0; a < 4; ++a) dst[a] = *reinterpret_cast<const vec4_t<T>*>(gr + 32 * t + 8 * a);
-  };
-  auto gate_prefetch = [&](int r, int t0, int t1) __attribute__((always_inline)) {
-    if (G) {
-#pragma unroll
-      for (int t = t0; t < t1; ++t) gload(grow(r), t, graw[r][t]);
-    }
-  };
-  constexpr int GHALF = GPRE > 1 && QT == 1 ? GPRE / 2 : 0;  // tiles loaded during the last slice
 
   // Cross-chunk term, added last. Fast path: O'^T += R^T Q^T (its row scale
   // xi is the final row factor). Otherwise O = xi (.) (O_intra / xi + Q R):
   // a row whose xi is below 2^-100 skips it (its Q fragments are zeroed and
   // its scale is 1), the term being far below fp32 resolution there. The R^T
-  // slices stream through the two stages, the first one already in flight;
+  // slices stream through two LDS arrays, the first one already in flight;
   // every R^T fragment feeds the QT query tiles.
   if constexpr (CROSS) {
-    if (nkb & 1) {  // the last key block sat in stage1
+    if (nkb & 1) {  // the last key block sat in arrays 2 and 3
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-      issue_slice(0, stage1);
+      issue_slice(0, l2);
     }
     float inv[QT];
 #pragma unroll
@@ -460,25 +450,17 @@ __device__ __forceinline__ void out_role(const FwdParams& p, int bh, int ci, int
         __builtin_amdgcn_sched_barrier(0);
       }
     };
-    // slice SL sits in stage `sa`; slice SL+1 goes into stage `sb` meanwhile
-    auto slices = [&](char* sa, char* sb) __attribute__((always_inline)) {
-      auto step = [&](auto sl_c, char* cur, char* nxt) __attribute__((always_inline)) {
-        constexpr int SL = decltype(sl_c)::value;
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if constexpr (SL + 1 < C::NRS) issue_slice(SL + 1, nxt);
-        if constexpr (SL + 1 == C::NRS) gate_prefetch(0, 0, GHALF);
-        cross_slice(sl_c, cur);
-      };
-      step(std::integral_constant<int, 0>{}, sa, sb);
-      step(std::integral_constant<int, 1>{}, sb, sa);
-      if constexpr (C::NRS > 2) {
-        step(std::integral_constant<int, 2>{}, sa, sb);
-        step(std::integral_constant<int, 3>{}, sb, sa);
-      }
-    };
-    static_assert(C::NRS == 2 || C::NRS == 4, "two or four R^T slices");
-    slices(stage1, stage0);
+    // slice SL sits in array 2 (even SL) or 0 (odd SL); slice SL+1 goes into
+    // the other one meanwhile
+    static_for<C::NRS>([&](auto sl_c) __attribute__((always_inline)) {
+      constexpr int SL = decltype(sl_c)::value;
+      char* cur = SL % 2 == 0 ? l2 : l0;
+      char* nxt = SL % 2 == 0 ? l0 : l2;
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if constexpr (SL + 1 < C::NRS) issue_slice(SL + 1, nxt);
+      cross_slice(sl_c, cur);
+    });
     if constexpr (!FAST) {
 #pragma unroll
       for (int r = 0; r < QT; ++r) {
@@ -490,13 +472,21 @@ __device__ __forceinline__ void out_role(const FwdParams& p, int bh, int ci, int
       }
     }
   }
-#pragma unroll
-  for (int r = 0; r < QT; ++r) gate_prefetch(r, CROSS && r == 0 ? GHALF : 0, GPRE);
-
-  // Epilogue, in registers: each lane holds half of one query row per tile
-  // (the other half is in lane ^ 32). GroupNorm over dv per (token, head) --
-  // with the fast path's row factor f: GN(f o') = (o' - mean') f / sqrt(f^2
-  // var' + eps) -- then the swish gate and 4-element stores.
+  // Epilogue. GroupNorm over dv per (token, head) from the registers (each
+  // lane holds half of one query row per tile, the other half in lane ^ 32)
+  // -- with the fast path's row factor f: GN(f o') = (o' - mean') f /
+  // sqrt(f^2 var' + eps) --, then the swish gate. The normalized rows pass
+  // through the wave's own LDS area, HALF dv columns at a time, so that the
+  // gate loads and the output stores run along rows: LPR lanes cover the
+  // HALF columns of one row with 16-byte accesses.
+  using SG = Stage<T, D>;
+  constexpr int CPL = 16 / (int)sizeof(T);  // columns per lane access
+  constexpr int LPR = SG::HALF / CPL;       // lanes per row
+  constexpr int RPA = 64 / LPR;             // rows per access
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();  // every wave is done with the LDS arrays
+  char* stg = (wave >> 1) == 0 ? l0 : (wave >> 1) == 1 ? l1 : (wave >> 1) == 2 ? l2 : l3;
+  stg += (wave & 1) * 32 * SG::EROW;
 #pragma unroll
   for (int r = 0; r < QT; ++r) {
     const int qrow = qw0 + 32 * r + n;
@@ -519,32 +509,44 @@ __device__ __forceinline__ void out_role(const FwdParams& p, int bh, int ci, int
         }
       scale = f * rsqrtf(f * f * (sum_pair32(s2) * (1.0f / D)) + p.eps);
     }
-    if (qrow < cend) {
-      T* orow = O + (int64_t)qrow * tstride + 4 * hh;
-      auto emit = [&](auto gate_c) __attribute__((always_inline)) {
-        constexpr bool GATE = decltype(gate_c)::value;
-        static_for<C::NT>([&](auto t_c) __attribute__((always_inline)) {
-          constexpr int t = decltype(t_c)::value;
+    static_for<D / SG::HALF>([&](auto h_c) __attribute__((always_inline)) {
+      constexpr int H = decltype(h_c)::value;
+      // this pass's gate values, 16 bytes per row access, ahead of their use
+      const int lrow = lane / LPR, lcol = (lane % LPR) * CPL;
+      float g[32 / RPA][CPL];
+      if (G) {
 #pragma unroll
-          for (int a = 0; a < 4; ++a) {
-            const int col = 32 * t + 8 * a;  // + 4 hh + e
-            float y[4];
+        for (int k = 0; k < 32 / RPA; ++k)
+          load16f(G + (int64_t)min(qw0 + 32 * r + k * RPA + lrow, cend - 1) * tstride + H * SG::HALF + lcol, g[k]);
+      }
+      // normalized values of dv tiles H HALF/32 .. into the staging rows
 #pragma unroll
-            for (int e = 0; e < 4; ++e) y[e] = (oacc[r][t][4 * a + e] - mean) * scale;
-            if constexpr (GATE) {
+      for (int t = H * SG::HALF / 32; t < (H + 1) * SG::HALF / 32; ++t)
 #pragma unroll
-              for (int e = 0; e < 4; ++e) y[e] *= swish((float)graw[r][t % GPRE][a][e]);
-            }
-            store4(orow + col, y);
-          }
-          if constexpr (GATE && t + GPRE < C::NT) gload(grow(r), t + GPRE, graw[r][t % GPRE]);
-        });
-      };
-      if (G)
-        emit(std::true_type{});
-      else
-        emit(std::false_type{});
-    }
+        for (int a = 0; a < 4; ++a) {
+          const int col = 32 * t - H * SG::HALF + 8 * a + 4 * hh;
+          *reinterpret_cast<f32x4*>(stg + n * SG::EROW + col * 4) =
+              f32x4{(oacc[r][t][4 * a] - mean) * scale, (oacc[r][t][4 * a + 1] - mean) * scale,
+                    (oacc[r][t][4 * a + 2] - mean) * scale, (oacc[r][t][4 * a + 3] - mean) * scale};
+        }
+      // along the rows: gate, store
+#pragma unroll
+      for (int k = 0; k < 32 / RPA; ++k) {
+        const int rr = k * RPA + lrow, orow = qw0 + 32 * r + rr;
+        float y[CPL];
+#pragma unroll
+        for (int e = 0; e < CPL; e += 4) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(stg + rr * SG::EROW + (lcol + e) * 4);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) y[e + i] = v[i];
+        }
+        if (G) {
+#pragma unroll
+          for (int e = 0; e < CPL; ++e) y[e] *= swish(g[k][e]);
+        }
+        if (orow < cend) store16f(O + (int64_t)orow * tstride + H * SG::HALF + lcol, y);
+      }
+    });
   }
 }
 
@@ -570,8 +572,8 @@ __device__ __forceinline__ void scale_frag(f32x8& f, const float* z, const bool*
 // workgroups. Wave (wr, wc) owns row tiles wr MTW .. +MTW-1 and dv tiles
 // wc NTW .. +NTW-1.
 template <typename T, int D>
-__device__ __forceinline__ void state_role(const FwdParams& p, int bh, int ci, int part, char* stage0,
-                                           char* stage1) {
+__device__ __forceinline__ void state_role(const FwdParams& p, int bh, int ci, int part, char* l0, char* l1,
+                                           char* l2, char* l3) {
   using SC = StTile<T, D>;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -657,7 +659,7 @@ __device__ __forceinline__ void state_role(const FwdParams& p, int bh, int ci, i
   TileLoads<T, typename SC::VT, SC::NW> vload;
   kload.init(tstride, lane);
   vload.init(tstride, lane);
-  auto issue_kv = [&](int j, char* buf) __attribute__((always_inline)) {
+  auto issue_kv = [&](int j, char* buf) __attribute__((always_inline)) {  // K^T then V tile
     const int kb0 = c0 + j * SC::BK;
     if (kb0 + SC::BK <= cend) {
       kload.issue(buf, K, tstride, kb0, wave);
@@ -716,19 +718,46 @@ __device__ __forceinline__ void state_role(const FwdParams& p, int bh, int ci, i
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  issue_kv(0, stage0);
-  auto sync_and_prefetch = [&](int j, char* nxt) __attribute__((always_inline)) {
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (j + 1 < nkb) issue_kv(j + 1, nxt);
+  // Four stages (one LDS array each), up to three blocks in flight: block j
+  // sits in array j % 4. Before block j is read every wave waits until at
+  // most its loads of the (up to two) later blocks are outstanding; the
+  // barrier then frees array (j - 1) % 4 for block j + 3. With an uneven
+  // split of the loads over the waves each step waits for all of them.
+  constexpr int LPB = TileLoads<T, typename SC::KT, SC::NW>::PER + TileLoads<T, typename SC::VT, SC::NW>::PER;
+  constexpr bool EVEN = SC::KT::NINST % SC::NW == 0 && SC::VT::NINST % SC::NW == 0;
+  auto arr = [&](auto s_c) __attribute__((always_inline)) {
+    constexpr int S = decltype(s_c)::value % 4;
+    if constexpr (S == 0) return l0;
+    else if constexpr (S == 1) return l1;
+    else if constexpr (S == 2) return l2;
+    else return l3;
   };
-  for (int j = 0; j < nkb; j += 2) {
-    sync_and_prefetch(j, stage1);
-    block(c0 + j * SC::BK, stage0);
-    if (j + 1 < nkb) {
-      sync_and_prefetch(j + 1, stage0);
-      block(c0 + (j + 1) * SC::BK, stage1);
-    }
+  auto wait_landed = [&](int later) __attribute__((always_inline)) {
+    // vmcnt <= later * LPB, lgkmcnt 0 (this wave's reads of the array about
+    // to be refilled are done), expcnt left alone
+    constexpr int kOthers = 0x7 << 4;
+    if (EVEN && later >= 2)
+      __builtin_amdgcn_s_waitcnt(kOthers | ((2 * LPB) & 15) | (((2 * LPB) >> 4) << 14));
+    else if (EVEN && later == 1)
+      __builtin_amdgcn_s_waitcnt(kOthers | (LPB & 15) | ((LPB >> 4) << 14));
+    else
+      __builtin_amdgcn_s_waitcnt(0);
+  };
+  static_assert(2 * LPB < 64, "vmcnt range");
+  if (0 < nkb) issue_kv(0, arr(std::integral_constant<int, 0>{}));
+  if (1 < nkb) issue_kv(1, arr(std::integral_constant<int, 1>{}));
+  if (2 < nkb) issue_kv(2, arr(std::integral_constant<int, 2>{}));
+  for (int j = 0; j < nkb; j += 4) {
+    static_for<4>([&](auto u_c) __attribute__((always_inline)) {
+      constexpr int u = decltype(u_c)::value;
+      const int jj = j + u;
+      if (jj < nkb) {
+        wait_landed(min(2, nkb - 1 - jj));
+        bare_barrier();
+        if (jj + 3 < nkb) issue_kv(jj + 3, arr(std::integral_constant<int, u + 3>{}));
+        block(c0 + jj * SC::BK, arr(u_c));
+      }
+    });
   }
 
   // R_i = g^b R_{i-1} + dR_i. The fp32 chain keeps R in this role's
@@ -803,8 +832,10 @@ __device__ __forceinline__ void state_role(const FwdParams& p, int bh, int ci, i
 template <typename T, int D, bool FAST>
 __global__ __launch_bounds__(kWaves<T> * 64, 1) void retention_parallel_kernel(FwdParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the kernel's signature
-  __shared__ __attribute__((aligned(1024))) char stage0[Stage<T, D>::BYTES];
-  __shared__ __attribute__((aligned(1024))) char stage1[Stage<T, D>::BYTES];
+  __shared__ __attribute__((aligned(1024))) char l0[Stage<T, D>::BYTES];
+  __shared__ __attribute__((aligned(1024))) char l1[Stage<T, D>::BYTES];
+  __shared__ __attribute__((aligned(1024))) char l2[Stage<T, D>::BYTES];
+  __shared__ __attribute__((aligned(1024))) char l3[Stage<T, D>::BYTES];
   int bh, qb;
   const int bid = blockIdx.x;
   const int groups = p.batch * p.heads;
@@ -816,15 +847,17 @@ __global__ __launch_bounds__(kWaves<T> * 64, 1) void retention_parallel_kernel(F
     bh = bid / p.qblocks;
     qb = p.qblocks - 1 - bid % p.qblocks;
   }
-  out_role<T, D, FAST, false>(p, bh, 0, qb, false, stage0, stage1);
+  out_role<T, D, FAST, false>(p, bh, 0, qb, false, l0, l1, l2, l3);
 #endif
 }
 
 template <typename T, int D, bool FAST>
 __global__ __launch_bounds__(kWaves<T> * 64, 1) void retention_chunkwise_kernel(FwdParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the kernel's signature
-  __shared__ __attribute__((aligned(1024))) char stage0[Stage<T, D>::BYTES];
-  __shared__ __attribute__((aligned(1024))) char stage1[Stage<T, D>::BYTES];
+  __shared__ __attribute__((aligned(1024))) char l0[Stage<T, D>::BYTES];
+  __shared__ __attribute__((aligned(1024))) char l1[Stage<T, D>::BYTES];
+  __shared__ __attribute__((aligned(1024))) char l2[Stage<T, D>::BYTES];
+  __shared__ __attribute__((aligned(1024))) char l3[Stage<T, D>::BYTES];
   __shared__ int s_ticket;
   constexpr int SPLIT = StTile<T, D>::SPLIT;
   const int bhs = p.batch * p.heads;
@@ -863,11 +896,11 @@ __global__ __launch_bounds__(kWaves<T> * 64, 1) void retention_chunkwise_kernel(
   // state parts, then the other query blocks
   const int qb = role == 0 ? p.qblocks - 1 : role <= SPLIT ? -1 : p.qblocks - 1 - (role - SPLIT);
   if (qb < 0)
-    state_role<T, D>(p, bh, ci, role - 1, stage0, stage1);
+    state_role<T, D>(p, bh, ci, role - 1, l0, l1, l2, l3);
   else if (ci > 0 || p.has_state0)
-    out_role<T, D, FAST, true>(p, bh, ci, qb, true, stage0, stage1);
+    out_role<T, D, FAST, true>(p, bh, ci, qb, true, l0, l1, l2, l3);
   else
-    out_role<T, D, FAST, false>(p, bh, ci, qb, true, stage0, stage1);
+    out_role<T, D, FAST, false>(p, bh, ci, qb, true, l0, l1, l2, l3);
 #endif
 }
 
