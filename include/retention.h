@@ -108,6 +108,17 @@ ret_status_t retention_chunkwise_fwd(const ret_desc_t *desc, int32_t chunk, cons
                                      float *state_out, void *workspace, size_t workspace_bytes,
                                      hipStream_t stream);
 
+/* The same call, for timing the chunkwise kernel on its own: when non-NULL,
+ * `before` and `after` (events created by the caller, for instance with
+ * hipEventCreate) are recorded on `stream` immediately before and after the
+ * launch of the chunkwise kernel, after the control-block reset and any
+ * rotation pass. The events stay owned by the caller; everything else is as
+ * retention_chunkwise_fwd, which equals this call with two NULL events. */
+ret_status_t retention_chunkwise_fwd_timed(const ret_desc_t *desc, int32_t chunk, const void *q, const void *k,
+                                           const void *v, const void *g, void *o, const float *state_in,
+                                           float *state_out, void *workspace, size_t workspace_bytes,
+                                           hipStream_t stream, hipEvent_t before, hipEvent_t after);
+
 /* Recurrent form, one decode step for a batch of single tokens (desc->seqlen
  * must be 1): state <- g * state + k^T v, then o = q state ("Summary": O(1)
  * per token, no KV cache). `state` is read and written in place. The rotation

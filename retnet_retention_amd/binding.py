@@ -34,6 +34,7 @@ EXPORTS = (
     "retention_parallel_fwd",
     "retention_chunkwise_workspace_bytes",
     "retention_chunkwise_fwd",
+    "retention_chunkwise_fwd_timed",
     "retention_recurrent_step",
     "retention_status_string",
     "retention_abi_version",
@@ -86,6 +87,8 @@ def lib():
         h.retention_chunkwise_workspace_bytes.restype = sz
         h.retention_chunkwise_fwd.argtypes = [pd, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         h.retention_chunkwise_fwd.restype = st
+        h.retention_chunkwise_fwd_timed.argtypes = [pd, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp]
+        h.retention_chunkwise_fwd_timed.restype = st
         h.retention_recurrent_step.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp]
         h.retention_recurrent_step.restype = st
         h.retention_status_string.argtypes = [st]
@@ -178,9 +181,11 @@ def chunkwise_workspace_bytes(q, v, chunk, rotary_base=0.0):
 
 
 def chunkwise_fwd(q, k, v, g=None, *, chunk=512, state_in=None, state_out=None, gammas=None, rotary_base=0.0,
-                  pos_offset=0, eps=1e-5, out=None, workspace=None):
+                  pos_offset=0, eps=1e-5, out=None, workspace=None, kernel_events=None):
     """Chunkwise form; returns the output tensor (state_out, if given, is
-    filled with the state after the last token)."""
+    filled with the state after the last token). kernel_events: optional pair
+    of torch.cuda.Event (timing enabled) recorded around the chunkwise kernel
+    alone."""
     out = torch.empty_like(v) if out is None else out
     _validate(q, k, v, g, out)
     for name, s in (("state_in", state_in), ("state_out", state_out)):
@@ -194,9 +199,15 @@ def chunkwise_fwd(q, k, v, g=None, *, chunk=512, state_in=None, state_out=None, 
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     ws_bytes = workspace.numel() * workspace.element_size()
-    _check(L.retention_chunkwise_fwd(ctypes.byref(desc), int(chunk), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
-                                     _ptr(out), _ptr(state_in), _ptr(state_out), _ptr(workspace), ws_bytes,
-                                     _stream(q)))
+    if kernel_events is None:
+        _check(L.retention_chunkwise_fwd(ctypes.byref(desc), int(chunk), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                         _ptr(out), _ptr(state_in), _ptr(state_out), _ptr(workspace), ws_bytes,
+                                         _stream(q)))
+    else:
+        before, after = (ctypes.c_void_p(e.cuda_event) for e in kernel_events)
+        _check(L.retention_chunkwise_fwd_timed(ctypes.byref(desc), int(chunk), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                               _ptr(out), _ptr(state_in), _ptr(state_out), _ptr(workspace),
+                                               ws_bytes, _stream(q), before, after))
     del keep
     return out
 

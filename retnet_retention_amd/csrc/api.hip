@@ -173,10 +173,10 @@ size_t retention_chunkwise_workspace_bytes(const ret_desc_t* desc, int32_t chunk
   return ctrl_bytes(desc, chunk) + rot_bytes(desc) + chain_bytes(desc) + snap_bytes(desc, chunk);
 }
 
-ret_status_t retention_chunkwise_fwd(const ret_desc_t* desc, int32_t chunk, const void* q, const void* k,
-                                     const void* v, const void* g, void* o, const float* state_in,
-                                     float* state_out, void* workspace, size_t workspace_bytes,
-                                     hipStream_t stream) {
+ret_status_t retention_chunkwise_fwd_timed(const ret_desc_t* desc, int32_t chunk, const void* q, const void* k,
+                                           const void* v, const void* g, void* o, const float* state_in,
+                                           float* state_out, void* workspace, size_t workspace_bytes,
+                                           hipStream_t stream, hipEvent_t before, hipEvent_t after) {
   ret_status_t st = check_desc(desc);
   if (st != RET_OK) return st;
   if (chunk < 1) return RET_ERR_SHAPE;
@@ -196,9 +196,17 @@ ret_status_t retention_chunkwise_fwd(const ret_desc_t* desc, int32_t chunk, cons
   float* chain = reinterpret_cast<float*>(ws + cb + rb);
   void* snap = ws + cb + rb + hb;
   if (ret::launch_retention_fwd(s, c, true, q, k, v, g, o, state_in, state_out, snap, chain, ctrl, desc->gn_eps,
-                                stream) != hipSuccess)
+                                stream, before, after) != hipSuccess)
     return RET_ERR_HIP;
   return RET_OK;
+}
+
+ret_status_t retention_chunkwise_fwd(const ret_desc_t* desc, int32_t chunk, const void* q, const void* k,
+                                     const void* v, const void* g, void* o, const float* state_in,
+                                     float* state_out, void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream) {
+  return retention_chunkwise_fwd_timed(desc, chunk, q, k, v, g, o, state_in, state_out, workspace, workspace_bytes,
+                                       stream, nullptr, nullptr);
 }
 
 ret_status_t retention_recurrent_step(const ret_desc_t* desc, const void* q, const void* k, const void* v,

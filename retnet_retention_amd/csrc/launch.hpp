@@ -30,9 +30,11 @@ hipError_t launch_rotate_qk(const void* q, const void* k, void* qr, void* kr, co
 // [d][d] of the input dtype, chain [BH][2][d][d] fp32 and a control block of
 // chunkwise_ctrl_bytes() ints, all device memory owned by the caller.
 size_t chunkwise_ctrl_bytes(int batch, int heads, int nchunks);
+// `before`/`after` (may be null) are recorded around the main kernel.
 hipError_t launch_retention_fwd(const Shape& s, int chunk, bool chunked, const void* q, const void* k, const void* v,
                                 const void* g, void* o, const float* state_in, float* state_out, void* snap,
-                                float* chain, int* ctrl, float eps, hipStream_t stream);
+                                float* chain, int* ctrl, float eps, hipStream_t stream,
+                                hipEvent_t before = nullptr, hipEvent_t after = nullptr);
 
 // One decode step, in place on `state`.
 hipError_t launch_recurrent_step(const Shape& s, const void* q, const void* k, const void* v, const void* g,

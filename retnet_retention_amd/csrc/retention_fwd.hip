@@ -909,15 +909,19 @@ __global__ void reset_ctrl_kernel(int* ctrl, int n) {
 }
 
 template <typename T, int D, bool FAST>
-static hipError_t launch_fwd_impl(const Shape& s, int chunk, FwdParams p, bool chunked, hipStream_t stream) {
+static hipError_t launch_fwd_impl(const Shape& s, int chunk, FwdParams p, bool chunked, hipStream_t stream,
+                                  hipEvent_t before, hipEvent_t after) {
   using C = OutTile<T, D, FAST>;
   p.qblocks = (chunk + C::BM - 1) / C::BM;
   const int bhs = s.batch * s.heads;
   if (!chunked) {
     const int64_t blocks = (int64_t)bhs * p.qblocks;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    if (before && hipEventRecord(before, stream) != hipSuccess) return hipErrorInvalidValue;
     hipLaunchKernelGGL((retention_parallel_kernel<T, D, FAST>), dim3((unsigned)blocks), dim3(64 * C::WAVES), 0, stream, p);
-    return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    if (e == hipSuccess && after && hipEventRecord(after, stream) != hipSuccess) return hipErrorInvalidValue;
+    return e;
   }
   const int64_t nctrl = kCtrlHead + (int64_t)bhs * (p.nchunks + 1) * kFlagsPerChunk;
   hipLaunchKernelGGL(reset_ctrl_kernel, dim3((unsigned)((nctrl + 255) / 256 < 1024 ? (nctrl + 255) / 256 : 1024)),
@@ -925,20 +929,24 @@ static hipError_t launch_fwd_impl(const Shape& s, int chunk, FwdParams p, bool c
   p.xcd_order = bhs % 8 == 0;
   const int64_t blocks = (int64_t)p.nchunks * bhs * (StTile<T, D>::SPLIT + p.qblocks);
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  if (before && hipEventRecord(before, stream) != hipSuccess) return hipErrorInvalidValue;
   hipLaunchKernelGGL((retention_chunkwise_kernel<T, D, FAST>), dim3((unsigned)blocks), dim3(64 * C::WAVES), 0, stream, p);
-  return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  if (e == hipSuccess && after && hipEventRecord(after, stream) != hipSuccess) return hipErrorInvalidValue;
+  return e;
 }
 
 // The fast path applies when every head's decay over the span of one
 // workgroup's factors (the chunk, or the parallel form's query block) stays
 // within 2^64.
 template <typename T, int D>
-static hipError_t launch_fwd_t(const Shape& s, int chunk, FwdParams p, bool chunked, hipStream_t stream) {
+static hipError_t launch_fwd_t(const Shape& s, int chunk, FwdParams p, bool chunked, hipStream_t stream,
+                               hipEvent_t before, hipEvent_t after) {
   const double span = chunked ? chunk : OutTile<T, D, true>::BM;
   bool fast = true;
   for (int h = 0; h < s.heads; ++h) fast = fast && -(double)s.log2g[h] * span <= kFastSpanLog2;
-  return fast ? launch_fwd_impl<T, D, true>(s, chunk, p, chunked, stream)
-              : launch_fwd_impl<T, D, false>(s, chunk, p, chunked, stream);
+  return fast ? launch_fwd_impl<T, D, true>(s, chunk, p, chunked, stream, before, after)
+              : launch_fwd_impl<T, D, false>(s, chunk, p, chunked, stream, before, after);
 }
 
 size_t chunkwise_ctrl_bytes(int batch, int heads, int nchunks) {
@@ -947,7 +955,8 @@ size_t chunkwise_ctrl_bytes(int batch, int heads, int nchunks) {
 
 hipError_t launch_retention_fwd(const Shape& s, int chunk, bool chunked, const void* q, const void* k, const void* v,
                                 const void* g, void* o, const float* state_in, float* state_out, void* snap,
-                                float* chain, int* ctrl, float eps, hipStream_t stream) {
+                                float* chain, int* ctrl, float eps, hipStream_t stream, hipEvent_t before,
+                                hipEvent_t after) {
   FwdParams p;
   p.q = q;
   p.k = k;
@@ -971,15 +980,15 @@ hipError_t launch_retention_fwd(const Shape& s, int chunk, bool chunked, const v
   for (int h = 0; h < kMaxHeads; ++h) p.log2g[h] = h < s.heads ? s.log2g[h] : 0.f;
   if (s.dtype == 1) {
     switch (s.d) {
-      case 64: return launch_fwd_t<bf16, 64>(s, chunk, p, chunked, stream);
-      case 128: return launch_fwd_t<bf16, 128>(s, chunk, p, chunked, stream);
-      case 256: return launch_fwd_t<bf16, 256>(s, chunk, p, chunked, stream);
+      case 64: return launch_fwd_t<bf16, 64>(s, chunk, p, chunked, stream, before, after);
+      case 128: return launch_fwd_t<bf16, 128>(s, chunk, p, chunked, stream, before, after);
+      case 256: return launch_fwd_t<bf16, 256>(s, chunk, p, chunked, stream, before, after);
     }
   } else {
     switch (s.d) {
-      case 64: return launch_fwd_t<float, 64>(s, chunk, p, chunked, stream);
-      case 128: return launch_fwd_t<float, 128>(s, chunk, p, chunked, stream);
-      case 256: return launch_fwd_t<float, 256>(s, chunk, p, chunked, stream);
+      case 64: return launch_fwd_t<float, 64>(s, chunk, p, chunked, stream, before, after);
+      case 128: return launch_fwd_t<float, 128>(s, chunk, p, chunked, stream, before, after);
+      case 256: return launch_fwd_t<float, 256>(s, chunk, p, chunked, stream, before, after);
     }
   }
   return hipErrorInvalidValue;

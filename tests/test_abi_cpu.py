@@ -123,6 +123,16 @@ def test_pointer_validation(L):
     assert _chk(L, d, ws=ALIGNED * 8 + 8, wsb=need) == 5
 
 
+def test_timed_chunkwise_validates_like_the_plain_call(L):
+    d, _ = _desc()
+    need = L.retention_chunkwise_workspace_bytes(ctypes.byref(d), 64)
+    args = (ctypes.byref(d), 64, ALIGNED, ALIGNED * 2, ALIGNED * 3, None, ALIGNED * 4, None, None)
+    fake_events = (ALIGNED * 9, ALIGNED * 10)  # never recorded: validation fails first
+    assert L.retention_chunkwise_fwd_timed(*args, None, 0, None, *fake_events) == 6
+    assert L.retention_chunkwise_fwd_timed(*args, ALIGNED * 8, need - 1, None, *fake_events) == 6
+    assert L.retention_chunkwise_fwd_timed(*args[:2], None, *args[3:], ALIGNED * 8, need, None, *fake_events) == 1
+
+
 def test_step_validation(L):
     d, _ = _desc()  # seqlen 100: a step takes exactly one token
     assert _step(L, d) == 2
