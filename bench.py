@@ -473,8 +473,10 @@ def profile(kinds, out):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    # the GPU's clocks take tens of milliseconds of load to settle: 5 warm-up
+    # calls time the chunkwise call 14% slower than 200 do
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--only", choices=["chunkwise", "decode", "parallel"], default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-batches", type=int, nargs="*", default=None)
