@@ -286,10 +286,18 @@ def cpu_baseline(sample_seqs=2, min_seconds=10.0, max_runs=20):
 # rocprofv3 runs (children of this process, which never touches the GPU in
 # this mode) and their text summaries
 # ---------------------------------------------------------------------------
+# counter passes: a few calls each (the counters are per dispatch)
 LEG_ARGS = {
     "chunkwise": ["--only", "chunkwise", "--steps", "10", "--warmup", "2"],
     "decode": ["--only", "decode", "--decode-batches", "64", "--decode-steps", "64"],
     "parallel": ["--only", "parallel", "--steps", "10", "--warmup", "2"],
+}
+# kernel statistics: the benchmark's own default calls (warm-up included, so
+# the averages are those of the timed, warmed-up calls to within a few %)
+STATS_ARGS = {
+    "chunkwise": ["--only", "chunkwise"],
+    "decode": ["--only", "decode", "--decode-batches", "64"],
+    "parallel": ["--only", "parallel"],
 }
 SQ_COUNTERS = ["SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "SQ_INSTS_LDS",
                "SQ_LDS_BANK_CONFLICT", "SQ_WAIT_INST_LDS", "SQ_INSTS_VALU", "GRBM_GUI_ACTIVE"]
@@ -346,7 +354,7 @@ def _per_dispatch(rows, counter, match):
 
 
 def profile_stats(out, raw):
-    for leg, leg_args in LEG_ARGS.items():
+    for leg, leg_args in STATS_ARGS.items():
         d = os.path.join(raw, f"stats_{leg}")
         cmd = ["rocprofv3", "--kernel-trace", "--stats", "-d", d, "-o", "run", "--output-format", "csv", "--",
                *_bench_cmd(leg_args)]
