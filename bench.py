@@ -465,6 +465,55 @@ def profile_counters(out, raw):
         print(f"wrote {name}_sq_counters.txt", file=sys.stderr, flush=True)
 
 
+# memory-system passes (at most 4 TCC counters per pass): L2 hits, the EA
+# read latency (requests in flight / requests), and back-pressure from DRAM
+TCC_SETS = [
+    ["TCC_HIT_sum", "TCC_MISS_sum", "TCC_EA0_RDREQ_sum", "TCC_EA0_RDREQ_LEVEL_sum"],
+    ["TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum", "TCC_EA0_WRREQ_STALL_sum", "TCC_EA0_WRREQ_sum", "TCC_BUSY_sum",
+     "GRBM_GUI_ACTIVE"],
+]
+
+
+def profile_memory(out, raw):
+    """TCC counter passes for the chunkwise and decode legs: how the memory
+    system behaves under each (L2 hit rate, loaded read latency, stalls)."""
+    for leg in ("chunkwise", "decode"):
+        leg_args = [*LEG_ARGS[leg]]
+        if leg != "decode":
+            leg_args[leg_args.index("--steps") + 1] = "2"
+        match = {"chunkwise": lambda n: CHUNKWISE_KERNEL in n, "decode": lambda n: "recurrent_step" in n}[leg]
+        name = {"chunkwise": "chunkwise_7b_8k", "decode": "decode_step_7b_b64"}[leg]
+        lines, vals = [], {}
+        for k, counters in enumerate(TCC_SETS):
+            d = os.path.join(raw, f"pmc_tcc_{leg}_{k}")
+            cmd = ["rocprofv3", "--pmc", *counters, "-d", d, "-o", "run", "--output-format", "csv", "--",
+                   *_bench_cmd(leg_args)]
+            _run_profiler(cmd, d + ".log", 180)
+            rows = _counter_rows(d)
+            lines.append(f"command: {_rel(cmd)}\n")
+            for c in counters:
+                v = _per_dispatch(rows, c, match)
+                vals[c] = sum(v) / len(v) if v else float("nan")
+                lines.append(f"  {c:38s} {vals[c]:.6g}  (dispatches {len(v)})\n")
+        with open(os.path.join(out, f"{name}_memory_counters.txt"), "w") as f:
+            f.write(f"rocprofv3 TCC (L2 / memory interface) counters, {leg} leg, mean per dispatch\n")
+            f.write("made by: python bench.py --profile memory --profile-out <out>\n")
+            f.write(f"kernel sources: {source_hash()}\n")
+            f.writelines(lines)
+            xcds, channels = 8, 128  # 16 L2 channels per XCD
+            gui = vals["GRBM_GUI_ACTIVE"] / xcds
+            hit, miss = vals["TCC_HIT_sum"], vals["TCC_MISS_sum"]
+            f.write(f"derived: kernel cycles (GRBM_GUI_ACTIVE / {xcds}) = {gui:.4g}\n")
+            f.write(f"derived: L2 hit rate = TCC_HIT / (TCC_HIT + TCC_MISS) = {hit / (hit + miss):.4f}\n")
+            f.write(f"derived: mean EA read latency = TCC_EA0_RDREQ_LEVEL / TCC_EA0_RDREQ = "
+                    f"{vals['TCC_EA0_RDREQ_LEVEL_sum'] / vals['TCC_EA0_RDREQ_sum']:.1f} cycles\n")
+            f.write(f"derived: mean EA reads in flight per channel = TCC_EA0_RDREQ_LEVEL / (cycles x {channels}) = "
+                    f"{vals['TCC_EA0_RDREQ_LEVEL_sum'] / (gui * channels):.1f}\n")
+            for c in ("TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum", "TCC_EA0_WRREQ_STALL_sum", "TCC_BUSY_sum"):
+                f.write(f"derived: {c} / (cycles x {channels} channels) = {vals[c] / (gui * channels):.4f}\n")
+        print(f"wrote {name}_memory_counters.txt", file=sys.stderr, flush=True)
+
+
 def profile(kinds, out):
     PROFILE_OUT[0] = out
     os.makedirs(out, exist_ok=True)
@@ -476,6 +525,8 @@ def profile(kinds, out):
         profile_traffic(out, raw)
     if "counters" in kinds:
         profile_counters(out, raw)
+    if "memory" in kinds:
+        profile_memory(out, raw)
 
 
 def main():
@@ -490,7 +541,7 @@ def main():
     ap.add_argument("--decode-batches", type=int, nargs="*", default=None)
     ap.add_argument("--decode-steps", type=int, default=256)
     ap.add_argument("--copy-probe", action="store_true", help="also run a plain copy of known size")
-    ap.add_argument("--profile", nargs="+", choices=["stats", "traffic", "counters"], default=None,
+    ap.add_argument("--profile", nargs="+", choices=["stats", "traffic", "counters", "memory"], default=None,
                     help="run the named rocprofv3 passes over this benchmark and write text summaries")
     ap.add_argument("--profile-out", default=os.path.join(ROOT, "profiles"))
     args = ap.parse_args()

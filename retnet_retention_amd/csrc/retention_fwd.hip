@@ -836,16 +836,22 @@ __global__ __launch_bounds__(kWaves<T> * 64, 1) void retention_parallel_kernel(F
   __shared__ __attribute__((aligned(1024))) char l1[Stage<T, D>::BYTES];
   __shared__ __attribute__((aligned(1024))) char l2[Stage<T, D>::BYTES];
   __shared__ __attribute__((aligned(1024))) char l3[Stage<T, D>::BYTES];
+  // Workgroups are dealt out longest first: a query block's work grows with
+  // its index (it reads every key up to its diagonal), so the last query
+  // blocks of all (sequence, head) pairs go first and the short ones fill the
+  // tail. When the pairs divide evenly over the 8 XCDs, the query blocks of
+  // one pair stay on one XCD (blockIdx mod 8), sharing its K and V through
+  // that XCD's L2.
   int bh, qb;
   const int bid = blockIdx.x;
   const int groups = p.batch * p.heads;
-  if (groups % 8 == 0) {  // the query blocks of one (sequence, head) share K and V through one XCD's L2
-    const int xcd = bid & 7, slot = bid >> 3;
-    bh = xcd + 8 * (slot / p.qblocks);
-    qb = p.qblocks - 1 - slot % p.qblocks;
+  if (groups % 8 == 0) {
+    const int xcd = bid & 7, slot = bid >> 3, per = groups / 8;
+    bh = xcd + 8 * (slot % per);
+    qb = p.qblocks - 1 - slot / per;
   } else {
-    bh = bid / p.qblocks;
-    qb = p.qblocks - 1 - bid % p.qblocks;
+    bh = bid % groups;
+    qb = p.qblocks - 1 - bid / groups;
   }
   out_role<T, D, FAST, false>(p, bh, 0, qb, false, l0, l1, l2, l3);
 #endif
