@@ -79,29 +79,28 @@ Shape make_shape(const ret_desc_t* d) {
   return s;
 }
 
-// Rotation needs the angle table and rotated copies of q and k.
+// Rotation needs the angle table and a rotated copy of k.
 size_t rot_bytes(const ret_desc_t* d) {
   if (d->rotary_base == 0.0) return 0;
-  const size_t qk = (size_t)d->batch * d->seqlen * d->heads * d->dk * elem_size(d->dtype);
-  return align_up((size_t)d->seqlen * (d->dk / 2) * sizeof(float2)) + 2 * align_up(qk);
+  const size_t kb = (size_t)d->batch * d->seqlen * d->heads * d->dk * elem_size(d->dtype);
+  return align_up((size_t)d->seqlen * (d->dk / 2) * sizeof(float2)) + align_up(kb);
 }
 
-// Launch the table and rotation passes when rotation is on; q and k are
-// replaced by their rotated copies in the workspace.
-bool rotate_inputs(const ret_desc_t* d, const void*& q, const void*& k, void* workspace, hipStream_t stream) {
+// Launch the table and key rotation passes when rotation is on: k is replaced
+// by its rotated copy in the workspace and *table is set for the retention
+// kernel, which turns q as it loads it (null when rotation is off).
+bool rotate_inputs(const ret_desc_t* d, const void*& k, const float2** table, void* workspace, hipStream_t stream) {
+  *table = nullptr;
   if (d->rotary_base == 0.0) return true;
-  const size_t qk = (size_t)d->batch * d->seqlen * d->heads * d->dk * elem_size(d->dtype);
   char* ws = static_cast<char*>(workspace);
-  float2* table = reinterpret_cast<float2*>(ws);
-  char* qr = ws + align_up((size_t)d->seqlen * (d->dk / 2) * sizeof(float2));
-  char* kr = qr + align_up(qk);
-  if (ret::launch_rotary_table(table, d->seqlen, d->dk, d->rotary_base, d->pos_offset, stream) != hipSuccess)
+  float2* tab = reinterpret_cast<float2*>(ws);
+  char* kr = ws + align_up((size_t)d->seqlen * (d->dk / 2) * sizeof(float2));
+  if (ret::launch_rotary_table(tab, d->seqlen, d->dk, d->rotary_base, d->pos_offset, stream) != hipSuccess)
     return false;
-  if (ret::launch_rotate_qk(q, k, qr, kr, table, d->batch, d->seqlen, d->heads, d->dk, d->dtype, stream) !=
-      hipSuccess)
+  if (ret::launch_rotate_keys(k, kr, tab, d->batch, d->seqlen, d->heads, d->dk, d->dtype, stream) != hipSuccess)
     return false;
-  q = qr;
   k = kr;
+  *table = tab;
   return true;
 }
 
@@ -161,9 +160,10 @@ ret_status_t retention_parallel_fwd(const ret_desc_t* desc, const void* q, const
   if (workspace && !aligned16(workspace)) return RET_ERR_ALIGN;
 
   const Shape s = make_shape(desc);
-  if (!rotate_inputs(desc, q, k, workspace, stream)) return RET_ERR_HIP;
+  const float2* table;
+  if (!rotate_inputs(desc, k, &table, workspace, stream)) return RET_ERR_HIP;
   if (ret::launch_retention_fwd(s, desc->seqlen, false, q, k, v, g, o, nullptr, nullptr, nullptr, nullptr, nullptr,
-                                desc->gn_eps, stream) != hipSuccess)
+                                table, desc->gn_eps, stream) != hipSuccess)
     return RET_ERR_HIP;
   return RET_OK;
 }
@@ -192,11 +192,12 @@ ret_status_t retention_chunkwise_fwd_timed(const ret_desc_t* desc, int32_t chunk
   const int32_t c = eff_chunk(desc, chunk);
   char* ws = static_cast<char*>(workspace);
   int* ctrl = reinterpret_cast<int*>(ws);
-  if (!rotate_inputs(desc, q, k, ws + cb, stream)) return RET_ERR_HIP;
+  const float2* table;
+  if (!rotate_inputs(desc, k, &table, ws + cb, stream)) return RET_ERR_HIP;
   float* chain = reinterpret_cast<float*>(ws + cb + rb);
   void* snap = ws + cb + rb + hb;
-  if (ret::launch_retention_fwd(s, c, true, q, k, v, g, o, state_in, state_out, snap, chain, ctrl, desc->gn_eps,
-                                stream, before, after) != hipSuccess)
+  if (ret::launch_retention_fwd(s, c, true, q, k, v, g, o, state_in, state_out, snap, chain, ctrl, table,
+                                desc->gn_eps, stream, before, after) != hipSuccess)
     return RET_ERR_HIP;
   return RET_OK;
 }

@@ -21,19 +21,22 @@ struct Shape {
 hipError_t launch_rotary_table(float2* table, int seqlen, int d, double base, int64_t pos_offset,
                                hipStream_t stream);
 
-// Rotated copies qr, kr of q, k ([batch][seqlen][heads][d], same dtype).
-hipError_t launch_rotate_qk(const void* q, const void* k, void* qr, void* kr, const float2* table, int batch,
-                            int seqlen, int heads, int d, int dtype, hipStream_t stream);
+// Rotated copy kr of k ([batch][seqlen][heads][d], same dtype); the
+// queries are turned by the retention kernels as they load them.
+hipError_t launch_rotate_keys(const void* k, void* kr, const float2* table, int batch, int seqlen, int heads, int d,
+                              int dtype, hipStream_t stream);
 
 // Parallel form (chunked == false: chunk == seqlen, no state) or chunkwise
 // form (chunked == true) in one launch. Chunkwise needs: snap [BH][nchunks]
 // [d][d] of the input dtype, chain [BH][2][d][d] fp32 and a control block of
 // chunkwise_ctrl_bytes() ints, all device memory owned by the caller.
 size_t chunkwise_ctrl_bytes(int batch, int heads, int nchunks);
+// `rot` (may be null): the cos/sin table of launch_rotary_table, with which
+// the kernels turn q as they load it (k must then arrive rotated).
 // `before`/`after` (may be null) are recorded around the main kernel.
 hipError_t launch_retention_fwd(const Shape& s, int chunk, bool chunked, const void* q, const void* k, const void* v,
                                 const void* g, void* o, const float* state_in, float* state_out, void* snap,
-                                float* chain, int* ctrl, float eps, hipStream_t stream,
+                                float* chain, int* ctrl, const float2* rot, float eps, hipStream_t stream,
                                 hipEvent_t before = nullptr, hipEvent_t after = nullptr);
 
 // One decode step, in place on `state`.

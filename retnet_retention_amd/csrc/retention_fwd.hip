@@ -142,6 +142,7 @@ struct FwdParams {
   void* snap;    // [BH][nchunks][D*D] of T: R_{i-1}^T for chunk i (output fragment order)
   float* chain;  // [BH][2][D*D] fp32: R_i handed to the next state workgroup (fragment order)
   int* ctrl;     // [0] count, [1] error, [8..15] tickets, [16 + (bh*(nchunks+1) + i)*4 + kind*2 + part]: R_{i-1} ready
+  const float2* rot;  // (cos, sin) per position and pair [seqlen][D/2]: q is turned on load; null: no rotation
   int batch, seqlen, heads, chunk, nchunks, qblocks;
   int has_state0, xcd_order;
   float eps;
@@ -279,13 +280,26 @@ __device__ __forceinline__ void out_role(const FwdParams& p, int bh, int ci, int
   // Query fragments of this lane's rows, kept in registers for the whole
   // workgroup life: qf[r][s] = Q[qw0 + 32 r + n][16 s + 8 hh .. +7]. Rows
   // past the chunk load a clamped in-range row: their outputs are never
-  // stored.
+  // stored. With the position rotation on, each adjacent pair of the 8
+  // elements (pairs 8 s + 4 hh .. +3) is turned by its row's angles here, in
+  // fp32, before the one rounding to the fragment type.
   frag_t<T> qf[QT][C::KS];
 #pragma unroll
   for (int r = 0; r < QT; ++r) {
-    const T* qr = Q + (int64_t)min(qw0 + 32 * r + n, cend - 1) * tstride + 8 * hh;
+    const int qrow = min(qw0 + 32 * r + n, cend - 1);
+    const T* qr = Q + (int64_t)qrow * tstride + 8 * hh;
+    if (p.rot) {
+      const float2* cs = p.rot + (int64_t)qrow * (D / 2) + 4 * hh;
 #pragma unroll
-    for (int s = 0; s < C::KS; ++s) qf[r][s] = to_frag(unpack8(ld_raw8(qr + 16 * s)), (T*)nullptr);
+      for (int s = 0; s < C::KS; ++s) {
+        F8 x = unpack8(ld_raw8(qr + 16 * s));
+        rotate4(x, ld_cs4(cs + 8 * s));
+        qf[r][s] = to_frag(x, (T*)nullptr);
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < C::KS; ++s) qf[r][s] = to_frag(unpack8(ld_raw8(qr + 16 * s)), (T*)nullptr);
+    }
   }
 
   // O^T accumulators: oacc[r][t] element i is O'[qw0 + 32 r + n][32 t + 8 (i/4) + 4 hh + i%4]
@@ -961,9 +975,10 @@ size_t chunkwise_ctrl_bytes(int batch, int heads, int nchunks) {
 
 hipError_t launch_retention_fwd(const Shape& s, int chunk, bool chunked, const void* q, const void* k, const void* v,
                                 const void* g, void* o, const float* state_in, float* state_out, void* snap,
-                                float* chain, int* ctrl, float eps, hipStream_t stream, hipEvent_t before,
-                                hipEvent_t after) {
+                                float* chain, int* ctrl, const float2* rot, float eps, hipStream_t stream,
+                                hipEvent_t before, hipEvent_t after) {
   FwdParams p;
+  p.rot = rot;
   p.q = q;
   p.k = k;
   p.v = v;

@@ -35,10 +35,9 @@ hipError_t launch_rotary_table(float2* table, int seqlen, int d, double base, in
 }
 
 template <typename T>
-__global__ __launch_bounds__(256) void rotate_qk_kernel(const T* __restrict__ q, const T* __restrict__ k,
-                                                         T* __restrict__ qr, T* __restrict__ kr,
-                                                         const float2* __restrict__ table, int64_t chunks,
-                                                         int seqlen, int heads, int d) {
+__global__ __launch_bounds__(256) void rotate_keys_kernel(const T* __restrict__ k, T* __restrict__ kr,
+                                                           const float2* __restrict__ table, int64_t chunks,
+                                                           int seqlen, int heads, int d) {
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;  // one 8-element chunk
   if (idx >= chunks) return;
   const int cpr = d / 8;                                     // chunks per head vector
@@ -47,24 +46,21 @@ __global__ __launch_bounds__(256) void rotate_qk_kernel(const T* __restrict__ q,
   const int n = (int)((vec / heads) % seqlen);
   const CS4 cs = ld_cs4(table + (int64_t)n * (d / 2) + c8 * 4);
   const int64_t off = idx * 8;
-  F8 x = unpack8(ld_raw8(q + off));
   F8 y = unpack8(ld_raw8(k + off));
-  rotate4(x, cs);
   rotate4(y, cs);
-  store8(qr + off, x);
   store8(kr + off, y);
 }
 
-hipError_t launch_rotate_qk(const void* q, const void* k, void* qr, void* kr, const float2* table, int batch,
-                            int seqlen, int heads, int d, int dtype, hipStream_t stream) {
+hipError_t launch_rotate_keys(const void* k, void* kr, const float2* table, int batch, int seqlen, int heads, int d,
+                              int dtype, hipStream_t stream) {
   const int64_t chunks = (int64_t)batch * seqlen * heads * (d / 8);
   const unsigned blocks = (unsigned)((chunks + 255) / 256);
   if (dtype == 1)
-    hipLaunchKernelGGL(rotate_qk_kernel<bf16>, dim3(blocks), dim3(256), 0, stream, (const bf16*)q, (const bf16*)k,
-                       (bf16*)qr, (bf16*)kr, table, chunks, seqlen, heads, d);
+    hipLaunchKernelGGL(rotate_keys_kernel<bf16>, dim3(blocks), dim3(256), 0, stream, (const bf16*)k, (bf16*)kr,
+                       table, chunks, seqlen, heads, d);
   else
-    hipLaunchKernelGGL(rotate_qk_kernel<float>, dim3(blocks), dim3(256), 0, stream, (const float*)q,
-                       (const float*)k, (float*)qr, (float*)kr, table, chunks, seqlen, heads, d);
+    hipLaunchKernelGGL(rotate_keys_kernel<float>, dim3(blocks), dim3(256), 0, stream, (const float*)k, (float*)kr,
+                       table, chunks, seqlen, heads, d);
   return hipGetLastError();
 }
 

@@ -78,8 +78,9 @@ def test_workspace_sizes(L):
     assert L.retention_chunkwise_workspace_bytes(ctypes.byref(d), 64) == (
         ctrl + up(2 * 3 * 2 * 128 * 128 * 4) + up(2 * 3 * 16 * 128 * 128 * 2))
     d, _ = _desc(batch=1, seqlen=10, heads=1, dk=64, dv=64, dtype=binding.RET_F32, rotary_base=10000.0)
-    # rotation: angle table + rotated copies of q and k, each rounded up to 256 bytes
-    rot = (10 * 32 * 8 + 255) // 256 * 256 + 2 * ((10 * 64 * 4 + 255) // 256 * 256)
+    # rotation: angle table + a rotated copy of k (q is turned as the kernels
+    # load it), each rounded up to 256 bytes
+    rot = (10 * 32 * 8 + 255) // 256 * 256 + (10 * 64 * 4 + 255) // 256 * 256
     assert L.retention_parallel_workspace_bytes(ctypes.byref(d)) == rot
     # chunk larger than the sequence counts as one chunk
     assert L.retention_chunkwise_workspace_bytes(ctypes.byref(d), 4096) == (
