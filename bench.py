@@ -514,6 +514,28 @@ def profile_memory(out, raw):
         print(f"wrote {name}_memory_counters.txt", file=sys.stderr, flush=True)
 
 
+def roofline_object(cw, alg_gbps, traffic):
+    """Roofline of the chunkwise kernel: bound by HBM when the workload's
+    algorithmic intensity lies below the ridge point, else by the matrix
+    cores; both fractions are given."""
+    intensity = cw["flops"] / cw["bytes"]
+    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9)
+    hbm = {"achieved": round(alg_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+           "frac": round(alg_gbps / PEAK_HBM_GBPS, 4)}
+    mfma = {"achieved": round(cw["kernel_tflops"], 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(cw["kernel_tflops"] / PEAK_BF16_TFLOPS, 4)}
+    bound, other = ("hbm", "mfma") if intensity < ridge else ("mfma", "hbm")
+    main, side = (hbm, mfma) if bound == "hbm" else (mfma, hbm)
+    return {"bound": bound, "kernel": f"{CHUNKWISE_KERNEL}<bf16,256>", **main,
+            "traffic": traffic["bytes"] if traffic else None,
+            "kernel_us": round(cw["kernel_ms"] * 1e3, 1),
+            "algorithmic_bytes": cw["bytes"], "flops_per_launch": cw["flops"],
+            "intensity_flop_per_byte": round(intensity, 1), "ridge_flop_per_byte": round(ridge, 1),
+            "attainable_tflops": round(min(PEAK_BF16_TFLOPS, intensity * PEAK_HBM_GBPS / 1e3), 1),
+            other: side,
+            "measured_gbps": (round(traffic["bytes"] / (cw["kernel_ms"] * 1e-3) / 1e9, 1) if traffic else None)}
+
+
 def profile(kinds, out):
     PROFILE_OUT[0] = out
     os.makedirs(out, exist_ok=True)
@@ -589,17 +611,11 @@ def main():
             # One chunkwise call = a control-block reset (a few microseconds)
             # and the fused chunkwise kernel; `value` charges the whole call,
             # the roofline the kernel's own duration (events recorded around
-            # it on the same stream, averaged over the timed calls).
-            "roofline": {"bound": "mfma", "kernel": f"{CHUNKWISE_KERNEL}<bf16,256>",
-                         "achieved": round(cw["kernel_tflops"], 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(cw["kernel_tflops"] / PEAK_BF16_TFLOPS, 4),
-                         "kernel_us": round(cw["kernel_ms"] * 1e3, 1),
-                         "traffic": traffic["bytes"] if traffic else None,
-                         "flops_per_launch": cw["flops"],
-                         "hbm": {"algorithmic_bytes": cw["bytes"], "achieved": round(alg_gbps, 1),
-                                 "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(alg_gbps / PEAK_HBM_GBPS, 4),
-                                 "measured_gbps": (round(traffic["bytes"] / (cw["kernel_ms"] * 1e-3) / 1e9, 1)
-                                                   if traffic else None)}},
+            # it on the same stream, averaged over the timed calls). The bound
+            # is the roofline's own: the workload's algorithmic intensity
+            # (flop per HBM byte) against the ridge point peak flops / peak
+            # bandwidth; the other ceiling is reported beside it.
+            "roofline": roofline_object(cw, alg_gbps, traffic),
         })
     if args.only in (None, "decode"):
         wd, dec = bench_decode(args.decode_steps, batches=args.decode_batches)
