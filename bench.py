@@ -82,6 +82,16 @@ def chunkwise_flops(batch, seqlen, heads, dk, dv, chunk):
     return batch * heads * total
 
 
+def chunkwise_dense_flops(batch, seqlen, heads, dk, dv, chunk):
+    """The same work counted dense (every chunk's full b x b score block),
+    reported beside the causal count, labelled."""
+    total = 0
+    for start in range(0, seqlen, chunk):
+        b = min(chunk, seqlen - start)
+        total += 2 * b * b * (dk + dv) + 4 * b * dk * dv
+    return batch * heads * total
+
+
 def chunkwise_split_flops(batch, seqlen, heads, dk, dv, chunk):
     """(state kernel, output kernel) shares of the chunkwise count."""
     state = out = 0
@@ -139,20 +149,31 @@ def copy_probe():
     del src, dst
 
 
-def bench_chunkwise(steps, warmup):
+def _pct(xs, q):
+    xs = sorted(xs)
+    return xs[min(len(xs) - 1, max(0, int(round(q * (len(xs) - 1)))))]
+
+
+def bench_chunkwise(steps, warmup, name="retention_7b_8k", cold_reps=0):
+    """Chunkwise calls on one workload: per-call time (reset + kernel) and the
+    kernel's own event time per call; with cold_reps, also the kernel after
+    a 512 MiB write that evicts L2 and the Infinity Cache."""
     import torch
 
     import retnet_retention_amd as rr
     from synth import get
 
-    w = get("retention_7b_8k")
+    w = get(name)
     q, k, v, g = (t.torch("cuda:0") for t in w.inputs())
     state = torch.empty((w.batch, w.heads, w.dk, w.dv), device="cuda:0")
     out = torch.empty_like(v)
-    ws = torch.empty(rr.chunkwise_workspace_bytes(q, v, w.chunk), dtype=torch.uint8, device="cuda:0")
+    rot = getattr(w, "rotary_base", 0.0) or 0.0
+    ws = torch.empty(rr.chunkwise_workspace_bytes(q, v, w.chunk, rotary_base=rot), dtype=torch.uint8,
+                     device="cuda:0")
 
     def step(events=None):
-        rr.chunkwise_fwd(q, k, v, g, chunk=w.chunk, state_out=state, out=out, workspace=ws, kernel_events=events)
+        rr.chunkwise_fwd(q, k, v, g, chunk=w.chunk, state_out=state, out=out, workspace=ws, rotary_base=rot,
+                         kernel_events=events)
 
     # every timed call also records a pair of events around the chunkwise
     # kernel itself (after the control-block reset): the roofline's duration
@@ -165,20 +186,36 @@ def bench_chunkwise(steps, warmup):
     torch.cuda.synchronize()
     it = iter(pairs)
     ms, wall = time_calls(lambda: step(next(it)), steps, 0)
-    kernel_ms = sum(a.elapsed_time(b) for a, b in pairs) / steps
+    kus = [a.elapsed_time(b) * 1e3 for a, b in pairs]
+    kernel_ms = sum(kus) / steps / 1e3
+    cold = []
+    if cold_reps:
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0")
+        for _ in range(cold_reps):
+            scratch.fill_(1)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()  # creates the events (the library records them again around the kernel)
+            b.record()
+            step((a, b))
+            torch.cuda.synchronize()
+            cold.append(a.elapsed_time(b) * 1e3)
+        del scratch
     flops = chunkwise_flops(w.batch, w.seqlen, w.heads, w.dk, w.dv, w.chunk)
     st_f, out_f = chunkwise_split_flops(w.batch, w.seqlen, w.heads, w.dk, w.dv, w.chunk)
     return {
         "workload": w,
         "ms": ms,
         "kernel_ms": kernel_ms,
+        "kernel_us_pct": (_pct(kus, 0.1), _pct(kus, 0.5), _pct(kus, 0.9)),
+        "cold_kernel_us": _pct(cold, 0.5) if cold else None,
         "wall_s": wall,
         "flops": flops,
+        "dense_flops": chunkwise_dense_flops(w.batch, w.seqlen, w.heads, w.dk, w.dv, w.chunk),
         "tflops": flops / (ms * 1e-3) / 1e12,
         "kernel_tflops": flops / (kernel_ms * 1e-3) / 1e12,
         "state_flops": st_f,
         "out_flops": out_f,
-        "bytes": chunkwise_bytes(w.batch, w.seqlen, w.heads, w.dk, w.dv),
+        "bytes": chunkwise_bytes(w.batch, w.seqlen, w.heads, w.dk, w.dv, gate=w.gate_scale is not None),
     }
 
 
@@ -200,7 +237,7 @@ def bench_parallel(steps, warmup):
     return {"workload": w, "ms": ms, "tflops": flops / (ms * 1e-3) / 1e12}
 
 
-def bench_decode(n_steps=256, warmup=16, batches=None):
+def bench_decode(n_steps=256, warmup=16, batches=None, graph=True):
     """Prefill 8 distinct sequences of 8192 tokens (chunkwise, seeded GPU
     normals / 16 in bf16), tile the states to the batch, then time decode."""
     import torch
@@ -243,8 +280,44 @@ def bench_decode(n_steps=256, warmup=16, batches=None):
         nbytes = step_bytes(bsz, w.heads, w.dk, w.dv)
         results[bsz] = {"us_per_step": ms * 1e3, "tokens_per_s": bsz / (ms * 1e-3),
                         "gbps": nbytes / (ms * 1e-3) / 1e9}
+        # the same steps replayed from a captured HIP graph (one graph of nin
+        # steps, launched back to back): no per-launch host work between steps
+        if graph:
+            graph_ms = _graph_step_ms(step, nin, max(n_steps // nin, 2))
+            results[bsz]["graph_us_per_step"] = graph_ms * 1e3
+            results[bsz]["graph_gbps"] = nbytes / (graph_ms * 1e-3) / 1e9
         del state, ins
     return w, results
+
+
+def _graph_step_ms(step, per_graph, replays):
+    """Device time per step of `per_graph` calls of `step` captured into one
+    graph and replayed `replays` times (after two untimed replays)."""
+    import torch
+
+    side = torch.cuda.Stream()  # default priority
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up off the capturing stream, as capture requires
+        for _ in range(3):
+            step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(per_graph):
+            step()
+    for _ in range(2):
+        graph.replay()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(replays):
+        graph.replay()
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / (replays * per_graph)
+    del graph
+    return ms
 
 
 def cpu_baseline(sample_seqs=2, min_seconds=10.0, max_runs=20):
@@ -288,15 +361,16 @@ def cpu_baseline(sample_seqs=2, min_seconds=10.0, max_runs=20):
 # ---------------------------------------------------------------------------
 # counter passes: a few calls each (the counters are per dispatch)
 LEG_ARGS = {
-    "chunkwise": ["--only", "chunkwise", "--steps", "10", "--warmup", "2"],
-    "decode": ["--only", "decode", "--decode-batches", "64", "--decode-steps", "64"],
+    "chunkwise": ["--only", "chunkwise", "--steps", "10", "--warmup", "2", "--no-other-chunkwise", "--cold-reps",
+                  "0"],
+    "decode": ["--only", "decode", "--decode-batches", "64", "--decode-steps", "64", "--no-decode-graph"],
     "parallel": ["--only", "parallel", "--steps", "10", "--warmup", "2"],
 }
 # kernel statistics: the benchmark's own default calls (warm-up included, so
 # the averages are those of the timed, warmed-up calls to within a few %)
 STATS_ARGS = {
-    "chunkwise": ["--only", "chunkwise"],
-    "decode": ["--only", "decode", "--decode-batches", "64"],
+    "chunkwise": ["--only", "chunkwise", "--no-other-chunkwise", "--cold-reps", "0"],
+    "decode": ["--only", "decode", "--decode-batches", "64", "--no-decode-graph"],
     "parallel": ["--only", "parallel"],
 }
 SQ_COUNTERS = ["SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "SQ_INSTS_LDS",
@@ -560,6 +634,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--only", choices=["chunkwise", "decode", "parallel"], default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-chunkwise", action="store_true",
+                    help="skip the chunkwise timings of the 200M and 3B workloads")
+    ap.add_argument("--no-decode-graph", action="store_true", help="skip the graph-replayed decode timing")
+    ap.add_argument("--cold-reps", type=int, default=10,
+                    help="chunkwise calls timed after evicting the caches (0: none)")
     ap.add_argument("--decode-batches", type=int, nargs="*", default=None)
     ap.add_argument("--decode-steps", type=int, default=256)
     ap.add_argument("--copy-probe", action="store_true", help="also run a plain copy of known size")
@@ -586,11 +665,27 @@ def main():
 
     line = {}
     if args.only in (None, "chunkwise"):
-        cw = bench_chunkwise(args.steps, args.warmup)
+        cw = bench_chunkwise(args.steps, args.warmup, cold_reps=args.cold_reps)
         w = cw["workload"]
         print(f"chunkwise {w.name}: {cw['ms']:.3f} ms/step, {cw['tflops']:.1f} TFLOP/s; kernel alone "
               f"{cw['kernel_ms'] * 1e3:.1f} us, {cw['kernel_tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
         alg_gbps = cw["bytes"] / (cw["kernel_ms"] * 1e-3) / 1e9
+        # the same form on the two smaller chunkwise workloads (warm, reported
+        # beside the headline workload, not as its value)
+        others = {}
+        if not args.no_other_chunkwise:
+            for oname in ("retention_200m", "retention_3b"):
+                o = bench_chunkwise(max(args.steps // 2, 3), max(args.warmup // 4, 3), name=oname)
+                ow = o["workload"]
+                print(f"chunkwise {oname}: {o['ms']:.3f} ms/step, {o['tflops']:.1f} TFLOP/s; kernel alone "
+                      f"{o['kernel_ms'] * 1e3:.1f} us, {o['kernel_tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
+                others[oname] = {
+                    "workload": f"batch {ow.batch}, {ow.seqlen} tokens, {ow.heads} x {ow.dk}, chunk {ow.chunk}"
+                                + (", rotation" if ow.rotary_base else "") + ", gate",
+                    "ms": round(o["ms"], 4), "kernel_us": round(o["kernel_ms"] * 1e3, 1),
+                    "kernel_tflops": round(o["kernel_tflops"], 2),
+                    "mfma_frac": round(o["kernel_tflops"] / PEAK_BF16_TFLOPS, 4),
+                    "hbm_frac": round(o["bytes"] / (o["kernel_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
         traffic = recorded_traffic()
         line.update({
             "metric": "chunkwise retention TFLOP/s (+% MFMA peak); decode-step tokens/s and HBM GB/s",
@@ -617,8 +712,15 @@ def main():
             # bandwidth; the other ceiling is reported beside it.
             "roofline": roofline_object(cw, alg_gbps, traffic),
         })
+        line["chunkwise_detail"] = {
+            "kernel_us_p10_p50_p90": [round(x, 1) for x in cw["kernel_us_pct"]],
+            "cold_kernel_us_p50": round(cw["cold_kernel_us"], 1) if cw["cold_kernel_us"] else None,
+            "cold": "each cold call follows a 512 MiB write that evicts L2 and the Infinity Cache",
+            "dense_equivalent_flops_per_launch": cw["dense_flops"],
+            "other_workloads": others,
+        }
     if args.only in (None, "decode"):
-        wd, dec = bench_decode(args.decode_steps, batches=args.decode_batches)
+        wd, dec = bench_decode(args.decode_steps, batches=args.decode_batches, graph=not args.no_decode_graph)
         for b, r in dec.items():
             print(f"decode batch {b}: {r['us_per_step']:.2f} us/step, {r['tokens_per_s']:.0f} tok/s, "
                   f"{r['gbps']:.0f} GB/s", file=sys.stderr, flush=True)
@@ -644,6 +746,8 @@ def main():
         print(f"cpu baseline: {cb['value'] * 1e3:.2f} GFLOP/s ({cb['seconds']:.1f} s in all)", file=sys.stderr,
               flush=True)
         cb.pop("seconds")
+        if "value" in line:
+            cb["gpu_speedup"] = round(line["value"] / cb["value"], 1)
         line["cpu_baseline"] = cb
     print(json.dumps(line), flush=True)
 

@@ -59,14 +59,17 @@ def test_bf16_chunkwise(b, n, h, d, chunk, gate, rot, state):
     assert_close(st, ref_s, "bf16", "state")
 
 
-@pytest.mark.parametrize("b,n,h,d,gate,rot", [(1, 1, 1, 256, True, False), (2, 63, 3, 64, True, True),
-                                              (1, 200, 2, 128, False, True), (1, 700, 2, 256, True, True)])
-def test_bf16_parallel(b, n, h, d, gate, rot):
-    _announce(form="parallel", b=b, n=n, h=h, d=d, gate=gate, rot=rot)
+# (2, 300, 4, ...): 8 (sequence, head) pairs, so the grid takes its XCD-aware
+# longest-first order, over two query blocks, with rotation from position 1000
+@pytest.mark.parametrize("b,n,h,d,gate,rot,pos", [(1, 1, 1, 256, True, False, 0), (2, 63, 3, 64, True, True, 0),
+                                                  (1, 200, 2, 128, False, True, 0), (1, 700, 2, 256, True, True, 0),
+                                                  (2, 300, 4, 64, True, True, 1000)])
+def test_bf16_parallel(b, n, h, d, gate, rot, pos):
+    _announce(form="parallel", b=b, n=n, h=h, d=d, gate=gate, rot=rot, pos=pos)
     q, k, v, g, _ = make_inputs(23 + n, b, n, h, d, "bf16", 1 / 16, 1 / 16 if gate else None)
     base = 10000.0 if rot else 0.0
-    ref, _ = oracle_run("parallel", q, k, v, g, rotary_base=base)
-    out, _ = gpu_run("parallel", q, k, v, g, rotary_base=base)
+    ref, _ = oracle_run("parallel", q, k, v, g, rotary_base=base, pos_offset=pos)
+    out, _ = gpu_run("parallel", q, k, v, g, rotary_base=base, pos_offset=pos)
     assert_close(out, ref, "bf16", "out")
 
 
