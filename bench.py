@@ -12,10 +12,14 @@ Beside it, on the same run:
   parallel  -- parallel form on the 3B workload (batch 4, 2048, 10 x 256,
                rotation, gate), TFLOP/s;
   roofline  -- the dominant kernel of the headline step against MI355X peak;
-  cpu_baseline -- the fp64 oracle timed on this host on a bounded sample.
+  cpu_baseline -- the fp64 oracle timed on this host on a bounded sample;
+  chunkwise_detail -- kernel-time percentiles, a cold-cache run and the
+               200M and 3B chunkwise workloads.
+With --sweep (or --only sweep): the chunkwise kernel over 2k-64k tokens and
+chunk sizes 64-1024.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only chunkwise|decode|parallel]
-                       [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only chunkwise|decode|parallel|sweep]
+                       [--no-cpu-baseline] [--sweep]
 """
 
 import argparse
@@ -288,6 +292,50 @@ def bench_decode(n_steps=256, warmup=16, batches=None, graph=True):
             results[bsz]["graph_gbps"] = nbytes / (graph_ms * 1e-3) / 1e9
         del state, ins
     return w, results
+
+
+def bench_sweep(steps=10, warmup=20):
+    """Chunkwise kernel time against context length (chunk 512) and against
+    chunk size (8192 tokens), at the 7B layer's heads: batch 1, 16 heads x
+    256, bf16, gate, state out. Inputs: seeded normals / 16 drawn on the GPU."""
+    import torch
+
+    import retnet_retention_amd as rr
+
+    h, d = 16, 256
+    gen = torch.Generator(device="cuda:0")
+    gen.manual_seed(7)
+
+    def run(n, chunk):
+        q, k, v, g = ((torch.randn((1, n, h, d), generator=gen, device="cuda:0") / 16).to(torch.bfloat16)
+                      for _ in range(4))
+        state = torch.empty((1, h, d, d), device="cuda:0")
+        out = torch.empty_like(v)
+        ws = torch.empty(rr.chunkwise_workspace_bytes(q, v, chunk), dtype=torch.uint8, device="cuda:0")
+        pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(steps)]
+        for a, b in pairs:
+            a.record()
+            b.record()
+        for _ in range(warmup):
+            rr.chunkwise_fwd(q, k, v, g, chunk=chunk, state_out=state, out=out, workspace=ws)
+        for ev in pairs:
+            rr.chunkwise_fwd(q, k, v, g, chunk=chunk, state_out=state, out=out, workspace=ws, kernel_events=ev)
+        torch.cuda.synchronize()
+        us = sorted(a.elapsed_time(b) * 1e3 for a, b in pairs)[steps // 2]
+        flops = chunkwise_flops(1, n, h, d, d, chunk)
+        row = {"tokens": n, "chunk": chunk, "kernel_us": round(us, 1), "us_per_1k_tokens": round(us * 1024 / n, 2),
+               "tflops": round(flops / (us * 1e-6) / 1e12, 1),
+               "hbm_frac": round(chunkwise_bytes(1, n, h, d, d) / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)}
+        print(f"sweep: {n} tokens, chunk {chunk}: {us:.1f} us, {row['us_per_1k_tokens']} us per 1k tokens, "
+              f"{row['tflops']} TFLOP/s", file=sys.stderr, flush=True)
+        del q, k, v, g, state, out, ws
+        return row
+
+    context = [run(n, 512) for n in (2048, 8192, 16384, 32768, 65536)]
+    chunks = [run(8192, c) for c in (64, 128, 256, 512, 1024)]
+    return {"shape": "batch 1, 16 heads x 256, bf16, gate, state out", "context_at_chunk_512": context,
+            "chunk_at_8192_tokens": chunks}
 
 
 def _graph_step_ms(step, per_graph, replays):
@@ -632,11 +680,13 @@ def main():
     # the GPU's clocks take tens of milliseconds of load to settle: 5 warm-up
     # calls time the chunkwise call 14% slower than 200 do
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--only", choices=["chunkwise", "decode", "parallel"], default=None)
+    ap.add_argument("--only", choices=["chunkwise", "decode", "parallel", "sweep"], default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-chunkwise", action="store_true",
                     help="skip the chunkwise timings of the 200M and 3B workloads")
     ap.add_argument("--no-decode-graph", action="store_true", help="skip the graph-replayed decode timing")
+    ap.add_argument("--sweep", action="store_true",
+                    help="also sweep the chunkwise kernel over context length and chunk size")
     ap.add_argument("--cold-reps", type=int, default=10,
                     help="chunkwise calls timed after evicting the caches (0: none)")
     ap.add_argument("--decode-batches", type=int, nargs="*", default=None)
@@ -739,6 +789,8 @@ def main():
         line["parallel"] = {"workload": f"{par['workload'].name}: batch 4, 2048 tokens, 10 x 256, rotation, gate",
                             "ms": round(par["ms"], 4), "tflops": round(par["tflops"], 2),
                             "mfma_frac": round(par["tflops"] / PEAK_BF16_TFLOPS, 4)}
+    if args.sweep or args.only == "sweep":
+        line["sweep"] = bench_sweep()
     if args.copy_probe:
         copy_probe()
     if args.only is None and not args.no_cpu_baseline:

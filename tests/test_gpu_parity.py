@@ -45,6 +45,7 @@ BF16_CASES = [
     (2, 300, 2, 64, 7, True, False, True),
     (1, 700, 2, 256, 512, True, True, False),
     (1, 520, 1, 256, 128, False, False, False),
+    (1, 1500, 2, 256, 1024, True, True, True),
 ]
 
 

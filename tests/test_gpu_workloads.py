@@ -110,3 +110,19 @@ def test_7b_decode_full_size():
     # the tiled copies of one prefill state evolve independently: sequences
     # 0 and 2 start from the same state but receive different inputs
     assert not np.array_equal(to64(state)[0], to64(state)[2])
+
+
+@pytest.mark.parametrize("chunk", [512, 1024])
+def test_long_context_chunkwise(chunk):
+    """65,536 tokens (128 or 64 chunks), 2 heads x 256, gate, state out: every
+    output and the state against the oracle (the context and chunk sweep runs
+    the same kernel at these shapes)."""
+    from tests.gpu_helpers import make_inputs
+
+    b, n, h, d = 1, 65536, 2, 256
+    _announce(case="long context", b=b, n=n, h=h, d=d, chunk=chunk)
+    q, k, v, g, _ = make_inputs(77 + chunk, b, n, h, d, "bf16", 1 / 16, 1 / 16)
+    out, st = gpu_run("chunkwise", q, k, v, g, chunk=chunk)
+    ref, ref_s = oracle_run("chunkwise", q, k, v, g, chunk=chunk)
+    assert_close(out, ref, "bf16", "out")
+    assert_close(st, ref_s, "bf16", "state")
