@@ -15,3 +15,4 @@ from .retention_oracle import (  # noqa: F401
     retention,
     rotate,
 )
+from .retention_grad import parallel_grad, unrotate  # noqa: F401
