@@ -126,6 +126,28 @@ ret_status_t retention_chunkwise_fwd_timed(const ret_desc_t *desc, int32_t chunk
 ret_status_t retention_recurrent_step(const ret_desc_t *desc, const void *q, const void *k, const void *v,
                                       const void *g, void *o, float *state, hipStream_t stream);
 
+/* Backward of the parallel form: the gradients of sum(dout (.) out), with
+ * out the output of retention_parallel_fwd on the same (desc, q, k, v, g),
+ * with respect to q, k, v and (when g != NULL) g. All of q, k, v, g, dout,
+ * dq, dk, dv and dg share the layout and dtype of the forward's tensors; dg
+ * must be NULL exactly when g is. The outputs must not overlap each other,
+ * the inputs or the workspace.
+ *
+ * Computed as the chain rule of the forward's definition (the parallel form
+ * is the training form, "Summary"): through the swish gate and GroupNorm
+ * (the raw retention output is recomputed), then, with A = (Q' K'^T) (.) D,
+ *     dV = A^T dO,   dQ' = ((dO V^T) (.) D) K',   dK' = ((dO V^T) (.) D)^T Q',
+ * each a causal retention product (the last two on token-reversed
+ * sequences), and dq, dk turned back by the rotation's angles. Gradients are
+ * stored in the input dtype; products accumulate in fp32.
+ *
+ * Workspace: at least retention_parallel_bwd_workspace_bytes(desc, g != NULL)
+ * bytes, never NULL. */
+size_t retention_parallel_bwd_workspace_bytes(const ret_desc_t *desc, int32_t has_gate);
+ret_status_t retention_parallel_bwd(const ret_desc_t *desc, const void *q, const void *k, const void *v,
+                                    const void *g, const void *dout, void *dq, void *dk, void *dv, void *dg,
+                                    void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char *retention_status_string(ret_status_t status);
 

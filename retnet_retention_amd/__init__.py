@@ -4,6 +4,7 @@ gfx950 behind a C ABI (include/retention.h), with a thin ctypes binding.
     parallel_fwd     parallel form (training)
     chunkwise_fwd    chunkwise recurrent form (long sequences, prefill)
     recurrent_step   recurrent form, one decode step, state in place
+    parallel_bwd     gradients of the parallel form (q, k, v and the gate)
 """
 
 from .binding import (  # noqa: F401
@@ -11,6 +12,7 @@ from .binding import (  # noqa: F401
     chunkwise_fwd,
     chunkwise_workspace_bytes,
     lib,
+    parallel_bwd,
     parallel_fwd,
     recurrent_step,
 )

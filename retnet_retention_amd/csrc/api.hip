@@ -168,6 +168,121 @@ ret_status_t retention_parallel_fwd(const ret_desc_t* desc, const void* q, const
   return RET_OK;
 }
 
+namespace {
+
+// Backward of the parallel form. Workspace slots, each one tensor
+// [batch][seqlen][heads][d] rounded up to 256 bytes: with rotation the angle
+// table and the rotated q and k; with a gate the recomputed retention output
+// and dO; then dQ', the reversed v, dO, q', k' and the reversed dK', dV.
+size_t bwd_tensor_bytes(const ret_desc_t* d) {
+  return align_up((size_t)d->batch * d->seqlen * d->heads * d->dk * elem_size(d->dtype));
+}
+size_t bwd_table_bytes(const ret_desc_t* d) {
+  return d->rotary_base == 0.0 ? 0 : align_up((size_t)d->seqlen * (d->dk / 2) * sizeof(float2));
+}
+size_t bwd_bytes(const ret_desc_t* d, bool gate) {
+  const int slots = (d->rotary_base == 0.0 ? 0 : 2) + (gate ? 2 : 0) + 7;
+  return bwd_table_bytes(d) + slots * bwd_tensor_bytes(d);
+}
+
+}  // namespace
+
+size_t retention_parallel_bwd_workspace_bytes(const ret_desc_t* desc, int32_t has_gate) {
+  if (check_desc(desc) != RET_OK) return 0;
+  return bwd_bytes(desc, has_gate != 0);
+}
+
+ret_status_t retention_parallel_bwd(const ret_desc_t* desc, const void* q, const void* k, const void* v,
+                                    const void* g, const void* dout, void* dq, void* dk, void* dv, void* dg,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  ret_status_t st = check_desc(desc);
+  if (st != RET_OK) return st;
+  if (!q || !k || !v || !dout || !dq || !dk || !dv) return RET_ERR_NULL;
+  if ((g == nullptr) != (dg == nullptr)) return RET_ERR_NULL;
+  const void* ins[] = {q, k, v, g, dout};
+  void* outs[] = {dq, dk, dv, dg};
+  for (const void* p : ins)
+    if (p && !aligned16(p)) return RET_ERR_ALIGN;
+  for (const void* p : outs)
+    if (p && !aligned16(p)) return RET_ERR_ALIGN;
+  const size_t n = (size_t)desc->batch * desc->seqlen * desc->heads * desc->dk * elem_size(desc->dtype);
+  for (int i = 0; i < 4; ++i) {
+    for (const void* p : ins)
+      if (overlaps(outs[i], n, p, n)) return RET_ERR_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(outs[i], n, outs[j], n)) return RET_ERR_ALIAS;
+  }
+  if ((st = check_eps(desc, g)) != RET_OK) return st;
+  const size_t need = bwd_bytes(desc, g != nullptr);
+  if (!workspace || workspace_bytes < need) return RET_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return RET_ERR_ALIGN;
+  if (overlaps(workspace, need, q, n) || overlaps(workspace, need, k, n) || overlaps(workspace, need, v, n) ||
+      overlaps(workspace, need, g, n) || overlaps(workspace, need, dout, n) || overlaps(workspace, need, dq, n) ||
+      overlaps(workspace, need, dk, n) || overlaps(workspace, need, dv, n) || overlaps(workspace, need, dg, n))
+    return RET_ERR_ALIAS;
+
+  const Shape s = make_shape(desc);
+  const size_t tb = bwd_tensor_bytes(desc);
+  char* ws = static_cast<char*>(workspace);
+  char* next = ws + bwd_table_bytes(desc);
+  auto slot = [&]() { char* p = next; next += tb; return p; };
+  const float2* table = nullptr;
+  const void *qr = q, *kr = k;
+  if (desc->rotary_base != 0.0) {
+    float2* tab = reinterpret_cast<float2*>(ws);
+    void* qs = slot();
+    void* ks = slot();
+    if (ret::launch_rotary_table(tab, desc->seqlen, desc->dk, desc->rotary_base, desc->pos_offset, stream) !=
+            hipSuccess ||
+        ret::launch_rotate_keys(q, qs, tab, desc->batch, desc->seqlen, desc->heads, desc->dk, desc->dtype,
+                                stream) != hipSuccess ||
+        ret::launch_rotate_keys(k, ks, tab, desc->batch, desc->seqlen, desc->heads, desc->dk, desc->dtype,
+                                stream) != hipSuccess)
+      return RET_ERR_HIP;
+    table = tab;
+    qr = qs;
+    kr = ks;
+  }
+  // the gradient of the retention output before the epilogue: through the
+  // gate and GroupNorm, from the recomputed raw output, or dout itself
+  const void* dov = dout;
+  if (g) {
+    void* o_raw = slot();
+    void* ds = slot();
+    if (ret::launch_retention_fwd(s, desc->seqlen, false, qr, kr, v, nullptr, o_raw, nullptr, nullptr, nullptr,
+                                  nullptr, nullptr, nullptr, desc->gn_eps, stream) != hipSuccess ||
+        ret::launch_gate_norm_bwd(s, o_raw, g, dout, ds, dg, desc->gn_eps, stream) != hipSuccess)
+      return RET_ERR_HIP;
+    dov = ds;
+  }
+  // dQ' = ((dO V^T) (.) D) K': the forward product with (q, k, v) = (dO, V, K')
+  void* dqr = slot();
+  // dK' = ((dO V^T) (.) D)^T Q' and dV = ((Q' K'^T) (.) D)^T dO: with every
+  // sequence reversed the transposed mask is causal again, so both are the
+  // forward product on reversed tensors, reversed back at the end
+  void* vf = slot();
+  void* dof = slot();
+  void* qf = slot();
+  void* kf = slot();
+  void* dkf = slot();
+  void* dvf = slot();
+  if (ret::launch_retention_fwd(s, desc->seqlen, false, dov, v, kr, nullptr, dqr, nullptr, nullptr, nullptr,
+                                nullptr, nullptr, nullptr, desc->gn_eps, stream) != hipSuccess ||
+      ret::launch_reverse_tokens(s, v, vf, stream) != hipSuccess ||
+      ret::launch_reverse_tokens(s, dov, dof, stream) != hipSuccess ||
+      ret::launch_reverse_tokens(s, qr, qf, stream) != hipSuccess ||
+      ret::launch_reverse_tokens(s, kr, kf, stream) != hipSuccess ||
+      ret::launch_retention_fwd(s, desc->seqlen, false, vf, dof, qf, nullptr, dkf, nullptr, nullptr, nullptr,
+                                nullptr, nullptr, nullptr, desc->gn_eps, stream) != hipSuccess ||
+      ret::launch_retention_fwd(s, desc->seqlen, false, kf, qf, dof, nullptr, dvf, nullptr, nullptr, nullptr,
+                                nullptr, nullptr, nullptr, desc->gn_eps, stream) != hipSuccess ||
+      ret::launch_finish_grad(s, dqr, dq, table, false, stream) != hipSuccess ||
+      ret::launch_finish_grad(s, dkf, dk, table, true, stream) != hipSuccess ||
+      ret::launch_finish_grad(s, dvf, dv, nullptr, true, stream) != hipSuccess)
+    return RET_ERR_HIP;
+  return RET_OK;
+}
+
 size_t retention_chunkwise_workspace_bytes(const ret_desc_t* desc, int32_t chunk) {
   if (check_desc(desc) != RET_OK || chunk < 1) return 0;
   return ctrl_bytes(desc, chunk) + rot_bytes(desc) + chain_bytes(desc) + snap_bytes(desc, chunk);

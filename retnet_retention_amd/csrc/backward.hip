@@ -1,0 +1,152 @@
+// Elementwise passes of the parallel form's backward ("Retentive Network: A
+// Successor to Transformer...", Elamur summary, Summary: the parallel form is
+// the training form). Every matrix product of the gradient is again a causal
+// retention product, which the forward kernel computes; these kernels do the
+// rest:
+//   * gate_norm_bwd_kernel: gradient through the swish gate and the per-head
+//     GroupNorm (one wave per token and head, wave reductions over dv);
+//   * reverse_tokens_kernel: a copy with the token order of every sequence
+//     reversed (the products with the transposed decay mask run on reversed
+//     sequences, where that mask is causal again);
+//   * finish_grad_kernel: the rotation's gradient (each pair turned back by
+//     its angle, from the same cos/sin table as the forward), optionally
+//     reading its source in reversed token order.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace ret {
+
+// One wave per (token, head) row of D values, D / 64 per lane. With
+// y = (o - mean) / sigma, sigma = sqrt(var + eps), s(x) = sigmoid(x):
+//   dg = dout * y * s(g) (1 + g (1 - s(g)))
+//   dy = dout * g s(g)
+//   do = (dy - mean(dy) - y mean(dy y)) / sigma
+template <typename T, int D>
+__global__ __launch_bounds__(256) void gate_norm_bwd_kernel(const T* __restrict__ o, const T* __restrict__ g,
+                                                            const T* __restrict__ dout, T* __restrict__ dov,
+                                                            T* __restrict__ dg, int64_t rows, float eps) {
+  constexpr int PER = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;  // whole waves leave together
+  const int64_t base = row * D + lane * PER;
+  float x[PER], gv[PER], dy[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) x[i] = (float)o[base + i];
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) s += x[i];
+  const float mean = sum64(s) * (1.0f / D);
+  float s2 = 0.f;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) s2 += (x[i] - mean) * (x[i] - mean);
+  const float rsig = rsqrtf(sum64(s2) * (1.0f / D) + eps);
+  float sdy = 0.f, sdyy = 0.f;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const float y = (x[i] - mean) * rsig;
+    gv[i] = (float)g[base + i];
+    const float d = (float)dout[base + i];
+    const float sg = 1.0f / (1.0f + __expf(-gv[i]));
+    dg[base + i] = (T)(d * y * (sg * (1.0f + gv[i] * (1.0f - sg))));
+    dy[i] = d * gv[i] * sg;
+    x[i] = y;
+    sdy += dy[i];
+    sdyy += dy[i] * y;
+  }
+  const float mdy = sum64(sdy) * (1.0f / D), mdyy = sum64(sdyy) * (1.0f / D);
+#pragma unroll
+  for (int i = 0; i < PER; ++i) dov[base + i] = (T)((dy[i] - mdy - x[i] * mdyy) * rsig);
+}
+
+// dst[b][n] = src[b][seqlen - 1 - n], 16 bytes per thread
+__global__ __launch_bounds__(256) void reverse_tokens_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                                             int64_t vecs, int64_t per_tok, int seqlen) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= vecs) return;
+  const int64_t tok = i / per_tok, c = i % per_tok;  // tok = b * seqlen + n
+  const int64_t b = tok / seqlen, n = tok % seqlen;
+  dst[(b * seqlen + (seqlen - 1 - n)) * per_tok + c] = src[i];
+}
+
+// dst[b][n][h] = rot(src[b][n'][h], -angle of n) with n' = n, or seqlen-1-n
+// when `reverse`; no table: a plain (reversing) copy. 8 elements per thread.
+template <typename T>
+__global__ __launch_bounds__(256) void finish_grad_kernel(const T* __restrict__ src, T* __restrict__ dst,
+                                                          const float2* __restrict__ table, int64_t chunks,
+                                                          int seqlen, int heads, int d, int reverse) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;  // one 8-element chunk of dst
+  if (idx >= chunks) return;
+  const int cpr = d / 8;
+  const int64_t vec = idx / cpr;  // (b, n, h) row of dst
+  const int c8 = (int)(idx % cpr);
+  const int h = (int)(vec % heads);
+  const int64_t tok = vec / heads;  // b * seqlen + n
+  const int n = (int)(tok % seqlen);
+  const int64_t b = tok / seqlen;
+  const int ns = reverse ? seqlen - 1 - n : n;
+  const int64_t soff = ((b * seqlen + ns) * heads + h) * d + c8 * 8;
+  F8 x = unpack8(ld_raw8(src + soff));
+  if (table) {
+    const CS4 cs = ld_cs4(table + (int64_t)n * (d / 2) + c8 * 4);
+    const float c[4] = {cs.a[0], cs.a[2], cs.b[0], cs.b[2]};
+    const float s[4] = {cs.a[1], cs.a[3], cs.b[1], cs.b[3]};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float e = x.x[2 * j], o = x.x[2 * j + 1];
+      x.x[2 * j] = e * c[j] + o * s[j];
+      x.x[2 * j + 1] = -e * s[j] + o * c[j];
+    }
+  }
+  store8(dst + idx * 8, x);
+}
+
+hipError_t launch_gate_norm_bwd(const Shape& s, const void* o, const void* g, const void* dout, void* dov, void* dg,
+                                float eps, hipStream_t stream) {
+  const int64_t rows = (int64_t)s.batch * s.seqlen * s.heads;
+  const unsigned blocks = (unsigned)((rows + 3) / 4);
+#define RET_GN_BWD(TT, DD)                                                                                       \
+  hipLaunchKernelGGL((gate_norm_bwd_kernel<TT, DD>), dim3(blocks), dim3(256), 0, stream, (const TT*)o,          \
+                     (const TT*)g, (const TT*)dout, (TT*)dov, (TT*)dg, rows, eps)
+  if (s.dtype == 1) {
+    switch (s.d) {
+      case 64: RET_GN_BWD(bf16, 64); break;
+      case 128: RET_GN_BWD(bf16, 128); break;
+      case 256: RET_GN_BWD(bf16, 256); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (s.d) {
+      case 64: RET_GN_BWD(float, 64); break;
+      case 128: RET_GN_BWD(float, 128); break;
+      case 256: RET_GN_BWD(float, 256); break;
+      default: return hipErrorInvalidValue;
+    }
+  }
+#undef RET_GN_BWD
+  return hipGetLastError();
+}
+
+hipError_t launch_reverse_tokens(const Shape& s, const void* src, void* dst, hipStream_t stream) {
+  const int64_t per_tok = (int64_t)s.heads * s.d * (s.dtype == 1 ? 2 : 4) / 16;
+  const int64_t vecs = (int64_t)s.batch * s.seqlen * per_tok;
+  const unsigned blocks = (unsigned)((vecs + 255) / 256);
+  hipLaunchKernelGGL(reverse_tokens_kernel, dim3(blocks), dim3(256), 0, stream, (const uint4*)src, (uint4*)dst, vecs,
+                     per_tok, s.seqlen);
+  return hipGetLastError();
+}
+
+hipError_t launch_finish_grad(const Shape& s, const void* src, void* dst, const float2* table, bool reverse,
+                              hipStream_t stream) {
+  const int64_t chunks = (int64_t)s.batch * s.seqlen * s.heads * (s.d / 8);
+  const unsigned blocks = (unsigned)((chunks + 255) / 256);
+  if (s.dtype == 1)
+    hipLaunchKernelGGL(finish_grad_kernel<bf16>, dim3(blocks), dim3(256), 0, stream, (const bf16*)src, (bf16*)dst,
+                       table, chunks, s.seqlen, s.heads, s.d, reverse ? 1 : 0);
+  else
+    hipLaunchKernelGGL(finish_grad_kernel<float>, dim3(blocks), dim3(256), 0, stream, (const float*)src,
+                       (float*)dst, table, chunks, s.seqlen, s.heads, s.d, reverse ? 1 : 0);
+  return hipGetLastError();
+}
+
+}  // namespace ret

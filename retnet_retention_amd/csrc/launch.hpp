@@ -39,6 +39,18 @@ hipError_t launch_retention_fwd(const Shape& s, int chunk, bool chunked, const v
                                 float* chain, int* ctrl, const float2* rot, float eps, hipStream_t stream,
                                 hipEvent_t before = nullptr, hipEvent_t after = nullptr);
 
+// Backward passes of the parallel form (all tensors [batch][seqlen][heads][d]
+// of the descriptor's dtype): the gradient through the swish gate and the
+// per-head GroupNorm (o: the retention output before GroupNorm), a copy with
+// each sequence's token order reversed, and the rotation's gradient (turning
+// back by the table's angles; null table: a copy), reading `src` in reversed
+// token order when asked.
+hipError_t launch_gate_norm_bwd(const Shape& s, const void* o, const void* g, const void* dout, void* dov, void* dg,
+                                float eps, hipStream_t stream);
+hipError_t launch_reverse_tokens(const Shape& s, const void* src, void* dst, hipStream_t stream);
+hipError_t launch_finish_grad(const Shape& s, const void* src, void* dst, const float2* table, bool reverse,
+                              hipStream_t stream);
+
 // One decode step, in place on `state`.
 hipError_t launch_recurrent_step(const Shape& s, const void* q, const void* k, const void* v, const void* g,
                                  void* o, float* state, double rotary_base, int64_t pos, float eps,

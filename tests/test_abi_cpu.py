@@ -152,3 +152,25 @@ def test_product_path_never_touches_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "retention_oracle" not in text, f
+
+
+def test_backward_validates_before_any_device_call(L):
+    d, _ = _desc(batch=1, seqlen=8, heads=2, dk=64, dv=64)
+    ws_gate = L.retention_parallel_bwd_workspace_bytes(ctypes.byref(d), 1)
+    ws_plain = L.retention_parallel_bwd_workspace_bytes(ctypes.byref(d), 0)
+    up = lambda x: (x + 255) // 256 * 256
+    tensor = up(1 * 8 * 2 * 64 * 2)
+    # no rotation: 7 tensor slots, two more (raw output, dO) with a gate
+    assert ws_plain == 7 * tensor and ws_gate == 9 * tensor
+    p = [ALIGNED * i for i in range(1, 11)]
+    bwd = L.retention_parallel_bwd
+    # g and dg: both or neither
+    assert bwd(ctypes.byref(d), p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7], None, p[9], ws_gate, None) == 1
+    # misaligned output
+    assert bwd(ctypes.byref(d), p[0], p[1], p[2], None, p[4], p[5] + 8, p[6], p[7], None, p[9], ws_plain,
+               None) == 5
+    # an output overlapping an input
+    assert bwd(ctypes.byref(d), p[0], p[1], p[2], None, p[4], p[0], p[6], p[7], None, p[9], ws_plain, None) == 8
+    # workspace too small
+    assert bwd(ctypes.byref(d), p[0], p[1], p[2], None, p[4], p[5], p[6], p[7], None, p[9], ws_plain - 1,
+               None) == 6
