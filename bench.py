@@ -241,6 +241,40 @@ def bench_parallel(steps, warmup):
     return {"workload": w, "ms": ms, "tflops": flops / (ms * 1e-3) / 1e12}
 
 
+def bench_parallel_bwd(steps, warmup):
+    """Backward of the parallel form on the 3B workload (rotation, gate):
+    dq, dk, dv, dg from a seeded dout."""
+    import torch
+
+    import retnet_retention_amd as rr
+    from synth import get
+
+    w = get("retention_3b")
+    q, k, v, g = (t.torch("cuda:0") for t in w.inputs())
+    gen = torch.Generator(device="cuda:0")
+    gen.manual_seed(w.seed + 7)
+    dout = (torch.randn(v.shape, generator=gen, device="cuda:0") / 8).to(v.dtype)
+    ws = torch.empty(_bwd_workspace_bytes(q, v, w.rotary_base), dtype=torch.uint8, device="cuda:0")
+
+    def step():
+        rr.parallel_bwd(q, k, v, dout, g, rotary_base=w.rotary_base, workspace=ws)
+
+    ms, _ = time_calls(step, steps, warmup)
+    flops = 3 * parallel_flops(w.batch, w.seqlen, w.heads, w.dk, w.dv)
+    return {"workload": w, "ms": ms, "flops": flops, "tflops": flops / (ms * 1e-3) / 1e12}
+
+
+def _bwd_workspace_bytes(q, v, rotary_base):
+    import ctypes
+
+    import retnet_retention_amd.binding as B
+
+    desc, keep = B._desc_for(q, v, None, rotary_base, 0, 1e-5)
+    n = B.lib().retention_parallel_bwd_workspace_bytes(ctypes.byref(desc), 1)
+    del keep
+    return n
+
+
 def bench_decode(n_steps=256, warmup=16, batches=None, graph=True):
     """Prefill 8 distinct sequences of 8192 tokens (chunkwise, seeded GPU
     normals / 16 in bf16), tile the states to the batch, then time decode."""
@@ -420,6 +454,7 @@ STATS_ARGS = {
     "chunkwise": ["--only", "chunkwise", "--no-other-chunkwise", "--cold-reps", "0"],
     "decode": ["--only", "decode", "--decode-batches", "64", "--no-decode-graph"],
     "parallel": ["--only", "parallel"],
+    "parallel_bwd": ["--only", "parallel_bwd"],
 }
 SQ_COUNTERS = ["SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "SQ_INSTS_LDS",
                "SQ_LDS_BANK_CONFLICT", "SQ_WAIT_INST_LDS", "SQ_INSTS_VALU", "GRBM_GUI_ACTIVE"]
@@ -483,7 +518,8 @@ def profile_stats(out, raw):
         _run_profiler(cmd, d + ".log", 600)
         line = [ln for ln in open(d + ".log") if ln.startswith("{")]
         stats = list(csv.DictReader(open(glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)[0])))
-        name = {"chunkwise": "chunkwise_7b_8k", "decode": "decode_step_7b_b64", "parallel": "parallel_3b"}[leg]
+        name = {"chunkwise": "chunkwise_7b_8k", "decode": "decode_step_7b_b64", "parallel": "parallel_3b",
+                "parallel_bwd": "parallel_backward_3b"}[leg]
         with open(os.path.join(out, f"{name}_kernel_stats.txt"), "w") as f:
             f.write(f"rocprofv3 kernel statistics, {leg} leg of the benchmark\n")
             f.write("made by: python bench.py --profile stats --profile-out <out>\n")
@@ -680,7 +716,7 @@ def main():
     # the GPU's clocks take tens of milliseconds of load to settle: 5 warm-up
     # calls time the chunkwise call 14% slower than 200 do
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--only", choices=["chunkwise", "decode", "parallel", "sweep"], default=None)
+    ap.add_argument("--only", choices=["chunkwise", "decode", "parallel", "parallel_bwd", "sweep"], default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-chunkwise", action="store_true",
                     help="skip the chunkwise timings of the 200M and 3B workloads")
@@ -789,6 +825,16 @@ def main():
         line["parallel"] = {"workload": f"{par['workload'].name}: batch 4, 2048 tokens, 10 x 256, rotation, gate",
                             "ms": round(par["ms"], 4), "tflops": round(par["tflops"], 2),
                             "mfma_frac": round(par["tflops"] / PEAK_BF16_TFLOPS, 4)}
+    if args.only in (None, "parallel_bwd"):
+        pb = bench_parallel_bwd(max(args.steps // 2, 3), max(args.warmup // 4, 3))
+        print(f"parallel backward {pb['workload'].name}: {pb['ms']:.3f} ms, {pb['tflops']:.1f} TFLOP/s",
+              file=sys.stderr, flush=True)
+        line["parallel_backward"] = {
+            "workload": f"{pb['workload'].name}: batch 4, 2048 tokens, 10 x 256, rotation, gate; dq, dk, dv, dg",
+            "ms": round(pb["ms"], 4), "tflops": round(pb["tflops"], 2),
+            "mfma_frac": round(pb["tflops"] / PEAK_BF16_TFLOPS, 4),
+            "flops": "3 x the forward's algorithmic count (dQ, dK, dV products); the recomputed forward "
+                     "for the GroupNorm gradient is not counted"}
     if args.sweep or args.only == "sweep":
         line["sweep"] = bench_sweep()
     if args.copy_probe:
