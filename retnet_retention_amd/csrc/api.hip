@@ -171,9 +171,10 @@ ret_status_t retention_parallel_fwd(const ret_desc_t* desc, const void* q, const
 namespace {
 
 // Backward of the parallel form. Workspace slots, each one tensor
-// [batch][seqlen][heads][d] rounded up to 256 bytes: with rotation the angle
-// table and the rotated q and k; with a gate the recomputed retention output
-// and dO; then dQ', the reversed v, dO, q', k' and the reversed dK', dV.
+// [batch][seqlen][heads][d] rounded up to 256 bytes: the angle table and the
+// rotated q', k' and reversed q' with rotation, else only the reversed q;
+// with a gate the recomputed retention output, dO and reversed dO, else only
+// the reversed dO.
 size_t bwd_tensor_bytes(const ret_desc_t* d) {
   return align_up((size_t)d->batch * d->seqlen * d->heads * d->dk * elem_size(d->dtype));
 }
@@ -181,7 +182,7 @@ size_t bwd_table_bytes(const ret_desc_t* d) {
   return d->rotary_base == 0.0 ? 0 : align_up((size_t)d->seqlen * (d->dk / 2) * sizeof(float2));
 }
 size_t bwd_bytes(const ret_desc_t* d, bool gate) {
-  const int slots = (d->rotary_base == 0.0 ? 0 : 2) + (gate ? 2 : 0) + 7;
+  const int slots = (d->rotary_base == 0.0 ? 1 : 3) + (gate ? 3 : 1);
   return bwd_table_bytes(d) + slots * bwd_tensor_bytes(d);
 }
 
@@ -226,59 +227,65 @@ ret_status_t retention_parallel_bwd(const ret_desc_t* desc, const void* q, const
   char* ws = static_cast<char*>(workspace);
   char* next = ws + bwd_table_bytes(desc);
   auto slot = [&]() { char* p = next; next += tb; return p; };
+  // q' and k' (rotated when rotation is on) and q' with each sequence's
+  // token order reversed
   const float2* table = nullptr;
   const void *qr = q, *kr = k;
+  void* qrev = nullptr;
   if (desc->rotary_base != 0.0) {
     float2* tab = reinterpret_cast<float2*>(ws);
     void* qs = slot();
     void* ks = slot();
+    qrev = slot();
     if (ret::launch_rotary_table(tab, desc->seqlen, desc->dk, desc->rotary_base, desc->pos_offset, stream) !=
             hipSuccess ||
-        ret::launch_rotate_keys(q, qs, tab, desc->batch, desc->seqlen, desc->heads, desc->dk, desc->dtype,
-                                stream) != hipSuccess ||
+        ret::launch_rotate_keys(q, qs, tab, desc->batch, desc->seqlen, desc->heads, desc->dk, desc->dtype, stream,
+                                qrev) != hipSuccess ||
         ret::launch_rotate_keys(k, ks, tab, desc->batch, desc->seqlen, desc->heads, desc->dk, desc->dtype,
                                 stream) != hipSuccess)
       return RET_ERR_HIP;
     table = tab;
     qr = qs;
     kr = ks;
+  } else {
+    qrev = slot();
+    if (ret::launch_reverse_tokens(s, q, qrev, stream) != hipSuccess) return RET_ERR_HIP;
   }
-  // the gradient of the retention output before the epilogue: through the
-  // gate and GroupNorm, from the recomputed raw output, or dout itself
+  // dO, the gradient of the retention output before the epilogue (through
+  // the gate and GroupNorm, from the recomputed raw output, or dout itself),
+  // and its reversed copy
   const void* dov = dout;
+  void* dorev = nullptr;
   if (g) {
     void* o_raw = slot();
     void* ds = slot();
+    dorev = slot();
     if (ret::launch_retention_fwd(s, desc->seqlen, false, qr, kr, v, nullptr, o_raw, nullptr, nullptr, nullptr,
                                   nullptr, nullptr, nullptr, desc->gn_eps, stream) != hipSuccess ||
-        ret::launch_gate_norm_bwd(s, o_raw, g, dout, ds, dg, desc->gn_eps, stream) != hipSuccess)
+        ret::launch_gate_norm_bwd(s, o_raw, g, dout, ds, dg, desc->gn_eps, stream, dorev) != hipSuccess)
       return RET_ERR_HIP;
     dov = ds;
+  } else {
+    dorev = slot();
+    if (ret::launch_reverse_tokens(s, dout, dorev, stream) != hipSuccess) return RET_ERR_HIP;
   }
-  // dQ' = ((dO V^T) (.) D) K': the forward product with (q, k, v) = (dO, V, K')
-  void* dqr = slot();
-  // dK' = ((dO V^T) (.) D)^T Q' and dV = ((Q' K'^T) (.) D)^T dO: with every
-  // sequence reversed the transposed mask is causal again, so both are the
-  // forward product on reversed tensors, reversed back at the end
-  void* vf = slot();
-  void* dof = slot();
-  void* qf = slot();
-  void* kf = slot();
-  void* dkf = slot();
-  void* dvf = slot();
-  if (ret::launch_retention_fwd(s, desc->seqlen, false, dov, v, kr, nullptr, dqr, nullptr, nullptr, nullptr,
-                                nullptr, nullptr, nullptr, desc->gn_eps, stream) != hipSuccess ||
-      ret::launch_reverse_tokens(s, v, vf, stream) != hipSuccess ||
-      ret::launch_reverse_tokens(s, dov, dof, stream) != hipSuccess ||
-      ret::launch_reverse_tokens(s, qr, qf, stream) != hipSuccess ||
-      ret::launch_reverse_tokens(s, kr, kf, stream) != hipSuccess ||
-      ret::launch_retention_fwd(s, desc->seqlen, false, vf, dof, qf, nullptr, dkf, nullptr, nullptr, nullptr,
-                                nullptr, nullptr, nullptr, desc->gn_eps, stream) != hipSuccess ||
-      ret::launch_retention_fwd(s, desc->seqlen, false, kf, qf, dof, nullptr, dvf, nullptr, nullptr, nullptr,
-                                nullptr, nullptr, nullptr, desc->gn_eps, stream) != hipSuccess ||
-      ret::launch_finish_grad(s, dqr, dq, table, false, stream) != hipSuccess ||
-      ret::launch_finish_grad(s, dkf, dk, table, true, stream) != hipSuccess ||
-      ret::launch_finish_grad(s, dvf, dv, nullptr, true, stream) != hipSuccess)
+  // Three forward products, each storing its gradient straight into the
+  // caller's tensor (turned back by the rotation where it applies):
+  //   dq = rot^T(P(dO, V, K'));
+  //   dk = rot^T(rev P(rev V, rev dO, rev Q')), the transposed mask made
+  //        causal by reversing every sequence (q read reversed, output
+  //        stored reversed);
+  //   dv = rev P(rev K', rev Q', rev dO).
+  const hipEvent_t none = nullptr;
+  if (ret::launch_retention_fwd(s, desc->seqlen, false, dov, v, kr, nullptr, dq, nullptr, nullptr, nullptr, nullptr,
+                                nullptr, nullptr, desc->gn_eps, stream, none, none, false, false, table) !=
+          hipSuccess ||
+      ret::launch_retention_fwd(s, desc->seqlen, false, v, dorev, qrev, nullptr, dk, nullptr, nullptr, nullptr,
+                                nullptr, nullptr, nullptr, desc->gn_eps, stream, none, none, true, true, table) !=
+          hipSuccess ||
+      ret::launch_retention_fwd(s, desc->seqlen, false, kr, qrev, dorev, nullptr, dv, nullptr, nullptr, nullptr,
+                                nullptr, nullptr, nullptr, desc->gn_eps, stream, none, none, true, true, nullptr) !=
+          hipSuccess)
     return RET_ERR_HIP;
   return RET_OK;
 }

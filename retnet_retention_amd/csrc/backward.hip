@@ -7,10 +7,10 @@
 //     GroupNorm (one wave per token and head, wave reductions over dv);
 //   * reverse_tokens_kernel: a copy with the token order of every sequence
 //     reversed (the products with the transposed decay mask run on reversed
-//     sequences, where that mask is causal again);
-//   * finish_grad_kernel: the rotation's gradient (each pair turned back by
-//     its angle, from the same cos/sin table as the forward), optionally
-//     reading its source in reversed token order.
+//     sequences, where that mask is causal again), for inputs that no other
+//     pass already writes reversed.
+// The rotation's gradient (each pair turned back by its angle) and the
+// reversal of the products' outputs happen in the retention kernel's stores.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -21,10 +21,13 @@ namespace ret {
 //   dg = dout * y * s(g) (1 + g (1 - s(g)))
 //   dy = dout * g s(g)
 //   do = (dy - mean(dy) - y mean(dy y)) / sigma
+// dov_rev (may be null) also receives dO at each sequence's reversed
+// token positions.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void gate_norm_bwd_kernel(const T* __restrict__ o, const T* __restrict__ g,
                                                             const T* __restrict__ dout, T* __restrict__ dov,
-                                                            T* __restrict__ dg, int64_t rows, float eps) {
+                                                            T* __restrict__ dg, T* __restrict__ dov_rev,
+                                                            int64_t rows, int seqlen, int heads, float eps) {
   constexpr int PER = D / 64;
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -55,8 +58,17 @@ __global__ __launch_bounds__(256) void gate_norm_bwd_kernel(const T* __restrict_
     sdyy += dy[i] * y;
   }
   const float mdy = sum64(sdy) * (1.0f / D), mdyy = sum64(sdyy) * (1.0f / D);
+  int64_t rbase = 0;
+  if (dov_rev) {
+    const int64_t tok = row / heads, b = tok / seqlen, n = tok % seqlen;
+    rbase = ((b * seqlen + (seqlen - 1 - n)) * heads + row % heads) * D + lane * PER;
+  }
 #pragma unroll
-  for (int i = 0; i < PER; ++i) dov[base + i] = (T)((dy[i] - mdy - x[i] * mdyy) * rsig);
+  for (int i = 0; i < PER; ++i) {
+    const T r = (T)((dy[i] - mdy - x[i] * mdyy) * rsig);
+    dov[base + i] = r;
+    if (dov_rev) dov_rev[rbase + i] = r;
+  }
 }
 
 // dst[b][n] = src[b][seqlen - 1 - n], 16 bytes per thread
@@ -69,45 +81,13 @@ __global__ __launch_bounds__(256) void reverse_tokens_kernel(const uint4* __rest
   dst[(b * seqlen + (seqlen - 1 - n)) * per_tok + c] = src[i];
 }
 
-// dst[b][n][h] = rot(src[b][n'][h], -angle of n) with n' = n, or seqlen-1-n
-// when `reverse`; no table: a plain (reversing) copy. 8 elements per thread.
-template <typename T>
-__global__ __launch_bounds__(256) void finish_grad_kernel(const T* __restrict__ src, T* __restrict__ dst,
-                                                          const float2* __restrict__ table, int64_t chunks,
-                                                          int seqlen, int heads, int d, int reverse) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;  // one 8-element chunk of dst
-  if (idx >= chunks) return;
-  const int cpr = d / 8;
-  const int64_t vec = idx / cpr;  // (b, n, h) row of dst
-  const int c8 = (int)(idx % cpr);
-  const int h = (int)(vec % heads);
-  const int64_t tok = vec / heads;  // b * seqlen + n
-  const int n = (int)(tok % seqlen);
-  const int64_t b = tok / seqlen;
-  const int ns = reverse ? seqlen - 1 - n : n;
-  const int64_t soff = ((b * seqlen + ns) * heads + h) * d + c8 * 8;
-  F8 x = unpack8(ld_raw8(src + soff));
-  if (table) {
-    const CS4 cs = ld_cs4(table + (int64_t)n * (d / 2) + c8 * 4);
-    const float c[4] = {cs.a[0], cs.a[2], cs.b[0], cs.b[2]};
-    const float s[4] = {cs.a[1], cs.a[3], cs.b[1], cs.b[3]};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float e = x.x[2 * j], o = x.x[2 * j + 1];
-      x.x[2 * j] = e * c[j] + o * s[j];
-      x.x[2 * j + 1] = -e * s[j] + o * c[j];
-    }
-  }
-  store8(dst + idx * 8, x);
-}
-
 hipError_t launch_gate_norm_bwd(const Shape& s, const void* o, const void* g, const void* dout, void* dov, void* dg,
-                                float eps, hipStream_t stream) {
+                                float eps, hipStream_t stream, void* dov_rev) {
   const int64_t rows = (int64_t)s.batch * s.seqlen * s.heads;
   const unsigned blocks = (unsigned)((rows + 3) / 4);
 #define RET_GN_BWD(TT, DD)                                                                                       \
   hipLaunchKernelGGL((gate_norm_bwd_kernel<TT, DD>), dim3(blocks), dim3(256), 0, stream, (const TT*)o,          \
-                     (const TT*)g, (const TT*)dout, (TT*)dov, (TT*)dg, rows, eps)
+                     (const TT*)g, (const TT*)dout, (TT*)dov, (TT*)dg, (TT*)dov_rev, rows, s.seqlen, s.heads, eps)
   if (s.dtype == 1) {
     switch (s.d) {
       case 64: RET_GN_BWD(bf16, 64); break;
@@ -133,19 +113,6 @@ hipError_t launch_reverse_tokens(const Shape& s, const void* src, void* dst, hip
   const unsigned blocks = (unsigned)((vecs + 255) / 256);
   hipLaunchKernelGGL(reverse_tokens_kernel, dim3(blocks), dim3(256), 0, stream, (const uint4*)src, (uint4*)dst, vecs,
                      per_tok, s.seqlen);
-  return hipGetLastError();
-}
-
-hipError_t launch_finish_grad(const Shape& s, const void* src, void* dst, const float2* table, bool reverse,
-                              hipStream_t stream) {
-  const int64_t chunks = (int64_t)s.batch * s.seqlen * s.heads * (s.d / 8);
-  const unsigned blocks = (unsigned)((chunks + 255) / 256);
-  if (s.dtype == 1)
-    hipLaunchKernelGGL(finish_grad_kernel<bf16>, dim3(blocks), dim3(256), 0, stream, (const bf16*)src, (bf16*)dst,
-                       table, chunks, s.seqlen, s.heads, s.d, reverse ? 1 : 0);
-  else
-    hipLaunchKernelGGL(finish_grad_kernel<float>, dim3(blocks), dim3(256), 0, stream, (const float*)src,
-                       (float*)dst, table, chunks, s.seqlen, s.heads, s.d, reverse ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -259,6 +259,23 @@ __device__ __forceinline__ void zero_unless(F8& v, bool keep) {
 }
 
 // (cos, sin) of 4 consecutive pairs, as two 16-byte loads
+// N consecutive elements (N/2 adjacent pairs) turned back by the angles at
+// cs[0 .. N/2): (x c + y s, -x s + y c), the transpose of the rotation
+template <int N>
+__device__ __forceinline__ void unrotate_pairs(float* v, const float2* cs) {
+#pragma unroll
+  for (int j = 0; j < N / 2; j += 2) {
+    const f32x4 t = *reinterpret_cast<const f32x4*>(cs + j);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const float c = t[2 * u], s = t[2 * u + 1];
+      const float e = v[2 * (j + u)], o = v[2 * (j + u) + 1];
+      v[2 * (j + u)] = e * c + o * s;
+      v[2 * (j + u) + 1] = -e * s + o * c;
+    }
+  }
+}
+
 struct CS4 { f32x4 a, b; };
 __device__ __forceinline__ CS4 ld_cs4(const float2* p) {
   return CS4{reinterpret_cast<const f32x4*>(p)[0], reinterpret_cast<const f32x4*>(p)[1]};

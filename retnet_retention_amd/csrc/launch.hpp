@@ -22,9 +22,11 @@ hipError_t launch_rotary_table(float2* table, int seqlen, int d, double base, in
                                hipStream_t stream);
 
 // Rotated copy kr of k ([batch][seqlen][heads][d], same dtype); the
-// queries are turned by the retention kernels as they load them.
+// queries are turned by the retention kernels as they load them. `krev`
+// (may be null) also receives the rotated rows with each sequence's token
+// order reversed; kr may be null when only that copy is wanted.
 hipError_t launch_rotate_keys(const void* k, void* kr, const float2* table, int batch, int seqlen, int heads, int d,
-                              int dtype, hipStream_t stream);
+                              int dtype, hipStream_t stream, void* krev = nullptr);
 
 // Parallel form (chunked == false: chunk == seqlen, no state) or chunkwise
 // form (chunked == true) in one launch. Chunkwise needs: snap [BH][nchunks]
@@ -32,24 +34,25 @@ hipError_t launch_rotate_keys(const void* k, void* kr, const float2* table, int 
 // chunkwise_ctrl_bytes() ints, all device memory owned by the caller.
 size_t chunkwise_ctrl_bytes(int batch, int heads, int nchunks);
 // `rot` (may be null): the cos/sin table of launch_rotary_table, with which
-// the kernels turn q as they load it (k must then arrive rotated).
+// the kernels turn q as they load it (k must then arrive rotated). Parallel
+// form only: `q_rev` reads q with each sequence's token order reversed (not
+// with `rot`), `out_rev` stores the output reversed, `out_rot` (may be null)
+// turns each stored output row back by its stored position's angles.
 // `before`/`after` (may be null) are recorded around the main kernel.
 hipError_t launch_retention_fwd(const Shape& s, int chunk, bool chunked, const void* q, const void* k, const void* v,
                                 const void* g, void* o, const float* state_in, float* state_out, void* snap,
                                 float* chain, int* ctrl, const float2* rot, float eps, hipStream_t stream,
-                                hipEvent_t before = nullptr, hipEvent_t after = nullptr);
+                                hipEvent_t before = nullptr, hipEvent_t after = nullptr, bool q_rev = false,
+                                bool out_rev = false, const float2* out_rot = nullptr);
 
 // Backward passes of the parallel form (all tensors [batch][seqlen][heads][d]
 // of the descriptor's dtype): the gradient through the swish gate and the
-// per-head GroupNorm (o: the retention output before GroupNorm), a copy with
-// each sequence's token order reversed, and the rotation's gradient (turning
-// back by the table's angles; null table: a copy), reading `src` in reversed
-// token order when asked.
+// per-head GroupNorm (o: the retention output before GroupNorm; `dov_rev`,
+// may be null, also receives dO in reversed token order) and a copy with
+// each sequence's token order reversed.
 hipError_t launch_gate_norm_bwd(const Shape& s, const void* o, const void* g, const void* dout, void* dov, void* dg,
-                                float eps, hipStream_t stream);
+                                float eps, hipStream_t stream, void* dov_rev = nullptr);
 hipError_t launch_reverse_tokens(const Shape& s, const void* src, void* dst, hipStream_t stream);
-hipError_t launch_finish_grad(const Shape& s, const void* src, void* dst, const float2* table, bool reverse,
-                              hipStream_t stream);
 
 // One decode step, in place on `state`.
 hipError_t launch_recurrent_step(const Shape& s, const void* q, const void* k, const void* v, const void* g,

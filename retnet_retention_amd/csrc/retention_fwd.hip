@@ -143,6 +143,11 @@ struct FwdParams {
   float* chain;  // [BH][2][D*D] fp32: R_i handed to the next state workgroup (fragment order)
   int* ctrl;     // [0] count, [1] error, [8..15] tickets, [16 + (bh*(nchunks+1) + i)*4 + kind*2 + part]: R_{i-1} ready
   const float2* rot;  // (cos, sin) per position and pair [seqlen][D/2]: q is turned on load; null: no rotation
+  // parallel form only (the backward's products): read q with each sequence's
+  // token order reversed; store the output reversed, and/or turned back by
+  // out_rot's angles of the stored position (null: as computed)
+  int q_rev, out_rev;
+  const float2* out_rot;
   int batch, seqlen, heads, chunk, nchunks, qblocks;
   int has_state0, xcd_order;
   float eps;
@@ -218,7 +223,10 @@ __device__ __forceinline__ u32x2 load2_coherent(__amdgpu_buffer_rsrc_t rs, uint3
 // ---------------------------------------------------------------------------
 // CROSS: the chunk has a previous state R_{i-1} (chunkwise form, chunk > 0
 // or an initial state); the parallel form and chunk 0 without one have none.
-template <typename T, int D, bool FAST, bool CROSS>
+// PAR: the parallel kernel's instantiation, the only one that reads q
+// reversed or stores its output reversed or turned back (the backward's
+// products); the chunkwise kernel's instantiations carry none of that code.
+template <typename T, int D, bool FAST, bool CROSS, bool PAR = false>
 __device__ __forceinline__ void out_role(const FwdParams& p, int bh, int ci, int qb, bool chunked, char* l0, char* l1,
                                          char* l2, char* l3) {
   using C = OutTile<T, D, FAST>;
@@ -287,7 +295,7 @@ __device__ __forceinline__ void out_role(const FwdParams& p, int bh, int ci, int
 #pragma unroll
   for (int r = 0; r < QT; ++r) {
     const int qrow = min(qw0 + 32 * r + n, cend - 1);
-    const T* qr = Q + (int64_t)qrow * tstride + 8 * hh;
+    const T* qr = Q + (int64_t)(PAR && p.q_rev ? p.seqlen - 1 - qrow : qrow) * tstride + 8 * hh;
     if (p.rot) {
       const float2* cs = p.rot + (int64_t)qrow * (D / 2) + 4 * hh;
 #pragma unroll
@@ -558,7 +566,14 @@ __device__ __forceinline__ void out_role(const FwdParams& p, int bh, int ci, int
 #pragma unroll
           for (int e = 0; e < CPL; ++e) y[e] *= swish(g[k][e]);
         }
-        if (orow < cend) store16f(O + (int64_t)orow * tstride + H * SG::HALF + lcol, y);
+        if (orow < cend) {
+          int mrow = orow;  // stored position
+          if constexpr (PAR) {
+            if (p.out_rev) mrow = p.seqlen - 1 - orow;
+            if (p.out_rot) unrotate_pairs<CPL>(y, p.out_rot + (int64_t)mrow * (D / 2) + (H * SG::HALF + lcol) / 2);
+          }
+          store16f(O + (int64_t)mrow * tstride + H * SG::HALF + lcol, y);
+        }
       }
     });
   }
@@ -867,7 +882,7 @@ __global__ __launch_bounds__(kWaves<T> * 64, 1) void retention_parallel_kernel(F
     bh = bid % groups;
     qb = p.qblocks - 1 - bid / groups;
   }
-  out_role<T, D, FAST, false>(p, bh, 0, qb, false, l0, l1, l2, l3);
+  out_role<T, D, FAST, false, true>(p, bh, 0, qb, false, l0, l1, l2, l3);
 #endif
 }
 
@@ -976,9 +991,15 @@ size_t chunkwise_ctrl_bytes(int batch, int heads, int nchunks) {
 hipError_t launch_retention_fwd(const Shape& s, int chunk, bool chunked, const void* q, const void* k, const void* v,
                                 const void* g, void* o, const float* state_in, float* state_out, void* snap,
                                 float* chain, int* ctrl, const float2* rot, float eps, hipStream_t stream,
-                                hipEvent_t before, hipEvent_t after) {
+                                hipEvent_t before, hipEvent_t after, bool q_rev, bool out_rev,
+                                const float2* out_rot) {
+  if (chunked && (q_rev || out_rev || out_rot)) return hipErrorInvalidValue;
+  if (rot && q_rev) return hipErrorInvalidValue;  // q's angles are those of its own positions
   FwdParams p;
   p.rot = rot;
+  p.q_rev = q_rev;
+  p.out_rev = out_rev;
+  p.out_rot = out_rot;
   p.q = q;
   p.k = k;
   p.v = v;

@@ -36,8 +36,8 @@ hipError_t launch_rotary_table(float2* table, int seqlen, int d, double base, in
 
 template <typename T>
 __global__ __launch_bounds__(256) void rotate_keys_kernel(const T* __restrict__ k, T* __restrict__ kr,
-                                                           const float2* __restrict__ table, int64_t chunks,
-                                                           int seqlen, int heads, int d) {
+                                                           T* __restrict__ krev, const float2* __restrict__ table,
+                                                           int64_t chunks, int seqlen, int heads, int d) {
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;  // one 8-element chunk
   if (idx >= chunks) return;
   const int cpr = d / 8;                                     // chunks per head vector
@@ -48,19 +48,24 @@ __global__ __launch_bounds__(256) void rotate_keys_kernel(const T* __restrict__ 
   const int64_t off = idx * 8;
   F8 y = unpack8(ld_raw8(k + off));
   rotate4(y, cs);
-  store8(kr + off, y);
+  if (kr) store8(kr + off, y);
+  if (krev) {  // the same row at the reversed position of its sequence
+    const int64_t b = vec / heads / seqlen;
+    const int h = (int)(vec % heads);
+    store8(krev + ((b * seqlen + (seqlen - 1 - n)) * heads + h) * d + c8 * 8, y);
+  }
 }
 
 hipError_t launch_rotate_keys(const void* k, void* kr, const float2* table, int batch, int seqlen, int heads, int d,
-                              int dtype, hipStream_t stream) {
+                              int dtype, hipStream_t stream, void* krev) {
   const int64_t chunks = (int64_t)batch * seqlen * heads * (d / 8);
   const unsigned blocks = (unsigned)((chunks + 255) / 256);
   if (dtype == 1)
     hipLaunchKernelGGL(rotate_keys_kernel<bf16>, dim3(blocks), dim3(256), 0, stream, (const bf16*)k, (bf16*)kr,
-                       table, chunks, seqlen, heads, d);
+                       (bf16*)krev, table, chunks, seqlen, heads, d);
   else
     hipLaunchKernelGGL(rotate_keys_kernel<float>, dim3(blocks), dim3(256), 0, stream, (const float*)k, (float*)kr,
-                       table, chunks, seqlen, heads, d);
+                       (float*)krev, table, chunks, seqlen, heads, d);
   return hipGetLastError();
 }
 

@@ -160,8 +160,9 @@ def test_backward_validates_before_any_device_call(L):
     ws_plain = L.retention_parallel_bwd_workspace_bytes(ctypes.byref(d), 0)
     up = lambda x: (x + 255) // 256 * 256
     tensor = up(1 * 8 * 2 * 64 * 2)
-    # no rotation: 7 tensor slots, two more (raw output, dO) with a gate
-    assert ws_plain == 7 * tensor and ws_gate == 9 * tensor
+    # no rotation: the reversed q and the reversed dO; with a gate the raw
+    # output and dO as well
+    assert ws_plain == 2 * tensor and ws_gate == 4 * tensor
     p = [ALIGNED * i for i in range(1, 11)]
     bwd = L.retention_parallel_bwd
     # g and dg: both or neither
