@@ -126,6 +126,16 @@ ret_status_t retention_chunkwise_fwd_timed(const ret_desc_t *desc, int32_t chunk
 ret_status_t retention_recurrent_step(const ret_desc_t *desc, const void *q, const void *k, const void *v,
                                       const void *g, void *o, float *state, hipStream_t stream);
 
+/* The same step with one rotation position per sequence (continuous
+ * batching: sequences of a batch at different lengths): `positions` is a
+ * DEVICE array of `batch` int64 positions, 8-byte aligned, each in
+ * [0, 2^52] (not checked: it lives on the device), read by the step's kernel
+ * in place of desc->pos_offset. Without rotation (rotary_base == 0) it is
+ * ignored, but must still be a valid pointer. */
+ret_status_t retention_recurrent_step_positions(const ret_desc_t *desc, const void *q, const void *k,
+                                                const void *v, const void *g, void *o, float *state,
+                                                const int64_t *positions, hipStream_t stream);
+
 /* Backward of the parallel form: the gradients of sum(dout (.) out), with
  * out the output of retention_parallel_fwd on the same (desc, q, k, v, g),
  * with respect to q, k, v and (when g != NULL) g. All of q, k, v, g, dout,

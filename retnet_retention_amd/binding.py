@@ -36,6 +36,7 @@ EXPORTS = (
     "retention_chunkwise_fwd",
     "retention_chunkwise_fwd_timed",
     "retention_recurrent_step",
+    "retention_recurrent_step_positions",
     "retention_parallel_bwd_workspace_bytes",
     "retention_parallel_bwd",
     "retention_status_string",
@@ -93,6 +94,8 @@ def lib():
         h.retention_chunkwise_fwd_timed.restype = st
         h.retention_recurrent_step.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp]
         h.retention_recurrent_step.restype = st
+        h.retention_recurrent_step_positions.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp]
+        h.retention_recurrent_step_positions.restype = st
         h.retention_parallel_bwd_workspace_bytes.argtypes = [pd, i32]
         h.retention_parallel_bwd_workspace_bytes.restype = sz
         h.retention_parallel_bwd.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -236,9 +239,12 @@ def chunkwise_fwd(q, k, v, g=None, *, chunk=512, state_in=None, state_out=None, 
     return out
 
 
-def recurrent_step(q, k, v, state, g=None, *, gammas=None, rotary_base=0.0, pos=0, eps=1e-5, out=None):
+def recurrent_step(q, k, v, state, g=None, *, gammas=None, rotary_base=0.0, pos=0, eps=1e-5, out=None,
+                   positions=None):
     """One decode step (q, k: [batch, 1, heads, dk]); updates `state` in place
-    and returns the output [batch, 1, heads, dv]."""
+    and returns the output [batch, 1, heads, dv]. `positions` (optional, a GPU
+    int64 tensor [batch]): each sequence's rotation position, in place of
+    `pos`."""
     out = torch.empty_like(v) if out is None else out
     _validate(q, k, v, g, out)
     if q.shape[1] != 1:
@@ -247,7 +253,14 @@ def recurrent_step(q, k, v, state, g=None, *, gammas=None, rotary_base=0.0, pos=
     if state.dtype != torch.float32 or not state.is_contiguous() or tuple(state.shape) != (b, h, dk, v.shape[-1]):
         raise ValueError("state must be a contiguous fp32 [batch, heads, dk, dv] tensor")
     desc, keep = _desc_for(q, v, gammas, rotary_base, pos, eps)
-    _check(lib().retention_recurrent_step(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(out),
-                                          _ptr(state), _stream(q)))
+    if positions is None:
+        _check(lib().retention_recurrent_step(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(out),
+                                              _ptr(state), _stream(q)))
+    else:
+        if (positions.dtype != torch.int64 or not positions.is_cuda or not positions.is_contiguous()
+                or tuple(positions.shape) != (b,)):
+            raise ValueError("positions must be a contiguous GPU int64 tensor [batch]")
+        _check(lib().retention_recurrent_step_positions(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                                        _ptr(out), _ptr(state), _ptr(positions), _stream(q)))
     del keep
     return out

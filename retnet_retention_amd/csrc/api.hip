@@ -348,4 +348,21 @@ ret_status_t retention_recurrent_step(const ret_desc_t* desc, const void* q, con
   return RET_OK;
 }
 
+ret_status_t retention_recurrent_step_positions(const ret_desc_t* desc, const void* q, const void* k,
+                                                const void* v, const void* g, void* o, float* state,
+                                                const int64_t* positions, hipStream_t stream) {
+  ret_status_t st = check_desc(desc);
+  if (st != RET_OK) return st;
+  if (desc->seqlen != 1) return RET_ERR_SHAPE;
+  if ((st = check_tensors(desc, q, k, v, g, o)) != RET_OK) return st;
+  if ((st = check_eps(desc, g)) != RET_OK) return st;
+  if (!state || !positions) return RET_ERR_NULL;
+  if (!aligned16(state) || (reinterpret_cast<uintptr_t>(positions) & 7u) != 0) return RET_ERR_ALIGN;
+  const Shape s = make_shape(desc);
+  if (ret::launch_recurrent_step(s, q, k, v, g, o, state, desc->rotary_base, desc->pos_offset, desc->gn_eps,
+                                 stream, positions) != hipSuccess)
+    return RET_ERR_HIP;
+  return RET_OK;
+}
+
 }  // extern "C"

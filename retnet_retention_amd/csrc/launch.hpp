@@ -54,9 +54,10 @@ hipError_t launch_gate_norm_bwd(const Shape& s, const void* o, const void* g, co
                                 float eps, hipStream_t stream, void* dov_rev = nullptr);
 hipError_t launch_reverse_tokens(const Shape& s, const void* src, void* dst, hipStream_t stream);
 
-// One decode step, in place on `state`.
+// One decode step, in place on `state`. `positions` (device, [batch], may
+// be null): each sequence's rotation position instead of `pos`.
 hipError_t launch_recurrent_step(const Shape& s, const void* q, const void* k, const void* v, const void* g,
                                  void* o, float* state, double rotary_base, int64_t pos, float eps,
-                                 hipStream_t stream);
+                                 hipStream_t stream, const int64_t* positions = nullptr);
 
 }  // namespace ret

@@ -23,6 +23,7 @@ struct StepParams {
   int rotary;
   double base;
   int64_t pos;
+  const int64_t* positions;  // device [batch]: each sequence's own position, or null (all at pos)
   float eps;
   float gam[kMaxHeads];
 };
@@ -55,10 +56,11 @@ __global__ __launch_bounds__(256) void recurrent_step_kernel(StepParams p) {
   }
   __syncthreads();
   if (p.rotary) {
+    const int64_t pos = p.positions ? p.positions[bh / p.heads] : p.pos;
     for (int j = tid; j < D / 2; j += 256) {
       const double theta = pow(p.base, -2.0 * j / D);
       double s, c;
-      sincos((double)p.pos * theta, &s, &c);
+      sincos((double)pos * theta, &s, &c);
       const float cf = (float)c, sf = (float)s;
       const float q0 = sq[2 * j], q1 = sq[2 * j + 1], k0 = sk[2 * j], k1 = sk[2 * j + 1];
       sq[2 * j] = q0 * cf - q1 * sf;
@@ -145,8 +147,9 @@ static hipError_t launch_step_t(const Shape& s, const StepParams& p, hipStream_t
 
 hipError_t launch_recurrent_step(const Shape& s, const void* q, const void* k, const void* v, const void* g,
                                  void* o, float* state, double rotary_base, int64_t pos, float eps,
-                                 hipStream_t stream) {
+                                 hipStream_t stream, const int64_t* positions) {
   StepParams p;
+  p.positions = positions;
   p.q = q;
   p.k = k;
   p.v = v;

@@ -175,3 +175,16 @@ def test_backward_validates_before_any_device_call(L):
     # workspace too small
     assert bwd(ctypes.byref(d), p[0], p[1], p[2], None, p[4], p[5], p[6], p[7], None, p[9], ws_plain - 1,
                None) == 6
+
+
+def test_step_positions_validates(L):
+    d, _ = _desc(batch=3, seqlen=1, heads=2, dk=64, dv=64, rotary_base=10000.0)
+    step = L.retention_recurrent_step_positions
+    a = [ALIGNED * i for i in range(1, 8)]
+    # positions NULL
+    assert step(ctypes.byref(d), a[0], a[1], a[2], None, a[3], a[4], None, None) == 1
+    # positions not 8-byte aligned
+    assert step(ctypes.byref(d), a[0], a[1], a[2], None, a[3], a[4], a[5] + 4, None) == 5
+    # seqlen must be 1
+    d2, _ = _desc(batch=3, seqlen=2, heads=2, dk=64, dv=64)
+    assert step(ctypes.byref(d2), a[0], a[1], a[2], None, a[3], a[4], a[5], None) == 2

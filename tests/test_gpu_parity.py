@@ -213,3 +213,32 @@ def test_chunkwise_handoff_completes(b, h):
     ref, ref_s = oracle_run("chunkwise", q, k, v, g, chunk=chunk, state_in=s0)
     assert_close(to64(out), ref, "bf16", "out")
     assert_close(to64(s_out), ref_s, "bf16", "state")
+
+
+def test_step_with_per_sequence_positions():
+    """Continuous batching: five sequences decode one token each at their own
+    positions. Each row must equal the oracle step at its position, and be
+    bit-identical to the single-position call made at that position."""
+    _announce(case="step with per-sequence positions")
+    b, h, d = 5, 3, 128
+    positions = [0, 7, 100, 8191, 123456]
+    q, k, v, g, s0 = make_inputs(97, b, 1, h, d, "bf16", 1 / 16, 1.0, True)
+    base = 10000.0
+    state = torch.from_numpy(s0.astype(np.float32)).to(DEV)
+    pos_t = torch.tensor(positions, dtype=torch.int64, device=DEV)
+    out = rr.recurrent_step(q.torch(DEV), k.torch(DEV), v.torch(DEV), state, g.torch(DEV), rotary_base=base,
+                            positions=pos_t)
+    torch.cuda.synchronize()
+    gam = oracle.default_gammas(h)
+    for i, pos in enumerate(positions):
+        sl = slice(i, i + 1)
+        ref_o, ref_s = oracle.recurrent_step(q.f64[sl], k.f64[sl], v.f64[sl], s0[sl], gam, g=g.f64[sl],
+                                             rotary_base=base, pos=pos)
+        assert_close(to64(out[sl]), ref_o, "bf16", f"out, position {pos}")
+        assert_close(to64(state[sl]), ref_s, "bf16", f"state, position {pos}")
+        one_state = torch.from_numpy(s0[sl].astype(np.float32)).to(DEV)
+        one = rr.recurrent_step(q.torch(DEV)[sl].contiguous(), k.torch(DEV)[sl].contiguous(),
+                                v.torch(DEV)[sl].contiguous(), one_state, g.torch(DEV)[sl].contiguous(),
+                                rotary_base=base, pos=pos)
+        torch.cuda.synchronize()
+        assert torch.equal(one, out[sl]) and torch.equal(one_state, state[sl]), f"position {pos}"
