@@ -158,6 +158,19 @@ ret_status_t retention_parallel_bwd(const ret_desc_t *desc, const void *q, const
                                     const void *g, const void *dout, void *dq, void *dk, void *dv, void *dg,
                                     void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Backward of the chunkwise form (no carried state: state_in and state_out
+ * of the forward both NULL): the same gradients as retention_parallel_bwd,
+ * since the two forms compute one function ("Summary": the forms are
+ * equivalent), with each product run as the chunkwise form at `chunk`, so the
+ * cost grows linearly with the sequence. Arguments as retention_parallel_bwd,
+ * plus chunk >= 1. Workspace: at least
+ * retention_chunkwise_bwd_workspace_bytes(desc, chunk, g != NULL) bytes; its
+ * first bytes are the chunkwise call's control block. */
+size_t retention_chunkwise_bwd_workspace_bytes(const ret_desc_t *desc, int32_t chunk, int32_t has_gate);
+ret_status_t retention_chunkwise_bwd(const ret_desc_t *desc, int32_t chunk, const void *q, const void *k,
+                                     const void *v, const void *g, const void *dout, void *dq, void *dk, void *dv,
+                                     void *dg, void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char *retention_status_string(ret_status_t status);
 

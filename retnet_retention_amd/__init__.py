@@ -5,10 +5,12 @@ gfx950 behind a C ABI (include/retention.h), with a thin ctypes binding.
     chunkwise_fwd    chunkwise recurrent form (long sequences, prefill)
     recurrent_step   recurrent form, one decode step, state in place
     parallel_bwd     gradients of the parallel form (q, k, v and the gate)
+    chunkwise_bwd    the same gradients, each product run as the chunkwise form
 """
 
 from .binding import (  # noqa: F401
     RetentionError,
+    chunkwise_bwd,
     chunkwise_fwd,
     chunkwise_workspace_bytes,
     lib,

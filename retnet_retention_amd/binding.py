@@ -39,6 +39,8 @@ EXPORTS = (
     "retention_recurrent_step_positions",
     "retention_parallel_bwd_workspace_bytes",
     "retention_parallel_bwd",
+    "retention_chunkwise_bwd_workspace_bytes",
+    "retention_chunkwise_bwd",
     "retention_status_string",
     "retention_abi_version",
 )
@@ -100,6 +102,10 @@ def lib():
         h.retention_parallel_bwd_workspace_bytes.restype = sz
         h.retention_parallel_bwd.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         h.retention_parallel_bwd.restype = st
+        h.retention_chunkwise_bwd_workspace_bytes.argtypes = [pd, i32, i32]
+        h.retention_chunkwise_bwd_workspace_bytes.restype = sz
+        h.retention_chunkwise_bwd.argtypes = [pd, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        h.retention_chunkwise_bwd.restype = st
         h.retention_status_string.argtypes = [st]
         h.retention_status_string.restype = ctypes.c_char_p
         h.retention_abi_version.argtypes = []
@@ -198,6 +204,26 @@ def parallel_bwd(q, k, v, dout, g=None, *, gammas=None, rotary_base=0.0, pos_off
     ws_bytes = workspace.numel() * workspace.element_size()
     _check(L.retention_parallel_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(dout), _ptr(dq),
                                     _ptr(dk), _ptr(dv), _ptr(dg), _ptr(workspace), ws_bytes, _stream(q)))
+    del keep
+    return dq, dk, dv, dg
+
+
+def chunkwise_bwd(q, k, v, dout, g=None, *, chunk=512, gammas=None, rotary_base=0.0, pos_offset=0, eps=1e-5,
+                  workspace=None):
+    """Gradients of sum(dout * chunkwise_fwd(q, k, v, g, chunk=chunk, ...))
+    (no carried state) with respect to q, k, v and g; returns
+    (dq, dk, dv, dg), dg None without a gate."""
+    _validate(q, k, v, g, dout)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dg = torch.empty_like(g) if g is not None else None
+    desc, keep = _desc_for(q, v, gammas, rotary_base, pos_offset, eps)
+    L = lib()
+    need = L.retention_chunkwise_bwd_workspace_bytes(ctypes.byref(desc), int(chunk), int(g is not None))
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(L.retention_chunkwise_bwd(ctypes.byref(desc), int(chunk), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(dout),
+                                     _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(workspace), ws_bytes, _stream(q)))
     del keep
     return dq, dk, dv, dg
 

@@ -290,6 +290,124 @@ ret_status_t retention_parallel_bwd(const ret_desc_t* desc, const void* q, const
   return RET_OK;
 }
 
+namespace {
+
+// Backward of the chunkwise form: the chunkwise kernel's own workspace
+// (control block, state chain, per-chunk states), the angle table, then
+// tensor slots: q', k' (rotation) and their reversed copies; the recomputed
+// output, dO and its reversed copy (gate), else the reversed dO; the
+// reversed v; the three products' outputs.
+size_t cbwd_bytes(const ret_desc_t* d, int32_t chunk, bool gate) {
+  const int slots = (d->rotary_base == 0.0 ? 2 : 4) + (gate ? 3 : 1) + 1 + 3;
+  return ctrl_bytes(d, chunk) + chain_bytes(d) + snap_bytes(d, chunk) + bwd_table_bytes(d) +
+         slots * bwd_tensor_bytes(d);
+}
+
+}  // namespace
+
+size_t retention_chunkwise_bwd_workspace_bytes(const ret_desc_t* desc, int32_t chunk, int32_t has_gate) {
+  if (check_desc(desc) != RET_OK || chunk < 1) return 0;
+  return cbwd_bytes(desc, chunk, has_gate != 0);
+}
+
+ret_status_t retention_chunkwise_bwd(const ret_desc_t* desc, int32_t chunk, const void* q, const void* k,
+                                     const void* v, const void* g, const void* dout, void* dq, void* dk, void* dv,
+                                     void* dg, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  ret_status_t st = check_desc(desc);
+  if (st != RET_OK) return st;
+  if (chunk < 1) return RET_ERR_SHAPE;
+  if (!q || !k || !v || !dout || !dq || !dk || !dv) return RET_ERR_NULL;
+  if ((g == nullptr) != (dg == nullptr)) return RET_ERR_NULL;
+  const void* ins[] = {q, k, v, g, dout};
+  void* outs[] = {dq, dk, dv, dg};
+  for (const void* p : ins)
+    if (p && !aligned16(p)) return RET_ERR_ALIGN;
+  for (const void* p : outs)
+    if (p && !aligned16(p)) return RET_ERR_ALIGN;
+  const size_t n = (size_t)desc->batch * desc->seqlen * desc->heads * desc->dk * elem_size(desc->dtype);
+  for (int i = 0; i < 4; ++i) {
+    for (const void* p : ins)
+      if (overlaps(outs[i], n, p, n)) return RET_ERR_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(outs[i], n, outs[j], n)) return RET_ERR_ALIAS;
+  }
+  if ((st = check_eps(desc, g)) != RET_OK) return st;
+  const size_t need = cbwd_bytes(desc, chunk, g != nullptr);
+  if (!workspace || workspace_bytes < need) return RET_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return RET_ERR_ALIGN;
+  for (const void* p : ins)
+    if (overlaps(workspace, need, p, n)) return RET_ERR_ALIAS;
+  for (const void* p : outs)
+    if (overlaps(workspace, need, p, n)) return RET_ERR_ALIAS;
+
+  const Shape s = make_shape(desc);
+  const int32_t c = eff_chunk(desc, chunk);
+  char* ws = static_cast<char*>(workspace);
+  int* ctrl = reinterpret_cast<int*>(ws);
+  float* chain = reinterpret_cast<float*>(ws + ctrl_bytes(desc, chunk));
+  void* snap = ws + ctrl_bytes(desc, chunk) + chain_bytes(desc);
+  char* tab_at = ws + ctrl_bytes(desc, chunk) + chain_bytes(desc) + snap_bytes(desc, chunk);
+  const size_t tb = bwd_tensor_bytes(desc);
+  char* next = tab_at + bwd_table_bytes(desc);
+  auto slot = [&]() { char* p = next; next += tb; return p; };
+  auto product = [&](const void* a, const void* b, const void* cc, void* out) {
+    return ret::launch_retention_fwd(s, c, true, a, b, cc, nullptr, out, nullptr, nullptr, snap, chain, ctrl, nullptr,
+                                     desc->gn_eps, stream) == hipSuccess;
+  };
+  // q', k' and their reversed copies
+  const float2* table = nullptr;
+  const void *qr = q, *kr = k;
+  void* qrev = slot();
+  void* krev = slot();
+  if (desc->rotary_base != 0.0) {
+    float2* tab = reinterpret_cast<float2*>(tab_at);
+    void* qs = slot();
+    void* ks = slot();
+    if (ret::launch_rotary_table(tab, desc->seqlen, desc->dk, desc->rotary_base, desc->pos_offset, stream) !=
+            hipSuccess ||
+        ret::launch_rotate_keys(q, qs, tab, desc->batch, desc->seqlen, desc->heads, desc->dk, desc->dtype, stream,
+                                qrev) != hipSuccess ||
+        ret::launch_rotate_keys(k, ks, tab, desc->batch, desc->seqlen, desc->heads, desc->dk, desc->dtype, stream,
+                                krev) != hipSuccess)
+      return RET_ERR_HIP;
+    table = tab;
+    qr = qs;
+    kr = ks;
+  } else if (ret::launch_reverse_tokens(s, q, qrev, stream) != hipSuccess ||
+             ret::launch_reverse_tokens(s, k, krev, stream) != hipSuccess) {
+    return RET_ERR_HIP;
+  }
+  // dO and its reversed copy
+  const void* dov = dout;
+  void* dorev = nullptr;
+  if (g) {
+    void* o_raw = slot();
+    void* ds = slot();
+    dorev = slot();
+    if (!product(qr, kr, v, o_raw) ||
+        ret::launch_gate_norm_bwd(s, o_raw, g, dout, ds, dg, desc->gn_eps, stream, dorev) != hipSuccess)
+      return RET_ERR_HIP;
+    dov = ds;
+  } else {
+    dorev = slot();
+    if (ret::launch_reverse_tokens(s, dout, dorev, stream) != hipSuccess) return RET_ERR_HIP;
+  }
+  void* vrev = slot();
+  void* dqr = slot();
+  void* dkf = slot();
+  void* dvf = slot();
+  // the three products of the parallel form's backward, each run as the
+  // chunkwise form (the same function): dQ' = P(dO, V, K'),
+  // dK' = rev P(rev V, rev dO, rev Q'), dV = rev P(rev K', rev Q', rev dO)
+  if (ret::launch_reverse_tokens(s, v, vrev, stream) != hipSuccess || !product(dov, v, kr, dqr) ||
+      !product(vrev, dorev, qrev, dkf) || !product(krev, qrev, dorev, dvf) ||
+      ret::launch_finish_grad(s, dqr, dq, table, false, stream) != hipSuccess ||
+      ret::launch_finish_grad(s, dkf, dk, table, true, stream) != hipSuccess ||
+      ret::launch_finish_grad(s, dvf, dv, nullptr, true, stream) != hipSuccess)
+    return RET_ERR_HIP;
+  return RET_OK;
+}
+
 size_t retention_chunkwise_workspace_bytes(const ret_desc_t* desc, int32_t chunk) {
   if (check_desc(desc) != RET_OK || chunk < 1) return 0;
   return ctrl_bytes(desc, chunk) + rot_bytes(desc) + chain_bytes(desc) + snap_bytes(desc, chunk);

@@ -53,6 +53,11 @@ hipError_t launch_retention_fwd(const Shape& s, int chunk, bool chunked, const v
 hipError_t launch_gate_norm_bwd(const Shape& s, const void* o, const void* g, const void* dout, void* dov, void* dg,
                                 float eps, hipStream_t stream, void* dov_rev = nullptr);
 hipError_t launch_reverse_tokens(const Shape& s, const void* src, void* dst, hipStream_t stream);
+// dst = rotation gradient of src (each pair turned back by the table's angle
+// of its position; null table: a copy), reading src in reversed token order
+// when `reverse`.
+hipError_t launch_finish_grad(const Shape& s, const void* src, void* dst, const float2* table, bool reverse,
+                              hipStream_t stream);
 
 // One decode step, in place on `state`. `positions` (device, [batch], may
 // be null): each sequence's rotation position instead of `pos`.

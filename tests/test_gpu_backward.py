@@ -79,3 +79,50 @@ def test_3b_backward_full_size():
                     gate_scale=w.gate_scale)
     for name, x, r in zip(("dq", "dk", "dv", "dg"), got, ref):
         assert_close(x, r, "bf16", name)
+
+
+def _run_chunk(seed, b, n, h, d, chunk, dtype, scale, gate, rot):
+    specs = [((b, n, h, d), scale)] * 3 + [((b, n, h, d), 1 / 8)]
+    if gate:
+        specs.append(((b, n, h, d), 1 / 16))
+    ts = draw(seed, specs, dtype)
+    q, k, v, dout = ts[:4]
+    g = ts[4] if gate else None
+    base = 10000.0 if rot else 0.0
+    args = (q.torch(DEV), k.torch(DEV), v.torch(DEV), dout.torch(DEV), g.torch(DEV) if gate else None)
+    got = rr.chunkwise_bwd(*args, chunk=chunk, rotary_base=base, pos_offset=11)
+    par = rr.parallel_bwd(*args, rotary_base=base, pos_offset=11)
+    ref = oracle.parallel_grad(q.f64, k.f64, v.f64, dout.f64, g=g.f64 if gate else None, rotary_base=base,
+                               pos_offset=11)
+    return [None if x is None else to64(x) for x in got], [None if x is None else to64(x) for x in par], ref
+
+
+CHUNK_CASES = [
+    # (batch, seqlen, heads, d, chunk, gate, rotary)
+    (1, 1, 1, 64, 64, True, False),
+    (2, 300, 2, 256, 64, True, True),
+    (1, 700, 2, 128, 512, False, True),
+    (2, 130, 4, 64, 7, True, False),
+    (1, 8192, 2, 256, 512, True, False),
+]
+
+
+@pytest.mark.parametrize("b,n,h,d,chunk,gate,rot", CHUNK_CASES)
+def test_bf16_chunkwise_backward(b, n, h, d, chunk, gate, rot):
+    """The chunkwise backward against the fp64 gradients of the (same)
+    function, and against the parallel backward on the GPU."""
+    _announce(form="chunkwise backward", b=b, n=n, h=h, d=d, chunk=chunk, gate=gate, rot=rot)
+    got, par, ref = _run_chunk(81 + n + chunk, b, n, h, d, chunk, "bf16", 1 / 16, gate, rot)
+    for name, x, p, r in zip(("dq", "dk", "dv", "dg"), got, par, ref):
+        if r is None:
+            assert x is None
+            continue
+        assert_close(x, r, "bf16", name)
+        assert_close(x, p, "bf16", name + " vs parallel backward")
+
+
+def test_f32_chunkwise_backward():
+    _announce(form="chunkwise backward", dtype="f32")
+    got, _, ref = _run_chunk(91, 1, 200, 2, 128, 64, "f32", 128 ** -0.5, True, True)
+    for name, x, r in zip(("dq", "dk", "dv", "dg"), got, ref):
+        assert_close(x, r, "f32", name)
