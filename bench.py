@@ -264,6 +264,35 @@ def bench_parallel_bwd(steps, warmup):
     return {"workload": w, "ms": ms, "flops": flops, "tflops": flops / (ms * 1e-3) / 1e12}
 
 
+def bench_chunkwise_bwd(steps, warmup):
+    """Backward of the chunkwise form on the 7B long-context workload (gate,
+    no rotation, no carried state): dq, dk, dv, dg from a seeded dout."""
+    import ctypes
+
+    import torch
+
+    import retnet_retention_amd as rr
+    import retnet_retention_amd.binding as B
+    from synth import get
+
+    w = get("retention_7b_8k")
+    q, k, v, g = (t.torch("cuda:0") for t in w.inputs())
+    gen = torch.Generator(device="cuda:0")
+    gen.manual_seed(w.seed + 7)
+    dout = (torch.randn(v.shape, generator=gen, device="cuda:0") / 8).to(v.dtype)
+    desc, keep = B._desc_for(q, v, None, 0.0, 0, 1e-5)
+    need = B.lib().retention_chunkwise_bwd_workspace_bytes(ctypes.byref(desc), w.chunk, 1)
+    del keep
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda:0")
+
+    def step():
+        rr.chunkwise_bwd(q, k, v, dout, g, chunk=w.chunk, workspace=ws)
+
+    ms, _ = time_calls(step, steps, warmup)
+    flops = 3 * chunkwise_flops(w.batch, w.seqlen, w.heads, w.dk, w.dv, w.chunk)
+    return {"workload": w, "ms": ms, "flops": flops, "tflops": flops / (ms * 1e-3) / 1e12}
+
+
 def _bwd_workspace_bytes(q, v, rotary_base):
     import ctypes
 
@@ -455,6 +484,7 @@ STATS_ARGS = {
     "decode": ["--only", "decode", "--decode-batches", "64", "--no-decode-graph"],
     "parallel": ["--only", "parallel"],
     "parallel_bwd": ["--only", "parallel_bwd"],
+    "chunkwise_bwd": ["--only", "chunkwise_bwd"],
 }
 SQ_COUNTERS = ["SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "SQ_INSTS_LDS",
                "SQ_LDS_BANK_CONFLICT", "SQ_WAIT_INST_LDS", "SQ_INSTS_VALU", "GRBM_GUI_ACTIVE"]
@@ -519,7 +549,7 @@ def profile_stats(out, raw):
         line = [ln for ln in open(d + ".log") if ln.startswith("{")]
         stats = list(csv.DictReader(open(glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)[0])))
         name = {"chunkwise": "chunkwise_7b_8k", "decode": "decode_step_7b_b64", "parallel": "parallel_3b",
-                "parallel_bwd": "parallel_backward_3b"}[leg]
+                "parallel_bwd": "parallel_backward_3b", "chunkwise_bwd": "chunkwise_backward_7b_8k"}[leg]
         with open(os.path.join(out, f"{name}_kernel_stats.txt"), "w") as f:
             f.write(f"rocprofv3 kernel statistics, {leg} leg of the benchmark\n")
             f.write("made by: python bench.py --profile stats --profile-out <out>\n")
@@ -716,7 +746,8 @@ def main():
     # the GPU's clocks take tens of milliseconds of load to settle: 5 warm-up
     # calls time the chunkwise call 14% slower than 200 do
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--only", choices=["chunkwise", "decode", "parallel", "parallel_bwd", "sweep"], default=None)
+    ap.add_argument("--only", choices=["chunkwise", "decode", "parallel", "parallel_bwd", "chunkwise_bwd", "sweep"],
+                    default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-chunkwise", action="store_true",
                     help="skip the chunkwise timings of the 200M and 3B workloads")
@@ -835,6 +866,15 @@ def main():
             "mfma_frac": round(pb["tflops"] / PEAK_BF16_TFLOPS, 4),
             "flops": "3 x the forward's algorithmic count (dQ, dK, dV products); the recomputed forward "
                      "for the GroupNorm gradient is not counted"}
+    if args.only in (None, "chunkwise_bwd"):
+        cb2 = bench_chunkwise_bwd(max(args.steps // 5, 3), max(args.warmup // 10, 3))
+        print(f"chunkwise backward {cb2['workload'].name}: {cb2['ms']:.3f} ms, {cb2['tflops']:.1f} TFLOP/s",
+              file=sys.stderr, flush=True)
+        line["chunkwise_backward"] = {
+            "workload": f"{cb2['workload'].name}: batch 2, 8192 tokens, 16 x 256, chunk 512, gate; dq, dk, dv, dg",
+            "ms": round(cb2["ms"], 4), "tflops": round(cb2["tflops"], 2),
+            "mfma_frac": round(cb2["tflops"] / PEAK_BF16_TFLOPS, 4),
+            "flops": "3 x the chunkwise form's algorithmic count; the recomputed forward is not counted"}
     if args.sweep or args.only == "sweep":
         line["sweep"] = bench_sweep()
     if args.copy_probe:
