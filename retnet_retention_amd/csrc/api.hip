@@ -293,14 +293,10 @@ ret_status_t retention_parallel_bwd(const ret_desc_t* desc, const void* q, const
 namespace {
 
 // Backward of the chunkwise form: the chunkwise kernel's own workspace
-// (control block, state chain, per-chunk states), the angle table, then
-// tensor slots: q', k' (rotation) and their reversed copies; the recomputed
-// output, dO and its reversed copy (gate), else the reversed dO; the
-// reversed v; the three products' outputs.
+// (control block, state chain, per-chunk states), then the parallel
+// backward's table and tensor slots.
 size_t cbwd_bytes(const ret_desc_t* d, int32_t chunk, bool gate) {
-  const int slots = (d->rotary_base == 0.0 ? 2 : 4) + (gate ? 3 : 1) + 1 + 3;
-  return ctrl_bytes(d, chunk) + chain_bytes(d) + snap_bytes(d, chunk) + bwd_table_bytes(d) +
-         slots * bwd_tensor_bytes(d);
+  return ctrl_bytes(d, chunk) + chain_bytes(d) + snap_bytes(d, chunk) + bwd_bytes(d, gate);
 }
 
 }  // namespace
@@ -350,32 +346,34 @@ ret_status_t retention_chunkwise_bwd(const ret_desc_t* desc, int32_t chunk, cons
   const size_t tb = bwd_tensor_bytes(desc);
   char* next = tab_at + bwd_table_bytes(desc);
   auto slot = [&]() { char* p = next; next += tb; return p; };
-  auto product = [&](const void* a, const void* b, const void* cc, void* out) {
+  // one chunkwise product; q_rev, out_rev, out_rot as in the parallel backward
+  auto product = [&](const void* a, const void* b, const void* cc, void* out, bool q_rev, bool out_rev,
+                     const float2* out_rot) {
     return ret::launch_retention_fwd(s, c, true, a, b, cc, nullptr, out, nullptr, nullptr, snap, chain, ctrl, nullptr,
-                                     desc->gn_eps, stream) == hipSuccess;
+                                     desc->gn_eps, stream, nullptr, nullptr, q_rev, out_rev, out_rot) == hipSuccess;
   };
-  // q', k' and their reversed copies
+  // q', k' and the reversed q'
   const float2* table = nullptr;
   const void *qr = q, *kr = k;
-  void* qrev = slot();
-  void* krev = slot();
+  void* qrev = nullptr;
   if (desc->rotary_base != 0.0) {
     float2* tab = reinterpret_cast<float2*>(tab_at);
     void* qs = slot();
     void* ks = slot();
+    qrev = slot();
     if (ret::launch_rotary_table(tab, desc->seqlen, desc->dk, desc->rotary_base, desc->pos_offset, stream) !=
             hipSuccess ||
         ret::launch_rotate_keys(q, qs, tab, desc->batch, desc->seqlen, desc->heads, desc->dk, desc->dtype, stream,
                                 qrev) != hipSuccess ||
-        ret::launch_rotate_keys(k, ks, tab, desc->batch, desc->seqlen, desc->heads, desc->dk, desc->dtype, stream,
-                                krev) != hipSuccess)
+        ret::launch_rotate_keys(k, ks, tab, desc->batch, desc->seqlen, desc->heads, desc->dk, desc->dtype,
+                                stream) != hipSuccess)
       return RET_ERR_HIP;
     table = tab;
     qr = qs;
     kr = ks;
-  } else if (ret::launch_reverse_tokens(s, q, qrev, stream) != hipSuccess ||
-             ret::launch_reverse_tokens(s, k, krev, stream) != hipSuccess) {
-    return RET_ERR_HIP;
+  } else {
+    qrev = slot();
+    if (ret::launch_reverse_tokens(s, q, qrev, stream) != hipSuccess) return RET_ERR_HIP;
   }
   // dO and its reversed copy
   const void* dov = dout;
@@ -384,7 +382,7 @@ ret_status_t retention_chunkwise_bwd(const ret_desc_t* desc, int32_t chunk, cons
     void* o_raw = slot();
     void* ds = slot();
     dorev = slot();
-    if (!product(qr, kr, v, o_raw) ||
+    if (!product(qr, kr, v, o_raw, false, false, nullptr) ||
         ret::launch_gate_norm_bwd(s, o_raw, g, dout, ds, dg, desc->gn_eps, stream, dorev) != hipSuccess)
       return RET_ERR_HIP;
     dov = ds;
@@ -392,18 +390,10 @@ ret_status_t retention_chunkwise_bwd(const ret_desc_t* desc, int32_t chunk, cons
     dorev = slot();
     if (ret::launch_reverse_tokens(s, dout, dorev, stream) != hipSuccess) return RET_ERR_HIP;
   }
-  void* vrev = slot();
-  void* dqr = slot();
-  void* dkf = slot();
-  void* dvf = slot();
-  // the three products of the parallel form's backward, each run as the
-  // chunkwise form (the same function): dQ' = P(dO, V, K'),
-  // dK' = rev P(rev V, rev dO, rev Q'), dV = rev P(rev K', rev Q', rev dO)
-  if (ret::launch_reverse_tokens(s, v, vrev, stream) != hipSuccess || !product(dov, v, kr, dqr) ||
-      !product(vrev, dorev, qrev, dkf) || !product(krev, qrev, dorev, dvf) ||
-      ret::launch_finish_grad(s, dqr, dq, table, false, stream) != hipSuccess ||
-      ret::launch_finish_grad(s, dkf, dk, table, true, stream) != hipSuccess ||
-      ret::launch_finish_grad(s, dvf, dv, nullptr, true, stream) != hipSuccess)
+  // the parallel backward's three products, each run as the chunkwise form
+  // (the same function), storing straight into the caller's tensors
+  if (!product(dov, v, kr, dq, false, false, table) || !product(v, dorev, qrev, dk, true, true, table) ||
+      !product(kr, qrev, dorev, dv, true, true, nullptr))
     return RET_ERR_HIP;
   return RET_OK;
 }

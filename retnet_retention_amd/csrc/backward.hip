@@ -9,9 +9,8 @@
 //     reversed (the products with the transposed decay mask run on reversed
 //     sequences, where that mask is causal again), for inputs that no other
 //     pass already writes reversed.
-//   * finish_grad_kernel: the rotation's gradient (each pair turned back by
-//     its angle) and the reversal of a product's output, for the chunkwise
-//     products; the parallel kernel does both in its own stores.
+// The rotation's gradient (each pair turned back by its angle) and the
+// reversal of the products' outputs happen in the retention kernels' stores.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -82,29 +81,6 @@ __global__ __launch_bounds__(256) void reverse_tokens_kernel(const uint4* __rest
   dst[(b * seqlen + (seqlen - 1 - n)) * per_tok + c] = src[i];
 }
 
-// dst[b][n][h] = rot(src[b][n'][h], -angle of n) with n' = n, or seqlen-1-n
-// when `reverse`; no table: a plain (reversing) copy. 8 elements per thread.
-// (The chunkwise kernel stores its rows as computed; the parallel kernel
-// does this in its own stores.)
-template <typename T>
-__global__ __launch_bounds__(256) void finish_grad_kernel(const T* __restrict__ src, T* __restrict__ dst,
-                                                          const float2* __restrict__ table, int64_t chunks,
-                                                          int seqlen, int heads, int d, int reverse) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;  // one 8-element chunk of dst
-  if (idx >= chunks) return;
-  const int cpr = d / 8;
-  const int64_t vec = idx / cpr;  // (b, n, h) row of dst
-  const int c8 = (int)(idx % cpr);
-  const int h = (int)(vec % heads);
-  const int64_t tok = vec / heads;  // b * seqlen + n
-  const int n = (int)(tok % seqlen);
-  const int64_t b = tok / seqlen;
-  const int ns = reverse ? seqlen - 1 - n : n;
-  F8 x = unpack8(ld_raw8(src + ((b * seqlen + ns) * heads + h) * d + c8 * 8));
-  if (table) unrotate_pairs<8>(x.x, table + (int64_t)n * (d / 2) + c8 * 4);
-  store8(dst + idx * 8, x);
-}
-
 hipError_t launch_gate_norm_bwd(const Shape& s, const void* o, const void* g, const void* dout, void* dov, void* dg,
                                 float eps, hipStream_t stream, void* dov_rev) {
   const int64_t rows = (int64_t)s.batch * s.seqlen * s.heads;
@@ -137,19 +113,6 @@ hipError_t launch_reverse_tokens(const Shape& s, const void* src, void* dst, hip
   const unsigned blocks = (unsigned)((vecs + 255) / 256);
   hipLaunchKernelGGL(reverse_tokens_kernel, dim3(blocks), dim3(256), 0, stream, (const uint4*)src, (uint4*)dst, vecs,
                      per_tok, s.seqlen);
-  return hipGetLastError();
-}
-
-hipError_t launch_finish_grad(const Shape& s, const void* src, void* dst, const float2* table, bool reverse,
-                              hipStream_t stream) {
-  const int64_t chunks = (int64_t)s.batch * s.seqlen * s.heads * (s.d / 8);
-  const unsigned blocks = (unsigned)((chunks + 255) / 256);
-  if (s.dtype == 1)
-    hipLaunchKernelGGL(finish_grad_kernel<bf16>, dim3(blocks), dim3(256), 0, stream, (const bf16*)src, (bf16*)dst,
-                       table, chunks, s.seqlen, s.heads, s.d, reverse ? 1 : 0);
-  else
-    hipLaunchKernelGGL(finish_grad_kernel<float>, dim3(blocks), dim3(256), 0, stream, (const float*)src,
-                       (float*)dst, table, chunks, s.seqlen, s.heads, s.d, reverse ? 1 : 0);
   return hipGetLastError();
 }
 

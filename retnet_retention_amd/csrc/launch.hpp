@@ -34,10 +34,11 @@ hipError_t launch_rotate_keys(const void* k, void* kr, const float2* table, int 
 // chunkwise_ctrl_bytes() ints, all device memory owned by the caller.
 size_t chunkwise_ctrl_bytes(int batch, int heads, int nchunks);
 // `rot` (may be null): the cos/sin table of launch_rotary_table, with which
-// the kernels turn q as they load it (k must then arrive rotated). Parallel
-// form only: `q_rev` reads q with each sequence's token order reversed (not
-// with `rot`), `out_rev` stores the output reversed, `out_rot` (may be null)
-// turns each stored output row back by its stored position's angles.
+// the kernels turn q as they load it (k must then arrive rotated). For the
+// backward's products (chunkwise: without carried state): `q_rev` reads q
+// with each sequence's token order reversed (not with `rot`), `out_rev`
+// stores the output reversed, `out_rot` (may be null) turns each stored
+// output row back by its stored position's angles.
 // `before`/`after` (may be null) are recorded around the main kernel.
 hipError_t launch_retention_fwd(const Shape& s, int chunk, bool chunked, const void* q, const void* k, const void* v,
                                 const void* g, void* o, const float* state_in, float* state_out, void* snap,
@@ -53,11 +54,6 @@ hipError_t launch_retention_fwd(const Shape& s, int chunk, bool chunked, const v
 hipError_t launch_gate_norm_bwd(const Shape& s, const void* o, const void* g, const void* dout, void* dov, void* dg,
                                 float eps, hipStream_t stream, void* dov_rev = nullptr);
 hipError_t launch_reverse_tokens(const Shape& s, const void* src, void* dst, hipStream_t stream);
-// dst = rotation gradient of src (each pair turned back by the table's angle
-// of its position; null table: a copy), reading src in reversed token order
-// when `reverse`.
-hipError_t launch_finish_grad(const Shape& s, const void* src, void* dst, const float2* table, bool reverse,
-                              hipStream_t stream);
 
 // One decode step, in place on `state`. `positions` (device, [batch], may
 // be null): each sequence's rotation position instead of `pos`.

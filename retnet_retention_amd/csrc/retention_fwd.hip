@@ -223,10 +223,11 @@ __device__ __forceinline__ u32x2 load2_coherent(__amdgpu_buffer_rsrc_t rs, uint3
 // ---------------------------------------------------------------------------
 // CROSS: the chunk has a previous state R_{i-1} (chunkwise form, chunk > 0
 // or an initial state); the parallel form and chunk 0 without one have none.
-// PAR: the parallel kernel's instantiation, the only one that reads q
-// reversed or stores its output reversed or turned back (the backward's
-// products); the chunkwise kernel's instantiations carry none of that code.
-template <typename T, int D, bool FAST, bool CROSS, bool PAR = false>
+// XF: the instantiations that may read q reversed and store their output
+// reversed and/or turned back (the backward's products: the parallel kernel,
+// and a second chunkwise instantiation launched only for them); the forward
+// chunkwise kernel carries none of that code.
+template <typename T, int D, bool FAST, bool CROSS, bool XF = false>
 __device__ __forceinline__ void out_role(const FwdParams& p, int bh, int ci, int qb, bool chunked, char* l0, char* l1,
                                          char* l2, char* l3) {
   using C = OutTile<T, D, FAST>;
@@ -295,7 +296,7 @@ __device__ __forceinline__ void out_role(const FwdParams& p, int bh, int ci, int
 #pragma unroll
   for (int r = 0; r < QT; ++r) {
     const int qrow = min(qw0 + 32 * r + n, cend - 1);
-    const T* qr = Q + (int64_t)(PAR && p.q_rev ? p.seqlen - 1 - qrow : qrow) * tstride + 8 * hh;
+    const T* qr = Q + (int64_t)(XF && p.q_rev ? p.seqlen - 1 - qrow : qrow) * tstride + 8 * hh;
     if (p.rot) {
       const float2* cs = p.rot + (int64_t)qrow * (D / 2) + 4 * hh;
 #pragma unroll
@@ -568,7 +569,7 @@ __device__ __forceinline__ void out_role(const FwdParams& p, int bh, int ci, int
         }
         if (orow < cend) {
           int mrow = orow;  // stored position
-          if constexpr (PAR) {
+          if constexpr (XF) {
             if (p.out_rev) mrow = p.seqlen - 1 - orow;
             if (p.out_rot) unrotate_pairs<CPL>(y, p.out_rot + (int64_t)mrow * (D / 2) + (H * SG::HALF + lcol) / 2);
           }
@@ -886,7 +887,7 @@ __global__ __launch_bounds__(kWaves<T> * 64, 1) void retention_parallel_kernel(F
 #endif
 }
 
-template <typename T, int D, bool FAST>
+template <typename T, int D, bool FAST, bool XF = false>
 __global__ __launch_bounds__(kWaves<T> * 64, 1) void retention_chunkwise_kernel(FwdParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the kernel's signature
   __shared__ __attribute__((aligned(1024))) char l0[Stage<T, D>::BYTES];
@@ -933,9 +934,9 @@ __global__ __launch_bounds__(kWaves<T> * 64, 1) void retention_chunkwise_kernel(
   if (qb < 0)
     state_role<T, D>(p, bh, ci, role - 1, l0, l1, l2, l3);
   else if (ci > 0 || p.has_state0)
-    out_role<T, D, FAST, true>(p, bh, ci, qb, true, l0, l1, l2, l3);
+    out_role<T, D, FAST, true, XF>(p, bh, ci, qb, true, l0, l1, l2, l3);
   else
-    out_role<T, D, FAST, false>(p, bh, ci, qb, true, l0, l1, l2, l3);
+    out_role<T, D, FAST, false, XF>(p, bh, ci, qb, true, l0, l1, l2, l3);
 #endif
 }
 
@@ -965,7 +966,12 @@ static hipError_t launch_fwd_impl(const Shape& s, int chunk, FwdParams p, bool c
   const int64_t blocks = (int64_t)p.nchunks * bhs * (StTile<T, D>::SPLIT + p.qblocks);
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   if (before && hipEventRecord(before, stream) != hipSuccess) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((retention_chunkwise_kernel<T, D, FAST>), dim3((unsigned)blocks), dim3(64 * C::WAVES), 0, stream, p);
+  if (p.q_rev || p.out_rev || p.out_rot)
+    hipLaunchKernelGGL((retention_chunkwise_kernel<T, D, FAST, true>), dim3((unsigned)blocks), dim3(64 * C::WAVES), 0,
+                       stream, p);
+  else
+    hipLaunchKernelGGL((retention_chunkwise_kernel<T, D, FAST>), dim3((unsigned)blocks), dim3(64 * C::WAVES), 0,
+                       stream, p);
   const hipError_t e = hipGetLastError();
   if (e == hipSuccess && after && hipEventRecord(after, stream) != hipSuccess) return hipErrorInvalidValue;
   return e;
@@ -993,8 +999,8 @@ hipError_t launch_retention_fwd(const Shape& s, int chunk, bool chunked, const v
                                 float* chain, int* ctrl, const float2* rot, float eps, hipStream_t stream,
                                 hipEvent_t before, hipEvent_t after, bool q_rev, bool out_rev,
                                 const float2* out_rot) {
-  if (chunked && (q_rev || out_rev || out_rot)) return hipErrorInvalidValue;
   if (rot && q_rev) return hipErrorInvalidValue;  // q's angles are those of its own positions
+  if (chunked && (q_rev || out_rev || out_rot) && (state_in || state_out)) return hipErrorInvalidValue;
   FwdParams p;
   p.rot = rot;
   p.q_rev = q_rev;
