@@ -14,5 +14,6 @@ from .retention_oracle import (  # noqa: F401
     recurrent_step,
     retention,
     rotate,
+    score_map,
 )
 from .retention_grad import parallel_grad, unrotate  # noqa: F401

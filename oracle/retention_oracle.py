@@ -53,6 +53,7 @@ __all__ = [
     "recurrent_step",
     "group_norm_swish",
     "retention",
+    "score_map",
 ]
 
 
@@ -219,3 +220,25 @@ def retention(form, q, k, v, g=None, gammas=None, rotary_base=0.0, pos_offset=0,
     if g is not None:
         out = group_norm_swish(out, g, eps)
     return out, state
+
+
+def score_map(q, k, gammas=None, rotary_base=0.0, pos_offset=0, query=-1):
+    """Retention weights of one query token over the tokens before it, summed
+    over heads, the "Visualization of the retention mechanism" section of the
+    SpiralAI model card page: the inner products of queries and keys, taken in
+    absolute value and added up over all heads. Reading taken: the weights are
+    those of the parallel form (Q K^T (.) D), so each carries its head's decay
+    g^(n-m); for query token n (default: the last) and key token m <= n,
+        w[b, m] = sum_h g_h^(n-m) |q'_{b,n,h} . k'_{b,m,h}|
+    with q', k' rotated by position; w[b, m] = 0 for m > n. Returns [B, N]."""
+    bsz, n_tok, heads, _ = q.shape
+    gam = default_gammas(heads) if gammas is None else np.asarray(gammas, dtype=np.float64)
+    n = n_tok - 1 if query < 0 else int(query)
+    qr = rotate(q, rotary_base, pos_offset)
+    kr = rotate(k, rotary_base, pos_offset)
+    out = np.zeros((bsz, n_tok))
+    for b in range(bsz):
+        for m in range(n + 1):
+            for h in range(heads):
+                out[b, m] += float(gam[h]) ** (n - m) * abs(float(np.dot(qr[b, n, h], kr[b, m, h])))
+    return out

@@ -289,3 +289,30 @@ def test_causality():
         b, _ = oracle.retention(form, q2, k2, v2, g=g, rotary_base=10000.0, chunk=8)
         assert np.array_equal(a[:, :t], b[:, :t]), form
         assert not np.allclose(a[:, t], b[:, t]), form
+
+
+def test_score_map_pins():
+    """The score map against the parallel form's weight matrix built
+    independently (scores times the decay mask), and its closed form for
+    identical tokens: w[m] = sum_h g_h^(n-m) |q.k|."""
+    rng = np.random.default_rng(21)
+    b, n, h, d = 2, 9, 3, 4
+    q, k = rng.standard_normal((b, n, h, d)), rng.standard_normal((b, n, h, d))
+    gam = oracle.default_gammas(h)
+    w = oracle.score_map(q, k, rotary_base=100.0, pos_offset=4, query=6)
+    qr, kr = oracle.rotate(q, 100.0, 4), oracle.rotate(k, 100.0, 4)
+    pos = np.arange(n)
+    want = np.zeros((b, n))
+    for hh in range(h):
+        decay = np.where(pos[:, None] >= pos[None, :], gam[hh] ** np.maximum(pos[:, None] - pos[None, :], 0), 0.0)
+        a = np.einsum("bnd,bmd->bnm", qr[:, :, hh], kr[:, :, hh]) * decay[None]
+        want += np.abs(a[:, 6, :])
+    assert np.allclose(w, want, rtol=1e-13, atol=1e-14)
+    assert np.all(w[:, 7:] == 0.0)
+    # identical tokens, no rotation: every weight is |q.k| times the decay
+    q1 = np.broadcast_to(rng.standard_normal((1, 1, h, d)), (1, n, h, d)).copy()
+    k1 = np.broadcast_to(rng.standard_normal((1, 1, h, d)), (1, n, h, d)).copy()
+    w1 = oracle.score_map(q1, k1)
+    dots = np.abs(np.einsum("hd,hd->h", q1[0, 0], k1[0, 0]))
+    for m in range(n):
+        assert np.isclose(w1[0, m], np.sum(gam ** (n - 1 - m) * dots), rtol=1e-14)
