@@ -293,6 +293,22 @@ def bench_chunkwise_bwd(steps, warmup):
     return {"workload": w, "ms": ms, "flops": flops, "tflops": flops / (ms * 1e-3) / 1e12}
 
 
+def bench_score_map(steps, warmup):
+    """Score map of the last token on the 3B workload's q, k (rotation): a
+    stream over k. Bytes: k once plus the query rows and the fp32 map."""
+    import torch
+
+    import retnet_retention_amd as rr
+    from synth import get
+
+    w = get("retention_3b")
+    q, k, _, _ = (t.torch("cuda:0") for t in w.inputs())
+    ws = torch.empty(w.seqlen * w.dk // 2 * 8 + 256, dtype=torch.uint8, device="cuda:0")
+    ms, _ = time_calls(lambda: rr.score_map(q, k, rotary_base=w.rotary_base, workspace=ws), steps, warmup)
+    nbytes = k.numel() * k.element_size() + w.batch * w.seqlen * 4
+    return {"workload": w, "us": ms * 1e3, "gbps": nbytes / (ms * 1e-3) / 1e9}
+
+
 def _bwd_workspace_bytes(q, v, rotary_base):
     import ctypes
 
@@ -746,7 +762,8 @@ def main():
     # the GPU's clocks take tens of milliseconds of load to settle: 5 warm-up
     # calls time the chunkwise call 14% slower than 200 do
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--only", choices=["chunkwise", "decode", "parallel", "parallel_bwd", "chunkwise_bwd", "sweep"],
+    ap.add_argument("--only", choices=["chunkwise", "decode", "parallel", "parallel_bwd", "chunkwise_bwd", "score_map",
+                                       "sweep"],
                     default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-chunkwise", action="store_true",
@@ -875,6 +892,14 @@ def main():
             "ms": round(cb2["ms"], 4), "tflops": round(cb2["tflops"], 2),
             "mfma_frac": round(cb2["tflops"] / PEAK_BF16_TFLOPS, 4),
             "flops": "3 x the chunkwise form's algorithmic count; the recomputed forward is not counted"}
+    if args.only in (None, "score_map"):
+        sm = bench_score_map(max(args.steps, 10), max(args.warmup // 4, 10))
+        print(f"score map {sm['workload'].name}: {sm['us']:.1f} us, {sm['gbps']:.0f} GB/s", file=sys.stderr,
+              flush=True)
+        line["score_map"] = {"workload": f"{sm['workload'].name}: last token over 2048, 10 heads x 256, rotation",
+                             "us": round(sm["us"], 2), "gbps": round(sm["gbps"], 1),
+                             "hbm_frac": round(sm["gbps"] / PEAK_HBM_GBPS, 4),
+                             "note": "includes the angle-table kernel (rotation) and launch gaps"}
     if args.sweep or args.only == "sweep":
         line["sweep"] = bench_sweep()
     if args.copy_probe:

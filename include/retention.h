@@ -171,6 +171,19 @@ ret_status_t retention_chunkwise_bwd(const ret_desc_t *desc, int32_t chunk, cons
                                      const void *v, const void *g, const void *dout, void *dq, void *dk, void *dv,
                                      void *dg, void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Retention score map of one query token over the tokens before it: the
+ * query-key inner products, in absolute value, each with its head's decay
+ * of the distance (the parallel form's weights), summed over heads ("Visual-
+ * ization of the retention mechanism", SpiralAI model card page):
+ *     scores[b, m] = sum_h g_h^(n-m) |q'_{b,n,h} . k'_{b,m,h}|   (m <= n)
+ * and 0 for m > n, with q', k' rotated by position and n = `query`
+ * (-1: the last token). scores: DEVICE fp32 [batch, seqlen], 16-byte
+ * aligned. Workspace: retention_score_map_workspace_bytes(desc) bytes (0
+ * without rotation; then `workspace` may be NULL). */
+size_t retention_score_map_workspace_bytes(const ret_desc_t *desc);
+ret_status_t retention_score_map(const ret_desc_t *desc, const void *q, const void *k, int32_t query, float *scores,
+                                 void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char *retention_status_string(ret_status_t status);
 

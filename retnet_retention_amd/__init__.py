@@ -6,6 +6,7 @@ gfx950 behind a C ABI (include/retention.h), with a thin ctypes binding.
     recurrent_step   recurrent form, one decode step, state in place
     parallel_bwd     gradients of the parallel form (q, k, v and the gate)
     chunkwise_bwd    the same gradients, each product run as the chunkwise form
+    score_map        one query token's retention weights, summed over heads
 """
 
 from .binding import (  # noqa: F401
@@ -17,4 +18,5 @@ from .binding import (  # noqa: F401
     parallel_bwd,
     parallel_fwd,
     recurrent_step,
+    score_map,
 )

@@ -41,6 +41,8 @@ EXPORTS = (
     "retention_parallel_bwd",
     "retention_chunkwise_bwd_workspace_bytes",
     "retention_chunkwise_bwd",
+    "retention_score_map_workspace_bytes",
+    "retention_score_map",
     "retention_status_string",
     "retention_abi_version",
 )
@@ -106,6 +108,10 @@ def lib():
         h.retention_chunkwise_bwd_workspace_bytes.restype = sz
         h.retention_chunkwise_bwd.argtypes = [pd, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         h.retention_chunkwise_bwd.restype = st
+        h.retention_score_map_workspace_bytes.argtypes = [pd]
+        h.retention_score_map_workspace_bytes.restype = sz
+        h.retention_score_map.argtypes = [pd, vp, vp, i32, vp, vp, sz, vp]
+        h.retention_score_map.restype = st
         h.retention_status_string.argtypes = [st]
         h.retention_status_string.restype = ctypes.c_char_p
         h.retention_abi_version.argtypes = []
@@ -226,6 +232,23 @@ def chunkwise_bwd(q, k, v, dout, g=None, *, chunk=512, gammas=None, rotary_base=
                                      _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(workspace), ws_bytes, _stream(q)))
     del keep
     return dq, dk, dv, dg
+
+
+def score_map(q, k, *, query=-1, gammas=None, rotary_base=0.0, pos_offset=0, workspace=None):
+    """Retention score map of query token `query` (-1: the last) over the
+    tokens before it, summed over heads; returns fp32 [batch, seqlen]."""
+    _validate(q, k, k, None, k)
+    out = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
+    desc, keep = _desc_for(q, k, gammas, rotary_base, pos_offset, 1e-5)
+    L = lib()
+    need = L.retention_score_map_workspace_bytes(ctypes.byref(desc))
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(L.retention_score_map(ctypes.byref(desc), _ptr(q), _ptr(k), int(query), _ptr(out), _ptr(workspace),
+                                 ws_bytes, _stream(q)))
+    del keep
+    return out
 
 
 def chunkwise_workspace_bytes(q, v, chunk, rotary_base=0.0):

@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libretention.so")
 
-SOURCES = ["api.hip", "rotary_table.hip", "recurrent_step.hip", "retention_fwd.hip", "backward.hip"]
+SOURCES = ["api.hip", "rotary_table.hip", "recurrent_step.hip", "retention_fwd.hip", "backward.hip", "score_map.hip"]
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}",

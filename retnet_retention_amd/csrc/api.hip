@@ -456,6 +456,40 @@ ret_status_t retention_recurrent_step(const ret_desc_t* desc, const void* q, con
   return RET_OK;
 }
 
+size_t retention_score_map_workspace_bytes(const ret_desc_t* desc) {
+  if (check_desc(desc) != RET_OK) return 0;
+  return bwd_table_bytes(desc);
+}
+
+ret_status_t retention_score_map(const ret_desc_t* desc, const void* q, const void* k, int32_t query,
+                                 float* scores, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  ret_status_t st = check_desc(desc);
+  if (st != RET_OK) return st;
+  if (!q || !k || !scores) return RET_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(scores)) return RET_ERR_ALIGN;
+  if (query < -1 || query >= desc->seqlen) return RET_ERR_ARG;
+  const size_t n = (size_t)desc->batch * desc->seqlen * desc->heads * desc->dk * elem_size(desc->dtype);
+  const size_t ns = (size_t)desc->batch * desc->seqlen * sizeof(float);
+  if (overlaps(scores, ns, q, n) || overlaps(scores, ns, k, n)) return RET_ERR_ALIAS;
+  const size_t need = bwd_table_bytes(desc);
+  if (need && (!workspace || workspace_bytes < need)) return RET_ERR_WORKSPACE;
+  if (need && !aligned16(workspace)) return RET_ERR_ALIGN;
+  if (need && (overlaps(workspace, need, q, n) || overlaps(workspace, need, k, n) ||
+               overlaps(workspace, need, scores, ns)))
+    return RET_ERR_ALIAS;
+  const Shape s = make_shape(desc);
+  float2* table = nullptr;
+  if (need) {
+    table = static_cast<float2*>(workspace);
+    if (ret::launch_rotary_table(table, desc->seqlen, desc->dk, desc->rotary_base, desc->pos_offset, stream) !=
+        hipSuccess)
+      return RET_ERR_HIP;
+  }
+  if (ret::launch_score_map(s, q, k, table, query < 0 ? desc->seqlen - 1 : query, scores, stream) != hipSuccess)
+    return RET_ERR_HIP;
+  return RET_OK;
+}
+
 ret_status_t retention_recurrent_step_positions(const ret_desc_t* desc, const void* q, const void* k,
                                                 const void* v, const void* g, void* o, float* state,
                                                 const int64_t* positions, hipStream_t stream) {

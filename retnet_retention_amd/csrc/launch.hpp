@@ -55,6 +55,11 @@ hipError_t launch_gate_norm_bwd(const Shape& s, const void* o, const void* g, co
                                 float eps, hipStream_t stream, void* dov_rev = nullptr);
 hipError_t launch_reverse_tokens(const Shape& s, const void* src, void* dst, hipStream_t stream);
 
+// Score map of query token `qpos`: out [batch][seqlen] fp32 (zeros past
+// qpos); `table` (may be null) the rotation's cos/sin table.
+hipError_t launch_score_map(const Shape& s, const void* q, const void* k, const float2* table, int qpos, float* out,
+                            hipStream_t stream);
+
 // One decode step, in place on `state`. `positions` (device, [batch], may
 // be null): each sequence's rotation position instead of `pos`.
 hipError_t launch_recurrent_step(const Shape& s, const void* q, const void* k, const void* v, const void* g,

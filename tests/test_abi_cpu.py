@@ -188,3 +188,17 @@ def test_step_positions_validates(L):
     # seqlen must be 1
     d2, _ = _desc(batch=3, seqlen=2, heads=2, dk=64, dv=64)
     assert step(ctypes.byref(d2), a[0], a[1], a[2], None, a[3], a[4], a[5], None) == 2
+
+
+def test_score_map_validates(L):
+    d, _ = _desc(batch=2, seqlen=10, heads=2, dk=64, dv=64)
+    sm = L.retention_score_map
+    assert L.retention_score_map_workspace_bytes(ctypes.byref(d)) == 0
+    # query past the sequence
+    assert sm(ctypes.byref(d), ALIGNED, ALIGNED * 2, 10, ALIGNED * 3, None, 0, None) == 9
+    # scores overlapping q
+    assert sm(ctypes.byref(d), ALIGNED, ALIGNED * 2, -1, ALIGNED, None, 0, None) == 8
+    # rotation needs the angle table in the workspace
+    d2, _ = _desc(batch=2, seqlen=10, heads=2, dk=64, dv=64, rotary_base=10000.0)
+    assert L.retention_score_map_workspace_bytes(ctypes.byref(d2)) == 10 * 32 * 8 + (256 - 10 * 32 * 8 % 256) % 256
+    assert sm(ctypes.byref(d2), ALIGNED, ALIGNED * 2, -1, ALIGNED * 3, None, 0, None) == 6

@@ -242,3 +242,20 @@ def test_step_with_per_sequence_positions():
                                 rotary_base=base, pos=pos)
         torch.cuda.synchronize()
         assert torch.equal(one, out[sl]) and torch.equal(one_state, state[sl]), f"position {pos}"
+
+
+@pytest.mark.parametrize("b,n,h,d,dtype,rot,query", [(1, 1, 1, 64, "bf16", False, -1), (2, 300, 3, 256, "bf16", True, -1),
+                                                     (2, 130, 10, 128, "bf16", True, 57),
+                                                     (1, 200, 2, 64, "f32", True, 150),
+                                                     (4, 2048, 10, 256, "bf16", True, -1)])
+def test_score_map(b, n, h, d, dtype, rot, query):
+    """One query token's retention weights over the tokens before it, summed
+    over heads (the last case is the 3B workload's shape)."""
+    _announce(case="score map", b=b, n=n, h=h, d=d, dtype=dtype, rot=rot, query=query)
+    q, k, _, _, _ = make_inputs(103 + n + d, b, n, h, d, dtype, d ** -0.5 if dtype == "f32" else 1 / 16)
+    base = 10000.0 if rot else 0.0
+    got = to64(rr.score_map(q.torch(DEV), k.torch(DEV), query=query, rotary_base=base, pos_offset=5))
+    ref = oracle.score_map(q.f64, k.f64, rotary_base=base, pos_offset=5, query=query)
+    assert_close(got, ref, dtype, "scores")
+    last = n - 1 if query < 0 else query
+    assert np.all(got[:, last + 1:] == 0.0)
