@@ -172,9 +172,9 @@ ret_status_t retention_chunkwise_bwd(const ret_desc_t *desc, int32_t chunk, cons
                                      void *dg, void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Retention score map of one query token over the tokens before it: the
- * query-key inner products, in absolute value, each with its head's decay
- * of the distance (the parallel form's weights), summed over heads ("Visual-
- * ization of the retention mechanism", SpiralAI model card page):
+ * magnitude of each head's query-key dot product, weighted by that head's
+ * decay of the distance (the parallel form's weights), summed across heads
+ * ("Visualization of the retention mechanism", SpiralAI model card page):
  *     scores[b, m] = sum_h g_h^(n-m) |q'_{b,n,h} . k'_{b,m,h}|   (m <= n)
  * and 0 for m > n, with q', k' rotated by position and n = `query`
  * (-1: the last token). scores: DEVICE fp32 [batch, seqlen], 16-byte

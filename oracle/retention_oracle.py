@@ -225,8 +225,8 @@ def retention(form, q, k, v, g=None, gammas=None, rotary_base=0.0, pos_offset=0,
 def score_map(q, k, gammas=None, rotary_base=0.0, pos_offset=0, query=-1):
     """Retention weights of one query token over the tokens before it, summed
     over heads, the "Visualization of the retention mechanism" section of the
-    SpiralAI model card page: the inner products of queries and keys, taken in
-    absolute value and added up over all heads. Reading taken: the weights are
+    SpiralAI model card page: the magnitude of each head's query-key dot
+    product, summed across heads. Reading taken: the weights are
     those of the parallel form (Q K^T (.) D), so each carries its head's decay
     g^(n-m); for query token n (default: the last) and key token m <= n,
         w[b, m] = sum_h g_h^(n-m) |q'_{b,n,h} . k'_{b,m,h}|

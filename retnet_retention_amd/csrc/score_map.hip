@@ -1,6 +1,6 @@
 // Retention score map of one query token ("Visualization of the retention
-// mechanism", SpiralAI model card page: query-key inner products, taken in
-// absolute value and added up over all heads; with the parallel form's
+// mechanism", SpiralAI model card page: the magnitude of each head's
+// query-key dot product, summed across heads; here with the parallel form's
 // per-head decay of the distance):
 //     w[b, m] = sum_h g_h^(n-m) |q'_{b,n,h} . k'_{b,m,h}|   for m <= n, else 0.
 // A pure stream over k (each key token read once) against one query row per
