@@ -16,4 +16,4 @@ from .retention_oracle import (  # noqa: F401
     rotate,
     score_map,
 )
-from .retention_grad import parallel_grad, unrotate  # noqa: F401
+from .retention_grad import chunkwise_state_grad, parallel_grad, unrotate  # noqa: F401

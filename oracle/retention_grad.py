@@ -28,7 +28,7 @@ import numpy as np
 
 from .retention_oracle import default_gammas, group_norm_swish, rotate
 
-__all__ = ["unrotate", "parallel_grad"]
+__all__ = ["unrotate", "parallel_grad", "chunkwise_state_grad"]
 
 
 def unrotate(x, rotary_base, pos_offset=0):
@@ -105,6 +105,74 @@ def parallel_grad(q, k, v, dout, g=None, gammas=None, rotary_base=0.0, pos_offse
     dq = unrotate(dqr, rotary_base, pos_offset)
     dk = unrotate(dkr, rotary_base, pos_offset)
     return dq, dk, dv, dg
+
+
+def chunkwise_state_grad(q, k, v, dout, g=None, state_in=None, d_state_out=None, gammas=None, rotary_base=0.0,
+                         pos_offset=0, eps=1e-5):
+    """Gradients with a carried state: the forward is the chunkwise form
+    (equivalently the recurrence) from state_in S0 (None: zeros), with output
+    out (GroupNorm + gate when ``g`` is given) and final state S_N; the loss
+    is sum(dout * out) + sum(d_state_out * S_N). Returns
+    (dq, dk, dv, dg, d_state_in); d_state_in is None when state_in is.
+
+    Each term follows the chain rule of the closed forms, per head:
+        o_n = sum_{m<=n} g^(n-m) (q'_n . k'_m) v_m + g^(n+1) q'_n S0
+        S_N = g^N S0 + sum_m g^(N-1-m) k'_m^T v_m
+    so, with dO the gradient at o and dS = d_state_out,
+        dq'_n += g^(n+1) S0 dO_n
+        dk'_m += g^(N-1-m) dS v_m,   dv_m += g^(N-1-m) k'_m dS   (dS terms)
+        dS0    = sum_n g^(n+1) q'_n^T dO_n + g^N dS."""
+    heads = q.shape[2]
+    n_tok = q.shape[1]
+    gam = default_gammas(heads) if gammas is None else np.asarray(gammas, dtype=np.float64)
+    qr = rotate(q, rotary_base, pos_offset)
+    kr = rotate(k, rotary_base, pos_offset)
+    bsz = q.shape[0]
+    s0 = np.zeros((bsz, heads, q.shape[3], v.shape[3])) if state_in is None else state_in
+    pos = np.arange(n_tok, dtype=np.float64)
+
+    # forward of the retention output (with the carried state)
+    o = np.zeros(v.shape)
+    for h in range(heads):
+        dmat = _decay_matrix(n_tok, gam[h])
+        a = (qr[:, :, h, :] @ np.swapaxes(kr[:, :, h, :], 1, 2)) * dmat[None]
+        o[:, :, h, :] = a @ v[:, :, h, :] + (gam[h] ** (pos + 1.0))[None, :, None] * (qr[:, :, h, :] @ s0[:, h])
+
+    if g is not None:
+        mu = o.mean(axis=-1, keepdims=True)
+        var = ((o - mu) ** 2).mean(axis=-1, keepdims=True)
+        sigma = np.sqrt(var + eps)
+        y = (o - mu) / sigma
+        sig = 1.0 / (1.0 + np.exp(-g))
+        dg = dout * y * (sig * (1.0 + g * (1.0 - sig)))
+        dy = dout * g * sig
+        do = (dy - dy.mean(axis=-1, keepdims=True) - y * (dy * y).mean(axis=-1, keepdims=True)) / sigma
+    else:
+        dg, do = None, dout
+
+    dqr = np.zeros(q.shape)
+    dkr = np.zeros(k.shape)
+    dv = np.zeros(v.shape)
+    ds0 = np.zeros(s0.shape)
+    for h in range(heads):
+        dmat = _decay_matrix(n_tok, gam[h])
+        qh, kh, vh, doh = qr[:, :, h, :], kr[:, :, h, :], v[:, :, h, :], do[:, :, h, :]
+        a = (qh @ np.swapaxes(kh, 1, 2)) * dmat[None]
+        da = (doh @ np.swapaxes(vh, 1, 2)) * dmat[None]
+        carry = gam[h] ** (pos + 1.0)                  # g^(n+1)
+        tail = gam[h] ** (n_tok - 1.0 - pos)           # g^(N-1-m)
+        dqr[:, :, h, :] = da @ kh + carry[None, :, None] * (doh @ np.swapaxes(s0[:, h], 1, 2))
+        dkr[:, :, h, :] = np.swapaxes(da, 1, 2) @ qh
+        dv[:, :, h, :] = np.swapaxes(a, 1, 2) @ doh
+        ds0[:, h] = np.swapaxes(qh * carry[None, :, None], 1, 2) @ doh
+        if d_state_out is not None:
+            dsh = d_state_out[:, h]                    # [B, dk, dv]
+            dkr[:, :, h, :] += tail[None, :, None] * (vh @ np.swapaxes(dsh, 1, 2))
+            dv[:, :, h, :] += tail[None, :, None] * (kh @ dsh)
+            ds0[:, h] += gam[h] ** n_tok * dsh
+    dq = unrotate(dqr, rotary_base, pos_offset)
+    dk = unrotate(dkr, rotary_base, pos_offset)
+    return dq, dk, dv, dg, (None if state_in is None else ds0)
 
 
 def forward_for_check(q, k, v, g=None, gammas=None, rotary_base=0.0, pos_offset=0, eps=1e-5):

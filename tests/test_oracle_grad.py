@@ -92,3 +92,41 @@ def test_unrotate_is_the_transpose_of_rotate():
     rx = oracle.rotate(x, 10000.0, 17)
     assert np.allclose(oracle.unrotate(rx, 10000.0, 17), x, atol=1e-13)
     assert abs((rx * y).sum() - (x * oracle.unrotate(y, 10000.0, 17)).sum()) < 1e-12
+
+
+@pytest.mark.parametrize("gate,rot,dso", [(True, True, True), (False, False, True), (True, False, False)])
+def test_state_gradients_match_finite_differences(gate, rot, dso):
+    """Carried state: finite differences of sum(dout * out) + sum(dS * S_N)
+    through the chunkwise oracle (its state in and state out)."""
+    rng = np.random.default_rng(31 + 4 * gate + 2 * rot + dso)
+    b, n, h, d, chunk = 1, 7, 2, 4, 3
+    q, k, v = (_rand(rng, b, n, h, d) * 0.7 for _ in range(3))
+    g = _rand(rng, b, n, h, d) if gate else None
+    dout = _rand(rng, b, n, h, d)
+    s0 = _rand(rng, b, h, d, d) * 0.5
+    dso_t = _rand(rng, b, h, d, d) if dso else None
+    gam = [0.9, 0.6]
+    base = 100.0 if rot else 0.0
+
+    def loss():
+        out, st = oracle.retention("chunkwise", q, k, v, g=g, gammas=gam, rotary_base=base, pos_offset=2,
+                                   chunk=chunk, state_in=s0)
+        total = float((dout * out).sum())
+        return total + (float((dso_t * st).sum()) if dso else 0.0)
+
+    got = oracle.chunkwise_state_grad(q, k, v, dout, g=g, state_in=s0, d_state_out=dso_t, gammas=gam,
+                                      rotary_base=base, pos_offset=2)
+    for name, x, an in (("q", q, got[0]), ("k", k, got[1]), ("v", v, got[2]), ("s0", s0, got[4])) + \
+            ((("g", g, got[3]),) if gate else ()):
+        fd = _fd_grad(loss, x)
+        assert np.max(np.abs(fd - an)) < 1e-6 * max(1.0, np.max(np.abs(fd))), name
+
+
+def test_state_gradients_reduce_to_the_stateless_ones():
+    rng = np.random.default_rng(41)
+    q, k, v, dout, g = (_rand(rng, 2, 5, 2, 4) for _ in range(5))
+    a = oracle.chunkwise_state_grad(q, k, v, dout, g=g, rotary_base=1000.0)
+    b = oracle.parallel_grad(q, k, v, dout, g=g, rotary_base=1000.0)
+    for x, y in zip(a[:4], b):
+        assert np.allclose(x, y, rtol=1e-12, atol=1e-13)
+    assert a[4] is None
