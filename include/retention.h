@@ -171,6 +171,24 @@ ret_status_t retention_chunkwise_bwd(const ret_desc_t *desc, int32_t chunk, cons
                                      const void *v, const void *g, const void *dout, void *dq, void *dk, void *dv,
                                      void *dg, void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* The chunkwise backward with a carried state: the forward ran from
+ * `state_in` (DEVICE fp32 [batch, heads, dk, dv]) and the loss may also
+ * depend on its state_out, whose gradient `d_state_out` (same layout; NULL:
+ * none) the caller passes. Besides dq, dk, dv, dg it writes `d_state_in`, the
+ * gradient with respect to state_in (non-NULL exactly when state_in is). The
+ * state terms run through the same three products: S0^T as the dq
+ * product's initial state, dS_out / g (per head) as the reversed products'
+ * initial states, and d_state_in = g Z^T from the reversed dk product's
+ * final state Z. Every decay must be >= 2^-60 when d_state_out is given
+ * (RET_ERR_GAMMA otherwise). Workspace: at least
+ * retention_chunkwise_bwd_state_workspace_bytes(desc, chunk, g != NULL). */
+size_t retention_chunkwise_bwd_state_workspace_bytes(const ret_desc_t *desc, int32_t chunk, int32_t has_gate);
+ret_status_t retention_chunkwise_bwd_state(const ret_desc_t *desc, int32_t chunk, const void *q, const void *k,
+                                           const void *v, const void *g, const void *dout, const float *state_in,
+                                           const float *d_state_out, void *dq, void *dk, void *dv, void *dg,
+                                           float *d_state_in, void *workspace, size_t workspace_bytes,
+                                           hipStream_t stream);
+
 /* Retention score map of one query token over the tokens before it: the
  * magnitude of each head's query-key dot product, weighted by that head's
  * decay of the distance (the parallel form's weights), summed across heads

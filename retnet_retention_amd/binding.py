@@ -41,6 +41,8 @@ EXPORTS = (
     "retention_parallel_bwd",
     "retention_chunkwise_bwd_workspace_bytes",
     "retention_chunkwise_bwd",
+    "retention_chunkwise_bwd_state_workspace_bytes",
+    "retention_chunkwise_bwd_state",
     "retention_score_map_workspace_bytes",
     "retention_score_map",
     "retention_status_string",
@@ -108,6 +110,10 @@ def lib():
         h.retention_chunkwise_bwd_workspace_bytes.restype = sz
         h.retention_chunkwise_bwd.argtypes = [pd, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         h.retention_chunkwise_bwd.restype = st
+        h.retention_chunkwise_bwd_state_workspace_bytes.argtypes = [pd, i32, i32]
+        h.retention_chunkwise_bwd_state_workspace_bytes.restype = sz
+        h.retention_chunkwise_bwd_state.argtypes = [pd, i32] + [vp] * 13 + [sz, vp]
+        h.retention_chunkwise_bwd_state.restype = st
         h.retention_score_map_workspace_bytes.argtypes = [pd]
         h.retention_score_map_workspace_bytes.restype = sz
         h.retention_score_map.argtypes = [pd, vp, vp, i32, vp, vp, sz, vp]
@@ -214,12 +220,17 @@ def parallel_bwd(q, k, v, dout, g=None, *, gammas=None, rotary_base=0.0, pos_off
     return dq, dk, dv, dg
 
 
-def chunkwise_bwd(q, k, v, dout, g=None, *, chunk=512, gammas=None, rotary_base=0.0, pos_offset=0, eps=1e-5,
-                  workspace=None):
-    """Gradients of sum(dout * chunkwise_fwd(q, k, v, g, chunk=chunk, ...))
-    (no carried state) with respect to q, k, v and g; returns
-    (dq, dk, dv, dg), dg None without a gate."""
+def chunkwise_bwd(q, k, v, dout, g=None, *, chunk=512, state_in=None, d_state_out=None, gammas=None,
+                  rotary_base=0.0, pos_offset=0, eps=1e-5, workspace=None):
+    """Gradients of sum(dout * out) (+ sum(d_state_out * state_out)) with
+    out, state_out = chunkwise_fwd(q, k, v, g, chunk=chunk, state_in=state_in,
+    ...), with respect to q, k, v, g and state_in. Returns (dq, dk, dv, dg)
+    without a carried state, (dq, dk, dv, dg, d_state_in) with one; dg is
+    None without a gate."""
     _validate(q, k, v, g, dout)
+    if state_in is not None or d_state_out is not None:
+        return _chunkwise_bwd_state(q, k, v, dout, g, chunk, state_in, d_state_out, gammas, rotary_base,
+                                    pos_offset, eps, workspace)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     dg = torch.empty_like(g) if g is not None else None
     desc, keep = _desc_for(q, v, gammas, rotary_base, pos_offset, eps)
@@ -249,6 +260,29 @@ def score_map(q, k, *, query=-1, gammas=None, rotary_base=0.0, pos_offset=0, wor
                                  ws_bytes, _stream(q)))
     del keep
     return out
+
+
+def _chunkwise_bwd_state(q, k, v, dout, g, chunk, state_in, d_state_out, gammas, rotary_base, pos_offset, eps,
+                         workspace):
+    b, _, h, dk = q.shape
+    for name, t in (("state_in", state_in), ("d_state_out", d_state_out)):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()
+                              or tuple(t.shape) != (b, h, dk, v.shape[-1])):
+            raise ValueError(f"{name} must be a contiguous fp32 [batch, heads, dk, dv] tensor")
+    dq, dk_, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dg = torch.empty_like(g) if g is not None else None
+    ds0 = torch.empty_like(state_in) if state_in is not None else None
+    desc, keep = _desc_for(q, v, gammas, rotary_base, pos_offset, eps)
+    L = lib()
+    need = L.retention_chunkwise_bwd_state_workspace_bytes(ctypes.byref(desc), int(chunk), int(g is not None))
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(L.retention_chunkwise_bwd_state(ctypes.byref(desc), int(chunk), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                           _ptr(dout), _ptr(state_in), _ptr(d_state_out), _ptr(dq), _ptr(dk_),
+                                           _ptr(dv), _ptr(dg), _ptr(ds0), _ptr(workspace), ws_bytes, _stream(q)))
+    del keep
+    return (dq, dk_, dv, dg) if state_in is None else (dq, dk_, dv, dg, ds0)
 
 
 def chunkwise_workspace_bytes(q, v, chunk, rotary_base=0.0):

@@ -293,48 +293,54 @@ ret_status_t retention_parallel_bwd(const ret_desc_t* desc, const void* q, const
 namespace {
 
 // Backward of the chunkwise form: the chunkwise kernel's own workspace
-// (control block, state chain, per-chunk states), then the parallel
-// backward's table and tensor slots.
-size_t cbwd_bytes(const ret_desc_t* d, int32_t chunk, bool gate) {
-  return ctrl_bytes(d, chunk) + chain_bytes(d) + snap_bytes(d, chunk) + bwd_bytes(d, gate);
+// (control block, state chain, per-chunk states), the parallel backward's
+// table and tensor slots, then with a carried state up to three fp32 states
+// (S0^T; the dS terms for the reversed products; their final state).
+size_t state_bytes(const ret_desc_t* d) { return align_up((size_t)d->batch * d->heads * d->dk * d->dv * 4); }
+size_t cbwd_bytes(const ret_desc_t* d, int32_t chunk, bool gate, bool states) {
+  return ctrl_bytes(d, chunk) + chain_bytes(d) + snap_bytes(d, chunk) + bwd_bytes(d, gate) +
+         (states ? 4 * state_bytes(d) : 0);
 }
 
-}  // namespace
-
-size_t retention_chunkwise_bwd_workspace_bytes(const ret_desc_t* desc, int32_t chunk, int32_t has_gate) {
-  if (check_desc(desc) != RET_OK || chunk < 1) return 0;
-  return cbwd_bytes(desc, chunk, has_gate != 0);
-}
-
-ret_status_t retention_chunkwise_bwd(const ret_desc_t* desc, int32_t chunk, const void* q, const void* k,
-                                     const void* v, const void* g, const void* dout, void* dq, void* dk, void* dv,
-                                     void* dg, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+ret_status_t chunkwise_bwd_impl(const ret_desc_t* desc, int32_t chunk, const void* q, const void* k, const void* v,
+                                const void* g, const void* dout, const float* state_in, const float* d_state_out,
+                                void* dq, void* dk, void* dv, void* dg, float* d_state_in, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
   ret_status_t st = check_desc(desc);
   if (st != RET_OK) return st;
   if (chunk < 1) return RET_ERR_SHAPE;
   if (!q || !k || !v || !dout || !dq || !dk || !dv) return RET_ERR_NULL;
-  if ((g == nullptr) != (dg == nullptr)) return RET_ERR_NULL;
-  const void* ins[] = {q, k, v, g, dout};
-  void* outs[] = {dq, dk, dv, dg};
+  if ((g == nullptr) != (dg == nullptr) || (state_in == nullptr) != (d_state_in == nullptr)) return RET_ERR_NULL;
+  const void* ins[] = {q, k, v, g, dout, state_in, d_state_out};
+  void* outs[] = {dq, dk, dv, dg, d_state_in};
   for (const void* p : ins)
     if (p && !aligned16(p)) return RET_ERR_ALIGN;
   for (const void* p : outs)
     if (p && !aligned16(p)) return RET_ERR_ALIGN;
   const size_t n = (size_t)desc->batch * desc->seqlen * desc->heads * desc->dk * elem_size(desc->dtype);
-  for (int i = 0; i < 4; ++i) {
-    for (const void* p : ins)
-      if (overlaps(outs[i], n, p, n)) return RET_ERR_ALIAS;
-    for (int j = i + 1; j < 4; ++j)
-      if (overlaps(outs[i], n, outs[j], n)) return RET_ERR_ALIAS;
+  const size_t ns = (size_t)desc->batch * desc->heads * desc->dk * desc->dv * 4;
+  const size_t in_n[] = {n, n, n, n, n, ns, ns};
+  const size_t out_n[] = {n, n, n, n, ns};
+  for (int i = 0; i < 5; ++i) {
+    for (int j = 0; j < 7; ++j)
+      if (overlaps(outs[i], out_n[i], ins[j], in_n[j])) return RET_ERR_ALIAS;
+    for (int j = i + 1; j < 5; ++j)
+      if (overlaps(outs[i], out_n[i], outs[j], out_n[j])) return RET_ERR_ALIAS;
   }
   if ((st = check_eps(desc, g)) != RET_OK) return st;
-  const size_t need = cbwd_bytes(desc, chunk, g != nullptr);
+  // the dS terms enter the reversed products as state_in = dS / g: keep 1/g
+  // within fp32 range
+  if (d_state_out)
+    for (int h = 0; h < desc->heads; ++h)
+      if (head_gamma(desc, h) < std::ldexp(1.0, -60)) return RET_ERR_GAMMA;
+  const bool states = state_in || d_state_out;
+  const size_t need = cbwd_bytes(desc, chunk, g != nullptr, states);
   if (!workspace || workspace_bytes < need) return RET_ERR_WORKSPACE;
   if (!aligned16(workspace)) return RET_ERR_ALIGN;
-  for (const void* p : ins)
-    if (overlaps(workspace, need, p, n)) return RET_ERR_ALIAS;
-  for (const void* p : outs)
-    if (overlaps(workspace, need, p, n)) return RET_ERR_ALIAS;
+  for (int j = 0; j < 7; ++j)
+    if (overlaps(workspace, need, ins[j], in_n[j])) return RET_ERR_ALIAS;
+  for (int i = 0; i < 5; ++i)
+    if (overlaps(workspace, need, outs[i], out_n[i])) return RET_ERR_ALIAS;
 
   const Shape s = make_shape(desc);
   const int32_t c = eff_chunk(desc, chunk);
@@ -346,12 +352,36 @@ ret_status_t retention_chunkwise_bwd(const ret_desc_t* desc, int32_t chunk, cons
   const size_t tb = bwd_tensor_bytes(desc);
   char* next = tab_at + bwd_table_bytes(desc);
   auto slot = [&]() { char* p = next; next += tb; return p; };
+  char* st_at = tab_at + bwd_bytes(desc, g != nullptr);
+  auto state_slot = [&](int i) { return reinterpret_cast<float*>(st_at + i * state_bytes(desc)); };
   // one chunkwise product; q_rev, out_rev, out_rot as in the parallel backward
-  auto product = [&](const void* a, const void* b, const void* cc, void* out, bool q_rev, bool out_rev,
-                     const float2* out_rot) {
-    return ret::launch_retention_fwd(s, c, true, a, b, cc, nullptr, out, nullptr, nullptr, snap, chain, ctrl, nullptr,
+  auto product = [&](const void* a, const void* b, const void* cc, void* out, const float* s_in, float* s_out,
+                     bool q_rev, bool out_rev, const float2* out_rot) {
+    return ret::launch_retention_fwd(s, c, true, a, b, cc, nullptr, out, s_in, s_out, snap, chain, ctrl, nullptr,
                                      desc->gn_eps, stream, nullptr, nullptr, q_rev, out_rev, out_rot) == hipSuccess;
   };
+  // states of the three products (per head g): S0^T for dq; dS^T / g and
+  // dS / g for the reversed ones (their g^(m'+1) then makes g^(N-1-m)); the
+  // reversed dK product's final state Z gives dS0 = g Z^T
+  float ones[ret::kMaxHeadsHost], inv[ret::kMaxHeadsHost], gam[ret::kMaxHeadsHost];
+  for (int h = 0; h < desc->heads; ++h) {
+    ones[h] = 1.f;
+    inv[h] = (float)(1.0 / head_gamma(desc, h));
+    gam[h] = (float)head_gamma(desc, h);
+  }
+  float *s0t = nullptr, *xs = nullptr, *ys = nullptr, *zs = nullptr;
+  if (state_in) {
+    s0t = state_slot(0);
+    zs = state_slot(3);
+    if (ret::launch_state_map(s, state_in, s0t, true, ones, stream) != hipSuccess) return RET_ERR_HIP;
+  }
+  if (d_state_out) {
+    xs = state_slot(1);
+    ys = state_slot(2);
+    if (ret::launch_state_map(s, d_state_out, xs, true, inv, stream) != hipSuccess ||
+        ret::launch_state_map(s, d_state_out, ys, false, inv, stream) != hipSuccess)
+      return RET_ERR_HIP;
+  }
   // q', k' and the reversed q'
   const float2* table = nullptr;
   const void *qr = q, *kr = k;
@@ -382,7 +412,7 @@ ret_status_t retention_chunkwise_bwd(const ret_desc_t* desc, int32_t chunk, cons
     void* o_raw = slot();
     void* ds = slot();
     dorev = slot();
-    if (!product(qr, kr, v, o_raw, false, false, nullptr) ||
+    if (!product(qr, kr, v, o_raw, state_in, nullptr, false, false, nullptr) ||
         ret::launch_gate_norm_bwd(s, o_raw, g, dout, ds, dg, desc->gn_eps, stream, dorev) != hipSuccess)
       return RET_ERR_HIP;
     dov = ds;
@@ -392,10 +422,40 @@ ret_status_t retention_chunkwise_bwd(const ret_desc_t* desc, int32_t chunk, cons
   }
   // the parallel backward's three products, each run as the chunkwise form
   // (the same function), storing straight into the caller's tensors
-  if (!product(dov, v, kr, dq, false, false, table) || !product(v, dorev, qrev, dk, true, true, table) ||
-      !product(kr, qrev, dorev, dv, true, true, nullptr))
+  if (!product(dov, v, kr, dq, s0t, nullptr, false, false, table) ||
+      !product(v, dorev, qrev, dk, xs, zs, true, true, table) ||
+      !product(kr, qrev, dorev, dv, ys, nullptr, true, true, nullptr))
     return RET_ERR_HIP;
+  if (state_in && ret::launch_state_map(s, zs, d_state_in, true, gam, stream) != hipSuccess) return RET_ERR_HIP;
   return RET_OK;
+}
+
+}  // namespace
+
+size_t retention_chunkwise_bwd_workspace_bytes(const ret_desc_t* desc, int32_t chunk, int32_t has_gate) {
+  if (check_desc(desc) != RET_OK || chunk < 1) return 0;
+  return cbwd_bytes(desc, chunk, has_gate != 0, false);
+}
+
+ret_status_t retention_chunkwise_bwd(const ret_desc_t* desc, int32_t chunk, const void* q, const void* k,
+                                     const void* v, const void* g, const void* dout, void* dq, void* dk, void* dv,
+                                     void* dg, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return chunkwise_bwd_impl(desc, chunk, q, k, v, g, dout, nullptr, nullptr, dq, dk, dv, dg, nullptr, workspace,
+                            workspace_bytes, stream);
+}
+
+size_t retention_chunkwise_bwd_state_workspace_bytes(const ret_desc_t* desc, int32_t chunk, int32_t has_gate) {
+  if (check_desc(desc) != RET_OK || chunk < 1) return 0;
+  return cbwd_bytes(desc, chunk, has_gate != 0, true);
+}
+
+ret_status_t retention_chunkwise_bwd_state(const ret_desc_t* desc, int32_t chunk, const void* q, const void* k,
+                                           const void* v, const void* g, const void* dout, const float* state_in,
+                                           const float* d_state_out, void* dq, void* dk, void* dv, void* dg,
+                                           float* d_state_in, void* workspace, size_t workspace_bytes,
+                                           hipStream_t stream) {
+  return chunkwise_bwd_impl(desc, chunk, q, k, v, g, dout, state_in, d_state_out, dq, dk, dv, dg, d_state_in,
+                            workspace, workspace_bytes, stream);
 }
 
 size_t retention_chunkwise_workspace_bytes(const ret_desc_t* desc, int32_t chunk) {

@@ -81,6 +81,45 @@ __global__ __launch_bounds__(256) void reverse_tokens_kernel(const uint4* __rest
   dst[(b * seqlen + (seqlen - 1 - n)) * per_tok + c] = src[i];
 }
 
+// Per (sequence, head) D x D fp32 states: dst = scale_h * src, or its
+// transpose; the scale per head comes from the host.
+struct StateMapParams {
+  const float* src;
+  float* dst;
+  int heads, transpose;
+  int64_t total;  // batch * heads * D * D
+  float scale[kMaxHeads];
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void state_map_kernel(StateMapParams p) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= p.total) return;
+  const int64_t mat = i / (D * D);
+  const int r = (int)((i / D) % D), c = (int)(i % D);
+  const float x = p.src[i] * p.scale[mat % p.heads];
+  p.dst[p.transpose ? mat * D * D + (int64_t)c * D + r : i] = x;
+}
+
+hipError_t launch_state_map(const Shape& s, const float* src, float* dst, bool transpose, const float* scale,
+                            hipStream_t stream) {
+  StateMapParams p;
+  p.src = src;
+  p.dst = dst;
+  p.heads = s.heads;
+  p.transpose = transpose ? 1 : 0;
+  p.total = (int64_t)s.batch * s.heads * s.d * s.d;
+  for (int h = 0; h < kMaxHeads; ++h) p.scale[h] = h < s.heads ? scale[h] : 0.f;
+  const unsigned blocks = (unsigned)((p.total + 255) / 256);
+  switch (s.d) {
+    case 64: hipLaunchKernelGGL(state_map_kernel<64>, dim3(blocks), dim3(256), 0, stream, p); break;
+    case 128: hipLaunchKernelGGL(state_map_kernel<128>, dim3(blocks), dim3(256), 0, stream, p); break;
+    case 256: hipLaunchKernelGGL(state_map_kernel<256>, dim3(blocks), dim3(256), 0, stream, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_gate_norm_bwd(const Shape& s, const void* o, const void* g, const void* dout, void* dov, void* dg,
                                 float eps, hipStream_t stream, void* dov_rev) {
   const int64_t rows = (int64_t)s.batch * s.seqlen * s.heads;

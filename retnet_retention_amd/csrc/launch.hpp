@@ -35,7 +35,7 @@ hipError_t launch_rotate_keys(const void* k, void* kr, const float2* table, int 
 size_t chunkwise_ctrl_bytes(int batch, int heads, int nchunks);
 // `rot` (may be null): the cos/sin table of launch_rotary_table, with which
 // the kernels turn q as they load it (k must then arrive rotated). For the
-// backward's products (chunkwise: without carried state): `q_rev` reads q
+// backward's products: `q_rev` reads q
 // with each sequence's token order reversed (not with `rot`), `out_rev`
 // stores the output reversed, `out_rot` (may be null) turns each stored
 // output row back by its stored position's angles.
@@ -54,6 +54,10 @@ hipError_t launch_retention_fwd(const Shape& s, int chunk, bool chunked, const v
 hipError_t launch_gate_norm_bwd(const Shape& s, const void* o, const void* g, const void* dout, void* dov, void* dg,
                                 float eps, hipStream_t stream, void* dov_rev = nullptr);
 hipError_t launch_reverse_tokens(const Shape& s, const void* src, void* dst, hipStream_t stream);
+// States [batch][heads][d][d] fp32: dst = scale[h] * src (transposed per
+// matrix when asked); scale: HOST array [heads].
+hipError_t launch_state_map(const Shape& s, const float* src, float* dst, bool transpose, const float* scale,
+                            hipStream_t stream);
 
 // Score map of query token `qpos`: out [batch][seqlen] fp32 (zeros past
 // qpos); `table` (may be null) the rotation's cos/sin table.

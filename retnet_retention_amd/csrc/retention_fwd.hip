@@ -1000,7 +1000,6 @@ hipError_t launch_retention_fwd(const Shape& s, int chunk, bool chunked, const v
                                 hipEvent_t before, hipEvent_t after, bool q_rev, bool out_rev,
                                 const float2* out_rot) {
   if (rot && q_rev) return hipErrorInvalidValue;  // q's angles are those of its own positions
-  if (chunked && (q_rev || out_rev || out_rot) && (state_in || state_out)) return hipErrorInvalidValue;
   FwdParams p;
   p.rot = rot;
   p.q_rev = q_rev;

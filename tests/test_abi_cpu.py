@@ -202,3 +202,18 @@ def test_score_map_validates(L):
     d2, _ = _desc(batch=2, seqlen=10, heads=2, dk=64, dv=64, rotary_base=10000.0)
     assert L.retention_score_map_workspace_bytes(ctypes.byref(d2)) == 10 * 32 * 8 + (256 - 10 * 32 * 8 % 256) % 256
     assert sm(ctypes.byref(d2), ALIGNED, ALIGNED * 2, -1, ALIGNED * 3, None, 0, None) == 6
+
+
+def test_stateful_backward_validates(L):
+    d, _ = _desc(batch=1, seqlen=16, heads=2, dk=64, dv=64)
+    bwd = L.retention_chunkwise_bwd_state
+    need = L.retention_chunkwise_bwd_state_workspace_bytes(ctypes.byref(d), 8, 0)
+    assert need > L.retention_chunkwise_bwd_workspace_bytes(ctypes.byref(d), 8, 0)
+    a = [ALIGNED * i for i in range(1, 16)]
+    # d_state_in without state_in
+    assert bwd(ctypes.byref(d), 8, a[0], a[1], a[2], None, a[3], None, None, a[4], a[5], a[6], None, a[7], a[8],
+               need, None) == 1
+    # a decay below 2^-60 with a state-out gradient
+    d2, _ = _desc(batch=1, seqlen=16, heads=2, dk=64, dv=64, gammas=[0.5, 2.0 ** -70])
+    assert bwd(ctypes.byref(d2), 8, a[0], a[1], a[2], None, a[3], a[9], a[10], a[4], a[5], a[6], None, a[7], a[8],
+               need, None) == 4

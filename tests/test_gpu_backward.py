@@ -126,3 +126,45 @@ def test_f32_chunkwise_backward():
     got, _, ref = _run_chunk(91, 1, 200, 2, 128, 64, "f32", 128 ** -0.5, True, True)
     for name, x, r in zip(("dq", "dk", "dv", "dg"), got, ref):
         assert_close(x, r, "f32", name)
+
+
+STATE_CASES = [
+    # (batch, seqlen, heads, d, chunk, dtype, gate, rotary, state_in, d_state_out)
+    (2, 300, 2, 256, 64, "bf16", True, True, True, True),
+    (1, 130, 3, 128, 512, "bf16", False, False, True, False),
+    (1, 200, 2, 64, 7, "bf16", True, False, False, True),
+    (1, 150, 2, 128, 64, "f32", True, True, True, True),
+]
+
+
+@pytest.mark.parametrize("b,n,h,d,chunk,dtype,gate,rot,s_in,dso", STATE_CASES)
+def test_chunkwise_backward_with_state(b, n, h, d, chunk, dtype, gate, rot, s_in, dso):
+    """Carried state: dq, dk, dv, dg and the state-in gradient, with the
+    state-out gradient in the loss, against the fp64 oracle."""
+    import torch
+
+    _announce(form="chunkwise backward with state", b=b, n=n, h=h, d=d, chunk=chunk, dtype=dtype, gate=gate, rot=rot,
+              state_in=s_in, d_state_out=dso)
+    scale = d ** -0.5 if dtype == "f32" else 1 / 16
+    specs = [((b, n, h, d), scale)] * 3 + [((b, n, h, d), 1 / 8)] + ([((b, n, h, d), 1 / 16)] if gate else [])
+    ts = draw(123 + n + d, specs, dtype)
+    q, k, v, dout = ts[:4]
+    g = ts[4] if gate else None
+    rng = np.random.default_rng(7 + n)
+    s0 = (rng.standard_normal((b, h, d, d)) * 0.05).astype(np.float32) if s_in else None
+    dso_a = (rng.standard_normal((b, h, d, d)) * 0.05).astype(np.float32) if dso else None
+    base = 10000.0 if rot else 0.0
+    t = lambda a: None if a is None else torch.from_numpy(a).to(DEV)
+    got = rr.chunkwise_bwd(q.torch(DEV), k.torch(DEV), v.torch(DEV), dout.torch(DEV), g.torch(DEV) if gate else None,
+                           chunk=chunk, state_in=t(s0), d_state_out=t(dso_a), rotary_base=base, pos_offset=4)
+    ref = oracle.chunkwise_state_grad(q.f64, k.f64, v.f64, dout.f64, g=g.f64 if gate else None,
+                                      state_in=None if s0 is None else s0.astype(np.float64),
+                                      d_state_out=None if dso_a is None else dso_a.astype(np.float64),
+                                      rotary_base=base, pos_offset=4)
+    names = ("dq", "dk", "dv", "dg", "d_state_in")
+    for i, name in enumerate(names[:len(got)]):
+        r = ref[i]
+        if r is None:
+            assert got[i] is None
+            continue
+        assert_close(to64(got[i]), r, dtype, name)
