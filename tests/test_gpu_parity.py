@@ -259,3 +259,18 @@ def test_score_map(b, n, h, d, dtype, rot, query):
     assert_close(got, ref, dtype, "scores")
     last = n - 1 if query < 0 else query
     assert np.all(got[:, last + 1:] == 0.0)
+
+
+@pytest.mark.parametrize("form", ["parallel", "chunkwise", "recurrent"])
+def test_max_heads_and_far_positions(form):
+    """128 heads (the most a call takes) at d = 64, rotation from position
+    10^9 (the angle table is formed in fp64 before rounding), every form."""
+    _announce(case="max heads, far positions", form=form)
+    b, n, h, d = 1, 70 if form != "recurrent" else 5, 128, 64
+    q, k, v, g, s0 = make_inputs(131, b, n, h, d, "bf16", 1 / 16, 1.0, form != "parallel")
+    kw = dict(rotary_base=10000.0, pos_offset=10 ** 9)
+    ref, ref_s = oracle_run(form, q, k, v, g, chunk=32, state_in=s0, **kw)
+    out, st = gpu_run(form, q, k, v, g, chunk=32, state_in=s0, **kw)
+    assert_close(out, ref, "bf16", "out")
+    if ref_s is not None:
+        assert_close(st, ref_s, "bf16", "state")
