@@ -585,7 +585,8 @@ def profile_traffic(out, raw):
     """Two counter passes (FETCH_SIZE, then WRITE_SIZE) over the chunkwise leg
     plus a plain copy of known size; each counter is scaled by what it reads
     for the copy."""
-    leg = ["--only", "chunkwise", "--steps", "2", "--warmup", "1", "--copy-probe"]
+    leg = ["--only", "chunkwise", "--steps", "2", "--warmup", "1", "--no-other-chunkwise", "--cold-reps", "0",
+           "--copy-probe"]
     res, cmds = {}, []
     for counter in ("FETCH_SIZE", "WRITE_SIZE"):
         d = os.path.join(raw, f"pmc_{counter.lower()}")
