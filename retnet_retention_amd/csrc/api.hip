@@ -121,54 +121,6 @@ size_t snap_bytes(const ret_desc_t* d, int32_t chunk) {
   return align_up((size_t)d->batch * d->heads * nchunks_of(d, chunk) * d->dk * d->dv * elem_size(d->dtype));
 }
 
-}  // namespace
-
-extern "C" {
-
-int32_t retention_abi_version(void) { return 1; }
-
-const char* retention_status_string(ret_status_t s) {
-  switch (s) {
-    case RET_OK: return "ok";
-    case RET_ERR_NULL: return "a required pointer is NULL";
-    case RET_ERR_SHAPE: return "batch, seqlen, heads or chunk out of range";
-    case RET_ERR_UNSUPPORTED: return "unsupported dk/dv/dtype (need dk == dv in {64,128,256}, fp32 or bf16)";
-    case RET_ERR_GAMMA: return "decay outside (0, 1]";
-    case RET_ERR_ALIGN: return "pointer not 16-byte aligned";
-    case RET_ERR_WORKSPACE: return "workspace NULL or too small";
-    case RET_ERR_HIP: return "HIP runtime error at kernel launch";
-    case RET_ERR_ALIAS: return "output overlaps an input";
-    case RET_ERR_ARG: return "invalid scalar argument (gn_eps, rotary_base or pos_offset)";
-  }
-  return "unknown status";
-}
-
-size_t retention_parallel_workspace_bytes(const ret_desc_t* desc) {
-  if (check_desc(desc) != RET_OK) return 0;
-  return rot_bytes(desc);
-}
-
-ret_status_t retention_parallel_fwd(const ret_desc_t* desc, const void* q, const void* k, const void* v,
-                                    const void* g, void* o, void* workspace, size_t workspace_bytes,
-                                    hipStream_t stream) {
-  ret_status_t st = check_desc(desc);
-  if (st != RET_OK) return st;
-  if ((st = check_tensors(desc, q, k, v, g, o)) != RET_OK) return st;
-  if ((st = check_eps(desc, g)) != RET_OK) return st;
-  const size_t need = rot_bytes(desc);
-  if (need && (!workspace || workspace_bytes < need)) return RET_ERR_WORKSPACE;
-  if (workspace && !aligned16(workspace)) return RET_ERR_ALIGN;
-
-  const Shape s = make_shape(desc);
-  const float2* table;
-  if (!rotate_inputs(desc, k, &table, workspace, stream)) return RET_ERR_HIP;
-  if (ret::launch_retention_fwd(s, desc->seqlen, false, q, k, v, g, o, nullptr, nullptr, nullptr, nullptr, nullptr,
-                                table, desc->gn_eps, stream) != hipSuccess)
-    return RET_ERR_HIP;
-  return RET_OK;
-}
-
-namespace {
 
 // Backward of the parallel form. Workspace slots, each one tensor
 // [batch][seqlen][heads][d] rounded up to 256 bytes: the angle table and the
@@ -186,111 +138,6 @@ size_t bwd_bytes(const ret_desc_t* d, bool gate) {
   return bwd_table_bytes(d) + slots * bwd_tensor_bytes(d);
 }
 
-}  // namespace
-
-size_t retention_parallel_bwd_workspace_bytes(const ret_desc_t* desc, int32_t has_gate) {
-  if (check_desc(desc) != RET_OK) return 0;
-  return bwd_bytes(desc, has_gate != 0);
-}
-
-ret_status_t retention_parallel_bwd(const ret_desc_t* desc, const void* q, const void* k, const void* v,
-                                    const void* g, const void* dout, void* dq, void* dk, void* dv, void* dg,
-                                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  ret_status_t st = check_desc(desc);
-  if (st != RET_OK) return st;
-  if (!q || !k || !v || !dout || !dq || !dk || !dv) return RET_ERR_NULL;
-  if ((g == nullptr) != (dg == nullptr)) return RET_ERR_NULL;
-  const void* ins[] = {q, k, v, g, dout};
-  void* outs[] = {dq, dk, dv, dg};
-  for (const void* p : ins)
-    if (p && !aligned16(p)) return RET_ERR_ALIGN;
-  for (const void* p : outs)
-    if (p && !aligned16(p)) return RET_ERR_ALIGN;
-  const size_t n = (size_t)desc->batch * desc->seqlen * desc->heads * desc->dk * elem_size(desc->dtype);
-  for (int i = 0; i < 4; ++i) {
-    for (const void* p : ins)
-      if (overlaps(outs[i], n, p, n)) return RET_ERR_ALIAS;
-    for (int j = i + 1; j < 4; ++j)
-      if (overlaps(outs[i], n, outs[j], n)) return RET_ERR_ALIAS;
-  }
-  if ((st = check_eps(desc, g)) != RET_OK) return st;
-  const size_t need = bwd_bytes(desc, g != nullptr);
-  if (!workspace || workspace_bytes < need) return RET_ERR_WORKSPACE;
-  if (!aligned16(workspace)) return RET_ERR_ALIGN;
-  if (overlaps(workspace, need, q, n) || overlaps(workspace, need, k, n) || overlaps(workspace, need, v, n) ||
-      overlaps(workspace, need, g, n) || overlaps(workspace, need, dout, n) || overlaps(workspace, need, dq, n) ||
-      overlaps(workspace, need, dk, n) || overlaps(workspace, need, dv, n) || overlaps(workspace, need, dg, n))
-    return RET_ERR_ALIAS;
-
-  const Shape s = make_shape(desc);
-  const size_t tb = bwd_tensor_bytes(desc);
-  char* ws = static_cast<char*>(workspace);
-  char* next = ws + bwd_table_bytes(desc);
-  auto slot = [&]() { char* p = next; next += tb; return p; };
-  // q' and k' (rotated when rotation is on) and q' with each sequence's
-  // token order reversed
-  const float2* table = nullptr;
-  const void *qr = q, *kr = k;
-  void* qrev = nullptr;
-  if (desc->rotary_base != 0.0) {
-    float2* tab = reinterpret_cast<float2*>(ws);
-    void* qs = slot();
-    void* ks = slot();
-    qrev = slot();
-    if (ret::launch_rotary_table(tab, desc->seqlen, desc->dk, desc->rotary_base, desc->pos_offset, stream) !=
-            hipSuccess ||
-        ret::launch_rotate_keys(q, qs, tab, desc->batch, desc->seqlen, desc->heads, desc->dk, desc->dtype, stream,
-                                qrev) != hipSuccess ||
-        ret::launch_rotate_keys(k, ks, tab, desc->batch, desc->seqlen, desc->heads, desc->dk, desc->dtype,
-                                stream) != hipSuccess)
-      return RET_ERR_HIP;
-    table = tab;
-    qr = qs;
-    kr = ks;
-  } else {
-    qrev = slot();
-    if (ret::launch_reverse_tokens(s, q, qrev, stream) != hipSuccess) return RET_ERR_HIP;
-  }
-  // dO, the gradient of the retention output before the epilogue (through
-  // the gate and GroupNorm, from the recomputed raw output, or dout itself),
-  // and its reversed copy
-  const void* dov = dout;
-  void* dorev = nullptr;
-  if (g) {
-    void* o_raw = slot();
-    void* ds = slot();
-    dorev = slot();
-    if (ret::launch_retention_fwd(s, desc->seqlen, false, qr, kr, v, nullptr, o_raw, nullptr, nullptr, nullptr,
-                                  nullptr, nullptr, nullptr, desc->gn_eps, stream) != hipSuccess ||
-        ret::launch_gate_norm_bwd(s, o_raw, g, dout, ds, dg, desc->gn_eps, stream, dorev) != hipSuccess)
-      return RET_ERR_HIP;
-    dov = ds;
-  } else {
-    dorev = slot();
-    if (ret::launch_reverse_tokens(s, dout, dorev, stream) != hipSuccess) return RET_ERR_HIP;
-  }
-  // Three forward products, each storing its gradient straight into the
-  // caller's tensor (turned back by the rotation where it applies):
-  //   dq = rot^T(P(dO, V, K'));
-  //   dk = rot^T(rev P(rev V, rev dO, rev Q')), the transposed mask made
-  //        causal by reversing every sequence (q read reversed, output
-  //        stored reversed);
-  //   dv = rev P(rev K', rev Q', rev dO).
-  const hipEvent_t none = nullptr;
-  if (ret::launch_retention_fwd(s, desc->seqlen, false, dov, v, kr, nullptr, dq, nullptr, nullptr, nullptr, nullptr,
-                                nullptr, nullptr, desc->gn_eps, stream, none, none, false, false, table) !=
-          hipSuccess ||
-      ret::launch_retention_fwd(s, desc->seqlen, false, v, dorev, qrev, nullptr, dk, nullptr, nullptr, nullptr,
-                                nullptr, nullptr, nullptr, desc->gn_eps, stream, none, none, true, true, table) !=
-          hipSuccess ||
-      ret::launch_retention_fwd(s, desc->seqlen, false, kr, qrev, dorev, nullptr, dv, nullptr, nullptr, nullptr,
-                                nullptr, nullptr, nullptr, desc->gn_eps, stream, none, none, true, true, nullptr) !=
-          hipSuccess)
-    return RET_ERR_HIP;
-  return RET_OK;
-}
-
-namespace {
 
 // Backward of the chunkwise form: the chunkwise kernel's own workspace
 // (control block, state chain, per-chunk states), the parallel backward's
@@ -431,6 +278,153 @@ ret_status_t chunkwise_bwd_impl(const ret_desc_t* desc, int32_t chunk, const voi
 }
 
 }  // namespace
+
+extern "C" {
+
+int32_t retention_abi_version(void) { return 1; }
+
+const char* retention_status_string(ret_status_t s) {
+  switch (s) {
+    case RET_OK: return "ok";
+    case RET_ERR_NULL: return "a required pointer is NULL";
+    case RET_ERR_SHAPE: return "batch, seqlen, heads or chunk out of range";
+    case RET_ERR_UNSUPPORTED: return "unsupported dk/dv/dtype (need dk == dv in {64,128,256}, fp32 or bf16)";
+    case RET_ERR_GAMMA: return "decay outside (0, 1]";
+    case RET_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case RET_ERR_WORKSPACE: return "workspace NULL or too small";
+    case RET_ERR_HIP: return "HIP runtime error at kernel launch";
+    case RET_ERR_ALIAS: return "output overlaps an input";
+    case RET_ERR_ARG: return "invalid scalar argument (gn_eps, rotary_base or pos_offset)";
+  }
+  return "unknown status";
+}
+
+size_t retention_parallel_workspace_bytes(const ret_desc_t* desc) {
+  if (check_desc(desc) != RET_OK) return 0;
+  return rot_bytes(desc);
+}
+
+ret_status_t retention_parallel_fwd(const ret_desc_t* desc, const void* q, const void* k, const void* v,
+                                    const void* g, void* o, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream) {
+  ret_status_t st = check_desc(desc);
+  if (st != RET_OK) return st;
+  if ((st = check_tensors(desc, q, k, v, g, o)) != RET_OK) return st;
+  if ((st = check_eps(desc, g)) != RET_OK) return st;
+  const size_t need = rot_bytes(desc);
+  if (need && (!workspace || workspace_bytes < need)) return RET_ERR_WORKSPACE;
+  if (workspace && !aligned16(workspace)) return RET_ERR_ALIGN;
+
+  const Shape s = make_shape(desc);
+  const float2* table;
+  if (!rotate_inputs(desc, k, &table, workspace, stream)) return RET_ERR_HIP;
+  if (ret::launch_retention_fwd(s, desc->seqlen, false, q, k, v, g, o, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                table, desc->gn_eps, stream) != hipSuccess)
+    return RET_ERR_HIP;
+  return RET_OK;
+}
+
+size_t retention_parallel_bwd_workspace_bytes(const ret_desc_t* desc, int32_t has_gate) {
+  if (check_desc(desc) != RET_OK) return 0;
+  return bwd_bytes(desc, has_gate != 0);
+}
+
+ret_status_t retention_parallel_bwd(const ret_desc_t* desc, const void* q, const void* k, const void* v,
+                                    const void* g, const void* dout, void* dq, void* dk, void* dv, void* dg,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  ret_status_t st = check_desc(desc);
+  if (st != RET_OK) return st;
+  if (!q || !k || !v || !dout || !dq || !dk || !dv) return RET_ERR_NULL;
+  if ((g == nullptr) != (dg == nullptr)) return RET_ERR_NULL;
+  const void* ins[] = {q, k, v, g, dout};
+  void* outs[] = {dq, dk, dv, dg};
+  for (const void* p : ins)
+    if (p && !aligned16(p)) return RET_ERR_ALIGN;
+  for (const void* p : outs)
+    if (p && !aligned16(p)) return RET_ERR_ALIGN;
+  const size_t n = (size_t)desc->batch * desc->seqlen * desc->heads * desc->dk * elem_size(desc->dtype);
+  for (int i = 0; i < 4; ++i) {
+    for (const void* p : ins)
+      if (overlaps(outs[i], n, p, n)) return RET_ERR_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(outs[i], n, outs[j], n)) return RET_ERR_ALIAS;
+  }
+  if ((st = check_eps(desc, g)) != RET_OK) return st;
+  const size_t need = bwd_bytes(desc, g != nullptr);
+  if (!workspace || workspace_bytes < need) return RET_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return RET_ERR_ALIGN;
+  if (overlaps(workspace, need, q, n) || overlaps(workspace, need, k, n) || overlaps(workspace, need, v, n) ||
+      overlaps(workspace, need, g, n) || overlaps(workspace, need, dout, n) || overlaps(workspace, need, dq, n) ||
+      overlaps(workspace, need, dk, n) || overlaps(workspace, need, dv, n) || overlaps(workspace, need, dg, n))
+    return RET_ERR_ALIAS;
+
+  const Shape s = make_shape(desc);
+  const size_t tb = bwd_tensor_bytes(desc);
+  char* ws = static_cast<char*>(workspace);
+  char* next = ws + bwd_table_bytes(desc);
+  auto slot = [&]() { char* p = next; next += tb; return p; };
+  // q' and k' (rotated when rotation is on) and q' with each sequence's
+  // token order reversed
+  const float2* table = nullptr;
+  const void *qr = q, *kr = k;
+  void* qrev = nullptr;
+  if (desc->rotary_base != 0.0) {
+    float2* tab = reinterpret_cast<float2*>(ws);
+    void* qs = slot();
+    void* ks = slot();
+    qrev = slot();
+    if (ret::launch_rotary_table(tab, desc->seqlen, desc->dk, desc->rotary_base, desc->pos_offset, stream) !=
+            hipSuccess ||
+        ret::launch_rotate_keys(q, qs, tab, desc->batch, desc->seqlen, desc->heads, desc->dk, desc->dtype, stream,
+                                qrev) != hipSuccess ||
+        ret::launch_rotate_keys(k, ks, tab, desc->batch, desc->seqlen, desc->heads, desc->dk, desc->dtype,
+                                stream) != hipSuccess)
+      return RET_ERR_HIP;
+    table = tab;
+    qr = qs;
+    kr = ks;
+  } else {
+    qrev = slot();
+    if (ret::launch_reverse_tokens(s, q, qrev, stream) != hipSuccess) return RET_ERR_HIP;
+  }
+  // dO, the gradient of the retention output before the epilogue (through
+  // the gate and GroupNorm, from the recomputed raw output, or dout itself),
+  // and its reversed copy
+  const void* dov = dout;
+  void* dorev = nullptr;
+  if (g) {
+    void* o_raw = slot();
+    void* ds = slot();
+    dorev = slot();
+    if (ret::launch_retention_fwd(s, desc->seqlen, false, qr, kr, v, nullptr, o_raw, nullptr, nullptr, nullptr,
+                                  nullptr, nullptr, nullptr, desc->gn_eps, stream) != hipSuccess ||
+        ret::launch_gate_norm_bwd(s, o_raw, g, dout, ds, dg, desc->gn_eps, stream, dorev) != hipSuccess)
+      return RET_ERR_HIP;
+    dov = ds;
+  } else {
+    dorev = slot();
+    if (ret::launch_reverse_tokens(s, dout, dorev, stream) != hipSuccess) return RET_ERR_HIP;
+  }
+  // Three forward products, each storing its gradient straight into the
+  // caller's tensor (turned back by the rotation where it applies):
+  //   dq = rot^T(P(dO, V, K'));
+  //   dk = rot^T(rev P(rev V, rev dO, rev Q')), the transposed mask made
+  //        causal by reversing every sequence (q read reversed, output
+  //        stored reversed);
+  //   dv = rev P(rev K', rev Q', rev dO).
+  const hipEvent_t none = nullptr;
+  if (ret::launch_retention_fwd(s, desc->seqlen, false, dov, v, kr, nullptr, dq, nullptr, nullptr, nullptr, nullptr,
+                                nullptr, nullptr, desc->gn_eps, stream, none, none, false, false, table) !=
+          hipSuccess ||
+      ret::launch_retention_fwd(s, desc->seqlen, false, v, dorev, qrev, nullptr, dk, nullptr, nullptr, nullptr,
+                                nullptr, nullptr, nullptr, desc->gn_eps, stream, none, none, true, true, table) !=
+          hipSuccess ||
+      ret::launch_retention_fwd(s, desc->seqlen, false, kr, qrev, dorev, nullptr, dv, nullptr, nullptr, nullptr,
+                                nullptr, nullptr, nullptr, desc->gn_eps, stream, none, none, true, true, nullptr) !=
+          hipSuccess)
+    return RET_ERR_HIP;
+  return RET_OK;
+}
 
 size_t retention_chunkwise_bwd_workspace_bytes(const ret_desc_t* desc, int32_t chunk, int32_t has_gate) {
   if (check_desc(desc) != RET_OK || chunk < 1) return 0;
