@@ -125,7 +125,7 @@ size_t snap_bytes(const ret_desc_t* d, int32_t chunk) {
 // Backward of the parallel form. Workspace slots, each one tensor
 // [batch][seqlen][heads][d] rounded up to 256 bytes: the angle table and the
 // rotated q', k' and reversed q' with rotation, else only the reversed q;
-// with a gate the recomputed retention output, dO and reversed dO, else only
+// with a gate the recomputed retention output and the reversed dO, else only
 // the reversed dO.
 size_t bwd_tensor_bytes(const ret_desc_t* d) {
   return align_up((size_t)d->batch * d->seqlen * d->heads * d->dk * elem_size(d->dtype));
@@ -134,7 +134,7 @@ size_t bwd_table_bytes(const ret_desc_t* d) {
   return d->rotary_base == 0.0 ? 0 : align_up((size_t)d->seqlen * (d->dk / 2) * sizeof(float2));
 }
 size_t bwd_bytes(const ret_desc_t* d, bool gate) {
-  const int slots = (d->rotary_base == 0.0 ? 1 : 3) + (gate ? 3 : 1);
+  const int slots = (d->rotary_base == 0.0 ? 1 : 3) + (gate ? 2 : 1);
   return bwd_table_bytes(d) + slots * bwd_tensor_bytes(d);
 }
 
@@ -257,19 +257,18 @@ ret_status_t chunkwise_bwd_impl(const ret_desc_t* desc, int32_t chunk, const voi
   void* dorev = nullptr;
   if (g) {
     void* o_raw = slot();
-    void* ds = slot();
     dorev = slot();
     if (!product(qr, kr, v, o_raw, state_in, nullptr, false, false, nullptr) ||
-        ret::launch_gate_norm_bwd(s, o_raw, g, dout, ds, dg, desc->gn_eps, stream, dorev) != hipSuccess)
+        ret::launch_gate_norm_bwd(s, o_raw, g, dout, nullptr, dg, desc->gn_eps, stream, dorev) != hipSuccess)
       return RET_ERR_HIP;
-    dov = ds;
+    dov = nullptr;  // the dq product reads the reversed copy back in order
   } else {
     dorev = slot();
     if (ret::launch_reverse_tokens(s, dout, dorev, stream) != hipSuccess) return RET_ERR_HIP;
   }
   // the parallel backward's three products, each run as the chunkwise form
   // (the same function), storing straight into the caller's tensors
-  if (!product(dov, v, kr, dq, s0t, nullptr, false, false, table) ||
+  if (!product(dov ? dov : dorev, v, kr, dq, s0t, nullptr, dov == nullptr, false, table) ||
       !product(v, dorev, qrev, dk, xs, zs, true, true, table) ||
       !product(kr, qrev, dorev, dv, ys, nullptr, true, true, nullptr))
     return RET_ERR_HIP;
@@ -390,17 +389,18 @@ ret_status_t retention_parallel_bwd(const ret_desc_t* desc, const void* q, const
   // dO, the gradient of the retention output before the epilogue (through
   // the gate and GroupNorm, from the recomputed raw output, or dout itself),
   // and its reversed copy
+  // (with a gate only the reversed copy is written: the dq product reads it
+  // back in forward order)
   const void* dov = dout;
   void* dorev = nullptr;
   if (g) {
     void* o_raw = slot();
-    void* ds = slot();
     dorev = slot();
     if (ret::launch_retention_fwd(s, desc->seqlen, false, qr, kr, v, nullptr, o_raw, nullptr, nullptr, nullptr,
                                   nullptr, nullptr, nullptr, desc->gn_eps, stream) != hipSuccess ||
-        ret::launch_gate_norm_bwd(s, o_raw, g, dout, ds, dg, desc->gn_eps, stream, dorev) != hipSuccess)
+        ret::launch_gate_norm_bwd(s, o_raw, g, dout, nullptr, dg, desc->gn_eps, stream, dorev) != hipSuccess)
       return RET_ERR_HIP;
-    dov = ds;
+    dov = nullptr;
   } else {
     dorev = slot();
     if (ret::launch_reverse_tokens(s, dout, dorev, stream) != hipSuccess) return RET_ERR_HIP;
@@ -413,8 +413,9 @@ ret_status_t retention_parallel_bwd(const ret_desc_t* desc, const void* q, const
   //        stored reversed);
   //   dv = rev P(rev K', rev Q', rev dO).
   const hipEvent_t none = nullptr;
-  if (ret::launch_retention_fwd(s, desc->seqlen, false, dov, v, kr, nullptr, dq, nullptr, nullptr, nullptr, nullptr,
-                                nullptr, nullptr, desc->gn_eps, stream, none, none, false, false, table) !=
+  if (ret::launch_retention_fwd(s, desc->seqlen, false, dov ? dov : dorev, v, kr, nullptr, dq, nullptr, nullptr,
+                                nullptr, nullptr, nullptr, nullptr, desc->gn_eps, stream, none, none, dov == nullptr,
+                                false, table) !=
           hipSuccess ||
       ret::launch_retention_fwd(s, desc->seqlen, false, v, dorev, qrev, nullptr, dk, nullptr, nullptr, nullptr,
                                 nullptr, nullptr, nullptr, desc->gn_eps, stream, none, none, true, true, table) !=

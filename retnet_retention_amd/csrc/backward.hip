@@ -21,8 +21,8 @@ namespace ret {
 //   dg = dout * y * s(g) (1 + g (1 - s(g)))
 //   dy = dout * g s(g)
 //   do = (dy - mean(dy) - y mean(dy y)) / sigma
-// dov_rev (may be null) also receives dO at each sequence's reversed
-// token positions.
+// dO goes to dov and/or dov_rev (either may be null), the latter at each
+// sequence's reversed token positions.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void gate_norm_bwd_kernel(const T* __restrict__ o, const T* __restrict__ g,
                                                             const T* __restrict__ dout, T* __restrict__ dov,
@@ -66,7 +66,7 @@ __global__ __launch_bounds__(256) void gate_norm_bwd_kernel(const T* __restrict_
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const T r = (T)((dy[i] - mdy - x[i] * mdyy) * rsig);
-    dov[base + i] = r;
+    if (dov) dov[base + i] = r;
     if (dov_rev) dov_rev[rbase + i] = r;
   }
 }
