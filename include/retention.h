@@ -129,9 +129,10 @@ ret_status_t retention_recurrent_step(const ret_desc_t *desc, const void *q, con
 /* The same step with one rotation position per sequence (continuous
  * batching: sequences of a batch at different lengths): `positions` is a
  * DEVICE array of `batch` int64 positions, 8-byte aligned, each in
- * [0, 2^52] (not checked: it lives on the device), read by the step's kernel
- * in place of desc->pos_offset. Without rotation (rotary_base == 0) it is
- * ignored, but must still be a valid pointer. */
+ * [0, 2^52] or negative (not checked: it lives on the device), read by the
+ * step's kernel in place of desc->pos_offset. A negative position marks an
+ * inactive slot of the batch: its state is left as it is and its output row
+ * is zero. Without rotation the positions only mark the inactive slots. */
 ret_status_t retention_recurrent_step_positions(const ret_desc_t *desc, const void *q, const void *k,
                                                 const void *v, const void *g, void *o, float *state,
                                                 const int64_t *positions, hipStream_t stream);

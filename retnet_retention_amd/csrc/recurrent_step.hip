@@ -51,6 +51,13 @@ __global__ __launch_bounds__(512) void recurrent_step_kernel(StepParams p) {
   const T* q = reinterpret_cast<const T*>(p.q) + vec;
   const T* k = reinterpret_cast<const T*>(p.k) + vec;
   const T* v = reinterpret_cast<const T*>(p.v) + vec;
+  // per-sequence positions: a negative one marks an inactive slot of the
+  // batch (its state stays as it is, its output is zero)
+  if (p.positions && p.positions[bh / p.heads] < 0) {
+    T* o = reinterpret_cast<T*>(p.o) + vec;
+    for (int i = tid; i < D; i += 512) o[i] = (T)0.f;
+    return;  // uniform for the workgroup
+  }
 
   for (int i = tid; i < D; i += 512) {
     sq[i] = ld1(q, i);

@@ -274,3 +274,28 @@ def test_max_heads_and_far_positions(form):
     assert_close(out, ref, "bf16", "out")
     if ref_s is not None:
         assert_close(st, ref_s, "bf16", "state")
+
+
+def test_step_inactive_slots():
+    """A negative position marks an inactive slot: its state is untouched and
+    its output is zero; the active rows match the oracle."""
+    _announce(case="step with inactive slots")
+    b, h, d = 4, 2, 64
+    positions = [5, -1, 300, -7]
+    q, k, v, g, s0 = make_inputs(111, b, 1, h, d, "bf16", 1 / 16, 1.0, True)
+    state = torch.from_numpy(s0.astype(np.float32)).to(DEV)
+    before = state.clone()
+    pos_t = torch.tensor(positions, dtype=torch.int64, device=DEV)
+    out = rr.recurrent_step(q.torch(DEV), k.torch(DEV), v.torch(DEV), state, g.torch(DEV), rotary_base=10000.0,
+                            positions=pos_t)
+    torch.cuda.synchronize()
+    gam = oracle.default_gammas(h)
+    for i, pos in enumerate(positions):
+        if pos < 0:
+            assert torch.equal(state[i], before[i]) and torch.count_nonzero(out[i]) == 0
+            continue
+        sl = slice(i, i + 1)
+        ref_o, ref_s = oracle.recurrent_step(q.f64[sl], k.f64[sl], v.f64[sl], s0[sl], gam, g=g.f64[sl],
+                                             rotary_base=10000.0, pos=pos)
+        assert_close(to64(out[sl]), ref_o, "bf16", f"out, position {pos}")
+        assert_close(to64(state[sl]), ref_s, "bf16", f"state, position {pos}")
