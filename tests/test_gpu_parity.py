@@ -299,3 +299,49 @@ def test_step_inactive_slots():
                                              rotary_base=10000.0, pos=pos)
         assert_close(to64(out[sl]), ref_o, "bf16", f"out, position {pos}")
         assert_close(to64(state[sl]), ref_s, "bf16", f"state, position {pos}")
+
+
+def test_graph_replay_matches_eager():
+    """A chunkwise prefill and a decode step captured into one HIP graph: every
+    replay (with eager work and synchronizations in between) must give the
+    eager results bit for bit (the control-block reset is a kernel, not a
+    memset, and nothing in the calls allocates)."""
+    _announce(case="graph replay")
+    b, n, h, d, chunk = 2, 300, 2, 128, 64
+    q, k, v, g, _ = make_inputs(141, b, n, h, d, "bf16", 1 / 16, 1.0)
+    q1, k1, v1, g1, _ = make_inputs(142, b, 1, h, d, "bf16", 1 / 16, 1.0)
+    tq, tk, tv, tg = (x.torch(DEV) for x in (q, k, v, g))
+    sq, sk, sv, sg = (x.torch(DEV) for x in (q1, k1, v1, g1))
+    out = torch.empty_like(tv)
+    state = torch.empty((b, h, d, d), device=DEV)
+    step_out = torch.empty_like(sv)
+    ws = torch.empty(rr.chunkwise_workspace_bytes(tq, tv, chunk, rotary_base=10000.0), dtype=torch.uint8,
+                     device=DEV)
+
+    def work():
+        rr.chunkwise_fwd(tq, tk, tv, tg, chunk=chunk, state_out=state, out=out, workspace=ws, rotary_base=10000.0)
+        rr.recurrent_step(sq, sk, sv, state, sg, rotary_base=10000.0, pos=n, out=step_out)
+
+    work()
+    torch.cuda.synchronize()
+    ref = (out.clone(), state.clone(), step_out.clone())
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        work()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        work()
+    for rep in range(3):
+        out.zero_()
+        state.fill_(7.0)
+        step_out.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for got, want, name in zip((out, state, step_out), ref, ("out", "state", "step")):
+            assert torch.equal(got, want), f"replay {rep}: {name}"
+        rr.parallel_fwd(tq, tk, tv, tg)  # eager work between replays
+        torch.cuda.synchronize()
