@@ -5,17 +5,20 @@
 //     O_i = (Q_i K_i^T (.) D) V_i  +  xi (.) (Q_i R_{i-1})       xi_r = g^(r+1)
 //     R_i = g^b R_{i-1} + K_i^T (V_i (.) zeta)                    zeta_r = g^(b-1-r)
 // followed by GroupNorm + swish gate. The parallel form is one chunk that
-// spans the whole sequence with no carried state. Q and K arrive rotated.
+// spans the whole sequence with no carried state. K arrives rotated; q is
+// turned by the angle table as the output role loads it.
 //
 // Two workgroup roles share one kernel for the chunkwise form:
-//   * output role: 4 waves, 128 query rows of one chunk of one (sequence,
-//     head); each wave owns 32 rows and the full dv-wide fp32 output tile in
-//     registers. It streams the chunk's K and V blocks up to its diagonal
-//     through two LDS stages (direct global->LDS loads, the next block's
-//     loads overlapping the matrix-core work on the current one), computes
-//     S^T = K Q^T, the decay mask and O += P V, then -- last -- waits for
-//     R_{i-1} and adds the cross-chunk term, then GroupNorm + gate.
-//   * state role: 4 waves, one chunk of one (sequence, head); accumulates
+//   * output role: 8 waves for bf16 (4 for fp32), 32 query rows each, so 256
+//     (128) rows of one chunk of one (sequence, head); each wave owns the
+//     full dv-wide fp32 output tile of its rows in registers. It streams the
+//     chunk's K and V blocks up to its diagonal through two LDS stages
+//     (direct global->LDS loads, the next block's loads overlapping the
+//     matrix-core work on the current one), computes S^T = K Q^T, the decay
+//     mask and O += P V, then -- last -- waits for R_{i-1} and adds the
+//     cross-chunk term, then GroupNorm + gate.
+//   * state role: one workgroup per chunk of one (sequence, head) for bf16
+//     (two, one per 128 dk rows, for fp32 at D = 256); accumulates
 //     dR_i = K_i^T (V_i (.) zeta) over the chunk's keys (fp32, in registers),
 //     waits for R_{i-1} from the previous chunk's state workgroup, forms
 //     R_i = g^b R_{i-1} + dR_i and publishes it: fp32 for the next state
@@ -27,6 +30,9 @@
 // its class that hold smaller tickets and are therefore already running or
 // done: the waits always end. Every wait is also
 // bounded; on expiry it sets an error word in the control block and goes on.
+// The backward's products use separate instantiations (XF) that can read q
+// in reversed token order and store their output reversed and turned back by
+// the rotation; the forward instantiations carry none of that code.
 #include <type_traits>
 
 #include "common.hpp"
