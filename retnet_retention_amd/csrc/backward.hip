@@ -16,8 +16,9 @@
 
 namespace ret {
 
-// One wave per (token, head) row of D values, D / 64 per lane. With
-// y = (o - mean) / sigma, sigma = sqrt(var + eps), s(x) = sigmoid(x):
+// One (token, head) row of D values per D/EPL lanes, EPL elements (16
+// bytes) per lane, so a wave takes 64/(D/EPL) rows with 16-byte accesses.
+// With y = (o - mean) / sigma, sigma = sqrt(var + eps), s(x) = sigmoid(x):
 //   dg = dout * y * s(g) (1 + g (1 - s(g)))
 //   dy = dout * g s(g)
 //   do = (dy - mean(dy) - y mean(dy y)) / sigma
@@ -28,46 +29,53 @@ __global__ __launch_bounds__(256) void gate_norm_bwd_kernel(const T* __restrict_
                                                             const T* __restrict__ dout, T* __restrict__ dov,
                                                             T* __restrict__ dg, T* __restrict__ dov_rev,
                                                             int64_t rows, int seqlen, int heads, float eps) {
-  constexpr int PER = D / 64;
+  constexpr int EPL = 16 / (int)sizeof(T);  // elements per lane
+  constexpr int LPR = D / EPL;              // lanes per row
+  constexpr int RPW = 64 / LPR;             // rows per wave
   const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;  // whole waves leave together
-  const int64_t base = row * D + lane * PER;
-  float x[PER], gv[PER], dy[PER];
+  const int64_t row0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW;
+  if (row0 >= rows) return;  // whole waves leave together
+  const int64_t row = row0 + lane / LPR;
+  const bool valid = row < rows;  // the last wave may hold fewer rows: the rest recompute a row and store nothing
+  const int64_t rr = valid ? row : rows - 1;
+  const int64_t base = rr * D + (lane % LPR) * EPL;
+  auto row_sum = [](float v) __attribute__((always_inline)) {
 #pragma unroll
-  for (int i = 0; i < PER; ++i) x[i] = (float)o[base + i];
+    for (int w = 1; w < LPR; w *= 2) v += __shfl_xor(v, w, 64);
+    return v;
+  };
+  float x[EPL], gv[EPL], d[EPL];
+  load16f(o + base, x);
+  load16f(g + base, gv);
+  load16f(dout + base, d);
   float s = 0.f;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) s += x[i];
-  const float mean = sum64(s) * (1.0f / D);
+  for (int i = 0; i < EPL; ++i) s += x[i];
+  const float mean = row_sum(s) * (1.0f / D);
   float s2 = 0.f;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) s2 += (x[i] - mean) * (x[i] - mean);
-  const float rsig = rsqrtf(sum64(s2) * (1.0f / D) + eps);
-  float sdy = 0.f, sdyy = 0.f;
+  for (int i = 0; i < EPL; ++i) s2 += (x[i] - mean) * (x[i] - mean);
+  const float rsig = rsqrtf(row_sum(s2) * (1.0f / D) + eps);
+  float sdy = 0.f, sdyy = 0.f, dgv[EPL];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
+  for (int i = 0; i < EPL; ++i) {
     const float y = (x[i] - mean) * rsig;
-    gv[i] = (float)g[base + i];
-    const float d = (float)dout[base + i];
     const float sg = 1.0f / (1.0f + __expf(-gv[i]));
-    dg[base + i] = (T)(d * y * (sg * (1.0f + gv[i] * (1.0f - sg))));
-    dy[i] = d * gv[i] * sg;
+    dgv[i] = d[i] * y * (sg * (1.0f + gv[i] * (1.0f - sg)));
+    d[i] = d[i] * gv[i] * sg;  // dy
     x[i] = y;
-    sdy += dy[i];
-    sdyy += dy[i] * y;
+    sdy += d[i];
+    sdyy += d[i] * y;
   }
-  const float mdy = sum64(sdy) * (1.0f / D), mdyy = sum64(sdyy) * (1.0f / D);
-  int64_t rbase = 0;
+  const float mdy = row_sum(sdy) * (1.0f / D), mdyy = row_sum(sdyy) * (1.0f / D);
+  if (!valid) return;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) d[i] = (d[i] - mdy - x[i] * mdyy) * rsig;
+  store16f(dg + base, dgv);
+  if (dov) store16f(dov + base, d);
   if (dov_rev) {
     const int64_t tok = row / heads, b = tok / seqlen, n = tok % seqlen;
-    rbase = ((b * seqlen + (seqlen - 1 - n)) * heads + row % heads) * D + lane * PER;
-  }
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const T r = (T)((dy[i] - mdy - x[i] * mdyy) * rsig);
-    if (dov) dov[base + i] = r;
-    if (dov_rev) dov_rev[rbase + i] = r;
+    store16f(dov_rev + ((b * seqlen + (seqlen - 1 - n)) * heads + row % heads) * D + (lane % LPR) * EPL, d);
   }
 }
 
@@ -123,7 +131,9 @@ hipError_t launch_state_map(const Shape& s, const float* src, float* dst, bool t
 hipError_t launch_gate_norm_bwd(const Shape& s, const void* o, const void* g, const void* dout, void* dov, void* dg,
                                 float eps, hipStream_t stream, void* dov_rev) {
   const int64_t rows = (int64_t)s.batch * s.seqlen * s.heads;
-  const unsigned blocks = (unsigned)((rows + 3) / 4);
+  // rows per block: 4 waves of 64 / (D / (16 / element size)) rows
+  const int64_t per_block = 4 * 64 / (s.d / (s.dtype == 1 ? 8 : 4));
+  const unsigned blocks = (unsigned)((rows + per_block - 1) / per_block);
 #define RET_GN_BWD(TT, DD)                                                                                       \
   hipLaunchKernelGGL((gate_norm_bwd_kernel<TT, DD>), dim3(blocks), dim3(256), 0, stream, (const TT*)o,          \
                      (const TT*)g, (const TT*)dout, (TT*)dov, (TT*)dg, (TT*)dov_rev, rows, s.seqlen, s.heads, eps)
