@@ -26,6 +26,7 @@ import argparse
 import csv
 import glob
 import hashlib
+import itertools
 import json
 import os
 import subprocess
@@ -417,6 +418,50 @@ def bench_sweep(steps=10, warmup=20):
             "chunk_at_8192_tokens": chunks}
 
 
+VARLEN_LENS = (8192, 3000, 2048, 1500, 1024, 400, 200, 20)  # 16384 tokens in all
+
+
+def bench_varlen(steps, warmup):
+    """Chunkwise form over a packed ragged batch (prefill of sequences of
+    different lengths) at the 7B layer's heads (16 x 256, bf16, gate, state
+    out, chunk 512): eight sequences of VARLEN_LENS tokens, 16384 in all,
+    beside the same 16384 tokens as two sequences of 8192. Both are timed
+    per call (control reset and kernel). Inputs: seeded normals / 16 drawn on
+    the GPU; the flops are the chunkwise count summed per sequence."""
+    import torch
+
+    import ctypes
+
+    import retnet_retention_amd as rr
+    from retnet_retention_amd import binding as B
+
+    h, d, chunk = 16, 256, 512
+    tot = sum(VARLEN_LENS)
+    gen = torch.Generator(device="cuda:0")
+    gen.manual_seed(11)
+    q, k, v, g = ((torch.randn((tot, h, d), generator=gen, device="cuda:0") / 16).to(torch.bfloat16)
+                  for _ in range(4))
+    cu = torch.tensor([0] + list(itertools.accumulate(VARLEN_LENS)), dtype=torch.int32, device="cuda:0")
+    out = torch.empty_like(v)
+    st = torch.empty((len(VARLEN_LENS), h, d, d), device="cuda:0")
+    maxlen = max(VARLEN_LENS)
+    # the packed call's workspace (8 sequences of up to 8192) also covers the batched one
+    desc, keep = B.make_desc(len(VARLEN_LENS), maxlen, h, d, d, B.RET_BF16)
+    ws = torch.empty(B.lib().retention_chunkwise_varlen_workspace_bytes(ctypes.byref(desc), chunk),
+                     dtype=torch.uint8, device="cuda:0")
+    ms_var, _ = time_calls(lambda: rr.chunkwise_varlen_fwd(q, k, v, cu, maxlen, g, chunk=chunk, state_out=st, out=out,
+                                                           workspace=ws), steps, warmup)
+    shp = (2, tot // 2, h, d)
+    st2 = torch.empty((2, h, d, d), device="cuda:0")
+    ms_fix, _ = time_calls(lambda: rr.chunkwise_fwd(q.view(shp), k.view(shp), v.view(shp), g.view(shp), chunk=chunk,
+                                                    state_out=st2, out=out.view(shp), workspace=ws), steps, warmup)
+    flops_var = sum(chunkwise_flops(1, n, h, d, d, chunk) for n in VARLEN_LENS)
+    flops_fix = chunkwise_flops(2, tot // 2, h, d, d, chunk)
+    return {"lens": list(VARLEN_LENS), "ms": ms_var, "tflops": flops_var / (ms_var * 1e-3) / 1e12,
+            "tokens_per_s": tot / (ms_var * 1e-3), "equal_ms": ms_fix,
+            "equal_tflops": flops_fix / (ms_fix * 1e-3) / 1e12}
+
+
 def _graph_step_ms(step, per_graph, replays):
     """Device time per step of `per_graph` calls of `step` captured into one
     graph and replayed `replays` times (after two untimed replays)."""
@@ -763,7 +808,7 @@ def main():
     # the GPU's clocks take tens of milliseconds of load to settle: 5 warm-up
     # calls time the chunkwise call 14% slower than 200 do
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--only", choices=["chunkwise", "decode", "parallel", "parallel_bwd", "chunkwise_bwd", "score_map",
+    ap.add_argument("--only", choices=["chunkwise", "decode", "parallel", "parallel_bwd", "chunkwise_bwd", "score_map", "varlen",
                                        "sweep"],
                     default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -901,6 +946,17 @@ def main():
                              "us": round(sm["us"], 2), "gbps": round(sm["gbps"], 1),
                              "hbm_frac": round(sm["gbps"] / PEAK_HBM_GBPS, 4),
                              "note": "includes the angle-table kernel (rotation) and launch gaps"}
+    if args.only in (None, "varlen"):
+        vl = bench_varlen(max(args.steps // 2, 10), max(args.warmup // 4, 10))
+        print(f"varlen {vl['lens']}: {vl['ms']:.3f} ms, {vl['tflops']:.1f} TFLOP/s; two x 8192: {vl['equal_ms']:.3f} ms",
+              file=sys.stderr, flush=True)
+        line["varlen"] = {
+            "workload": "packed ragged batch: 8 sequences of " + "/".join(map(str, vl["lens"])) +
+                        " tokens (16384 in all), 16 x 256, chunk 512, bf16, gate, state out",
+            "ms": round(vl["ms"], 4), "tflops": round(vl["tflops"], 2), "tokens_per_s": round(vl["tokens_per_s"]),
+            "same_tokens_as_2x8192_ms": round(vl["equal_ms"], 4),
+            "same_tokens_as_2x8192_tflops": round(vl["equal_tflops"], 2),
+            "note": "per call: control reset and kernel; flops are the chunkwise count summed per sequence"}
     if args.sweep or args.only == "sweep":
         line["sweep"] = bench_sweep()
     if args.copy_probe:

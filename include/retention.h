@@ -100,8 +100,9 @@ ret_status_t retention_parallel_fwd(const ret_desc_t *desc, const void *q, const
  * workgroups that carry the state from chunk to chunk). Its first two int32
  * words form a control block that the call resets: after the call has
  * completed, word 0 counts the workgroups that ran and word 1 is nonzero only
- * if a cross-workgroup wait gave up after its bound (an internal error; the
- * output is then not valid). */
+ * on an error, after which the output is not valid: bit 0 (value 1) when a
+ * cross-workgroup wait gave up after its bound (an internal error), bit 1
+ * (value 2) for invalid packed-sequence bounds (retention_chunkwise_varlen_fwd). */
 size_t retention_chunkwise_workspace_bytes(const ret_desc_t *desc, int32_t chunk);
 ret_status_t retention_chunkwise_fwd(const ret_desc_t *desc, int32_t chunk, const void *q, const void *k,
                                      const void *v, const void *g, void *o, const float *state_in,
@@ -118,6 +119,38 @@ ret_status_t retention_chunkwise_fwd_timed(const ret_desc_t *desc, int32_t chunk
                                            const void *v, const void *g, void *o, const float *state_in,
                                            float *state_out, void *workspace, size_t workspace_bytes,
                                            hipStream_t stream, hipEvent_t before, hipEvent_t after);
+
+/* Chunkwise form over packed sequences of different lengths (prefill of a
+ * ragged batch; "Summary": the chunkwise form for long inputs, and the
+ * serving claim that latency hardly depends on batch size or input length).
+ * Every sequence is its own chunkwise recurrence, exactly as
+ * retention_chunkwise_fwd computes it for that sequence alone, with its own
+ * state_in/state_out slot and rotation positions pos_offset + n (n = 0 at
+ * its first token).
+ *     q, k          [total_tokens, heads, dk]  packed: sequence b occupies
+ *     v, g, o       [total_tokens, heads, dv]  rows cu_seqlens[b] ..
+ *                                               cu_seqlens[b+1]-1
+ *     cu_seqlens    DEVICE int32 [batch + 1], non-decreasing, from 0 to
+ *                   total_tokens (4-byte aligned)
+ *     state_in/out  [batch, heads, dk, dv] fp32, as retention_chunkwise_fwd
+ * desc->batch is the number of sequences and desc->seqlen an upper bound on
+ * every length (it sizes the launch and the workspace; the rotation table
+ * covers that many positions). 0 <= total_tokens <= batch * seqlen; empty
+ * sequences are allowed (their state_out = state_in, or zeros). Rows of `o`
+ * outside every sequence are not written. The host cannot read cu_seqlens:
+ * the kernels clamp each sequence's rows into [0, total_tokens) and its
+ * length to seqlen, so no access leaves the tensors whatever it holds, and a
+ * clamp sets bit 1 (value 2) of control word 1 (see retention_chunkwise_fwd;
+ * the output is then not valid). Workspace: at least
+ * retention_chunkwise_varlen_workspace_bytes(desc, chunk) bytes, never NULL:
+ * the chunkwise call's workspace plus a schedule of the launch (16 bytes per
+ * workgroup), so that the workgroups of chunks past a sequence's end come
+ * last and leave at once. */
+size_t retention_chunkwise_varlen_workspace_bytes(const ret_desc_t *desc, int32_t chunk);
+ret_status_t retention_chunkwise_varlen_fwd(const ret_desc_t *desc, int32_t chunk, const int32_t *cu_seqlens,
+                                            int64_t total_tokens, const void *q, const void *k, const void *v,
+                                            const void *g, void *o, const float *state_in, float *state_out,
+                                            void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Recurrent form, one decode step for a batch of single tokens (desc->seqlen
  * must be 1): state <- g * state + k^T v, then o = q state ("Summary": O(1)

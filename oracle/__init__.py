@@ -13,6 +13,7 @@ from .retention_oracle import (  # noqa: F401
     recurrent,
     recurrent_step,
     retention,
+    retention_varlen,
     rotate,
     score_map,
 )

@@ -222,6 +222,35 @@ def retention(form, q, k, v, g=None, gammas=None, rotary_base=0.0, pos_offset=0,
     return out, state
 
 
+def retention_varlen(form, q, k, v, cu_seqlens, g=None, gammas=None, rotary_base=0.0, pos_offset=0, eps=1e-5,
+                     chunk=None, state_in=None):
+    """A ragged batch in packed layout: q, k, v, g are [T, H, d] and sequence
+    b holds rows cu_seqlens[b] .. cu_seqlens[b+1]-1. Reading taken: every
+    sequence is its own retention run (own state slot, positions counted from
+    pos_offset at its first token), so this is ``retention`` applied to each
+    slice alone; an empty sequence passes its state through. Returns
+    (out [T, H, dv], final states [B, H, dk, dv]); rows outside every
+    sequence stay zero."""
+    cu = [int(x) for x in cu_seqlens]
+    nseq, heads, dk, dv = len(cu) - 1, q.shape[1], q.shape[2], v.shape[2]
+    out = np.zeros(v.shape[:2] + (dv,))
+    states = np.zeros((nseq, heads, dk, dv))
+    for b in range(nseq):
+        a, e = cu[b], cu[b + 1]
+        s0 = None if state_in is None else np.asarray(state_in[b:b + 1], dtype=np.float64)
+        if e == a:
+            if s0 is not None:
+                states[b] = s0[0]
+            continue
+        piece = lambda x: None if x is None else np.asarray(x[a:e], dtype=np.float64)[None]
+        o_b, s_b = retention(form, piece(q), piece(k), piece(v), g=piece(g), gammas=gammas,
+                             rotary_base=rotary_base, pos_offset=pos_offset, eps=eps, chunk=chunk, state_in=s0)
+        out[a:e] = o_b[0]
+        if s_b is not None:
+            states[b] = s_b[0]
+    return out, states
+
+
 def score_map(q, k, gammas=None, rotary_base=0.0, pos_offset=0, query=-1):
     """Retention weights of one query token over the tokens before it, summed
     over heads, the "Visualization of the retention mechanism" section of the

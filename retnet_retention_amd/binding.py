@@ -35,6 +35,8 @@ EXPORTS = (
     "retention_chunkwise_workspace_bytes",
     "retention_chunkwise_fwd",
     "retention_chunkwise_fwd_timed",
+    "retention_chunkwise_varlen_workspace_bytes",
+    "retention_chunkwise_varlen_fwd",
     "retention_recurrent_step",
     "retention_recurrent_step_positions",
     "retention_parallel_bwd_workspace_bytes",
@@ -98,6 +100,10 @@ def lib():
         h.retention_chunkwise_fwd.restype = st
         h.retention_chunkwise_fwd_timed.argtypes = [pd, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp]
         h.retention_chunkwise_fwd_timed.restype = st
+        h.retention_chunkwise_varlen_workspace_bytes.argtypes = [pd, i32]
+        h.retention_chunkwise_varlen_workspace_bytes.restype = sz
+        h.retention_chunkwise_varlen_fwd.argtypes = [pd, i32, vp, ctypes.c_int64] + [vp] * 8 + [sz, vp]
+        h.retention_chunkwise_varlen_fwd.restype = st
         h.retention_recurrent_step.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp]
         h.retention_recurrent_step.restype = st
         h.retention_recurrent_step_positions.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, vp]
@@ -320,6 +326,53 @@ def chunkwise_fwd(q, k, v, g=None, *, chunk=512, state_in=None, state_out=None, 
                                                ws_bytes, _stream(q), before, after))
     del keep
     return out
+
+
+def chunkwise_varlen_fwd(q, k, v, cu_seqlens, max_seqlen, g=None, *, chunk=512, state_in=None, state_out=None,
+                         gammas=None, rotary_base=0.0, pos_offset=0, eps=1e-5, out=None, workspace=None):
+    """Chunkwise form over packed sequences of different lengths: q, k, v, g
+    are [total_tokens, heads, d], sequence b holds rows cu_seqlens[b] ..
+    cu_seqlens[b+1]-1 (cu_seqlens: GPU int32 [batch + 1]); max_seqlen bounds
+    every length. state_in / state_out: fp32 [batch, heads, dk, dv] or None.
+    Returns the output (rows outside every sequence are left as they were)."""
+    out = torch.empty_like(v) if out is None else out
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("out", out)):
+        if t is None:
+            continue
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype or t.dim() != 3:
+            raise ValueError(f"{name} must be a contiguous GPU [total_tokens, heads, d] tensor of q's dtype")
+    if k.shape != q.shape or v.shape[:2] != q.shape[:2] or (g is not None and g.shape != v.shape) \
+            or out.shape != v.shape:
+        raise ValueError("q, k, v, g and out must agree on [total_tokens, heads]")
+    if not cu_seqlens.is_cuda or cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 \
+            or not cu_seqlens.is_contiguous():
+        raise ValueError("cu_seqlens must be a contiguous GPU int32 tensor [batch + 1]")
+    batch = cu_seqlens.numel() - 1
+    total, h, dk = q.shape
+    for name, st in (("state_in", state_in), ("state_out", state_out)):
+        if st is not None and (st.dtype != torch.float32 or not st.is_contiguous()
+                               or tuple(st.shape) != (batch, h, dk, v.shape[-1])):
+            raise ValueError(f"{name} must be a contiguous fp32 [batch, heads, dk, dv] tensor")
+    desc, keep = make_desc(batch, int(max_seqlen), h, dk, v.shape[-1], _dtype_code(q), gammas, rotary_base,
+                           pos_offset, eps)
+    L = lib()
+    need = L.retention_chunkwise_varlen_workspace_bytes(ctypes.byref(desc), int(chunk))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(L.retention_chunkwise_varlen_fwd(ctypes.byref(desc), int(chunk), _ptr(cu_seqlens), int(total), _ptr(q),
+                                            _ptr(k), _ptr(v), _ptr(g), _ptr(out), _ptr(state_in), _ptr(state_out),
+                                            _ptr(workspace), ws_bytes, _stream(q)))
+    del keep
+    return out
+
+
+def chunkwise_varlen_workspace_bytes(batch, max_seqlen, heads, d, dtype, chunk, rotary_base=0.0):
+    """Workspace bytes of chunkwise_varlen_fwd for `batch` sequences of at
+    most max_seqlen tokens (dtype: torch.bfloat16 or torch.float32)."""
+    code = RET_BF16 if dtype == torch.bfloat16 else RET_F32
+    desc, keep = make_desc(batch, max_seqlen, heads, d, d, code, rotary_base=rotary_base)
+    return lib().retention_chunkwise_varlen_workspace_bytes(ctypes.byref(desc), int(chunk))
 
 
 def recurrent_step(q, k, v, state, g=None, *, gammas=None, rotary_base=0.0, pos=0, eps=1e-5, out=None,

@@ -89,7 +89,10 @@ size_t rot_bytes(const ret_desc_t* d) {
 // Launch the table and key rotation passes when rotation is on: k is replaced
 // by its rotated copy in the workspace and *table is set for the retention
 // kernel, which turns q as it loads it (null when rotation is off).
-bool rotate_inputs(const ret_desc_t* d, const void*& k, const float2** table, void* workspace, hipStream_t stream) {
+// Packed sequences (cu set): k holds `total` rows, sequence b the rows
+// cu[b] .. cu[b+1]-1, each token turned by its position in its sequence.
+bool rotate_inputs(const ret_desc_t* d, const void*& k, const float2** table, void* workspace, hipStream_t stream,
+                   const int32_t* cu = nullptr, int total = 0) {
   *table = nullptr;
   if (d->rotary_base == 0.0) return true;
   char* ws = static_cast<char*>(workspace);
@@ -97,8 +100,11 @@ bool rotate_inputs(const ret_desc_t* d, const void*& k, const float2** table, vo
   char* kr = ws + align_up((size_t)d->seqlen * (d->dk / 2) * sizeof(float2));
   if (ret::launch_rotary_table(tab, d->seqlen, d->dk, d->rotary_base, d->pos_offset, stream) != hipSuccess)
     return false;
-  if (ret::launch_rotate_keys(k, kr, tab, d->batch, d->seqlen, d->heads, d->dk, d->dtype, stream) != hipSuccess)
-    return false;
+  const hipError_t e =
+      cu ? ret::launch_rotate_keys_packed(k, kr, tab, cu, d->batch, total, d->seqlen, d->heads, d->dk, d->dtype,
+                                          stream)
+         : ret::launch_rotate_keys(k, kr, tab, d->batch, d->seqlen, d->heads, d->dk, d->dtype, stream);
+  if (e != hipSuccess) return false;
   k = kr;
   *table = tab;
   return true;
@@ -493,6 +499,57 @@ ret_status_t retention_chunkwise_fwd(const ret_desc_t* desc, int32_t chunk, cons
                                      hipStream_t stream) {
   return retention_chunkwise_fwd_timed(desc, chunk, q, k, v, g, o, state_in, state_out, workspace, workspace_bytes,
                                        stream, nullptr, nullptr);
+}
+
+size_t retention_chunkwise_varlen_workspace_bytes(const ret_desc_t* desc, int32_t chunk) {
+  if (check_desc(desc) != RET_OK || chunk < 1) return 0;
+  return retention_chunkwise_workspace_bytes(desc, chunk) +
+         align_up(ret::chunkwise_sched_bytes(make_shape(desc), eff_chunk(desc, chunk)));
+}
+
+ret_status_t retention_chunkwise_varlen_fwd(const ret_desc_t* desc, int32_t chunk, const int32_t* cu_seqlens,
+                                            int64_t total_tokens, const void* q, const void* k, const void* v,
+                                            const void* g, void* o, const float* state_in, float* state_out,
+                                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  ret_status_t st = check_desc(desc);
+  if (st != RET_OK) return st;
+  if (chunk < 1) return RET_ERR_SHAPE;
+  if (total_tokens < 0 || total_tokens > (int64_t)desc->batch * desc->seqlen) return RET_ERR_SHAPE;
+  if (!cu_seqlens || !q || !k || !v || !o) return RET_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0) return RET_ERR_ALIGN;
+  const void* tens[] = {q, k, v, g, o, state_in, state_out};
+  for (const void* t : tens)
+    if (t && !aligned16(t)) return RET_ERR_ALIGN;
+  const size_t n = (size_t)total_tokens * desc->heads * desc->dk * elem_size(desc->dtype);
+  const size_t ns = (size_t)desc->batch * desc->heads * desc->dk * desc->dv * 4;
+  const size_t cb = ((size_t)desc->batch + 1) * sizeof(int32_t);
+  if (overlaps(o, n, q, n) || overlaps(o, n, k, n) || overlaps(o, n, v, n) || overlaps(o, n, g, n) ||
+      overlaps(o, n, state_in, ns) || overlaps(o, n, state_out, ns) || overlaps(o, n, cu_seqlens, cb) ||
+      overlaps(state_out, ns, cu_seqlens, cb))
+    return RET_ERR_ALIAS;
+  if ((st = check_eps(desc, g)) != RET_OK) return st;
+  const Shape s = make_shape(desc);
+  const int32_t c = eff_chunk(desc, chunk);
+  const size_t rb = rot_bytes(desc), kb = ctrl_bytes(desc, chunk), hb = chain_bytes(desc);
+  const size_t sb = snap_bytes(desc, chunk);
+  const size_t need = kb + rb + hb + sb + align_up(ret::chunkwise_sched_bytes(s, c));
+  if (!workspace || workspace_bytes < need) return RET_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return RET_ERR_ALIGN;
+  const void* ins[] = {q, k, v, g, o, state_in, state_out, cu_seqlens};
+  const size_t in_n[] = {n, n, n, n, n, ns, ns, cb};
+  for (int j = 0; j < 8; ++j)
+    if (overlaps(workspace, need, ins[j], in_n[j])) return RET_ERR_ALIAS;
+
+  char* ws = static_cast<char*>(workspace);
+  int* ctrl = reinterpret_cast<int*>(ws);
+  const float2* table;
+  if (!rotate_inputs(desc, k, &table, ws + kb, stream, cu_seqlens, (int)total_tokens)) return RET_ERR_HIP;
+  if (ret::launch_retention_fwd(s, c, true, q, k, v, g, o, state_in, state_out, ws + kb + rb + hb,
+                                reinterpret_cast<float*>(ws + kb + rb), ctrl, table, desc->gn_eps, stream, nullptr,
+                                nullptr, false, false, nullptr, cu_seqlens, (int)total_tokens,
+                                ws + kb + rb + hb + sb) != hipSuccess)
+    return RET_ERR_HIP;
+  return RET_OK;
 }
 
 ret_status_t retention_recurrent_step(const ret_desc_t* desc, const void* q, const void* k, const void* v,

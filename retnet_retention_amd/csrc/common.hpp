@@ -174,6 +174,22 @@ __device__ __forceinline__ void bare_barrier() { __asm__ volatile("s_barrier" ::
 // a wave-uniform int held in a scalar register
 __device__ __forceinline__ int uniform_i(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// Rows of sequence b in a packed (varlen) tensor whose sequence boundaries
+// are cu[0..batch]: first row tok0 and length len, clamped into the tensor's
+// `total` rows and to at most `maxlen` tokens. b must be wave-uniform; the
+// results are. Returns false when a clamp changed the boundaries (the caller
+// reports it), so every access stays inside the tensor for any cu.
+__device__ __forceinline__ bool clamp_span(int a, int e, int total, int maxlen, int& tok0, int& len) {
+  const int a2 = min(max(a, 0), total);
+  const int e2 = min(max(e, a2), total);
+  tok0 = a2;
+  len = min(e2 - a2, maxlen);
+  return a2 == a && e2 == e && e2 - a2 <= maxlen;
+}
+__device__ __forceinline__ bool packed_span(const int* cu, int b, int total, int maxlen, int& tok0, int& len) {
+  return clamp_span(uniform_i(cu[b]), uniform_i(cu[b + 1]), total, maxlen, tok0, len);
+}
+
 // a wave-uniform float held in a scalar register
 __device__ __forceinline__ float uniform_f(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));

@@ -27,12 +27,20 @@ hipError_t launch_rotary_table(float2* table, int seqlen, int d, double base, in
 // order reversed; kr may be null when only that copy is wanted.
 hipError_t launch_rotate_keys(const void* k, void* kr, const float2* table, int batch, int seqlen, int heads, int d,
                               int dtype, hipStream_t stream, void* krev = nullptr);
+// The same rotation for packed sequences: sequence b holds rows cu[b] ..
+// cu[b+1]-1 of `total` (clamped as the chunkwise kernel clamps them), token n
+// of a sequence turns by the table's row n; at most maxlen tokens each.
+hipError_t launch_rotate_keys_packed(const void* k, void* kr, const float2* table, const int* cu, int batch,
+                                     int total, int maxlen, int heads, int d, int dtype, hipStream_t stream);
 
 // Parallel form (chunked == false: chunk == seqlen, no state) or chunkwise
 // form (chunked == true) in one launch. Chunkwise needs: snap [BH][nchunks]
 // [d][d] of the input dtype, chain [BH][2][d][d] fp32 and a control block of
 // chunkwise_ctrl_bytes() ints, all device memory owned by the caller.
 size_t chunkwise_ctrl_bytes(int batch, int heads, int nchunks);
+// Schedule buffer of a packed (varlen) chunkwise launch: one 16-byte entry
+// per workgroup of the grid (s.seqlen bounds every sequence's length).
+size_t chunkwise_sched_bytes(const Shape& s, int chunk);
 // `rot` (may be null): the cos/sin table of launch_rotary_table, with which
 // the kernels turn q as they load it (k must then arrive rotated). For the
 // backward's products: `q_rev` reads q
@@ -44,7 +52,8 @@ hipError_t launch_retention_fwd(const Shape& s, int chunk, bool chunked, const v
                                 const void* g, void* o, const float* state_in, float* state_out, void* snap,
                                 float* chain, int* ctrl, const float2* rot, float eps, hipStream_t stream,
                                 hipEvent_t before = nullptr, hipEvent_t after = nullptr, bool q_rev = false,
-                                bool out_rev = false, const float2* out_rot = nullptr);
+                                bool out_rev = false, const float2* out_rot = nullptr, const int* cu = nullptr,
+                                int total = 0, void* sched = nullptr);
 
 // Backward passes of the parallel form (all tensors [batch][seqlen][heads][d]
 // of the descriptor's dtype): the gradient through the swish gate and the

@@ -154,6 +154,15 @@ struct FwdParams {
   // out_rot's angles of the stored position (null: as computed)
   int q_rev, out_rev;
   const float2* out_rot;
+  // packed sequences of different lengths (chunkwise form only): sequence b
+  // holds rows cu[b] .. cu[b+1]-1 of `total`, seqlen bounds every length;
+  // null: batch sequences of seqlen tokens each
+  const int* cu;
+  int total;
+  // their schedule: per ticket class, the (chunk, pair, role) of every
+  // workgroup with work in ticket order, then entries with chunk -1
+  const int4* sched;
+  int per_class;
   int batch, seqlen, heads, chunk, nchunks, qblocks;
   int has_state0, xcd_order;
   float eps;
@@ -224,6 +233,21 @@ __device__ __forceinline__ u32x2 load2_coherent(__amdgpu_buffer_rsrc_t rs, uint3
   return __builtin_amdgcn_raw_buffer_load_b64(rs, voff, soff, kSc1 | (int)0x80000000u);
 }
 
+// First row and length of sequence b: b * seqlen and seqlen for a batch of
+// equal lengths; packed sequences take theirs from cu, clamped into the
+// tensor, and a clamp sets bit 2 of the error word (the output is then not
+// valid).
+__device__ __forceinline__ int seq_rows(const FwdParams& p, int b, int64_t& tok0) {
+  if (!p.cu) {
+    tok0 = (int64_t)b * p.seqlen;
+    return p.seqlen;
+  }
+  int t0, len;
+  if (!packed_span(p.cu, b, p.total, p.seqlen, t0, len) && threadIdx.x == 0) atomicOr(p.ctrl + 1, 2);
+  tok0 = t0;
+  return len;
+}
+
 // ---------------------------------------------------------------------------
 // Output role.
 // ---------------------------------------------------------------------------
@@ -245,15 +269,17 @@ __device__ __forceinline__ void out_role(const FwdParams& p, int bh, int ci, int
   // integer division runs on the vector unit: bring the uniform results back
   // to scalar registers
   const int h = uniform_i(bh % p.heads), b = uniform_i(bh / p.heads);
+  int64_t tok0;
+  const int len = seq_rows(p, b, tok0);
   const int c0 = ci * p.chunk;
-  const int cend = min(c0 + p.chunk, p.seqlen);
+  const int cend = min(c0 + p.chunk, len);
   const int q0 = c0 + qb * C::BM;
   if (q0 >= cend) return;  // uniform for the whole workgroup
 
   const float lg = p.log2g[h];
   const int ref = chunked ? c0 - 1 : q0 - 1;  // reference row of the fast path
   const int64_t tstride = (int64_t)p.heads * D;  // elements between tokens
-  const int64_t head0 = ((int64_t)b * p.seqlen * p.heads + h) * D;
+  const int64_t head0 = (tok0 * p.heads + h) * D;
   const T* Q = reinterpret_cast<const T*>(p.q) + head0;
   const T* K = reinterpret_cast<const T*>(p.k) + head0;
   const T* V = reinterpret_cast<const T*>(p.v) + head0;
@@ -617,12 +643,18 @@ __device__ __forceinline__ void state_role(const FwdParams& p, int bh, int ci, i
   // integer division runs on the vector unit: bring the uniform results back
   // to scalar registers
   const int h = uniform_i(bh % p.heads), b = uniform_i(bh / p.heads);
+  int64_t tok0;
+  const int len = seq_rows(p, b, tok0);
+  // chunks of this sequence (an empty one still carries state_in to state_out
+  // in its chunk 0); the workgroups of the chunks past them have no work
+  const int nch = len > 0 ? (len + p.chunk - 1) / p.chunk : 1;
+  if (ci >= nch) return;
   const float lg = p.log2g[h];
   const int c0 = ci * p.chunk;
-  const int cend = min(c0 + p.chunk, p.seqlen);
+  const int cend = min(c0 + p.chunk, len);
   const int nkb = (cend - c0 + SC::BK - 1) / SC::BK;
   const int64_t tstride = (int64_t)p.heads * D;
-  const int64_t head0 = ((int64_t)b * p.seqlen * p.heads + h) * D;
+  const int64_t head0 = (tok0 * p.heads + h) * D;
   const int dk0 = part * SC::ROWS;
   const T* K = reinterpret_cast<const T*>(p.k) + head0 + dk0;
   const T* V = reinterpret_cast<const T*>(p.v) + head0;
@@ -836,7 +868,7 @@ __device__ __forceinline__ void state_role(const FwdParams& p, int bh, int ci, i
       }
     }
   }
-  if (ci + 1 < p.nchunks) {
+  if (ci + 1 < nch) {
     // the next state workgroup needs only the chain: release it first
     if (active) {
       const __amdgpu_buffer_rsrc_t rs = chain_rsrc(ci & 1);
@@ -914,7 +946,15 @@ __global__ __launch_bounds__(kWaves<T> * 64, 1) void retention_chunkwise_kernel(
   __syncthreads();
   const int t = __builtin_amdgcn_readfirstlane(s_ticket);  // uniform: scalar registers for all it derives
   int ci, bh, role;  // role slot inside the chunk (see below)
-  if (p.xcd_order) {
+  if (p.sched) {
+    // packed sequences: the schedule skips the chunks past each sequence's
+    // end, so the workgroups without work come last
+    const int4 e = p.sched[(int64_t)cls * p.per_class + t];
+    ci = uniform_i(e.x);
+    if (ci < 0) return;
+    bh = e.y;
+    role = e.z;
+  } else if (p.xcd_order) {
     // Class c owns the (sequence, head) pairs bh = 8j + c and takes them
     // chunk-major, role-major: every dependency stays inside the class, and
     // the workgroups of one chunk share an XCD and its L2 when the class is
@@ -935,15 +975,92 @@ __global__ __launch_bounds__(kWaves<T> * 64, 1) void retention_chunkwise_kernel(
   role = uniform_i(role);
   // role order inside a chunk: the longest query block first (it pulls the
   // chunk's K and V from HBM while the state workgroups follow into L2), the
-  // state parts, then the other query blocks
-  const int qb = role == 0 ? p.qblocks - 1 : role <= SPLIT ? -1 : p.qblocks - 1 - (role - SPLIT);
+  // state parts, then the other query blocks. Every wait must be for a
+  // workgroup with an earlier ticket, which is already running, so that no
+  // number of waiting workgroups can fill the chip: in chunk 0 with a
+  // carried-in state, whose output workgroups wait for the state parts to
+  // publish R_{-1}, the state parts come first.
+  const bool state_first = ci == 0 && p.has_state0;
+  const int qb = state_first ? (role < SPLIT ? -1 : p.qblocks - 1 - (role - SPLIT))
+                             : (role == 0 ? p.qblocks - 1 : role <= SPLIT ? -1 : p.qblocks - 1 - (role - SPLIT));
   if (qb < 0)
-    state_role<T, D>(p, bh, ci, role - 1, l0, l1, l2, l3);
+    state_role<T, D>(p, bh, ci, state_first ? role : role - 1, l0, l1, l2, l3);
   else if (ci > 0 || p.has_state0)
     out_role<T, D, FAST, true, XF>(p, bh, ci, qb, true, l0, l1, l2, l3);
   else
     out_role<T, D, FAST, false, XF>(p, bh, ci, qb, true, l0, l1, l2, l3);
 #endif
+}
+
+// Schedule of a packed batch, one workgroup per ticket class (8 with the
+// XCD classes, else 1). Each sequence's chunks are spread evenly over the
+// launch's nc slots: with n chunks, chunk ci sits in slot
+// floor((2 ci + 1) nc / (2 n)), one slot apart for the longest sequences,
+// further apart for shorter ones. So the longest chains of chunks, which set
+// the critical path, advance from the first tickets on while the other
+// sequences' chunks fill the chip beside them, instead of all sequences
+// crowding the first slots and the longest chain running alone at the end.
+// Slots go in order; inside a slot the entries keep the equal-length
+// mapping's order (role-major over the class's pairs, or pair-major over all
+// pairs), and the rest of the class's share of the grid gets chunk -1. Every
+// wait stays on an earlier ticket: a chunk's predecessor sits in an earlier
+// slot (nc / n >= 1), and inside chunk 0 the roles keep their order.
+__global__ __launch_bounds__(256) void varlen_schedule_kernel(FwdParams p, int4* sched, int roles) {
+  __shared__ int s_part[4];
+  const int cls = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int bhs = p.batch * p.heads;
+  const int npairs = p.xcd_order ? bhs / 8 : bhs;
+  int4* out = sched + (int64_t)cls * p.per_class;
+  // chunk of pair j in slot s (negative: none)
+  auto chunk_in = [&](int j, int s) {
+    const int bh = p.xcd_order ? j * 8 + cls : j;
+    const int b = bh / p.heads;
+    int tok0, len;
+    clamp_span(p.cu[b], p.cu[b + 1], p.total, p.seqlen, tok0, len);
+    const int n = len > 0 ? (len + p.chunk - 1) / p.chunk : 1;
+    // the smallest ci with (2 ci + 1) nc >= 2 n s, if it is in slot s
+    const int64_t nc = p.nchunks, num = 2 * (int64_t)n * s - nc;
+    const int ci = num <= 0 ? 0 : (int)((num + 2 * nc - 1) / (2 * nc));
+    return ci < n && (2 * (int64_t)ci + 1) * nc < 2 * (int64_t)n * (s + 1) ? ci : -1;
+  };
+  // block-wide sum of one int per thread
+  auto block_sum = [&](int x) {
+    x = (int)sum64((float)x);  // exact: at most 64 x 256 per wave
+    __syncthreads();
+    if (lane == 0) s_part[wave] = x;
+    __syncthreads();
+    return s_part[0] + s_part[1] + s_part[2] + s_part[3];
+  };
+  int base = 0;
+  for (int sl = 0; sl < p.nchunks; ++sl) {
+    int c = 0;
+    for (int j = tid; j < npairs; j += 256) c += chunk_in(j, sl) >= 0 ? 1 : 0;
+    const int count = block_sum(c);
+    if (count == 0) continue;
+    int rank0 = 0;  // pairs with work before this tile
+    for (int j0 = 0; j0 < npairs; j0 += 256) {
+      const int j = j0 + tid;
+      const int ci = j < npairs ? chunk_in(j, sl) : -1;
+      const bool real = ci >= 0;
+      const uint64_t m = __ballot(real);
+      const int below = __builtin_popcountll(m & ((uint64_t(1) << lane) - 1));
+      __syncthreads();
+      if (lane == 0) s_part[wave] = __builtin_popcountll(m);
+      __syncthreads();
+      int rank = rank0 + below;
+      for (int w = 0; w < wave; ++w) rank += s_part[w];
+      if (real) {
+        const int bh = p.xcd_order ? j * 8 + cls : j;
+        for (int r = 0; r < roles; ++r) {
+          const int pos = p.xcd_order ? base + r * count + rank : base + rank * roles + r;
+          out[pos] = make_int4(ci, bh, r, 0);
+        }
+      }
+      rank0 += s_part[0] + s_part[1] + s_part[2] + s_part[3];
+    }
+    base += count * roles;
+  }
+  for (int i = base + tid; i < p.per_class; i += 256) out[i] = make_int4(-1, 0, 0, 0);
 }
 
 __global__ void reset_ctrl_kernel(int* ctrl, int n) {
@@ -969,8 +1086,15 @@ static hipError_t launch_fwd_impl(const Shape& s, int chunk, FwdParams p, bool c
   hipLaunchKernelGGL(reset_ctrl_kernel, dim3((unsigned)((nctrl + 255) / 256 < 1024 ? (nctrl + 255) / 256 : 1024)),
                      dim3(256), 0, stream, p.ctrl, (int)nctrl);
   p.xcd_order = bhs % 8 == 0;
-  const int64_t blocks = (int64_t)p.nchunks * bhs * (StTile<T, D>::SPLIT + p.qblocks);
+  const int roles = StTile<T, D>::SPLIT + p.qblocks;
+  const int64_t blocks = (int64_t)p.nchunks * bhs * roles;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  if (p.cu) {
+    const int classes = p.xcd_order ? 8 : 1;
+    p.per_class = (int)(blocks / classes);
+    hipLaunchKernelGGL(varlen_schedule_kernel, dim3(classes), dim3(256), 0, stream, p, const_cast<int4*>(p.sched),
+                       roles);
+  }
   if (before && hipEventRecord(before, stream) != hipSuccess) return hipErrorInvalidValue;
   if (p.q_rev || p.out_rev || p.out_rot)
     hipLaunchKernelGGL((retention_chunkwise_kernel<T, D, FAST, true>), dim3((unsigned)blocks), dim3(64 * C::WAVES), 0,
@@ -996,6 +1120,18 @@ static hipError_t launch_fwd_t(const Shape& s, int chunk, FwdParams p, bool chun
               : launch_fwd_impl<T, D, false>(s, chunk, p, chunked, stream, before, after);
 }
 
+size_t chunkwise_sched_bytes(const Shape& s, int chunk) {
+  const int nchunks = (s.seqlen + chunk - 1) / chunk;
+  const int bm = s.dtype == 1 ? OutTile<bf16, 64, true>::BM : OutTile<float, 64, true>::BM;
+  int split = 1;
+  if (s.dtype == 1)
+    split = s.d == 256 ? StTile<bf16, 256>::SPLIT : s.d == 128 ? StTile<bf16, 128>::SPLIT : StTile<bf16, 64>::SPLIT;
+  else
+    split = s.d == 256 ? StTile<float, 256>::SPLIT : s.d == 128 ? StTile<float, 128>::SPLIT : StTile<float, 64>::SPLIT;
+  const size_t roles = (size_t)split + (chunk + bm - 1) / bm;
+  return (size_t)nchunks * s.batch * s.heads * roles * sizeof(int4);
+}
+
 size_t chunkwise_ctrl_bytes(int batch, int heads, int nchunks) {
   return ((size_t)kCtrlHead + (size_t)batch * heads * (nchunks + 1) * kFlagsPerChunk) * sizeof(int);
 }
@@ -1004,9 +1140,15 @@ hipError_t launch_retention_fwd(const Shape& s, int chunk, bool chunked, const v
                                 const void* g, void* o, const float* state_in, float* state_out, void* snap,
                                 float* chain, int* ctrl, const float2* rot, float eps, hipStream_t stream,
                                 hipEvent_t before, hipEvent_t after, bool q_rev, bool out_rev,
-                                const float2* out_rot) {
+                                const float2* out_rot, const int* cu, int total, void* sched) {
   if (rot && q_rev) return hipErrorInvalidValue;  // q's angles are those of its own positions
+  // packed sequences: chunkwise form, forward only, with a schedule buffer
+  if (cu && (!chunked || q_rev || out_rev || out_rot || !sched)) return hipErrorInvalidValue;
   FwdParams p;
+  p.cu = cu;
+  p.total = total;
+  p.sched = cu ? static_cast<const int4*>(sched) : nullptr;
+  p.per_class = 0;
   p.rot = rot;
   p.q_rev = q_rev;
   p.out_rev = out_rev;

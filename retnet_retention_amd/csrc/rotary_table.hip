@@ -56,6 +56,42 @@ __global__ __launch_bounds__(256) void rotate_keys_kernel(const T* __restrict__ 
   }
 }
 
+// Packed sequences: blocks of one sequence each (per_seq blocks per
+// sequence), thread = one 8-element chunk of the sequence's rows.
+template <typename T>
+__global__ __launch_bounds__(256) void rotate_keys_packed_kernel(const T* __restrict__ k, T* __restrict__ kr,
+                                                                 const float2* __restrict__ table,
+                                                                 const int* __restrict__ cu, int per_seq, int total,
+                                                                 int maxlen, int heads, int d) {
+  const int b = uniform_i((int)(blockIdx.x / per_seq));
+  int tok0, len;
+  packed_span(cu, b, total, maxlen, tok0, len);  // a clamp is reported by the chunkwise kernel
+  const int cpr = d / 8;  // chunks per head vector
+  const int64_t idx = (int64_t)(blockIdx.x % per_seq) * 256 + threadIdx.x;
+  if (idx >= (int64_t)len * heads * cpr) return;
+  const int n = (int)(idx / ((int64_t)heads * cpr));
+  const int c8 = (int)(idx % cpr);
+  const CS4 cs = ld_cs4(table + (int64_t)n * (d / 2) + c8 * 4);
+  const int64_t off = ((int64_t)tok0 * heads * cpr + idx) * 8;
+  F8 y = unpack8(ld_raw8(k + off));
+  rotate4(y, cs);
+  store8(kr + off, y);
+}
+
+hipError_t launch_rotate_keys_packed(const void* k, void* kr, const float2* table, const int* cu, int batch,
+                                     int total, int maxlen, int heads, int d, int dtype, hipStream_t stream) {
+  const int64_t per = ((int64_t)maxlen * heads * (d / 8) + 255) / 256;
+  if (per < 1 || per * batch > 0x7fffffff) return hipErrorInvalidConfiguration;
+  const unsigned blocks = (unsigned)(per * batch);
+  if (dtype == 1)
+    hipLaunchKernelGGL(rotate_keys_packed_kernel<bf16>, dim3(blocks), dim3(256), 0, stream, (const bf16*)k,
+                       (bf16*)kr, table, cu, (int)per, total, maxlen, heads, d);
+  else
+    hipLaunchKernelGGL(rotate_keys_packed_kernel<float>, dim3(blocks), dim3(256), 0, stream, (const float*)k,
+                       (float*)kr, table, cu, (int)per, total, maxlen, heads, d);
+  return hipGetLastError();
+}
+
 hipError_t launch_rotate_keys(const void* k, void* kr, const float2* table, int batch, int seqlen, int heads, int d,
                               int dtype, hipStream_t stream, void* krev) {
   const int64_t chunks = (int64_t)batch * seqlen * heads * (d / 8);

@@ -217,3 +217,39 @@ def test_stateful_backward_validates(L):
     d2, _ = _desc(batch=1, seqlen=16, heads=2, dk=64, dv=64, gammas=[0.5, 2.0 ** -70])
     assert bwd(ctypes.byref(d2), 8, a[0], a[1], a[2], None, a[3], a[9], a[10], a[4], a[5], a[6], None, a[7], a[8],
                need, None) == 4
+
+
+def _declared_param_counts():
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    counts = {}
+    for name, params in re.findall(r"\b(retention_\w+)\s*\(([^)]*)\)\s*;", text):
+        params = params.strip()
+        counts[name] = 0 if params in ("", "void") else params.count(",") + 1
+    return counts
+
+
+def test_binding_argtypes_match_the_header(L):
+    """Every ctypes prototype has as many arguments as the C declaration."""
+    counts = _declared_param_counts()
+    assert sorted(counts) == sorted(binding.EXPORTS)
+    for name, n in counts.items():
+        assert len(getattr(L, name).argtypes) == n, name
+
+
+def test_varlen_validates(L):
+    d, keep = _desc(batch=3, seqlen=100)
+    cu = ALIGNED * 9
+
+    def call(d=d, chunk=64, cu=cu, total=250, q=ALIGNED, o=ALIGNED * 4, ws=ALIGNED * 8, wsb=1 << 40):
+        return L.retention_chunkwise_varlen_fwd(ctypes.byref(d), chunk, cu, total, q, ALIGNED * 2, ALIGNED * 3,
+                                                None, o, None, None, ws, wsb, None)
+
+    assert call(total=301) == 2  # more rows than batch * seqlen
+    assert call(total=-1) == 2
+    assert call(chunk=0) == 2
+    assert call(cu=None) == 1
+    assert call(q=None) == 1
+    assert call(cu=ALIGNED * 9 + 2) == 5
+    assert call(o=ALIGNED + 16) == 8  # out overlaps q
+    assert call(wsb=16) == 6
+    assert call(ws=None) == 6

@@ -122,6 +122,27 @@ def test_state_in_out_alias():
     assert_close(to64(st), ref_s, "bf16", "state")
 
 
+# --- many (sequence, head) pairs with a carried-in state --------------------
+def test_many_pairs_with_carried_state():
+    """1024 pairs, far more than the chip holds workgroups of this kernel at
+    once, with a carried-in state: chunk 0's output workgroups wait for their
+    state parts, which must not queue behind them. The control word stays
+    clear (no wait gave up) and the results match."""
+    b, n, h, d, chunk = 64, 77, 16, 64, 64
+    _announce(case="many pairs with state", b=b, n=n, h=h, d=d, chunk=chunk)
+    q, k, v, g, s0 = make_inputs(83, b, n, h, d, "bf16", 1 / 16, 1.0, True)
+    ref, ref_s = oracle_run("chunkwise", q, k, v, g, chunk=chunk, state_in=s0)
+    tq, tv = q.torch(DEV), v.torch(DEV)
+    ws = torch.empty(rr.chunkwise_workspace_bytes(tq, tv, chunk), dtype=torch.uint8, device=DEV)
+    st = torch.empty((b, h, d, d), device=DEV)
+    out = rr.chunkwise_fwd(tq, k.torch(DEV), tv, g.torch(DEV), chunk=chunk,
+                           state_in=torch.from_numpy(s0.astype(np.float32)).to(DEV), state_out=st, workspace=ws)
+    torch.cuda.synchronize()
+    assert int(ws[4:8].view(torch.int32).item()) == 0
+    assert_close(to64(out), ref, "bf16", "out")
+    assert_close(to64(st), ref_s, "bf16", "state")
+
+
 # --- prefill, then decode steps: the state is the checkpoint ---------------
 def test_decode_after_prefill_matches_longer_prefill():
     _announce(case="prefill+decode")

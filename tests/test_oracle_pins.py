@@ -316,3 +316,42 @@ def test_score_map_pins():
     dots = np.abs(np.einsum("hd,hd->h", q1[0, 0], k1[0, 0]))
     for m in range(n):
         assert np.isclose(w1[0, m], np.sum(gam ** (n - 1 - m) * dots), rtol=1e-14)
+
+
+def test_varlen_pins():
+    """Packed sequences of different lengths: each slice against the brute
+    force sum (integer inputs, dyadic decays: exact), an empty sequence
+    passes its state through, positions restart at each sequence, and equal
+    lengths reproduce the batched layout."""
+    rng = np.random.default_rng(33)
+    h, d = 2, 3
+    lens = [4, 0, 1, 6]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    tot = int(cu[-1])
+    q, k, v = (rng.integers(-3, 4, size=(tot, h, d)).astype(np.float64) for _ in range(3))
+    s0 = rng.integers(-3, 4, size=(len(lens), h, d, d)).astype(np.float64)
+    gammas = np.array([0.5, 0.75])
+    for form, chunk in (("chunkwise", 4), ("recurrent", None), ("parallel", None)):
+        out, st = oracle.retention_varlen(form, q, k, v, cu, gammas=gammas, chunk=chunk,
+                                          state_in=None if form == "parallel" else s0)
+        for b in range(len(lens)):
+            a, e = cu[b], cu[b + 1]
+            if e > a:
+                s_b = None if form == "parallel" else s0[b:b + 1]
+                want = _brute(q[None, a:e], k[None, a:e], v[None, a:e], gammas,
+                              s_b if s_b is not None else np.zeros((1, h, d, d)))
+                assert np.array_equal(out[None, a:e], want), (form, b)
+        if form != "parallel":
+            assert np.array_equal(st[1], s0[1])  # the empty sequence
+    # rotation positions count from each sequence's first token
+    qf, kf, vf = (rng.standard_normal((tot, h, d + 1)) for _ in range(3))
+    out, _ = oracle.retention_varlen("chunkwise", qf, kf, vf, cu, rotary_base=50.0, pos_offset=2, chunk=3)
+    alone, _ = oracle.retention("chunkwise", qf[None, 5:11], kf[None, 5:11], vf[None, 5:11], rotary_base=50.0,
+                                pos_offset=2, chunk=3)
+    assert np.allclose(out[5:11], alone[0], rtol=0, atol=1e-14)
+    # equal lengths: the packed layout of a batch
+    qb, kb, vb, gb = (rng.standard_normal((2, 5, h, 4)) for _ in range(4))
+    ref, ref_s = oracle.retention("chunkwise", qb, kb, vb, g=gb, rotary_base=10.0, chunk=2)
+    out, st = oracle.retention_varlen("chunkwise", *(x.reshape(10, h, 4) for x in (qb, kb, vb)), [0, 5, 10],
+                                      g=gb.reshape(10, h, 4), rotary_base=10.0, chunk=2)
+    assert np.array_equal(out, ref.reshape(10, h, 4)) and np.array_equal(st, ref_s)
