@@ -546,6 +546,7 @@ STATS_ARGS = {
     "parallel": ["--only", "parallel"],
     "parallel_bwd": ["--only", "parallel_bwd"],
     "chunkwise_bwd": ["--only", "chunkwise_bwd"],
+    "varlen": ["--only", "varlen"],
 }
 SQ_COUNTERS = ["SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "SQ_INSTS_LDS",
                "SQ_LDS_BANK_CONFLICT", "SQ_WAIT_INST_LDS", "SQ_INSTS_VALU", "GRBM_GUI_ACTIVE"]
@@ -610,7 +611,8 @@ def profile_stats(out, raw):
         line = [ln for ln in open(d + ".log") if ln.startswith("{")]
         stats = list(csv.DictReader(open(glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)[0])))
         name = {"chunkwise": "chunkwise_7b_8k", "decode": "decode_step_7b_b64", "parallel": "parallel_3b",
-                "parallel_bwd": "parallel_backward_3b", "chunkwise_bwd": "chunkwise_backward_7b_8k"}[leg]
+                "parallel_bwd": "parallel_backward_3b", "chunkwise_bwd": "chunkwise_backward_7b_8k",
+                "varlen": "chunkwise_varlen_ragged_16k"}[leg]
         with open(os.path.join(out, f"{name}_kernel_stats.txt"), "w") as f:
             f.write(f"rocprofv3 kernel statistics, {leg} leg of the benchmark\n")
             f.write("made by: python bench.py --profile stats --profile-out <out>\n")
