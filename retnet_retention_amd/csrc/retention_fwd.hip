@@ -992,8 +992,8 @@ __global__ __launch_bounds__(kWaves<T> * 64, 1) void retention_chunkwise_kernel(
 #endif
 }
 
-// Schedule of a packed batch, one workgroup per ticket class (8 with the
-// XCD classes, else 1). Each sequence's chunks are spread evenly over the
+// Schedule of a packed batch, one workgroup per slot and ticket class (8
+// classes with the XCD order, else 1). Each sequence's chunks are spread evenly over the
 // launch's nc slots: with n chunks, chunk ci sits in slot
 // floor((2 ci + 1) nc / (2 n)), one slot apart for the longest sequences,
 // further apart for shorter ones. So the longest chains of chunks, which set
@@ -1005,42 +1005,63 @@ __global__ __launch_bounds__(kWaves<T> * 64, 1) void retention_chunkwise_kernel(
 // pairs), and the rest of the class's share of the grid gets chunk -1. Every
 // wait stays on an earlier ticket: a chunk's predecessor sits in an earlier
 // slot (nc / n >= 1), and inside chunk 0 the roles keep their order.
-__global__ __launch_bounds__(256) void varlen_schedule_kernel(FwdParams p, int4* sched, int roles) {
+constexpr int kSchedCache = 8192;  // pairs whose chunk counts the schedule kernel keeps in LDS
+
+__global__ __launch_bounds__(256) void varlen_schedule_kernel(FwdParams p, int4* sched, int roles, int classes) {
   __shared__ int s_part[4];
-  const int cls = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ int s_nch[kSchedCache];
+  // one workgroup per (slot, class): the slots' entries are written in parallel
+  const int cls = blockIdx.x % classes, sl = blockIdx.x / classes;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int bhs = p.batch * p.heads;
   const int npairs = p.xcd_order ? bhs / 8 : bhs;
   int4* out = sched + (int64_t)cls * p.per_class;
-  // chunk of pair j in slot s (negative: none)
-  auto chunk_in = [&](int j, int s) {
+  // chunks of pair j's sequence
+  auto chunks_of = [&](int j) {
     const int bh = p.xcd_order ? j * 8 + cls : j;
     const int b = bh / p.heads;
     int tok0, len;
     clamp_span(p.cu[b], p.cu[b + 1], p.total, p.seqlen, tok0, len);
-    const int n = len > 0 ? (len + p.chunk - 1) / p.chunk : 1;
-    // the smallest ci with (2 ci + 1) nc >= 2 n s, if it is in slot s
-    const int64_t nc = p.nchunks, num = 2 * (int64_t)n * s - nc;
-    const int ci = num <= 0 ? 0 : (int)((num + 2 * nc - 1) / (2 * nc));
-    return ci < n && (2 * (int64_t)ci + 1) * nc < 2 * (int64_t)n * (s + 1) ? ci : -1;
+    return len > 0 ? (len + p.chunk - 1) / p.chunk : 1;
+  };
+  for (int j = tid; j < min(npairs, kSchedCache); j += 256) s_nch[j] = chunks_of(j);
+  __syncthreads();
+  auto nch_of = [&](int j) { return j < kSchedCache ? s_nch[j] : chunks_of(j); };
+  // of a pair with n chunks: the chunks in slots before sl, i.e. those with
+  // (2 ci + 1) nc < 2 n sl; that count is also the index of its first chunk
+  // at or after slot sl, which lies in sl when (2 ci + 1) nc < 2 n (sl + 1)
+  const int64_t nc = p.nchunks;
+  auto before = [&](int n) {
+    const int64_t num = 2 * (int64_t)n * sl - nc;
+    return num <= 0 ? 0 : (int)min((num + 2 * nc - 1) / (2 * nc), (int64_t)n);
+  };
+  auto chunk_here = [&](int n) {
+    const int ci = before(n);
+    return ci < n && (2 * (int64_t)ci + 1) * nc < 2 * (int64_t)n * (sl + 1) ? ci : -1;
   };
   // block-wide sum of one int per thread
   auto block_sum = [&](int x) {
-    x = (int)sum64((float)x);  // exact: at most 64 x 256 per wave
+    x = (int)sum64((float)x);  // exact: far below 2^24 per wave
     __syncthreads();
     if (lane == 0) s_part[wave] = x;
     __syncthreads();
     return s_part[0] + s_part[1] + s_part[2] + s_part[3];
   };
-  int base = 0;
-  for (int sl = 0; sl < p.nchunks; ++sl) {
-    int c = 0;
-    for (int j = tid; j < npairs; j += 256) c += chunk_in(j, sl) >= 0 ? 1 : 0;
-    const int count = block_sum(c);
-    if (count == 0) continue;
+  int cb = 0, cc = 0, ct = 0;  // this thread's pairs: chunks before the slot, in it, in all
+  for (int j = tid; j < npairs; j += 256) {
+    const int n = nch_of(j);
+    cb += before(n);
+    cc += chunk_here(n) >= 0 ? 1 : 0;
+    ct += n;
+  }
+  const int base = roles * block_sum(cb);
+  const int count = block_sum(cc);
+  const int total = roles * block_sum(ct);
+  if (count > 0) {
     int rank0 = 0;  // pairs with work before this tile
     for (int j0 = 0; j0 < npairs; j0 += 256) {
       const int j = j0 + tid;
-      const int ci = j < npairs ? chunk_in(j, sl) : -1;
+      const int ci = j < npairs ? chunk_here(nch_of(j)) : -1;
       const bool real = ci >= 0;
       const uint64_t m = __ballot(real);
       const int below = __builtin_popcountll(m & ((uint64_t(1) << lane) - 1));
@@ -1058,9 +1079,9 @@ __global__ __launch_bounds__(256) void varlen_schedule_kernel(FwdParams p, int4*
       }
       rank0 += s_part[0] + s_part[1] + s_part[2] + s_part[3];
     }
-    base += count * roles;
   }
-  for (int i = base + tid; i < p.per_class; i += 256) out[i] = make_int4(-1, 0, 0, 0);
+  // the class's entries past its last item, shared among its slots' workgroups
+  for (int i = total + sl * 256 + tid; i < p.per_class; i += 256 * p.nchunks) out[i] = make_int4(-1, 0, 0, 0);
 }
 
 __global__ void reset_ctrl_kernel(int* ctrl, int n) {
@@ -1092,8 +1113,8 @@ static hipError_t launch_fwd_impl(const Shape& s, int chunk, FwdParams p, bool c
   if (p.cu) {
     const int classes = p.xcd_order ? 8 : 1;
     p.per_class = (int)(blocks / classes);
-    hipLaunchKernelGGL(varlen_schedule_kernel, dim3(classes), dim3(256), 0, stream, p, const_cast<int4*>(p.sched),
-                       roles);
+    hipLaunchKernelGGL(varlen_schedule_kernel, dim3((unsigned)(classes * p.nchunks)), dim3(256), 0, stream, p,
+                       const_cast<int4*>(p.sched), roles, classes);
   }
   if (before && hipEventRecord(before, stream) != hipSuccess) return hipErrorInvalidValue;
   if (p.q_rev || p.out_rev || p.out_rot)
