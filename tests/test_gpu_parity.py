@@ -323,7 +323,8 @@ def test_step_inactive_slots():
 
 
 def test_graph_replay_matches_eager():
-    """A chunkwise prefill and a decode step captured into one HIP graph: every
+    """A chunkwise prefill, a decode step and a packed (varlen) prefill
+    captured into one HIP graph: every
     replay (with eager work and synchronizations in between) must give the
     eager results bit for bit (the control-block reset is a kernel, not a
     memset, and nothing in the calls allocates)."""
@@ -338,14 +339,26 @@ def test_graph_replay_matches_eager():
     step_out = torch.empty_like(sv)
     ws = torch.empty(rr.chunkwise_workspace_bytes(tq, tv, chunk, rotary_base=10000.0), dtype=torch.uint8,
                      device=DEV)
+    # the same tokens packed as three sequences of 300, 0 and 177 tokens
+    lens = (300, 0, 177)
+    cu = torch.tensor([0, 300, 300, 477], dtype=torch.int32, device=DEV)
+    pq, pk, pv, pg = (x.reshape(b * n, h, d)[:477].contiguous() for x in (tq, tk, tv, tg))
+    pout = torch.empty_like(pv)
+    pstate = torch.empty((len(lens), h, d, d), device=DEV)
+    pws = torch.empty(rr.chunkwise_varlen_workspace_bytes(len(lens), n, h, d, torch.bfloat16, chunk, 10000.0),
+                      dtype=torch.uint8, device=DEV)
 
     def work():
         rr.chunkwise_fwd(tq, tk, tv, tg, chunk=chunk, state_out=state, out=out, workspace=ws, rotary_base=10000.0)
         rr.recurrent_step(sq, sk, sv, state, sg, rotary_base=10000.0, pos=n, out=step_out)
+        rr.chunkwise_varlen_fwd(pq, pk, pv, cu, n, pg, chunk=chunk, state_out=pstate, out=pout, workspace=pws,
+                                rotary_base=10000.0)
 
     work()
     torch.cuda.synchronize()
-    ref = (out.clone(), state.clone(), step_out.clone())
+    ref = (out.clone(), state.clone(), step_out.clone(), pout.clone(), pstate.clone())
+    # the packed call's first sequence is the batched call's first sequence
+    assert torch.equal(pout[:300], out[0])
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -359,10 +372,13 @@ def test_graph_replay_matches_eager():
         out.zero_()
         state.fill_(7.0)
         step_out.zero_()
+        pout.zero_()
+        pstate.fill_(7.0)
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
-        for got, want, name in zip((out, state, step_out), ref, ("out", "state", "step")):
+        for got, want, name in zip((out, state, step_out, pout, pstate), ref,
+                                   ("out", "state", "step", "packed out", "packed state")):
             assert torch.equal(got, want), f"replay {rep}: {name}"
         rr.parallel_fwd(tq, tk, tv, tg)  # eager work between replays
         torch.cuda.synchronize()
