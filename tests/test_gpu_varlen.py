@@ -66,6 +66,10 @@ CASES = [
     ([200, 7], 256, 1, 256, 100, "f32", True, False, False),
     # 300 sequences x 8 heads: 300 pairs per ticket class, more than one tile of the schedule
     (list(np.random.default_rng(3).integers(0, 100, 300)), 100, 8, 64, 64, "f32", True, True, True),
+    # 40 short sequences at chunk 7: eight slots, most sequences spread over a few of them
+    (list(np.random.default_rng(4).integers(0, 50, 40)), 50, 2, 64, 7, "f32", False, False, True),
+    # 16 heads (two per ticket class and sequence), rotation, a carried state, chunk 64
+    ([130, 64, 0, 1, 200, 77, 5, 500], 512, 16, 128, 64, "bf16", True, True, True),
 ]
 
 
