@@ -120,3 +120,16 @@ def test_varlen_invalid_boundaries_are_clamped_and_reported():
     ref, _ = oracle.retention_varlen("chunkwise", q.f64[:100], k.f64[:100], v.f64[:100], [0, 100],
                                      g=g.f64[:100], chunk=chunk)
     assert_close(to64(out[:50]), ref[:50], "f32", "valid sequence")
+
+
+def test_varlen_bitwise_deterministic():
+    """Workgroups take their items from tickets in whatever order the chip
+    runs them, but each item's arithmetic is fixed: two calls agree bit for
+    bit."""
+    lens = [700, 3, 0, 512, 129]
+    _announce(lens=lens, case="determinism")
+    q, k, v, g, s0, cu = _packed(77, lens, 4, 256, "bf16", True, True)
+    a = _run(q, k, v, g, s0, cu, 700, 256, 10000.0, 0, B.RET_BF16)
+    b = _run(q, k, v, g, s0, cu, 700, 256, 10000.0, 0, B.RET_BF16)
+    assert a[2] == 0 and b[2] == 0
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
