@@ -501,6 +501,10 @@ ret_status_t retention_chunkwise_fwd(const ret_desc_t* desc, int32_t chunk, cons
                                        stream, nullptr, nullptr);
 }
 
+// Packed sequences of different lengths (prefill of a ragged batch): the
+// chunkwise form per sequence, the sequences' boundaries in a device array
+// the host never reads. Workspace: the chunkwise layout for batch sequences
+// of up to seqlen tokens, then the launch schedule.
 size_t retention_chunkwise_varlen_workspace_bytes(const ret_desc_t* desc, int32_t chunk) {
   if (check_desc(desc) != RET_OK || chunk < 1) return 0;
   return retention_chunkwise_workspace_bytes(desc, chunk) +
