@@ -180,17 +180,22 @@ def bench_chunkwise(steps, warmup, name="retention_7b_8k", cold_reps=0):
         rr.chunkwise_fwd(q, k, v, g, chunk=w.chunk, state_out=state, out=out, workspace=ws, rotary_base=rot,
                          kernel_events=events)
 
-    # every timed call also records a pair of events around the chunkwise
-    # kernel itself (after the control-block reset): the roofline's duration
+    # the step rate: `steps` plain back-to-back calls (reset + kernel)
     for _ in range(warmup):
         step()
+    ms, wall = time_calls(step, steps, 0)
+    # then as many calls that each also record a pair of events around the
+    # chunkwise kernel itself (after the control-block reset): the roofline's
+    # duration (the event records add a little gap between calls, so these
+    # calls do not time the step)
     pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for a, b in pairs:  # creates the underlying events
         a.record()
         b.record()
     torch.cuda.synchronize()
-    it = iter(pairs)
-    ms, wall = time_calls(lambda: step(next(it)), steps, 0)
+    for ev in pairs:
+        step(ev)
+    torch.cuda.synchronize()
     kus = [a.elapsed_time(b) * 1e3 for a, b in pairs]
     kernel_ms = sum(kus) / steps / 1e3
     cold = []
