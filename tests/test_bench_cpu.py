@@ -37,3 +37,21 @@ def test_roofline_bound_follows_the_ridge_point():
     r = bench.roofline_object(above, above["bytes"] / 500e-6 / 1e9, {"bytes": 123})
     assert r["bound"] == "mfma" and r["unit"] == "TFLOP/s" and r["hbm"]["unit"] == "GB/s"
     assert r["traffic"] == 123 and r["attainable_tflops"] == bench.PEAK_BF16_TFLOPS
+
+
+def test_packed_batch_leg_and_profile_names():
+    # the ragged batch holds the same 16384 tokens as 2 x 8192
+    assert sum(bench.VARLEN_LENS) == 16384 and max(bench.VARLEN_LENS) == 8192
+    # its flops are the chunkwise count summed per sequence: less than the
+    # two full sequences' (shorter chunks hold fewer causal pairs)
+    per_seq = sum(bench.chunkwise_flops(1, n, 16, 256, 256, 512) for n in bench.VARLEN_LENS)
+    assert 0 < per_seq < bench.chunkwise_flops(2, 8192, 16, 256, 256, 512)
+    # every kernel-statistics leg runs a benchmark leg that --only accepts
+    for leg, args in bench.STATS_ARGS.items():
+        assert args[:2] == ["--only", leg]
+
+
+def test_gpus_above_one_exits_with_a_message():
+    import subprocess
+    r = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0 and "one GPU" in (r.stdout + r.stderr)
