@@ -198,6 +198,7 @@ def bench_chunkwise(steps, warmup, name="retention_7b_8k", cold_reps=0):
     torch.cuda.synchronize()
     kus = [a.elapsed_time(b) * 1e3 for a, b in pairs]
     kernel_ms = sum(kus) / steps / 1e3
+    rr.check_chunkwise(ws)  # no wait of the timed calls gave up (control word clear)
     cold = []
     if cold_reps:
         scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0")
@@ -295,6 +296,7 @@ def bench_chunkwise_bwd(steps, warmup):
         rr.chunkwise_bwd(q, k, v, dout, g, chunk=w.chunk, workspace=ws)
 
     ms, _ = time_calls(step, steps, warmup)
+    rr.check_chunkwise(ws)
     flops = 3 * chunkwise_flops(w.batch, w.seqlen, w.heads, w.dk, w.dv, w.chunk)
     return {"workload": w, "ms": ms, "flops": flops, "tflops": flops / (ms * 1e-3) / 1e12}
 
@@ -407,6 +409,7 @@ def bench_sweep(steps=10, warmup=20):
         for ev in pairs:
             rr.chunkwise_fwd(q, k, v, g, chunk=chunk, state_out=state, out=out, workspace=ws, kernel_events=ev)
         torch.cuda.synchronize()
+        rr.check_chunkwise(ws)
         us = sorted(a.elapsed_time(b) * 1e3 for a, b in pairs)[steps // 2]
         flops = chunkwise_flops(1, n, h, d, d, chunk)
         row = {"tokens": n, "chunk": chunk, "kernel_us": round(us, 1), "us_per_1k_tokens": round(us * 1024 / n, 2),
@@ -456,10 +459,12 @@ def bench_varlen(steps, warmup):
                      dtype=torch.uint8, device="cuda:0")
     ms_var, _ = time_calls(lambda: rr.chunkwise_varlen_fwd(q, k, v, cu, maxlen, g, chunk=chunk, state_out=st, out=out,
                                                            workspace=ws), steps, warmup)
+    rr.check_chunkwise(ws)
     shp = (2, tot // 2, h, d)
     st2 = torch.empty((2, h, d, d), device="cuda:0")
     ms_fix, _ = time_calls(lambda: rr.chunkwise_fwd(q.view(shp), k.view(shp), v.view(shp), g.view(shp), chunk=chunk,
                                                     state_out=st2, out=out.view(shp), workspace=ws), steps, warmup)
+    rr.check_chunkwise(ws)
     flops_var = sum(chunkwise_flops(1, n, h, d, d, chunk) for n in VARLEN_LENS)
     flops_fix = chunkwise_flops(2, tot // 2, h, d, d, chunk)
     return {"lens": list(VARLEN_LENS), "ms": ms_var, "tflops": flops_var / (ms_var * 1e-3) / 1e12,
@@ -514,6 +519,12 @@ def cpu_baseline(sample_seqs=2, min_seconds=10.0, max_runs=20):
     except Exception:
         pass
     cores = len(os.sched_getaffinity(0))
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+    except OSError:
+        pass
     runs, t0 = 0, time.perf_counter()
     while runs < max_runs and (runs == 0 or time.perf_counter() - t0 < min_seconds):
         oracle.retention("chunkwise", q.f64, k.f64, v.f64, g=g.f64, chunk=w.chunk)
@@ -524,6 +535,7 @@ def cpu_baseline(sample_seqs=2, min_seconds=10.0, max_runs=20):
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": threads or cores,
+        "cpu_model": cpu_model,
         "kind": "oracle",
         "sample": f"chunkwise fp64 oracle on {sample_seqs} of 2 sequences of retention_7b_8k "
                   f"(8192 tokens, 16 heads x 256, chunk 512, gate), {runs} runs of {dt:.2f} s each on "
@@ -851,61 +863,10 @@ def main():
     rr.lib()  # fail loudly if the HIP library is missing
 
     line = {}
-    if args.only in (None, "chunkwise"):
-        cw = bench_chunkwise(args.steps, args.warmup, cold_reps=args.cold_reps)
-        w = cw["workload"]
-        print(f"chunkwise {w.name}: {cw['ms']:.3f} ms/step, {cw['tflops']:.1f} TFLOP/s; kernel alone "
-              f"{cw['kernel_ms'] * 1e3:.1f} us, {cw['kernel_tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
-        alg_gbps = cw["bytes"] / (cw["kernel_ms"] * 1e-3) / 1e9
-        # the same form on the two smaller chunkwise workloads (warm, reported
-        # beside the headline workload, not as its value)
-        others = {}
-        if not args.no_other_chunkwise:
-            for oname in ("retention_200m", "retention_3b"):
-                o = bench_chunkwise(max(args.steps // 2, 3), max(args.warmup // 4, 3), name=oname)
-                ow = o["workload"]
-                print(f"chunkwise {oname}: {o['ms']:.3f} ms/step, {o['tflops']:.1f} TFLOP/s; kernel alone "
-                      f"{o['kernel_ms'] * 1e3:.1f} us, {o['kernel_tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
-                others[oname] = {
-                    "workload": f"batch {ow.batch}, {ow.seqlen} tokens, {ow.heads} x {ow.dk}, chunk {ow.chunk}"
-                                + (", rotation" if ow.rotary_base else "") + ", gate",
-                    "ms": round(o["ms"], 4), "kernel_us": round(o["kernel_ms"] * 1e3, 1),
-                    "kernel_tflops": round(o["kernel_tflops"], 2),
-                    "mfma_frac": round(o["kernel_tflops"] / PEAK_BF16_TFLOPS, 4),
-                    "hbm_frac": round(o["bytes"] / (o["kernel_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
-        traffic = recorded_traffic()
-        line.update({
-            "metric": "chunkwise retention TFLOP/s (+% MFMA peak); decode-step tokens/s and HBM GB/s",
-            "value": round(cw["tflops"], 2),
-            "unit": "TFLOP/s",
-            "n_gpus": 1,
-            "steps": args.steps,
-            "warmup": args.warmup,
-            "ms_per_step": round(cw["ms"], 4),
-            "higher_is_better": True,
-            "scaling": "weak",
-            "vs_baseline": None,
-            "dtype": "bf16",
-            "data": "synthetic",
-            "config": {"workload": w.name, "form": "chunkwise", "batch": w.batch, "seq_len": w.seqlen,
-                       "heads": w.heads, "head_dim": w.dk, "chunk": w.chunk, "gate": True, "rotary": False,
-                       "state_out": True, "parallelism": "single GPU"},
-            # One chunkwise call = a control-block reset (a few microseconds)
-            # and the fused chunkwise kernel; `value` charges the whole call,
-            # the roofline the kernel's own duration (events recorded around
-            # it on the same stream, averaged over the timed calls). The bound
-            # is the roofline's own: the workload's algorithmic intensity
-            # (flop per HBM byte) against the ridge point peak flops / peak
-            # bandwidth; the other ceiling is reported beside it.
-            "roofline": roofline_object(cw, alg_gbps, traffic),
-        })
-        line["chunkwise_detail"] = {
-            "kernel_us_p10_p50_p90": [round(x, 1) for x in cw["kernel_us_pct"]],
-            "cold_kernel_us_p50": round(cw["cold_kernel_us"], 1) if cw["cold_kernel_us"] else None,
-            "cold": "each cold call follows a 512 MiB write that evicts L2 and the Infinity Cache",
-            "dense_equivalent_flops_per_launch": cw["dense_flops"],
-            "other_workloads": others,
-        }
+    # The headline leg runs last: the legs before it keep the GPU busy for
+    # seconds, so its W warm-up and K timed calls run at settled clocks (with
+    # a cold GPU, 5 warm-up calls time the chunkwise call about 14% slower
+    # than 200 do).
     if args.only in (None, "decode"):
         wd, dec = bench_decode(args.decode_steps, batches=args.decode_batches, graph=not args.no_decode_graph)
         for b, r in dec.items():
@@ -964,6 +925,61 @@ def main():
             "same_tokens_as_2x8192_ms": round(vl["equal_ms"], 4),
             "same_tokens_as_2x8192_tflops": round(vl["equal_tflops"], 2),
             "note": "per call: control reset and kernel; flops are the chunkwise count summed per sequence"}
+    if args.only in (None, "chunkwise"):
+        cw = bench_chunkwise(args.steps, args.warmup, cold_reps=args.cold_reps)
+        w = cw["workload"]
+        print(f"chunkwise {w.name}: {cw['ms']:.3f} ms/step, {cw['tflops']:.1f} TFLOP/s; kernel alone "
+              f"{cw['kernel_ms'] * 1e3:.1f} us, {cw['kernel_tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
+        alg_gbps = cw["bytes"] / (cw["kernel_ms"] * 1e-3) / 1e9
+        # the same form on the two smaller chunkwise workloads (warm, reported
+        # beside the headline workload, not as its value)
+        others = {}
+        if not args.no_other_chunkwise:
+            for oname in ("retention_200m", "retention_3b"):
+                o = bench_chunkwise(max(args.steps // 2, 3), max(args.warmup // 4, 3), name=oname)
+                ow = o["workload"]
+                print(f"chunkwise {oname}: {o['ms']:.3f} ms/step, {o['tflops']:.1f} TFLOP/s; kernel alone "
+                      f"{o['kernel_ms'] * 1e3:.1f} us, {o['kernel_tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
+                others[oname] = {
+                    "workload": f"batch {ow.batch}, {ow.seqlen} tokens, {ow.heads} x {ow.dk}, chunk {ow.chunk}"
+                                + (", rotation" if ow.rotary_base else "") + ", gate",
+                    "ms": round(o["ms"], 4), "kernel_us": round(o["kernel_ms"] * 1e3, 1),
+                    "kernel_tflops": round(o["kernel_tflops"], 2),
+                    "mfma_frac": round(o["kernel_tflops"] / PEAK_BF16_TFLOPS, 4),
+                    "hbm_frac": round(o["bytes"] / (o["kernel_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
+        traffic = recorded_traffic()
+        line.update({
+            "metric": "chunkwise retention TFLOP/s (+% MFMA peak); decode-step tokens/s and HBM GB/s",
+            "value": round(cw["tflops"], 2),
+            "unit": "TFLOP/s",
+            "n_gpus": 1,
+            "steps": args.steps,
+            "warmup": args.warmup,
+            "ms_per_step": round(cw["ms"], 4),
+            "higher_is_better": True,
+            "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": "bf16",
+            "data": "synthetic",
+            "config": {"workload": w.name, "form": "chunkwise", "batch": w.batch, "seq_len": w.seqlen,
+                       "heads": w.heads, "head_dim": w.dk, "chunk": w.chunk, "gate": True, "rotary": False,
+                       "state_out": True, "parallelism": "single GPU"},
+            # One chunkwise call = a control-block reset (a few microseconds)
+            # and the fused chunkwise kernel; `value` charges the whole call,
+            # the roofline the kernel's own duration (events recorded around
+            # it on the same stream, averaged over the timed calls). The bound
+            # is the roofline's own: the workload's algorithmic intensity
+            # (flop per HBM byte) against the ridge point peak flops / peak
+            # bandwidth; the other ceiling is reported beside it.
+            "roofline": roofline_object(cw, alg_gbps, traffic),
+        })
+        line["chunkwise_detail"] = {
+            "kernel_us_p10_p50_p90": [round(x, 1) for x in cw["kernel_us_pct"]],
+            "cold_kernel_us_p50": round(cw["cold_kernel_us"], 1) if cw["cold_kernel_us"] else None,
+            "cold": "each cold call follows a 512 MiB write that evicts L2 and the Infinity Cache",
+            "dense_equivalent_flops_per_launch": cw["dense_flops"],
+            "other_workloads": others,
+        }
     if args.sweep or args.only == "sweep":
         line["sweep"] = bench_sweep()
     if args.copy_probe:
@@ -976,6 +992,10 @@ def main():
         if "value" in line:
             cb["gpu_speedup"] = round(line["value"] / cb["value"], 1)
         line["cpu_baseline"] = cb
+    # the contract's keys first, then the legs
+    first = [k for k in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better",
+                         "scaling", "vs_baseline", "dtype", "data", "config", "roofline", "cpu_baseline") if k in line]
+    line = {**{k: line[k] for k in first}, **{k: v for k, v in line.items() if k not in first}}
     print(json.dumps(line), flush=True)
 
 

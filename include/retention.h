@@ -21,7 +21,9 @@
  *     q, k          [batch, seqlen, heads, dk]     dtype of the descriptor
  *     v, g, o       [batch, seqlen, heads, dv]     dtype of the descriptor
  *     state         [batch, heads, dk, dv]         fp32, always
- * Every pointer must be 16-byte aligned. `o` must not overlap q, k, v or g.
+ * Every pointer must be 16-byte aligned. A buffer a call writes (o, a state
+ * it writes, the workspace) must not overlap any other argument
+ * (RET_ERR_ALIAS), except state_in == state_out exactly where allowed.
  *
  * Every call validates its arguments on the host first and returns an error
  * status without touching the device when they are invalid. On success it
@@ -102,14 +104,17 @@ ret_status_t retention_parallel_fwd(const ret_desc_t *desc, const void *q, const
  * completed, word 0 counts the workgroups that ran and word 1 is nonzero only
  * on an error, after which the output is not valid: bit 0 (value 1) when a
  * cross-workgroup wait gave up after its bound (an internal error), bit 1
- * (value 2) for invalid packed-sequence bounds (retention_chunkwise_varlen_fwd). */
+ * (value 2) for invalid packed-sequence bounds (retention_chunkwise_varlen_fwd).
+ * retention_chunkwise_error reads the word. */
 size_t retention_chunkwise_workspace_bytes(const ret_desc_t *desc, int32_t chunk);
 ret_status_t retention_chunkwise_fwd(const ret_desc_t *desc, int32_t chunk, const void *q, const void *k,
                                      const void *v, const void *g, void *o, const float *state_in,
                                      float *state_out, void *workspace, size_t workspace_bytes,
                                      hipStream_t stream);
 
-/* The same call, for timing the chunkwise kernel on its own: when non-NULL,
+/* The chunkwise call of "Summary" (above), for measuring the chunkwise kernel
+ * on its own against the chunkwise cost that "Key points" (fifth item) gives,
+ * O(dn(b+h)): when non-NULL,
  * `before` and `after` (events created by the caller, for instance with
  * hipEventCreate) are recorded on `stream` immediately before and after the
  * launch of the chunkwise kernel, after the control-block reset and any
@@ -159,8 +164,11 @@ ret_status_t retention_chunkwise_varlen_fwd(const ret_desc_t *desc, int32_t chun
 ret_status_t retention_recurrent_step(const ret_desc_t *desc, const void *q, const void *k, const void *v,
                                       const void *g, void *o, float *state, hipStream_t stream);
 
-/* The same step with one rotation position per sequence (continuous
- * batching: sequences of a batch at different lengths): `positions` is a
+/* The same step with one rotation position per sequence, for serving a
+ * batch whose sequences sit at different lengths ("Key points", first item:
+ * decoding latency barely changes with batch size or input length; "Summary":
+ * the positions are encoded like xPos, i.e. by each token's own position):
+ * `positions` is a
  * DEVICE array of `batch` int64 positions, 8-byte aligned, each in
  * [0, 2^52] or negative (not checked: it lives on the device), read by the
  * step's kernel in place of desc->pos_offset. A negative position marks an
@@ -235,6 +243,21 @@ ret_status_t retention_chunkwise_bwd_state(const ret_desc_t *desc, int32_t chunk
 size_t retention_score_map_workspace_bytes(const ret_desc_t *desc);
 ret_status_t retention_score_map(const ret_desc_t *desc, const void *q, const void *k, int32_t query, float *scores,
                                  void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Control word 1 of a chunkwise workspace, after the call that used it:
+ * waits for the work enqueued on `stream` (hipStreamSynchronize), then copies
+ * the word to *error_word (HOST pointer). The chunkwise calls
+ * (retention_chunkwise_fwd, _fwd_timed, _varlen_fwd, _bwd, _bwd_state) reset
+ * it at their start and set it only on an error, after which their outputs
+ * are not valid: bit 0 (value 1) when a wait between the workgroups that
+ * carry the state from chunk to chunk gave up after its bound, bit 1 (value
+ * 2) for packed-sequence bounds that had to be clamped. The backward's
+ * word covers all of its launches. The chunkwise form itself is the one of
+ * "Summary": the recurrent state passed between chunks. Returns RET_ERR_NULL,
+ * RET_ERR_WORKSPACE (fewer than 8 bytes), RET_ERR_ALIGN or RET_ERR_HIP (the
+ * copy or the wait failed, for instance after a fault of an earlier kernel). */
+ret_status_t retention_chunkwise_error(const void *workspace, size_t workspace_bytes, int32_t *error_word,
+                                       hipStream_t stream);
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char *retention_status_string(ret_status_t status);

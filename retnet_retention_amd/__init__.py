@@ -8,11 +8,14 @@ gfx950 behind a C ABI (include/retention.h), with a thin ctypes binding.
     parallel_bwd     gradients of the parallel form (q, k, v and the gate)
     chunkwise_bwd    the same gradients, each product run as the chunkwise form
     score_map        one query token's retention weights, summed over heads
+    check_chunkwise  raise if a chunkwise call's control word reports an error
 """
 
 from .binding import (  # noqa: F401
     RetentionError,
+    check_chunkwise,
     chunkwise_bwd,
+    chunkwise_error,
     chunkwise_fwd,
     chunkwise_varlen_fwd,
     chunkwise_varlen_workspace_bytes,

@@ -52,6 +52,23 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
+// bytes of one [batch][seqlen][heads][d] tensor and of one fp32 state
+size_t tensor_bytes(const ret_desc_t* d) {
+  return (size_t)d->batch * d->seqlen * d->heads * d->dk * elem_size(d->dtype);
+}
+size_t state_bytes_exact(const ret_desc_t* d) { return (size_t)d->batch * d->heads * d->dk * d->dv * 4; }
+
+// the decode step's state (read and written in place) overlaps none of q, k,
+// v, g, o
+ret_status_t check_step_state(const ret_desc_t* d, const void* q, const void* k, const void* v, const void* g,
+                              const void* o, const float* state) {
+  const size_t n = tensor_bytes(d), ns = state_bytes_exact(d);
+  if (overlaps(state, ns, q, n) || overlaps(state, ns, k, n) || overlaps(state, ns, v, n) ||
+      overlaps(state, ns, g, n) || overlaps(state, ns, o, n))
+    return RET_ERR_ALIAS;
+  return RET_OK;
+}
+
 ret_status_t check_tensors(const ret_desc_t* d, const void* q, const void* k, const void* v, const void* g,
                            const void* o) {
   if (!q || !k || !v || !o) return RET_ERR_NULL;
@@ -207,11 +224,17 @@ ret_status_t chunkwise_bwd_impl(const ret_desc_t* desc, int32_t chunk, const voi
   auto slot = [&]() { char* p = next; next += tb; return p; };
   char* st_at = tab_at + bwd_bytes(desc, g != nullptr);
   auto state_slot = [&](int i) { return reinterpret_cast<float*>(st_at + i * state_bytes(desc)); };
-  // one chunkwise product; q_rev, out_rev, out_rot as in the parallel backward
+  // one chunkwise product; q_rev, out_rev, out_rot as in the parallel backward.
+  // The first one clears the control block's error word, the later ones keep
+  // it, so the word reports an error of any of the call's launches.
+  bool first = true;
   auto product = [&](const void* a, const void* b, const void* cc, void* out, const float* s_in, float* s_out,
                      bool q_rev, bool out_rev, const float2* out_rot) {
+    const bool keep = !first;
+    first = false;
     return ret::launch_retention_fwd(s, c, true, a, b, cc, nullptr, out, s_in, s_out, snap, chain, ctrl, nullptr,
-                                     desc->gn_eps, stream, nullptr, nullptr, q_rev, out_rev, out_rot) == hipSuccess;
+                                     desc->gn_eps, stream, nullptr, nullptr, q_rev, out_rev, out_rot, nullptr, 0,
+                                     nullptr, keep) == hipSuccess;
   };
   // states of the three products (per head g): S0^T for dq; dS^T / g and
   // dS / g for the reversed ones (their g^(m'+1) then makes g^(N-1-m)); the
@@ -319,6 +342,12 @@ ret_status_t retention_parallel_fwd(const ret_desc_t* desc, const void* q, const
   const size_t need = rot_bytes(desc);
   if (need && (!workspace || workspace_bytes < need)) return RET_ERR_WORKSPACE;
   if (workspace && !aligned16(workspace)) return RET_ERR_ALIGN;
+  if (need) {
+    const size_t n = tensor_bytes(desc);
+    if (overlaps(workspace, need, q, n) || overlaps(workspace, need, k, n) || overlaps(workspace, need, v, n) ||
+        overlaps(workspace, need, g, n) || overlaps(workspace, need, o, n))
+      return RET_ERR_ALIAS;
+  }
 
   const Shape s = make_shape(desc);
   const float2* table;
@@ -478,6 +507,20 @@ ret_status_t retention_chunkwise_fwd_timed(const ret_desc_t* desc, int32_t chunk
   const size_t need = cb + rb + hb + snap_bytes(desc, chunk);
   if (!workspace || workspace_bytes < need) return RET_ERR_WORKSPACE;
   if (!aligned16(workspace)) return RET_ERR_ALIGN;
+  // the written buffers (o, state_out, workspace) overlap nothing else;
+  // state_in == state_out exactly is allowed (the kernel reads every state_in
+  // value before the last chunk writes state_out)
+  {
+    const size_t n = tensor_bytes(desc), ns = state_bytes_exact(desc);
+    if (overlaps(o, n, state_in, ns) || overlaps(o, n, state_out, ns)) return RET_ERR_ALIAS;
+    if (overlaps(state_out, ns, q, n) || overlaps(state_out, ns, k, n) || overlaps(state_out, ns, v, n) ||
+        overlaps(state_out, ns, g, n) || (state_out != state_in && overlaps(state_out, ns, state_in, ns)))
+      return RET_ERR_ALIAS;
+    const void* all[] = {q, k, v, g, o, state_in, state_out};
+    const size_t all_n[] = {n, n, n, n, n, ns, ns};
+    for (int j = 0; j < 7; ++j)
+      if (overlaps(workspace, need, all[j], all_n[j])) return RET_ERR_ALIAS;
+  }
 
   const Shape s = make_shape(desc);
   const int32_t c = eff_chunk(desc, chunk);
@@ -565,6 +608,7 @@ ret_status_t retention_recurrent_step(const ret_desc_t* desc, const void* q, con
   if ((st = check_eps(desc, g)) != RET_OK) return st;
   if (!state) return RET_ERR_NULL;
   if (!aligned16(state)) return RET_ERR_ALIGN;
+  if ((st = check_step_state(desc, q, k, v, g, o, state)) != RET_OK) return st;
   const Shape s = make_shape(desc);
   if (ret::launch_recurrent_step(s, q, k, v, g, o, state, desc->rotary_base, desc->pos_offset, desc->gn_eps,
                                  stream) != hipSuccess)
@@ -616,10 +660,28 @@ ret_status_t retention_recurrent_step_positions(const ret_desc_t* desc, const vo
   if ((st = check_eps(desc, g)) != RET_OK) return st;
   if (!state || !positions) return RET_ERR_NULL;
   if (!aligned16(state) || (reinterpret_cast<uintptr_t>(positions) & 7u) != 0) return RET_ERR_ALIGN;
+  if ((st = check_step_state(desc, q, k, v, g, o, state)) != RET_OK) return st;
+  if (overlaps(positions, (size_t)desc->batch * 8, o, tensor_bytes(desc)) ||
+      overlaps(positions, (size_t)desc->batch * 8, state, state_bytes_exact(desc)))
+    return RET_ERR_ALIAS;
   const Shape s = make_shape(desc);
   if (ret::launch_recurrent_step(s, q, k, v, g, o, state, desc->rotary_base, desc->pos_offset, desc->gn_eps,
                                  stream, positions) != hipSuccess)
     return RET_ERR_HIP;
+  return RET_OK;
+}
+
+ret_status_t retention_chunkwise_error(const void* workspace, size_t workspace_bytes, int32_t* error_word,
+                                       hipStream_t stream) {
+  if (!workspace || !error_word) return RET_ERR_NULL;
+  if (workspace_bytes < 2 * sizeof(int32_t)) return RET_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return RET_ERR_ALIGN;
+  int32_t word = 0;
+  const int32_t* src = static_cast<const int32_t*>(workspace) + 1;
+  if (hipMemcpyAsync(&word, src, sizeof(word), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess)
+    return RET_ERR_HIP;
+  *error_word = word;
   return RET_OK;
 }
 

@@ -48,12 +48,14 @@ size_t chunkwise_sched_bytes(const Shape& s, int chunk);
 // stores the output reversed, `out_rot` (may be null) turns each stored
 // output row back by its stored position's angles.
 // `before`/`after` (may be null) are recorded around the main kernel.
+// keep_err: the control block's reset leaves its error word (word 1) as it
+// is, for the second and later launches of one call.
 hipError_t launch_retention_fwd(const Shape& s, int chunk, bool chunked, const void* q, const void* k, const void* v,
                                 const void* g, void* o, const float* state_in, float* state_out, void* snap,
                                 float* chain, int* ctrl, const float2* rot, float eps, hipStream_t stream,
                                 hipEvent_t before = nullptr, hipEvent_t after = nullptr, bool q_rev = false,
                                 bool out_rev = false, const float2* out_rot = nullptr, const int* cu = nullptr,
-                                int total = 0, void* sched = nullptr);
+                                int total = 0, void* sched = nullptr, bool keep_err = false);
 
 // Backward passes of the parallel form (all tensors [batch][seqlen][heads][d]
 // of the descriptor's dtype): the gradient through the swish gate and the

@@ -1084,13 +1084,17 @@ __global__ __launch_bounds__(256) void varlen_schedule_kernel(FwdParams p, int4*
   for (int i = total + sl * 256 + tid; i < p.per_class; i += 256 * p.nchunks) out[i] = make_int4(-1, 0, 0, 0);
 }
 
-__global__ void reset_ctrl_kernel(int* ctrl, int n) {
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) ctrl[i] = 0;
+// Zero the control block before a chunkwise launch; keep_err leaves word 1
+// (the error word) as it is, so that a call made of several launches (the
+// backward's products) reports an error of any of them.
+__global__ void reset_ctrl_kernel(int* ctrl, int n, int keep_err) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x)
+    if (!(keep_err && i == 1)) ctrl[i] = 0;
 }
 
 template <typename T, int D, bool FAST>
 static hipError_t launch_fwd_impl(const Shape& s, int chunk, FwdParams p, bool chunked, hipStream_t stream,
-                                  hipEvent_t before, hipEvent_t after) {
+                                  hipEvent_t before, hipEvent_t after, bool keep_err) {
   using C = OutTile<T, D, FAST>;
   p.qblocks = (chunk + C::BM - 1) / C::BM;
   const int bhs = s.batch * s.heads;
@@ -1105,7 +1109,7 @@ static hipError_t launch_fwd_impl(const Shape& s, int chunk, FwdParams p, bool c
   }
   const int64_t nctrl = kCtrlHead + (int64_t)bhs * (p.nchunks + 1) * kFlagsPerChunk;
   hipLaunchKernelGGL(reset_ctrl_kernel, dim3((unsigned)((nctrl + 255) / 256 < 1024 ? (nctrl + 255) / 256 : 1024)),
-                     dim3(256), 0, stream, p.ctrl, (int)nctrl);
+                     dim3(256), 0, stream, p.ctrl, (int)nctrl, keep_err ? 1 : 0);
   p.xcd_order = bhs % 8 == 0;
   const int roles = StTile<T, D>::SPLIT + p.qblocks;
   const int64_t blocks = (int64_t)p.nchunks * bhs * roles;
@@ -1133,12 +1137,12 @@ static hipError_t launch_fwd_impl(const Shape& s, int chunk, FwdParams p, bool c
 // within 2^64.
 template <typename T, int D>
 static hipError_t launch_fwd_t(const Shape& s, int chunk, FwdParams p, bool chunked, hipStream_t stream,
-                               hipEvent_t before, hipEvent_t after) {
+                               hipEvent_t before, hipEvent_t after, bool keep_err) {
   const double span = chunked ? chunk : OutTile<T, D, true>::BM;
   bool fast = true;
   for (int h = 0; h < s.heads; ++h) fast = fast && -(double)s.log2g[h] * span <= kFastSpanLog2;
-  return fast ? launch_fwd_impl<T, D, true>(s, chunk, p, chunked, stream, before, after)
-              : launch_fwd_impl<T, D, false>(s, chunk, p, chunked, stream, before, after);
+  return fast ? launch_fwd_impl<T, D, true>(s, chunk, p, chunked, stream, before, after, keep_err)
+              : launch_fwd_impl<T, D, false>(s, chunk, p, chunked, stream, before, after, keep_err);
 }
 
 size_t chunkwise_sched_bytes(const Shape& s, int chunk) {
@@ -1161,7 +1165,7 @@ hipError_t launch_retention_fwd(const Shape& s, int chunk, bool chunked, const v
                                 const void* g, void* o, const float* state_in, float* state_out, void* snap,
                                 float* chain, int* ctrl, const float2* rot, float eps, hipStream_t stream,
                                 hipEvent_t before, hipEvent_t after, bool q_rev, bool out_rev,
-                                const float2* out_rot, const int* cu, int total, void* sched) {
+                                const float2* out_rot, const int* cu, int total, void* sched, bool keep_err) {
   if (rot && q_rev) return hipErrorInvalidValue;  // q's angles are those of its own positions
   // packed sequences: chunkwise form, forward only, with a schedule buffer
   if (cu && (!chunked || q_rev || out_rev || out_rot || !sched)) return hipErrorInvalidValue;
@@ -1196,15 +1200,15 @@ hipError_t launch_retention_fwd(const Shape& s, int chunk, bool chunked, const v
   for (int h = 0; h < kMaxHeads; ++h) p.log2g[h] = h < s.heads ? s.log2g[h] : 0.f;
   if (s.dtype == 1) {
     switch (s.d) {
-      case 64: return launch_fwd_t<bf16, 64>(s, chunk, p, chunked, stream, before, after);
-      case 128: return launch_fwd_t<bf16, 128>(s, chunk, p, chunked, stream, before, after);
-      case 256: return launch_fwd_t<bf16, 256>(s, chunk, p, chunked, stream, before, after);
+      case 64: return launch_fwd_t<bf16, 64>(s, chunk, p, chunked, stream, before, after, keep_err);
+      case 128: return launch_fwd_t<bf16, 128>(s, chunk, p, chunked, stream, before, after, keep_err);
+      case 256: return launch_fwd_t<bf16, 256>(s, chunk, p, chunked, stream, before, after, keep_err);
     }
   } else {
     switch (s.d) {
-      case 64: return launch_fwd_t<float, 64>(s, chunk, p, chunked, stream, before, after);
-      case 128: return launch_fwd_t<float, 128>(s, chunk, p, chunked, stream, before, after);
-      case 256: return launch_fwd_t<float, 256>(s, chunk, p, chunked, stream, before, after);
+      case 64: return launch_fwd_t<float, 64>(s, chunk, p, chunked, stream, before, after, keep_err);
+      case 128: return launch_fwd_t<float, 128>(s, chunk, p, chunked, stream, before, after, keep_err);
+      case 256: return launch_fwd_t<float, 256>(s, chunk, p, chunked, stream, before, after, keep_err);
     }
   }
   return hipErrorInvalidValue;

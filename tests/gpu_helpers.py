@@ -24,7 +24,62 @@ def rel_frob(got, ref):
     return float(np.linalg.norm((got - ref).ravel()) / (den if den > 0 else 1.0))
 
 
-def assert_close(got, ref, dtype, what=""):
+# rows per block of the localized bf16 check
+BLOCK_ROWS = 64
+
+
+def _units(x, kind):
+    """x split into the units of the localized check, as rows of a 2-D array:
+    "state" [batch, heads, dk, dv] -> one unit per (sequence, head);
+    "seq"   [batch, tokens, heads, d] -> per (sequence, block of BLOCK_ROWS
+            tokens, head), the last block ragged (zero-padded);
+    "packed" [tokens, heads, d] -> per (block of tokens, head);
+    "rows"  anything [..., heads, d] -> per (leading index, head);
+    "flat2" [batch, tokens] -> per (sequence, block of tokens)."""
+    if kind == "state":
+        return x.reshape(x.shape[0] * x.shape[1], -1)
+    if kind == "rows":
+        return x.reshape(-1, x.shape[-1])
+    if kind == "packed":
+        x = x[None]
+        kind = "seq"
+    if kind == "flat2":
+        x = x[:, :, None, None]
+        kind = "seq"
+    assert kind == "seq" and x.ndim == 4, kind
+    b, n, h, d = x.shape
+    nb = -(-n // BLOCK_ROWS)
+    pad = np.zeros((b, nb * BLOCK_ROWS, h, d), dtype=x.dtype)
+    pad[:, :n] = x
+    return pad.reshape(b, nb, BLOCK_ROWS, h, d).transpose(0, 1, 3, 2, 4).reshape(b * nb * h, BLOCK_ROWS * d)
+
+
+def _default_kind(x, what):
+    if x.ndim == 4 and "state" in what:
+        return "state"
+    return {2: "flat2", 3: "packed", 4: "seq"}.get(x.ndim, "rows")
+
+
+def worst_block(got, ref, kind):
+    """Largest relative Frobenius error over the units of `kind` (a unit whose
+    reference is all zero is measured against a small floor instead), and
+    the unit's index."""
+    g, r = _units(got, kind), _units(ref, kind)
+    num = np.linalg.norm(g - r, axis=1)
+    den = np.linalg.norm(r, axis=1)
+    floor = 1e-3 * max(float(np.sqrt(np.mean(den ** 2))), 1e-30)
+    errs = num / np.maximum(den, floor)
+    i = int(np.argmax(errs))
+    return float(errs[i]), i, len(errs)
+
+
+def assert_close(got, ref, dtype, what="", kind=None):
+    """fp32: max-abs over every element. bf16: relative Frobenius over the
+    whole tensor, and the same bar on every unit of the localized split
+    (per (sequence, head, block of 64 rows) for outputs, per (sequence, head)
+    for states), so that one wrong row, chunk boundary or head cannot hide in
+    the norm of a large tensor."""
+    assert got.shape == ref.shape, f"{what}: shape {got.shape} != {ref.shape}"
     assert np.all(np.isfinite(got)), f"{what}: non-finite output"
     if dtype == "f32":
         err = float(np.max(np.abs(got - ref)))
@@ -32,8 +87,12 @@ def assert_close(got, ref, dtype, what=""):
         assert err <= F32_MAX_ABS, f"{what}: max-abs {err:.3e} > {F32_MAX_ABS}"
     else:
         err = rel_frob(got, ref)
-        print(f"  {what}: rel-Frobenius {err:.3e}", flush=True)
+        kind = kind or _default_kind(got, what)
+        worst, at, units = worst_block(got, ref, kind)
+        print(f"  {what}: rel-Frobenius {err:.3e}; worst of {units} {kind} units {worst:.3e} (unit {at})",
+              flush=True)
         assert err <= BF16_REL_FROB, f"{what}: rel-Frobenius {err:.3e} > {BF16_REL_FROB}"
+        assert worst <= BF16_REL_FROB, f"{what}: unit {at} of {units} ({kind}): rel-Frobenius {worst:.3e}"
     return err
 
 

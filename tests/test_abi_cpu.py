@@ -253,3 +253,33 @@ def test_varlen_validates(L):
     assert call(o=ALIGNED + 16) == 8  # out overlaps q
     assert call(wsb=16) == 6
     assert call(ws=None) == 6
+
+
+def test_written_buffers_must_not_overlap(L):
+    """A state the call writes, the output and the workspace overlap nothing
+    else (RET_ERR_ALIAS); state_in == state_out is the one allowed alias."""
+    d, _ = _desc()
+    need = L.retention_chunkwise_workspace_bytes(ctypes.byref(d), 64)
+    ok = dict(ws=ALIGNED * 8, wsb=need)
+    assert _chk(L, d, so=ALIGNED + 4096, **ok) == 8           # state_out inside q
+    assert _chk(L, d, si=ALIGNED * 4 + 512, **ok) == 8        # state_in inside o
+    assert _chk(L, d, si=ALIGNED * 6, so=ALIGNED * 6 + 1024, **ok) == 8  # partial state alias
+    assert _chk(L, d, ws=ALIGNED * 3 + 256, wsb=need) == 8    # workspace inside v
+    assert _chk(L, d, si=ALIGNED * 8 + 256, **ok) == 8        # state_in inside the workspace
+    d1, _ = _desc(seqlen=1)
+    assert _step(L, d1, s=ALIGNED * 4) == 8                    # state is the output
+    assert _step(L, d1, s=ALIGNED * 2 + 512) == 8              # state inside k
+    d3, _ = _desc(rotary_base=10000.0)
+    nr = L.retention_parallel_workspace_bytes(ctypes.byref(d3))
+    assert _par(L, d3, ws=ALIGNED * 4, wsb=nr) == 8            # rotation workspace is the output
+    pos_bad = L.retention_recurrent_step_positions(ctypes.byref(d1), ALIGNED, ALIGNED * 2, ALIGNED * 3, None,
+                                                   ALIGNED * 4, ALIGNED * 5, ALIGNED * 5 + 64, None)
+    assert pos_bad == 8                                        # positions inside the state
+
+
+def test_chunkwise_error_reader_validates(L):
+    word = ctypes.c_int32(0)
+    assert L.retention_chunkwise_error(None, 64, ctypes.byref(word), None) == 1
+    assert L.retention_chunkwise_error(ALIGNED, 64, None, None) == 1
+    assert L.retention_chunkwise_error(ALIGNED, 4, ctypes.byref(word), None) == 6
+    assert L.retention_chunkwise_error(ALIGNED + 4, 64, ctypes.byref(word), None) == 5

@@ -109,6 +109,33 @@ def test_custom_gammas():
         assert_close(out, ref, "f32", form)
 
 
+# --- bf16 with decays that take the generic decay path ---------------------
+GENERIC_GAMMAS = [1.0, 0.25, 2.0 ** -40, 0.999]
+
+
+@pytest.mark.parametrize("form,gate", [("chunkwise", True), ("chunkwise", False), ("parallel", True),
+                                       ("parallel", False)])
+def test_bf16_generic_decay_path(form, gate):
+    """Decays 0.25 and 2^-40 give |log2 g| x span > 64 at chunk 512 (and over
+    the parallel form's 256-row query blocks), so the host launches the
+    generic instantiation: an exact decay factor per score, the cross term as
+    O = xi (O / xi + Q R) with rows whose xi is below 2^-100 skipping it.
+    bf16, d = 256, rotation, chunk 512 over 1100 tokens (a ragged last chunk),
+    the chunkwise form from a carried state; every (sequence, head, 64-row
+    block) is held to the bar on its own, with and without the gate."""
+    b, n, h, d = 2, 1100, 4, 256
+    _announce(case="generic decay path", form=form, gate=gate, gammas=GENERIC_GAMMAS)
+    q, k, v, g, s0 = make_inputs(151 + gate, b, n, h, d, "bf16", 1 / 16, 1.0 if gate else None, form == "chunkwise")
+    kw = dict(chunk=512, rotary_base=10000.0, pos_offset=9, gammas=GENERIC_GAMMAS, state_in=s0)
+    ref, ref_s = oracle_run(form, q, k, v, g, **kw)
+    out, st = gpu_run(form, q, k, v, g, **kw)
+    assert_close(out, ref, "bf16", "out")
+    for hh in range(h):
+        assert_close(out[:, :, hh:hh + 1], ref[:, :, hh:hh + 1], "bf16", f"out head {hh}")
+    if ref_s is not None:
+        assert_close(st, ref_s, "bf16", "state")
+
+
 # --- state in == state out (in place) ---------------------------------------
 def test_state_in_out_alias():
     _announce(case="state alias")
@@ -139,6 +166,7 @@ def test_many_pairs_with_carried_state():
                            state_in=torch.from_numpy(s0.astype(np.float32)).to(DEV), state_out=st, workspace=ws)
     torch.cuda.synchronize()
     assert int(ws[4:8].view(torch.int32).item()) == 0
+    rr.check_chunkwise(ws)
     assert_close(to64(out), ref, "bf16", "out")
     assert_close(to64(st), ref_s, "bf16", "state")
 

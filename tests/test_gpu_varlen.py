@@ -55,7 +55,9 @@ def _run(q, k, v, g, s0, cu, maxlen, chunk, base, pos, dtype_code, workspace=Non
     rr.chunkwise_varlen_fwd(tq, tk, tv, torch.from_numpy(cu).to(DEV), maxlen, tg, chunk=chunk, state_in=s_in,
                             state_out=s_out, rotary_base=base, pos_offset=pos, out=out, workspace=ws)
     torch.cuda.synchronize()
-    return out, s_out, int(ws[4:8].view(torch.int32).item())
+    word = rr.chunkwise_error(ws)  # the C ABI's reader of control word 1
+    assert word == int(ws[4:8].view(torch.int32).item())
+    return out, s_out, word
 
 
 CASES = [
@@ -115,8 +117,16 @@ def test_varlen_invalid_boundaries_are_clamped_and_reported():
     q, k, v, g, _, _ = _packed(9, [200], h, d, "f32", True, False)
     cu = np.array([0, 100, 50, 300], dtype=np.int32)  # 100 -> 50 backwards; 300 past 200 rows
     _announce(cu=cu.tolist(), total=200, maxlen=maxlen)
-    out, _, err = _run(q, k, v, g, None, cu, maxlen, chunk, 0.0, 0, B.RET_F32)
+    ws = _workspace(len(cu) - 1, maxlen, h, d, B.RET_F32, chunk, 0.0)
+    out, _, err = _run(q, k, v, g, None, cu, maxlen, chunk, 0.0, 0, B.RET_F32, workspace=ws)
     assert err & 2
+    with pytest.raises(rr.RetentionError) as info:
+        rr.check_chunkwise(ws)
+    assert info.value.word == err
+    # a call with the binding's own workspace checks the word by itself
+    with pytest.raises(rr.RetentionError):
+        rr.chunkwise_varlen_fwd(q.torch(DEV), k.torch(DEV), v.torch(DEV), torch.from_numpy(cu).to(DEV), maxlen,
+                                g.torch(DEV), chunk=chunk)
     ref, _ = oracle.retention_varlen("chunkwise", q.f64[:100], k.f64[:100], v.f64[:100], [0, 100],
                                      g=g.f64[:100], chunk=chunk)
     assert_close(to64(out[:50]), ref[:50], "f32", "valid sequence")

@@ -112,6 +112,46 @@ def test_7b_decode_full_size():
     assert not np.array_equal(to64(state)[0], to64(state)[2])
 
 
+def test_7b_decode_batch256_streaming_path():
+    """Batch 256, the largest of the decode sweep: 256 x 16 states of 256 x 256
+    fp32 are 1 GiB, above the 512 MiB past which the step streams its state
+    with non-temporal accesses (its own instantiation). Two seeded 8192-token
+    prefills tiled to 256 sequences, then 16 steps; every step's output and
+    the final state of five sampled sequences (spread over the tiles) against
+    oracle steps started from the GPU's prefill state."""
+    w = get("retention_7b_decode")
+    distinct, batch, steps, sampled = 2, 256, 16, (0, 77, 130, 201, 255)
+    assert batch * w.heads * w.dk * w.dv * 4 > 512 << 20
+    _announce(workload=w.name, prefill_sequences=distinct, batch=batch, steps=steps)
+    q, k, v, g = w.inputs(batch=distinct)
+    pre_state = torch.empty((distinct, w.heads, w.dk, w.dv), device=DEV)
+    rr.chunkwise_fwd(q.torch(DEV), k.torch(DEV), v.torch(DEV), g.torch(DEV), chunk=w.chunk, state_out=pre_state)
+    del q, k, v, g
+    state = pre_state.repeat(batch // distinct, 1, 1, 1).contiguous()
+    idx = list(sampled)
+    start = to64(state[idx])
+    shp = (steps, batch, 1, w.heads, w.dk)
+    sq, sk, sv, sg = draw(w.seed + 2, [(shp, w.qkv_scale)] * 3 + [(shp, w.gate_scale)], "bf16")
+    tq, tk, tv, tg = (x.torch(DEV) for x in (sq, sk, sv, sg))
+    outs = torch.empty((steps, batch, 1, w.heads, w.dv), dtype=torch.bfloat16, device=DEV)
+    for t in range(steps):
+        rr.recurrent_step(tq[t], tk[t], tv[t], state, tg[t], pos=w.seqlen + t, out=outs[t])
+    torch.cuda.synchronize()
+    got = to64(outs)[:, idx]
+    got_state = to64(state[idx])
+    del state, tq, tk, tv, tg, outs
+
+    gam = oracle.default_gammas(w.heads)
+    ref_state = start
+    ref = np.empty_like(got)
+    for t in range(steps):
+        o, ref_state = oracle.recurrent_step(sq.f64[t][idx], sk.f64[t][idx], sv.f64[t][idx], ref_state, gam,
+                                             g=sg.f64[t][idx], pos=w.seqlen + t)
+        ref[t] = o
+    assert_close(got, ref, "bf16", "decode outputs")
+    assert_close(got_state, ref_state, "bf16", "decode state")
+
+
 @pytest.mark.parametrize("chunk", [512, 1024])
 def test_long_context_chunkwise(chunk):
     """65,536 tokens (128 or 64 chunks), 2 heads x 256, gate, state out: every
