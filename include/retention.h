@@ -30,8 +30,9 @@
  * enqueues its kernels on `stream` and returns at once; faults inside the
  * kernels surface at the caller's next synchronisation. The library keeps no
  * pointer after a call returns, allocates no device memory and holds no
- * global mutable state, so calls on different streams may run concurrently
- * when their buffers (workspace included) are distinct. Results are bitwise
+ * global mutable state (except the static scratch of
+ * retention_chunkwise_fwd_noalloc), so calls on different streams may run
+ * concurrently when their buffers (workspace included) are distinct. Results are bitwise
  * deterministic for a given build, shape and input.
  *
  * Supported: dk == dv in {64, 128, 256}; dtype fp32 or bf16; heads <= 128.
@@ -61,7 +62,8 @@ typedef enum {
   RET_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than required          */
   RET_ERR_HIP = 7,         /* the HIP runtime rejected a kernel launch          */
   RET_ERR_ALIAS = 8,       /* the output overlaps an input                      */
-  RET_ERR_ARG = 9          /* another scalar argument is invalid (eps, base...) */
+  RET_ERR_ARG = 9,         /* another scalar argument is invalid (eps, base...) */
+  RET_ERR_SCRATCH = 10     /* needs more than the static scratch (_noalloc only) */
 } ret_status_t;
 
 typedef enum { RET_F32 = 0, RET_BF16 = 1 } ret_dtype_t;
@@ -124,6 +126,25 @@ ret_status_t retention_chunkwise_fwd_timed(const ret_desc_t *desc, int32_t chunk
                                            const void *v, const void *g, void *o, const float *state_in,
                                            float *state_out, void *workspace, size_t workspace_bytes,
                                            hipStream_t stream, hipEvent_t before, hipEvent_t after);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * chunkwise call above without a workspace argument. Its scratch (control
+ * block, rotation, state chain, per-chunk states: the bytes
+ * retention_chunkwise_workspace_bytes gives) lives in a static device array
+ * of 128 MiB that the library holds on each device it runs on until the
+ * process ends; a call that needs more returns RET_ERR_SCRATCH. The call
+ * allocates nothing: no hipMalloc, hipFree or allocating library routine.
+ * Its first call on a device looks up the array's address there. Every call
+ * on one device shares that device's array and leaves its contents behind
+ * (each call resets what must start at zero), so calls that overlap in time
+ * on one device, on any streams, race and give wrong results: serialize
+ * them. `error_word` (DEVICE int32, 4-byte aligned, may be NULL) receives
+ * control word 1 of the call (0: no error; see retention_chunkwise_fwd) in
+ * stream order. Arguments and errors otherwise as retention_chunkwise_fwd. */
+ret_status_t retention_chunkwise_fwd_noalloc(const ret_desc_t *desc, int32_t chunk, const void *q, const void *k,
+                                             const void *v, const void *g, void *o, const float *state_in,
+                                             float *state_out, int32_t *error_word, hipStream_t stream);
 
 /* Chunkwise form over packed sequences of different lengths (prefill of a
  * ragged batch; "Summary": the chunkwise form for long inputs, and the

@@ -3,6 +3,7 @@ gfx950 behind a C ABI (include/retention.h), with a thin ctypes binding.
 
     parallel_fwd     parallel form (training)
     chunkwise_fwd    chunkwise recurrent form (long sequences, prefill)
+    chunkwise_fwd_noalloc the same without a workspace (a static scratch; allocates nothing)
     chunkwise_varlen_fwd  the same over packed sequences of different lengths
     recurrent_step   recurrent form, one decode step, state in place
     parallel_bwd     gradients of the parallel form (q, k, v and the gate)
@@ -17,6 +18,7 @@ from .binding import (  # noqa: F401
     chunkwise_bwd,
     chunkwise_error,
     chunkwise_fwd,
+    chunkwise_fwd_noalloc,
     chunkwise_varlen_fwd,
     chunkwise_varlen_workspace_bytes,
     chunkwise_workspace_bytes,

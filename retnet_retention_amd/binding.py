@@ -26,6 +26,7 @@ STATUS = {
     7: "RET_ERR_HIP",
     8: "RET_ERR_ALIAS",
     9: "RET_ERR_ARG",
+    10: "RET_ERR_SCRATCH",
 }
 
 # names declared in include/retention.h
@@ -35,6 +36,7 @@ EXPORTS = (
     "retention_chunkwise_workspace_bytes",
     "retention_chunkwise_fwd",
     "retention_chunkwise_fwd_timed",
+    "retention_chunkwise_fwd_noalloc",
     "retention_chunkwise_varlen_workspace_bytes",
     "retention_chunkwise_varlen_fwd",
     "retention_recurrent_step",
@@ -105,6 +107,8 @@ def lib():
         h.retention_chunkwise_fwd.restype = st
         h.retention_chunkwise_fwd_timed.argtypes = [pd, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp]
         h.retention_chunkwise_fwd_timed.restype = st
+        h.retention_chunkwise_fwd_noalloc.argtypes = [pd, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        h.retention_chunkwise_fwd_noalloc.restype = st
         h.retention_chunkwise_varlen_workspace_bytes.argtypes = [pd, i32]
         h.retention_chunkwise_varlen_workspace_bytes.restype = sz
         h.retention_chunkwise_varlen_fwd.argtypes = [pd, i32, vp, ctypes.c_int64] + [vp] * 8 + [sz, vp]
@@ -379,6 +383,34 @@ def chunkwise_fwd(q, k, v, g=None, *, chunk=512, state_in=None, state_out=None, 
     del keep
     if check or (check is None and own):
         check_chunkwise(workspace)
+    return out
+
+
+def chunkwise_fwd_noalloc(q, k, v, g=None, *, chunk=512, state_in=None, state_out=None, gammas=None,
+                          rotary_base=0.0, pos_offset=0, eps=1e-5, out=None, error_word=None):
+    """The chunkwise form through the entry point that allocates nothing: the
+    library's static scratch replaces the workspace (calls on one device must
+    not overlap in time). `out` must be given (nothing is allocated here
+    either); error_word: optional GPU int32 tensor [1] that receives the
+    call's control word 1 in stream order."""
+    if out is None:
+        raise ValueError("chunkwise_fwd_noalloc allocates nothing: pass `out`")
+    _validate(q, k, v, g, out)
+    for name, t in (("state_in", state_in), ("state_out", state_out)):
+        if t is not None:
+            b, _, h, dk = q.shape
+            _on_device(name, t, q)
+            if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != (b, h, dk, v.shape[-1]):
+                raise ValueError(f"{name} must be a contiguous fp32 [batch, heads, dk, dv] tensor")
+    if error_word is not None:
+        _on_device("error_word", error_word, q)
+        if error_word.dtype != torch.int32 or error_word.numel() < 1 or not error_word.is_contiguous():
+            raise ValueError("error_word must be a contiguous GPU int32 tensor of at least one element")
+    desc, keep = _desc_for(q, v, gammas, rotary_base, pos_offset, eps)
+    _check(lib().retention_chunkwise_fwd_noalloc(ctypes.byref(desc), int(chunk), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                                 _ptr(out), _ptr(state_in), _ptr(state_out), _ptr(error_word),
+                                                 _stream(q)))
+    del keep
     return out
 
 

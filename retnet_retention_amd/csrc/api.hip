@@ -3,6 +3,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "launch.hpp"
 #include "retention.h"
@@ -172,6 +173,89 @@ size_t cbwd_bytes(const ret_desc_t* d, int32_t chunk, bool gate, bool states) {
          (states ? 4 * state_bytes(d) : 0);
 }
 
+// Chunkwise forward: every check that does not involve the workspace.
+ret_status_t check_chunkwise_args(const ret_desc_t* desc, int32_t chunk, const void* q, const void* k,
+                                  const void* v, const void* g, const void* o, const float* state_in,
+                                  const float* state_out) {
+  ret_status_t st = check_desc(desc);
+  if (st != RET_OK) return st;
+  if (chunk < 1) return RET_ERR_SHAPE;
+  if ((st = check_tensors(desc, q, k, v, g, o)) != RET_OK) return st;
+  if ((st = check_eps(desc, g)) != RET_OK) return st;
+  if ((state_in && !aligned16(state_in)) || (state_out && !aligned16(state_out))) return RET_ERR_ALIGN;
+  // the written buffers (o, state_out) overlap nothing else; state_in ==
+  // state_out exactly is allowed (the kernel reads every state_in value
+  // before the last chunk writes state_out)
+  const size_t n = tensor_bytes(desc), ns = state_bytes_exact(desc);
+  if (overlaps(o, n, state_in, ns) || overlaps(o, n, state_out, ns)) return RET_ERR_ALIAS;
+  if (overlaps(state_out, ns, q, n) || overlaps(state_out, ns, k, n) || overlaps(state_out, ns, v, n) ||
+      overlaps(state_out, ns, g, n) || (state_out != state_in && overlaps(state_out, ns, state_in, ns)))
+    return RET_ERR_ALIAS;
+  return RET_OK;
+}
+
+// Workspace bytes of the chunkwise forward: control block | rotation
+// (optional) | fp32 state chain | per-chunk states.
+size_t chunkwise_bytes(const ret_desc_t* desc, int32_t chunk) {
+  return ctrl_bytes(desc, chunk) + rot_bytes(desc) + chain_bytes(desc) + snap_bytes(desc, chunk);
+}
+
+// The chunkwise forward's launches over a checked workspace `ws` of at
+// least chunkwise_bytes() bytes.
+ret_status_t launch_chunkwise(const ret_desc_t* desc, int32_t chunk, const void* q, const void* k, const void* v,
+                              const void* g, void* o, const float* state_in, float* state_out, char* ws,
+                              hipStream_t stream, hipEvent_t before, hipEvent_t after) {
+  const size_t cb = ctrl_bytes(desc, chunk), rb = rot_bytes(desc), hb = chain_bytes(desc);
+  const Shape s = make_shape(desc);
+  const int32_t c = eff_chunk(desc, chunk);
+  int* ctrl = reinterpret_cast<int*>(ws);
+  const float2* table;
+  if (!rotate_inputs(desc, k, &table, ws + cb, stream)) return RET_ERR_HIP;
+  float* chain = reinterpret_cast<float*>(ws + cb + rb);
+  void* snap = ws + cb + rb + hb;
+  if (ret::launch_retention_fwd(s, c, true, q, k, v, g, o, state_in, state_out, snap, chain, ctrl, table,
+                                desc->gn_eps, stream, before, after) != hipSuccess)
+    return RET_ERR_HIP;
+  return RET_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Static scratch of retention_chunkwise_fwd_noalloc, for callers that cannot
+// allocate device memory. Each device the library runs on holds one copy of
+// this array for the life of the process. Host code never uses the array's
+// name as an address (on the host it names a stand-in, not device memory):
+// the device address comes from hipGetSymbolAddress, once per device, with
+// that device current, and only that pointer is passed on.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = size_t(128) << 20;
+static __device__ __align__(256) __attribute__((used)) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device, null until looked up
+
+// The scratch's device address on the device of `stream` (the current device
+// for the null stream).
+ret_status_t scratch_for(hipStream_t stream, char** out) {
+  int dev = 0;
+  if (stream ? hipStreamGetDevice(stream, &dev) != hipSuccess : hipGetDevice(&dev) != hipSuccess)
+    return RET_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return RET_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = 0;
+    if (hipGetDevice(&cur) != hipSuccess) return RET_ERR_HIP;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return RET_ERR_HIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev && hipSetDevice(cur) != hipSuccess) return RET_ERR_HIP;
+    if (e != hipSuccess || !p) return RET_ERR_HIP;
+    g_scratch_ptr[dev] = static_cast<char*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return RET_OK;
+}
+
 ret_status_t chunkwise_bwd_impl(const ret_desc_t* desc, int32_t chunk, const void* q, const void* k, const void* v,
                                 const void* g, const void* dout, const float* state_in, const float* d_state_out,
                                 void* dq, void* dk, void* dv, void* dg, float* d_state_in, void* workspace,
@@ -323,6 +407,7 @@ const char* retention_status_string(ret_status_t s) {
     case RET_ERR_HIP: return "HIP runtime error at kernel launch";
     case RET_ERR_ALIAS: return "output overlaps an input";
     case RET_ERR_ARG: return "invalid scalar argument (gn_eps, rotary_base or pos_offset)";
+    case RET_ERR_SCRATCH: return "the call needs more scratch than the library's static buffer holds (128 MiB)";
   }
   return "unknown status";
 }
@@ -490,48 +575,49 @@ ret_status_t retention_chunkwise_bwd_state(const ret_desc_t* desc, int32_t chunk
 
 size_t retention_chunkwise_workspace_bytes(const ret_desc_t* desc, int32_t chunk) {
   if (check_desc(desc) != RET_OK || chunk < 1) return 0;
-  return ctrl_bytes(desc, chunk) + rot_bytes(desc) + chain_bytes(desc) + snap_bytes(desc, chunk);
+  return chunkwise_bytes(desc, chunk);
 }
 
 ret_status_t retention_chunkwise_fwd_timed(const ret_desc_t* desc, int32_t chunk, const void* q, const void* k,
                                            const void* v, const void* g, void* o, const float* state_in,
                                            float* state_out, void* workspace, size_t workspace_bytes,
                                            hipStream_t stream, hipEvent_t before, hipEvent_t after) {
-  ret_status_t st = check_desc(desc);
+  ret_status_t st = check_chunkwise_args(desc, chunk, q, k, v, g, o, state_in, state_out);
   if (st != RET_OK) return st;
-  if (chunk < 1) return RET_ERR_SHAPE;
-  if ((st = check_tensors(desc, q, k, v, g, o)) != RET_OK) return st;
-  if ((st = check_eps(desc, g)) != RET_OK) return st;
-  if ((state_in && !aligned16(state_in)) || (state_out && !aligned16(state_out))) return RET_ERR_ALIGN;
-  const size_t cb = ctrl_bytes(desc, chunk), rb = rot_bytes(desc), hb = chain_bytes(desc);
-  const size_t need = cb + rb + hb + snap_bytes(desc, chunk);
+  const size_t need = chunkwise_bytes(desc, chunk);
   if (!workspace || workspace_bytes < need) return RET_ERR_WORKSPACE;
   if (!aligned16(workspace)) return RET_ERR_ALIGN;
-  // the written buffers (o, state_out, workspace) overlap nothing else;
-  // state_in == state_out exactly is allowed (the kernel reads every state_in
-  // value before the last chunk writes state_out)
   {
     const size_t n = tensor_bytes(desc), ns = state_bytes_exact(desc);
-    if (overlaps(o, n, state_in, ns) || overlaps(o, n, state_out, ns)) return RET_ERR_ALIAS;
-    if (overlaps(state_out, ns, q, n) || overlaps(state_out, ns, k, n) || overlaps(state_out, ns, v, n) ||
-        overlaps(state_out, ns, g, n) || (state_out != state_in && overlaps(state_out, ns, state_in, ns)))
-      return RET_ERR_ALIAS;
     const void* all[] = {q, k, v, g, o, state_in, state_out};
     const size_t all_n[] = {n, n, n, n, n, ns, ns};
     for (int j = 0; j < 7; ++j)
       if (overlaps(workspace, need, all[j], all_n[j])) return RET_ERR_ALIAS;
   }
+  return launch_chunkwise(desc, chunk, q, k, v, g, o, state_in, state_out, static_cast<char*>(workspace), stream,
+                          before, after);
+}
 
-  const Shape s = make_shape(desc);
-  const int32_t c = eff_chunk(desc, chunk);
-  char* ws = static_cast<char*>(workspace);
-  int* ctrl = reinterpret_cast<int*>(ws);
-  const float2* table;
-  if (!rotate_inputs(desc, k, &table, ws + cb, stream)) return RET_ERR_HIP;
-  float* chain = reinterpret_cast<float*>(ws + cb + rb);
-  void* snap = ws + cb + rb + hb;
-  if (ret::launch_retention_fwd(s, c, true, q, k, v, g, o, state_in, state_out, snap, chain, ctrl, table,
-                                desc->gn_eps, stream, before, after) != hipSuccess)
+ret_status_t retention_chunkwise_fwd_noalloc(const ret_desc_t* desc, int32_t chunk, const void* q, const void* k,
+                                             const void* v, const void* g, void* o, const float* state_in,
+                                             float* state_out, int32_t* error_word, hipStream_t stream) {
+  ret_status_t st = check_chunkwise_args(desc, chunk, q, k, v, g, o, state_in, state_out);
+  if (st != RET_OK) return st;
+  if (chunkwise_bytes(desc, chunk) > kScratchBytes) return RET_ERR_SCRATCH;
+  if (error_word) {
+    if ((reinterpret_cast<uintptr_t>(error_word) & 3u) != 0) return RET_ERR_ALIGN;
+    const size_t n = tensor_bytes(desc), ns = state_bytes_exact(desc);
+    const void* all[] = {q, k, v, g, o, state_in, state_out};
+    const size_t all_n[] = {n, n, n, n, n, ns, ns};
+    for (int j = 0; j < 7; ++j)
+      if (overlaps(error_word, sizeof(int32_t), all[j], all_n[j])) return RET_ERR_ALIAS;
+  }
+  char* ws = nullptr;
+  if ((st = scratch_for(stream, &ws)) != RET_OK) return st;
+  if ((st = launch_chunkwise(desc, chunk, q, k, v, g, o, state_in, state_out, ws, stream, nullptr, nullptr)) !=
+      RET_OK)
+    return st;
+  if (error_word && ret::launch_copy_word(reinterpret_cast<const int*>(ws) + 1, error_word, stream) != hipSuccess)
     return RET_ERR_HIP;
   return RET_OK;
 }

@@ -57,6 +57,9 @@ hipError_t launch_retention_fwd(const Shape& s, int chunk, bool chunked, const v
                                 bool out_rev = false, const float2* out_rot = nullptr, const int* cu = nullptr,
                                 int total = 0, void* sched = nullptr, bool keep_err = false);
 
+// *dst = *src on the device, in stream order (one int).
+hipError_t launch_copy_word(const int* src, int* dst, hipStream_t stream);
+
 // Backward passes of the parallel form (all tensors [batch][seqlen][heads][d]
 // of the descriptor's dtype): the gradient through the swish gate and the
 // per-head GroupNorm (o: the retention output before GroupNorm; `dov_rev`,

@@ -1092,6 +1092,16 @@ __global__ void reset_ctrl_kernel(int* ctrl, int n, int keep_err) {
     if (!(keep_err && i == 1)) ctrl[i] = 0;
 }
 
+// One int copied on the device (a caller's copy of the error word).
+__global__ void copy_word_kernel(const int* src, int* dst) {
+  if (threadIdx.x == 0) *dst = *src;
+}
+
+hipError_t launch_copy_word(const int* src, int* dst, hipStream_t stream) {
+  hipLaunchKernelGGL(copy_word_kernel, dim3(1), dim3(64), 0, stream, src, dst);
+  return hipGetLastError();
+}
+
 template <typename T, int D, bool FAST>
 static hipError_t launch_fwd_impl(const Shape& s, int chunk, FwdParams p, bool chunked, hipStream_t stream,
                                   hipEvent_t before, hipEvent_t after, bool keep_err) {

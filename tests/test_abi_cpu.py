@@ -63,8 +63,9 @@ def _step(L, d, q=ALIGNED, k=ALIGNED * 2, v=ALIGNED * 3, g=None, o=ALIGNED * 4, 
 
 
 def test_status_strings(L):
-    for code in range(10):
+    for code in range(11):
         assert L.retention_status_string(code)
+    assert b"scratch" in L.retention_status_string(10)
     assert L.retention_status_string(0) == b"ok"
 
 
@@ -283,3 +284,27 @@ def test_chunkwise_error_reader_validates(L):
     assert L.retention_chunkwise_error(ALIGNED, 64, None, None) == 1
     assert L.retention_chunkwise_error(ALIGNED, 4, ctypes.byref(word), None) == 6
     assert L.retention_chunkwise_error(ALIGNED + 4, 64, ctypes.byref(word), None) == 5
+
+
+def test_noalloc_validates_before_any_device_call(L):
+    """The allocation-free chunkwise call checks its arguments like the
+    workspace call and rejects calls needing more than its 128 MiB scratch
+    (RET_ERR_SCRATCH) before it looks anything up on a device."""
+    def call(d, q=ALIGNED, o=ALIGNED * 4, si=None, so=None, err=None, chunk=64):
+        return L.retention_chunkwise_fwd_noalloc(ctypes.byref(d), chunk, q, ALIGNED * 2, ALIGNED * 3, None, o, si,
+                                                 so, err, None)
+
+    d, _ = _desc()
+    assert call(d, chunk=0) == 2
+    assert call(d, q=None) == 1
+    assert call(d, o=ALIGNED + 256) == 8
+    assert call(d, so=ALIGNED * 2 + 64) == 8
+    assert call(d, err=ALIGNED * 7 + 2) == 5
+    assert call(d, err=ALIGNED * 4 + 64) == 8  # the error word inside the output
+    # 8 x 8192 tokens, 16 heads x 256: 268 MB of per-chunk states alone
+    big, _ = _desc(batch=8, seqlen=8192, heads=16)
+    assert L.retention_chunkwise_workspace_bytes(ctypes.byref(big), 512) > 128 << 20
+    assert call(big, chunk=512) == 10
+    # the 7B long-context shape fits
+    d7, _ = _desc(batch=2, seqlen=8192, heads=16)
+    assert L.retention_chunkwise_workspace_bytes(ctypes.byref(d7), 512) <= 128 << 20
