@@ -477,13 +477,41 @@ struct LTile {
 // each lane's row. Completion: s_waitcnt vmcnt + barrier.
 constexpr int kBufferWord3 = 0x00020000;  // raw 32-bit buffer descriptor, gfx9 family
 
-// buffer descriptor of a wave-uniform base address, in scalar registers
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t scalar_rsrc(const void* base) {
+// buffer descriptor of a wave-uniform base address, in scalar registers;
+// accesses at byte offsets from `bytes` on are dropped (stores) or read as
+// zero (loads) by the hardware
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t scalar_rsrc(const void* base, uint32_t bytes = 0xffffffffu) {
   const uint64_t a = reinterpret_cast<uint64_t>(base);
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
-  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(((uint64_t)hi << 32) | lo), (short)0, -1,
-                                           kBufferWord3);
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(((uint64_t)hi << 32) | lo), (short)0,
+                                           (int)__builtin_amdgcn_readfirstlane(bytes), kBufferWord3);
+}
+
+// 16 loaded bytes of T (8 bf16 or 4 fp32 elements) to floats, and floats
+// to 16 bytes of T stored through a buffer descriptor
+typedef uint32_t u32x4b __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void load16f_raw(u32x4b w, float* v, bf16*) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void load16f_raw(u32x4b w, float* v, float*) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = __uint_as_float(w[i]);
+}
+__device__ __forceinline__ void store16f_raw(__amdgpu_buffer_rsrc_t rs, uint32_t off, const float* v, bf16*) {
+  bf16x8 o;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = (bf16)v[i];
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4b, o), rs, off, 0, 0);
+}
+__device__ __forceinline__ void store16f_raw(__amdgpu_buffer_rsrc_t rs, uint32_t off, const float* v, float*) {
+  __builtin_amdgcn_raw_buffer_store_b128(u32x4b{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                                                __float_as_uint(v[3])},
+                                         rs, off, 0, 0);
 }
 
 template <typename T, typename TL, int NW>

@@ -222,15 +222,10 @@ __device__ __forceinline__ void store4_coherent(__amdgpu_buffer_rsrc_t rs, uint3
                                                 const f32x4& x) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), rs, voff, soff, kSc1);
 }
-__device__ __forceinline__ void store2_coherent(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff, float x0,
-                                                float x1) {
-  typedef float f32x2 __attribute__((ext_vector_type(2)));
-  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, f32x2{x0, x1}), rs, voff, soff, kSc1);
-}
 // volatile (bit 31 of the policy word, a compiler-side flag): the loads keep
 // their place relative to scheduling barriers
-__device__ __forceinline__ u32x2 load2_coherent(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff) {
-  return __builtin_amdgcn_raw_buffer_load_b64(rs, voff, soff, kSc1 | (int)0x80000000u);
+__device__ __forceinline__ u32x4 load4_coherent(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, kSc1 | (int)0x80000000u);
 }
 
 // First row and length of sequence b: b * seqlen and seqlen for a batch of
@@ -564,15 +559,32 @@ __device__ __forceinline__ void out_role(const FwdParams& p, int bh, int ci, int
         }
       scale = f * rsqrtf(f * f * (sum_pair32(s2) * (1.0f / D)) + p.eps);
     }
+    const float shift = -mean * scale;  // normalized value: o scale + shift
+    // The rows of this tile: gate loads and output stores as buffer
+    // accesses from a wave-uniform base (the tile's first row) and a 32-bit
+    // lane offset. The forward's stores go through a descriptor whose size
+    // ends at the chunk's last row, so the stores of rows past it are
+    // dropped by the hardware instead of branched around.
+    const int row0 = qw0 + 32 * r;
+    // rows of the tile inside the chunk: none for a wave past a short last
+    // chunk's end (its gate rows clamp to the chunk's last row, and nothing
+    // of it is stored)
+    const int rows_in = cend - row0;
+    const int grow0 = min(row0, cend - 1);  // gate base row: every clamped row is at or after it
+    constexpr uint32_t RB = (uint32_t)sizeof(T);
     static_for<D / SG::HALF>([&](auto h_c) __attribute__((always_inline)) {
       constexpr int H = decltype(h_c)::value;
       // this pass's gate values, 16 bytes per row access, ahead of their use
       const int lrow = lane / LPR, lcol = (lane % LPR) * CPL;
       float g[32 / RPA][CPL];
       if (G) {
+        const __amdgpu_buffer_rsrc_t grs = scalar_rsrc(G + (int64_t)grow0 * tstride + H * SG::HALF);
 #pragma unroll
-        for (int k = 0; k < 32 / RPA; ++k)
-          load16f(G + (int64_t)min(qw0 + 32 * r + k * RPA + lrow, cend - 1) * tstride + H * SG::HALF + lcol, g[k]);
+        for (int k = 0; k < 32 / RPA; ++k) {
+          const int grow = min(row0 + k * RPA + lrow, cend - 1);
+          const uint32_t off = (uint32_t)(((grow - grow0) * tstride + lcol) * RB);
+          load16f_raw(__builtin_amdgcn_raw_buffer_load_b128(grs, off, 0, 0), g[k], (T*)nullptr);
+        }
       }
       // normalized values of dv tiles H HALF/32 .. into the staging rows
 #pragma unroll
@@ -581,10 +593,17 @@ __device__ __forceinline__ void out_role(const FwdParams& p, int bh, int ci, int
         for (int a = 0; a < 4; ++a) {
           const int col = 32 * t - H * SG::HALF + 8 * a + 4 * hh;
           *reinterpret_cast<f32x4*>(stg + n * SG::EROW + col * 4) =
-              f32x4{(oacc[r][t][4 * a] - mean) * scale, (oacc[r][t][4 * a + 1] - mean) * scale,
-                    (oacc[r][t][4 * a + 2] - mean) * scale, (oacc[r][t][4 * a + 3] - mean) * scale};
+              f32x4{__builtin_fmaf(oacc[r][t][4 * a], scale, shift), __builtin_fmaf(oacc[r][t][4 * a + 1], scale, shift),
+                    __builtin_fmaf(oacc[r][t][4 * a + 2], scale, shift),
+                    __builtin_fmaf(oacc[r][t][4 * a + 3], scale, shift)};
         }
-      // along the rows: gate, store
+      // along the rows: gate, store; the descriptor covers rows row0 ..
+      // cend - 1 (the last row only up to this half's end: its bytes past
+      // that belong to the next head)
+      [[maybe_unused]] __amdgpu_buffer_rsrc_t ors;
+      if constexpr (!XF)
+        ors = scalar_rsrc(O + (int64_t)grow0 * tstride + H * SG::HALF,
+                          rows_in > 0 ? (uint32_t)(((rows_in - 1) * tstride + SG::HALF) * RB) : 0u);
 #pragma unroll
       for (int k = 0; k < 32 / RPA; ++k) {
         const int rr = k * RPA + lrow, orow = qw0 + 32 * r + rr;
@@ -599,13 +618,15 @@ __device__ __forceinline__ void out_role(const FwdParams& p, int bh, int ci, int
 #pragma unroll
           for (int e = 0; e < CPL; ++e) y[e] *= swish(g[k][e]);
         }
-        if (orow < cend) {
-          int mrow = orow;  // stored position
-          if constexpr (XF) {
+        if constexpr (XF) {
+          if (orow < cend) {
+            int mrow = orow;  // stored position
             if (p.out_rev) mrow = p.seqlen - 1 - orow;
             if (p.out_rot) unrotate_pairs<CPL>(y, p.out_rot + (int64_t)mrow * (D / 2) + (H * SG::HALF + lcol) / 2);
+            store16f(O + (int64_t)mrow * tstride + H * SG::HALF + lcol, y);
           }
-          store16f(O + (int64_t)mrow * tstride + H * SG::HALF + lcol, y);
+        } else {
+          store16f_raw(ors, (uint32_t)((rr * tstride + lcol) * RB), y, (T*)nullptr);
         }
       }
     });
@@ -830,39 +851,37 @@ __device__ __forceinline__ void state_role(const FwdParams& p, int bh, int ci, i
 
   // R_i = g^b R_{i-1} + dR_i. The fp32 chain keeps R in this role's
   // accumulator layout (16 contiguous floats per lane and tile), so the next
-  // chunk's workgroup of the same part reads it back coalesced: element pair
-  // q of tile (mt, nt) of a wave sits at a wave-uniform offset, its lanes'
-  // 8-byte accesses covering 512 contiguous bytes.
+  // chunk's workgroup of the same part reads it back coalesced: element
+  // group q (4 floats) of tile (mt, nt) of a wave sits at a wave-uniform
+  // offset, its lanes' 16-byte accesses covering 1 KiB of contiguous bytes.
   auto chain_rsrc = [&](int slot) __attribute__((always_inline)) {
     return scalar_rsrc(p.chain + ((int64_t)bh * 2 + slot) * D * D);
   };
   auto chain_soff = [&](int mt, int nt, int q) __attribute__((always_inline)) {
-    return (uint32_t)((((((part * SC::NW + wave) * SC::MTW + mt) * SC::NTW + nt) * 8 + q) * 64) * 8);
+    return (uint32_t)((((((part * SC::NW + wave) * SC::MTW + mt) * SC::NTW + nt) * 4 + q) * 64) * 16);
   };
-  const uint32_t chain_voff = (uint32_t)lane * 8u;
+  const uint32_t chain_voff = (uint32_t)lane * 16u;
   if (ci > 0) {
     wait_flag(flag_of(ci, 0), p.ctrl + 1);
     if (active) {
       const __amdgpu_buffer_rsrc_t rs = chain_rsrc((ci - 1) & 1);
-      typedef float f32x2 __attribute__((ext_vector_type(2)));
       // one 32-row tile at a time, every load of the tile in flight before
       // the first use (the compiler would otherwise wait on each in turn)
 #pragma unroll
       for (int mt = 0; mt < SC::MTW; ++mt) {
-        uint64_t r[SC::NTW][8];
+        u32x4 r[SC::NTW][4];
 #pragma unroll
         for (int nt = 0; nt < SC::NTW; ++nt)
 #pragma unroll
-          for (int q = 0; q < 8; ++q)
-            r[nt][q] = __builtin_bit_cast(uint64_t, load2_coherent(rs, chain_voff, chain_soff(mt, nt, q)));
+          for (int q = 0; q < 4; ++q) r[nt][q] = load4_coherent(rs, chain_voff, chain_soff(mt, nt, q));
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int nt = 0; nt < SC::NTW; ++nt)
 #pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            const f32x2 x = __builtin_bit_cast(f32x2, r[nt][q]);
-            racc[mt][nt][2 * q] += dec * x[0];
-            racc[mt][nt][2 * q + 1] += dec * x[1];
+          for (int q = 0; q < 4; ++q) {
+            const f32x4 x = __builtin_bit_cast(f32x4, r[nt][q]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) racc[mt][nt][4 * q + e] += dec * x[e];
           }
         __builtin_amdgcn_sched_barrier(0);  // the next tile's loads stay behind this one's uses
       }
@@ -877,8 +896,10 @@ __device__ __forceinline__ void state_role(const FwdParams& p, int bh, int ci, i
 #pragma unroll
         for (int nt = 0; nt < SC::NTW; ++nt)
 #pragma unroll
-          for (int q = 0; q < 8; ++q)
-            store2_coherent(rs, chain_voff, chain_soff(mt, nt, q), racc[mt][nt][2 * q], racc[mt][nt][2 * q + 1]);
+          for (int q = 0; q < 4; ++q)
+            store4_coherent(rs, chain_voff, chain_soff(mt, nt, q), (float*)nullptr,
+                            f32x4{racc[mt][nt][4 * q], racc[mt][nt][4 * q + 1], racc[mt][nt][4 * q + 2],
+                                  racc[mt][nt][4 * q + 3]});
     }
     release_flag(flag_of(ci + 1, 0));
     if (active) write_snapshot(snap_next, racc);
