@@ -918,7 +918,9 @@ __device__ __forceinline__ void state_role(const FwdParams& p, int bh, int ci, i
 // ---------------------------------------------------------------------------
 // Kernels.
 // ---------------------------------------------------------------------------
-template <typename T, int D, bool FAST>
+// XF: the instantiation for the backward's products (reversed query reads,
+// transforming stores); the forward's carries none of that code.
+template <typename T, int D, bool FAST, bool XF = false>
 __global__ __launch_bounds__(kWaves<T> * 64, 1) void retention_parallel_kernel(FwdParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the kernel's signature
   __shared__ __attribute__((aligned(1024))) char l0[Stage<T, D>::BYTES];
@@ -942,7 +944,7 @@ __global__ __launch_bounds__(kWaves<T> * 64, 1) void retention_parallel_kernel(F
     bh = bid % groups;
     qb = p.qblocks - 1 - bid / groups;
   }
-  out_role<T, D, FAST, false, true>(p, bh, 0, qb, false, l0, l1, l2, l3);
+  out_role<T, D, FAST, false, XF>(p, bh, 0, qb, false, l0, l1, l2, l3);
 #endif
 }
 
@@ -1133,7 +1135,12 @@ static hipError_t launch_fwd_impl(const Shape& s, int chunk, FwdParams p, bool c
     const int64_t blocks = (int64_t)bhs * p.qblocks;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     if (before && hipEventRecord(before, stream) != hipSuccess) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((retention_parallel_kernel<T, D, FAST>), dim3((unsigned)blocks), dim3(64 * C::WAVES), 0, stream, p);
+    if (p.q_rev || p.out_rev || p.out_rot)
+      hipLaunchKernelGGL((retention_parallel_kernel<T, D, FAST, true>), dim3((unsigned)blocks), dim3(64 * C::WAVES), 0,
+                         stream, p);
+    else
+      hipLaunchKernelGGL((retention_parallel_kernel<T, D, FAST>), dim3((unsigned)blocks), dim3(64 * C::WAVES), 0,
+                         stream, p);
     const hipError_t e = hipGetLastError();
     if (e == hipSuccess && after && hipEventRecord(after, stream) != hipSuccess) return hipErrorInvalidValue;
     return e;
