@@ -526,24 +526,19 @@ ret_status_t retention_parallel_bwd(const ret_desc_t* desc, const void* q, const
     if (ret::launch_reverse_tokens(s, dout, dorev, stream) != hipSuccess) return RET_ERR_HIP;
   }
   // Three forward products, each storing its gradient straight into the
-  // caller's tensor (turned back by the rotation where it applies):
+  // caller's tensor (turned back by the rotation where it applies), in one
+  // grid:
   //   dq = rot^T(P(dO, V, K'));
   //   dk = rot^T(rev P(rev V, rev dO, rev Q')), the transposed mask made
   //        causal by reversing every sequence (q read reversed, output
   //        stored reversed);
   //   dv = rev P(rev K', rev Q', rev dO).
-  const hipEvent_t none = nullptr;
-  if (ret::launch_retention_fwd(s, desc->seqlen, false, dov ? dov : dorev, v, kr, nullptr, dq, nullptr, nullptr,
-                                nullptr, nullptr, nullptr, nullptr, desc->gn_eps, stream, none, none, dov == nullptr,
-                                false, table) !=
-          hipSuccess ||
-      ret::launch_retention_fwd(s, desc->seqlen, false, v, dorev, qrev, nullptr, dk, nullptr, nullptr, nullptr,
-                                nullptr, nullptr, nullptr, desc->gn_eps, stream, none, none, true, true, table) !=
-          hipSuccess ||
-      ret::launch_retention_fwd(s, desc->seqlen, false, kr, qrev, dorev, nullptr, dv, nullptr, nullptr, nullptr,
-                                nullptr, nullptr, nullptr, desc->gn_eps, stream, none, none, true, true, nullptr) !=
-          hipSuccess)
-    return RET_ERR_HIP;
+  const ret::ParallelProduct prods[3] = {
+      {dov ? dov : dorev, v, kr, dq, dov == nullptr, false, table},
+      {v, dorev, qrev, dk, true, true, table},
+      {kr, qrev, dorev, dv, true, true, nullptr},
+  };
+  if (ret::launch_parallel_products(s, 3, prods, desc->gn_eps, stream) != hipSuccess) return RET_ERR_HIP;
   return RET_OK;
 }
 

@@ -57,6 +57,20 @@ hipError_t launch_retention_fwd(const Shape& s, int chunk, bool chunked, const v
                                 bool out_rev = false, const float2* out_rot = nullptr, const int* cu = nullptr,
                                 int total = 0, void* sched = nullptr, bool keep_err = false);
 
+// Up to three parallel-form products of shape s with no state in one grid
+// (q_rev, out_rev, out_rot as above; no rotation of q on load): the
+// backward's gradient products, none of which reads another's output.
+struct ParallelProduct {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  bool q_rev, out_rev;
+  const float2* out_rot;
+};
+hipError_t launch_parallel_products(const Shape& s, int n, const ParallelProduct* products, float eps,
+                                    hipStream_t stream);
+
 // *dst = *src on the device, in stream order (one int).
 hipError_t launch_copy_word(const int* src, int* dst, hipStream_t stream);
 

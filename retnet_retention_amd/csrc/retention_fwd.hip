@@ -948,6 +948,45 @@ __global__ __launch_bounds__(kWaves<T> * 64, 1) void retention_parallel_kernel(F
 #endif
 }
 
+// Several parallel-form products of one shape in one grid (the backward's
+// three gradient products, which share no inputs' roles but none waits for
+// another): dealt out longest query block first across all of them, so that
+// the long blocks of every product start at once and the short blocks of all
+// fill the end, instead of each launch ending on its own long blocks.
+constexpr int kMaxProducts = 3;
+struct MultiParams {
+  FwdParams p[kMaxProducts];
+  int nprod;
+};
+
+template <typename T, int D, bool FAST>
+__global__ __launch_bounds__(kWaves<T> * 64, 1) void retention_parallel_multi_kernel(MultiParams mp) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __shared__ __attribute__((aligned(1024))) char l0[Stage<T, D>::BYTES];
+  __shared__ __attribute__((aligned(1024))) char l1[Stage<T, D>::BYTES];
+  __shared__ __attribute__((aligned(1024))) char l2[Stage<T, D>::BYTES];
+  __shared__ __attribute__((aligned(1024))) char l3[Stage<T, D>::BYTES];
+  const int nprod = mp.nprod;
+  const int groups = mp.p[0].batch * mp.p[0].heads;
+  const int bid = blockIdx.x;
+  int prod, bh, qb;
+  if (groups % 8 == 0) {  // a pair's query blocks stay on one XCD, as in the single launch
+    const int xcd = bid & 7, slot = bid >> 3, per = groups / 8;
+    qb = mp.p[0].qblocks - 1 - slot / (per * nprod);
+    const int r = slot % (per * nprod);
+    prod = r / per;
+    bh = xcd + 8 * (r % per);
+  } else {
+    qb = mp.p[0].qblocks - 1 - bid / (groups * nprod);
+    const int r = bid % (groups * nprod);
+    prod = r / groups;
+    bh = r % groups;
+  }
+  prod = uniform_i(prod);
+  out_role<T, D, FAST, false, true>(mp.p[prod], uniform_i(bh), 0, uniform_i(qb), false, l0, l1, l2, l3);
+#endif
+}
+
 template <typename T, int D, bool FAST, bool XF = false>
 __global__ __launch_bounds__(kWaves<T> * 64, 1) void retention_chunkwise_kernel(FwdParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the kernel's signature
@@ -1199,14 +1238,12 @@ size_t chunkwise_ctrl_bytes(int batch, int heads, int nchunks) {
   return ((size_t)kCtrlHead + (size_t)batch * heads * (nchunks + 1) * kFlagsPerChunk) * sizeof(int);
 }
 
-hipError_t launch_retention_fwd(const Shape& s, int chunk, bool chunked, const void* q, const void* k, const void* v,
-                                const void* g, void* o, const float* state_in, float* state_out, void* snap,
-                                float* chain, int* ctrl, const float2* rot, float eps, hipStream_t stream,
-                                hipEvent_t before, hipEvent_t after, bool q_rev, bool out_rev,
-                                const float2* out_rot, const int* cu, int total, void* sched, bool keep_err) {
-  if (rot && q_rev) return hipErrorInvalidValue;  // q's angles are those of its own positions
-  // packed sequences: chunkwise form, forward only, with a schedule buffer
-  if (cu && (!chunked || q_rev || out_rev || out_rot || !sched)) return hipErrorInvalidValue;
+// Kernel parameters of one launch (see launch_retention_fwd for the fields'
+// meaning); qblocks and xcd_order are set by the launcher.
+static FwdParams make_params(const Shape& s, int chunk, const void* q, const void* k, const void* v, const void* g,
+                             void* o, const float* state_in, float* state_out, void* snap, float* chain, int* ctrl,
+                             const float2* rot, float eps, bool q_rev, bool out_rev, const float2* out_rot,
+                             const int* cu, int total, void* sched) {
   FwdParams p;
   p.cu = cu;
   p.total = total;
@@ -1236,6 +1273,19 @@ hipError_t launch_retention_fwd(const Shape& s, int chunk, bool chunked, const v
   p.xcd_order = 0;
   p.eps = eps;
   for (int h = 0; h < kMaxHeads; ++h) p.log2g[h] = h < s.heads ? s.log2g[h] : 0.f;
+  return p;
+}
+
+hipError_t launch_retention_fwd(const Shape& s, int chunk, bool chunked, const void* q, const void* k, const void* v,
+                                const void* g, void* o, const float* state_in, float* state_out, void* snap,
+                                float* chain, int* ctrl, const float2* rot, float eps, hipStream_t stream,
+                                hipEvent_t before, hipEvent_t after, bool q_rev, bool out_rev,
+                                const float2* out_rot, const int* cu, int total, void* sched, bool keep_err) {
+  if (rot && q_rev) return hipErrorInvalidValue;  // q's angles are those of its own positions
+  // packed sequences: chunkwise form, forward only, with a schedule buffer
+  if (cu && (!chunked || q_rev || out_rev || out_rot || !sched)) return hipErrorInvalidValue;
+  FwdParams p = make_params(s, chunk, q, k, v, g, o, state_in, state_out, snap, chain, ctrl, rot, eps, q_rev, out_rev,
+                            out_rot, cu, total, sched);
   if (s.dtype == 1) {
     switch (s.d) {
       case 64: return launch_fwd_t<bf16, 64>(s, chunk, p, chunked, stream, before, after, keep_err);
@@ -1247,6 +1297,52 @@ hipError_t launch_retention_fwd(const Shape& s, int chunk, bool chunked, const v
       case 64: return launch_fwd_t<float, 64>(s, chunk, p, chunked, stream, before, after, keep_err);
       case 128: return launch_fwd_t<float, 128>(s, chunk, p, chunked, stream, before, after, keep_err);
       case 256: return launch_fwd_t<float, 256>(s, chunk, p, chunked, stream, before, after, keep_err);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename T, int D, bool FAST>
+static hipError_t launch_multi_impl(const Shape& s, MultiParams& mp, hipStream_t stream) {
+  using C = OutTile<T, D, FAST>;
+  const int qblocks = (s.seqlen + C::BM - 1) / C::BM;
+  for (int i = 0; i < mp.nprod; ++i) mp.p[i].qblocks = qblocks;
+  const int64_t blocks = (int64_t)s.batch * s.heads * qblocks * mp.nprod;
+  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((retention_parallel_multi_kernel<T, D, FAST>), dim3((unsigned)blocks), dim3(64 * C::WAVES), 0,
+                     stream, mp);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t launch_multi_t(const Shape& s, MultiParams& mp, hipStream_t stream) {
+  bool fast = true;
+  for (int h = 0; h < s.heads; ++h) fast = fast && -(double)s.log2g[h] * OutTile<T, D, true>::BM <= kFastSpanLog2;
+  return fast ? launch_multi_impl<T, D, true>(s, mp, stream) : launch_multi_impl<T, D, false>(s, mp, stream);
+}
+
+hipError_t launch_parallel_products(const Shape& s, int n, const ParallelProduct* pr, float eps,
+                                    hipStream_t stream) {
+  if (n < 1 || n > kMaxProducts) return hipErrorInvalidValue;
+  MultiParams mp;
+  mp.nprod = n;
+  for (int i = 0; i < kMaxProducts; ++i) {
+    const ParallelProduct& x = pr[i < n ? i : 0];
+    mp.p[i] = make_params(s, s.seqlen, x.q, x.k, x.v, nullptr, x.o, nullptr, nullptr, nullptr, nullptr, nullptr,
+                          nullptr, eps, x.q_rev, x.out_rev, x.out_rot, nullptr, 0, nullptr);
+  }
+  if (s.dtype == 1) {
+    switch (s.d) {
+      case 64: return launch_multi_t<bf16, 64>(s, mp, stream);
+      case 128: return launch_multi_t<bf16, 128>(s, mp, stream);
+      case 256: return launch_multi_t<bf16, 256>(s, mp, stream);
+    }
+  } else {
+    switch (s.d) {
+      case 64: return launch_multi_t<float, 64>(s, mp, stream);
+      case 128: return launch_multi_t<float, 128>(s, mp, stream);
+      case 256: return launch_multi_t<float, 256>(s, mp, stream);
     }
   }
   return hipErrorInvalidValue;

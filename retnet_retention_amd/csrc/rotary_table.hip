@@ -12,22 +12,32 @@
 
 namespace ret {
 
+// One thread per pair j and kRotPositions consecutive positions: the
+// frequency base^(-2j/d) is formed once per thread, the angles per position.
+constexpr int kRotPositions = 4;
 __global__ __launch_bounds__(256) void rotary_table_kernel(float2* __restrict__ table, int seqlen, int half,
                                                            double base, int64_t pos_offset, int d) {
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (int64_t)seqlen * half) return;
-  const int n = (int)(idx / half), j = (int)(idx % half);
+  const int64_t groups = (seqlen + kRotPositions - 1) / kRotPositions;
+  if (idx >= groups * half) return;
+  const int j = (int)(idx % half);
+  const int n0 = (int)(idx / half) * kRotPositions;
   const double theta = pow(base, -2.0 * j / d);
-  const double phi = (double)(pos_offset + n) * theta;
-  double s, c;
-  sincos(phi, &s, &c);
-  table[idx] = make_float2((float)c, (float)s);
+#pragma unroll
+  for (int i = 0; i < kRotPositions; ++i) {
+    const int n = n0 + i;
+    if (n >= seqlen) break;
+    const double phi = (double)(pos_offset + n) * theta;
+    double s, c;
+    sincos(phi, &s, &c);
+    table[(int64_t)n * half + j] = make_float2((float)c, (float)s);
+  }
 }
 
 hipError_t launch_rotary_table(float2* table, int seqlen, int d, double base, int64_t pos_offset,
                                hipStream_t stream) {
   const int half = d / 2;
-  const int64_t total = (int64_t)seqlen * half;
+  const int64_t total = (int64_t)((seqlen + kRotPositions - 1) / kRotPositions) * half;
   const unsigned blocks = (unsigned)((total + 255) / 256);
   hipLaunchKernelGGL(rotary_table_kernel, dim3(blocks), dim3(256), 0, stream, table, seqlen, half, base,
                      pos_offset, d);
