@@ -163,13 +163,17 @@ size_t bwd_bytes(const ret_desc_t* d, bool gate) {
 }
 
 
-// Backward of the chunkwise form: the chunkwise kernel's own workspace
-// (control block, state chain, per-chunk states), the parallel backward's
-// table and tensor slots, then with a carried state up to three fp32 states
-// (S0^T; the dS terms for the reversed products; their final state).
+// Backward of the chunkwise form: the chunkwise kernel's own workspace for
+// each of the three gradient products, which run in one launch (three
+// control blocks, then three state chains, then three sets of per-chunk
+// states; the recomputed forward uses the first of each), the parallel
+// backward's table and tensor slots, then with a carried state up to three
+// fp32 states (S0^T; the dS terms for the reversed products; their final
+// state).
+constexpr int kBwdProducts = 3;
 size_t state_bytes(const ret_desc_t* d) { return align_up((size_t)d->batch * d->heads * d->dk * d->dv * 4); }
 size_t cbwd_bytes(const ret_desc_t* d, int32_t chunk, bool gate, bool states) {
-  return ctrl_bytes(d, chunk) + chain_bytes(d) + snap_bytes(d, chunk) + bwd_bytes(d, gate) +
+  return kBwdProducts * (ctrl_bytes(d, chunk) + chain_bytes(d) + snap_bytes(d, chunk)) + bwd_bytes(d, gate) +
          (states ? 4 * state_bytes(d) : 0);
 }
 
@@ -299,10 +303,13 @@ ret_status_t chunkwise_bwd_impl(const ret_desc_t* desc, int32_t chunk, const voi
   const Shape s = make_shape(desc);
   const int32_t c = eff_chunk(desc, chunk);
   char* ws = static_cast<char*>(workspace);
+  const size_t cb = ctrl_bytes(desc, chunk), hb = chain_bytes(desc), sb = snap_bytes(desc, chunk);
   int* ctrl = reinterpret_cast<int*>(ws);
-  float* chain = reinterpret_cast<float*>(ws + ctrl_bytes(desc, chunk));
-  void* snap = ws + ctrl_bytes(desc, chunk) + chain_bytes(desc);
-  char* tab_at = ws + ctrl_bytes(desc, chunk) + chain_bytes(desc) + snap_bytes(desc, chunk);
+  auto chain_of = [&](int i) { return reinterpret_cast<float*>(ws + kBwdProducts * cb + i * hb); };
+  auto snap_of = [&](int i) { return static_cast<void*>(ws + kBwdProducts * (cb + hb) + i * sb); };
+  float* chain = chain_of(0);
+  void* snap = snap_of(0);
+  char* tab_at = ws + kBwdProducts * (cb + hb + sb);
   const size_t tb = bwd_tensor_bytes(desc);
   char* next = tab_at + bwd_table_bytes(desc);
   auto slot = [&]() { char* p = next; next += tb; return p; };
@@ -380,10 +387,16 @@ ret_status_t chunkwise_bwd_impl(const ret_desc_t* desc, int32_t chunk, const voi
     if (ret::launch_reverse_tokens(s, dout, dorev, stream) != hipSuccess) return RET_ERR_HIP;
   }
   // the parallel backward's three products, each run as the chunkwise form
-  // (the same function), storing straight into the caller's tensors
-  if (!product(dov ? dov : dorev, v, kr, dq, s0t, nullptr, dov == nullptr, false, table) ||
-      !product(v, dorev, qrev, dk, xs, zs, true, true, table) ||
-      !product(kr, qrev, dorev, dv, ys, nullptr, true, true, nullptr))
+  // (the same function), storing straight into the caller's tensors, in one
+  // launch
+  const ret::ChunkProduct prods[kBwdProducts] = {
+      {dov ? dov : dorev, v, kr, dq, s0t, nullptr, snap_of(0), chain_of(0), dov == nullptr, false, table},
+      {v, dorev, qrev, dk, xs, zs, snap_of(1), chain_of(1), true, true, table},
+      {kr, qrev, dorev, dv, ys, nullptr, snap_of(2), chain_of(2), true, true, nullptr},
+  };
+  const bool keep = !first;  // a recomputed forward before them cleared the error word
+  if (ret::launch_chunkwise_products(s, c, kBwdProducts, prods, ctrl, (int64_t)(cb / sizeof(int)), desc->gn_eps,
+                                     stream, keep) != hipSuccess)
     return RET_ERR_HIP;
   if (state_in && ret::launch_state_map(s, zs, d_state_in, true, gam, stream) != hipSuccess) return RET_ERR_HIP;
   return RET_OK;

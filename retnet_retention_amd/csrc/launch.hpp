@@ -71,6 +71,26 @@ struct ParallelProduct {
 hipError_t launch_parallel_products(const Shape& s, int n, const ParallelProduct* products, float eps,
                                     hipStream_t stream);
 
+// Up to three chunkwise products of shape s in one grid (the chunkwise
+// backward's gradient products): each with its own snapshots (snap), chain
+// and control block, the blocks ctrl_stride ints apart from `ctrl` on (each
+// at least chunkwise_ctrl_bytes() / 4 ints); the first block's error word
+// reports every product's errors. keep_err as for launch_retention_fwd.
+struct ChunkProduct {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  const float* state_in;
+  float* state_out;
+  void* snap;
+  float* chain;
+  bool q_rev, out_rev;
+  const float2* out_rot;
+};
+hipError_t launch_chunkwise_products(const Shape& s, int chunk, int n, const ChunkProduct* products, int* ctrl,
+                                     int64_t ctrl_stride, float eps, hipStream_t stream, bool keep_err);
+
 // *dst = *src on the device, in stream order (one int).
 hipError_t launch_copy_word(const int* src, int* dst, hipStream_t stream);
 

@@ -148,6 +148,10 @@ struct FwdParams {
   void* snap;    // [BH][nchunks][D*D] of T: R_{i-1}^T for chunk i (output fragment order)
   float* chain;  // [BH][2][D*D] fp32: R_i handed to the next state workgroup (fragment order)
   int* ctrl;     // [0] count, [1] error, [8..15] tickets, [16 + (bh*(nchunks+1) + i)*4 + kind*2 + part]: R_{i-1} ready
+  // ints from ctrl to this product's ready flags' block (0 but for the
+  // second and third products of a launch of several, which share the first
+  // one's count, tickets and error word)
+  int fbase;
   const float2* rot;  // (cos, sin) per position and pair [seqlen][D/2]: q is turned on load; null: no rotation
   // parallel form only (the backward's products): read q with each sequence's
   // token order reversed; store the output reversed, and/or turned back by
@@ -305,7 +309,7 @@ __device__ __forceinline__ void out_role(const FwdParams& p, int bh, int ci, int
   // the snapshot of R_{i-1} to be published
   auto issue_slice = [&](int sl, char* buf) __attribute__((always_inline)) {
     if (sl == 0) {
-      const int* flags = p.ctrl + kCtrlHead + (bh * (p.nchunks + 1) + ci) * kFlagsPerChunk + kMaxSplit;
+      const int* flags = p.ctrl + p.fbase + kCtrlHead + (bh * (p.nchunks + 1) + ci) * kFlagsPerChunk + kMaxSplit;
 #pragma unroll
       for (int q = 0; q < StTile<T, D>::SPLIT; ++q) wait_flag(flags + q, p.ctrl + 1);
     }
@@ -681,7 +685,7 @@ __device__ __forceinline__ void state_role(const FwdParams& p, int bh, int ci, i
   const T* V = reinterpret_cast<const T*>(p.v) + head0;
   // flags of chunk index j for this part: kind 0 = chain, 1 = snapshot
   auto flag_of = [&](int j, int kind) __attribute__((always_inline)) {
-    return p.ctrl + kCtrlHead + (bh * (p.nchunks + 1) + j) * kFlagsPerChunk + kind * kMaxSplit + part;
+    return p.ctrl + p.fbase + kCtrlHead + (bh * (p.nchunks + 1) + j) * kFlagsPerChunk + kind * kMaxSplit + part;
   };
   // rows 4 hh + {0..3} + 8 a (a = 0..3) of the wave's row tile mt hold
   // accumulator elements 4a .. 4a+3; the columns are dv = dvw + 32 nt + n
@@ -987,6 +991,16 @@ __global__ __launch_bounds__(kWaves<T> * 64, 1) void retention_parallel_multi_ke
 #endif
 }
 
+// A workgroup's item: chunk ci of pair bh, role slot `role` of the chunk
+// (the dispatch is written out in both chunkwise kernels: as a called
+// function, even inlined, it cost the kernel registers). Role order inside a
+// chunk: the longest query block first (it pulls the chunk's K and V from
+// HBM while the state workgroups follow into L2), the state parts, then the
+// other query blocks. Every wait must be for a
+// workgroup with an earlier ticket, which is already running, so that no
+// number of waiting workgroups can fill the chip: in chunk 0 with a
+// carried-in state, whose output workgroups wait for the state parts to
+// publish R_{-1}, the state parts come first.
 template <typename T, int D, bool FAST, bool XF = false>
 __global__ __launch_bounds__(kWaves<T> * 64, 1) void retention_chunkwise_kernel(FwdParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the kernel's signature
@@ -1007,7 +1021,7 @@ __global__ __launch_bounds__(kWaves<T> * 64, 1) void retention_chunkwise_kernel(
   }
   __syncthreads();
   const int t = __builtin_amdgcn_readfirstlane(s_ticket);  // uniform: scalar registers for all it derives
-  int ci, bh, role;  // role slot inside the chunk (see below)
+  int ci, bh, role;  // role slot inside the chunk
   if (p.sched) {
     // packed sequences: the schedule skips the chunks past each sequence's
     // end, so the workgroups without work come last
@@ -1035,13 +1049,66 @@ __global__ __launch_bounds__(kWaves<T> * 64, 1) void retention_chunkwise_kernel(
   ci = uniform_i(ci);
   bh = uniform_i(bh);
   role = uniform_i(role);
-  // role order inside a chunk: the longest query block first (it pulls the
-  // chunk's K and V from HBM while the state workgroups follow into L2), the
-  // state parts, then the other query blocks. Every wait must be for a
-  // workgroup with an earlier ticket, which is already running, so that no
-  // number of waiting workgroups can fill the chip: in chunk 0 with a
-  // carried-in state, whose output workgroups wait for the state parts to
-  // publish R_{-1}, the state parts come first.
+  const bool state_first = ci == 0 && p.has_state0;
+  const int qb = state_first ? (role < SPLIT ? -1 : p.qblocks - 1 - (role - SPLIT))
+                             : (role == 0 ? p.qblocks - 1 : role <= SPLIT ? -1 : p.qblocks - 1 - (role - SPLIT));
+  if (qb < 0)
+    state_role<T, D>(p, bh, ci, state_first ? role : role - 1, l0, l1, l2, l3);
+  else if (ci > 0 || p.has_state0)
+    out_role<T, D, FAST, true, XF>(p, bh, ci, qb, true, l0, l1, l2, l3);
+  else
+    out_role<T, D, FAST, false, XF>(p, bh, ci, qb, true, l0, l1, l2, l3);
+#endif
+}
+
+// Several chunkwise products of one shape in one grid (the backward's three
+// gradient products): one ticket sequence for all of them, chunk-major with
+// the products interleaved inside each chunk, so every wait is still for an
+// earlier ticket of the same product, and the products' last chunks end
+// together instead of each launch ending on its own. Each product has its
+// own ready flags, chain and snapshots; the tickets, the count and the error
+// word are those of the first product's control block.
+template <typename T, int D, bool FAST>
+__global__ __launch_bounds__(kWaves<T> * 64, 1) void retention_chunkwise_multi_kernel(MultiParams mp) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __shared__ __attribute__((aligned(1024))) char l0[Stage<T, D>::BYTES];
+  __shared__ __attribute__((aligned(1024))) char l1[Stage<T, D>::BYTES];
+  __shared__ __attribute__((aligned(1024))) char l2[Stage<T, D>::BYTES];
+  __shared__ __attribute__((aligned(1024))) char l3[Stage<T, D>::BYTES];
+  __shared__ int s_ticket;
+  constexpr int SPLIT = StTile<T, D>::SPLIT;
+  const FwdParams& p0 = mp.p[0];
+  const int nprod = mp.nprod;
+  const int bhs = p0.batch * p0.heads;
+  const int roles = SPLIT + p0.qblocks;
+  const int cls = p0.xcd_order ? (int)(blockIdx.x & 7) : 0;
+  if (threadIdx.x == 0) {
+    atomicAdd(p0.ctrl, 1);
+    s_ticket = p0.xcd_order ? atomicAdd(p0.ctrl + kTicketWord + cls, 1) : atomicAdd(p0.ctrl + kTicketWord, 1);
+  }
+  __syncthreads();
+  const int t = __builtin_amdgcn_readfirstlane(s_ticket);
+  int ci, bh, role, prod;
+  if (p0.xcd_order) {
+    const int nbl = bhs / 8, per = nbl * roles;
+    ci = t / (nprod * per);
+    const int r = t % (nprod * per);
+    prod = r / per;
+    role = (r % per) / nbl;
+    bh = ((r % per) % nbl) * 8 + cls;
+  } else {
+    const int per = bhs * roles;
+    ci = t / (nprod * per);
+    const int r = t % (nprod * per);
+    prod = r / per;
+    bh = (r % per) / roles;
+    role = (r % per) % roles;
+  }
+  ci = uniform_i(ci);
+  bh = uniform_i(bh);
+  role = uniform_i(role);
+  constexpr bool XF = true;
+  const FwdParams& p = mp.p[uniform_i(prod)];
   const bool state_first = ci == 0 && p.has_state0;
   const int qb = state_first ? (role < SPLIT ? -1 : p.qblocks - 1 - (role - SPLIT))
                              : (role == 0 ? p.qblocks - 1 : role <= SPLIT ? -1 : p.qblocks - 1 - (role - SPLIT));
@@ -1263,6 +1330,7 @@ static FwdParams make_params(const Shape& s, int chunk, const void* q, const voi
   p.snap = snap;
   p.chain = chain;
   p.ctrl = ctrl;
+  p.fbase = 0;
   p.batch = s.batch;
   p.seqlen = s.seqlen;
   p.heads = s.heads;
@@ -1320,6 +1388,69 @@ static hipError_t launch_multi_t(const Shape& s, MultiParams& mp, hipStream_t st
   bool fast = true;
   for (int h = 0; h < s.heads; ++h) fast = fast && -(double)s.log2g[h] * OutTile<T, D, true>::BM <= kFastSpanLog2;
   return fast ? launch_multi_impl<T, D, true>(s, mp, stream) : launch_multi_impl<T, D, false>(s, mp, stream);
+}
+
+template <typename T, int D, bool FAST>
+static hipError_t launch_cmulti_impl(const Shape& s, int chunk, MultiParams& mp, int* ctrl0, int64_t stride,
+                                     hipStream_t stream, bool keep_err) {
+  using C = OutTile<T, D, FAST>;
+  const int bhs = s.batch * s.heads;
+  const int nchunks = (s.seqlen + chunk - 1) / chunk;
+  const int64_t nctrl = kCtrlHead + (int64_t)bhs * (nchunks + 1) * kFlagsPerChunk;
+  if (stride < nctrl) return hipErrorInvalidValue;
+  const int64_t all = stride * (mp.nprod - 1) + nctrl;  // every product's block, from the first one's start
+  if (all > 0x7fffffff) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(reset_ctrl_kernel, dim3((unsigned)((all + 255) / 256 < 1024 ? (all + 255) / 256 : 1024)),
+                     dim3(256), 0, stream, ctrl0, (int)all, keep_err ? 1 : 0);
+  const int qblocks = (chunk + C::BM - 1) / C::BM;
+  for (int i = 0; i < mp.nprod; ++i) {
+    mp.p[i].qblocks = qblocks;
+    mp.p[i].xcd_order = bhs % 8 == 0;
+    mp.p[i].ctrl = ctrl0;
+    mp.p[i].fbase = (int)(stride * i);
+  }
+  const int roles = StTile<T, D>::SPLIT + qblocks;
+  const int64_t blocks = (int64_t)mp.nprod * nchunks * bhs * roles;
+  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  if (blocks == 0) return hipGetLastError();
+  hipLaunchKernelGGL((retention_chunkwise_multi_kernel<T, D, FAST>), dim3((unsigned)blocks), dim3(64 * C::WAVES), 0,
+                     stream, mp);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t launch_cmulti_t(const Shape& s, int chunk, MultiParams& mp, int* ctrl0, int64_t stride,
+                                  hipStream_t stream, bool keep_err) {
+  bool fast = true;
+  for (int h = 0; h < s.heads; ++h) fast = fast && -(double)s.log2g[h] * chunk <= kFastSpanLog2;
+  return fast ? launch_cmulti_impl<T, D, true>(s, chunk, mp, ctrl0, stride, stream, keep_err)
+              : launch_cmulti_impl<T, D, false>(s, chunk, mp, ctrl0, stride, stream, keep_err);
+}
+
+hipError_t launch_chunkwise_products(const Shape& s, int chunk, int n, const ChunkProduct* pr, int* ctrl,
+                                     int64_t ctrl_stride, float eps, hipStream_t stream, bool keep_err) {
+  if (n < 1 || n > kMaxProducts || chunk < 1 || !ctrl) return hipErrorInvalidValue;
+  MultiParams mp;
+  mp.nprod = n;
+  for (int i = 0; i < kMaxProducts; ++i) {
+    const ChunkProduct& x = pr[i < n ? i : 0];
+    mp.p[i] = make_params(s, chunk, x.q, x.k, x.v, nullptr, x.o, x.state_in, x.state_out, x.snap, x.chain, ctrl,
+                          nullptr, eps, x.q_rev, x.out_rev, x.out_rot, nullptr, 0, nullptr);
+  }
+  if (s.dtype == 1) {
+    switch (s.d) {
+      case 64: return launch_cmulti_t<bf16, 64>(s, chunk, mp, ctrl, ctrl_stride, stream, keep_err);
+      case 128: return launch_cmulti_t<bf16, 128>(s, chunk, mp, ctrl, ctrl_stride, stream, keep_err);
+      case 256: return launch_cmulti_t<bf16, 256>(s, chunk, mp, ctrl, ctrl_stride, stream, keep_err);
+    }
+  } else {
+    switch (s.d) {
+      case 64: return launch_cmulti_t<float, 64>(s, chunk, mp, ctrl, ctrl_stride, stream, keep_err);
+      case 128: return launch_cmulti_t<float, 128>(s, chunk, mp, ctrl, ctrl_stride, stream, keep_err);
+      case 256: return launch_cmulti_t<float, 256>(s, chunk, mp, ctrl, ctrl_stride, stream, keep_err);
+    }
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_parallel_products(const Shape& s, int n, const ParallelProduct* pr, float eps,
