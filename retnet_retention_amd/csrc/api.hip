@@ -149,16 +149,16 @@ size_t snap_bytes(const ret_desc_t* d, int32_t chunk) {
 // Backward of the parallel form. Workspace slots, each one tensor
 // [batch][seqlen][heads][d] rounded up to 256 bytes: the angle table and the
 // rotated q', k' and reversed q' with rotation, else only the reversed q;
-// with a gate the recomputed retention output and the reversed dO, else only
-// the reversed dO.
+// then the reversed dO (with a gate, written by the recomputed forward's
+// epilogue).
 size_t bwd_tensor_bytes(const ret_desc_t* d) {
   return align_up((size_t)d->batch * d->seqlen * d->heads * d->dk * elem_size(d->dtype));
 }
 size_t bwd_table_bytes(const ret_desc_t* d) {
   return d->rotary_base == 0.0 ? 0 : align_up((size_t)d->seqlen * (d->dk / 2) * sizeof(float2));
 }
-size_t bwd_bytes(const ret_desc_t* d, bool gate) {
-  const int slots = (d->rotary_base == 0.0 ? 1 : 3) + (gate ? 2 : 1);
+size_t bwd_bytes(const ret_desc_t* d, bool /*gate*/) {
+  const int slots = (d->rotary_base == 0.0 ? 1 : 3) + 1;
   return bwd_table_bytes(d) + slots * bwd_tensor_bytes(d);
 }
 
@@ -315,18 +315,9 @@ ret_status_t chunkwise_bwd_impl(const ret_desc_t* desc, int32_t chunk, const voi
   auto slot = [&]() { char* p = next; next += tb; return p; };
   char* st_at = tab_at + bwd_bytes(desc, g != nullptr);
   auto state_slot = [&](int i) { return reinterpret_cast<float*>(st_at + i * state_bytes(desc)); };
-  // one chunkwise product; q_rev, out_rev, out_rot as in the parallel backward.
-  // The first one clears the control block's error word, the later ones keep
-  // it, so the word reports an error of any of the call's launches.
+  // The call's first chunkwise launch clears the control block's error word,
+  // the later one keeps it, so the word reports an error of either.
   bool first = true;
-  auto product = [&](const void* a, const void* b, const void* cc, void* out, const float* s_in, float* s_out,
-                     bool q_rev, bool out_rev, const float2* out_rot) {
-    const bool keep = !first;
-    first = false;
-    return ret::launch_retention_fwd(s, c, true, a, b, cc, nullptr, out, s_in, s_out, snap, chain, ctrl, nullptr,
-                                     desc->gn_eps, stream, nullptr, nullptr, q_rev, out_rev, out_rot, nullptr, 0,
-                                     nullptr, keep) == hipSuccess;
-  };
   // states of the three products (per head g): S0^T for dq; dS^T / g and
   // dS / g for the reversed ones (their g^(m'+1) then makes g^(N-1-m)); the
   // reversed dK product's final state Z gives dS0 = g Z^T
@@ -376,10 +367,14 @@ ret_status_t chunkwise_bwd_impl(const ret_desc_t* desc, int32_t chunk, const voi
   const void* dov = dout;
   void* dorev = nullptr;
   if (g) {
-    void* o_raw = slot();
+    // the recomputed forward forms dg and dO (stored reversed) in its
+    // epilogue, from the gate, dout and its output in registers; it clears
+    // the error word, the products' launch keeps it
     dorev = slot();
-    if (!product(qr, kr, v, o_raw, state_in, nullptr, false, false, nullptr) ||
-        ret::launch_gate_norm_bwd(s, o_raw, g, dout, nullptr, dg, desc->gn_eps, stream, dorev) != hipSuccess)
+    first = false;
+    if (ret::launch_retention_fwd(s, c, true, qr, kr, v, g, dorev, state_in, nullptr, snap, chain, ctrl, nullptr,
+                                  desc->gn_eps, stream, nullptr, nullptr, false, true, nullptr, nullptr, 0, nullptr,
+                                  false, dout, dg) != hipSuccess)
       return RET_ERR_HIP;
     dov = nullptr;  // the dq product reads the reversed copy back in order
   } else {
@@ -527,11 +522,12 @@ ret_status_t retention_parallel_bwd(const ret_desc_t* desc, const void* q, const
   const void* dov = dout;
   void* dorev = nullptr;
   if (g) {
-    void* o_raw = slot();
+    // the recomputed forward forms dg and dO (stored reversed) in its
+    // epilogue, from the gate, dout and its output in registers
     dorev = slot();
-    if (ret::launch_retention_fwd(s, desc->seqlen, false, qr, kr, v, nullptr, o_raw, nullptr, nullptr, nullptr,
-                                  nullptr, nullptr, nullptr, desc->gn_eps, stream) != hipSuccess ||
-        ret::launch_gate_norm_bwd(s, o_raw, g, dout, nullptr, dg, desc->gn_eps, stream, dorev) != hipSuccess)
+    if (ret::launch_retention_fwd(s, desc->seqlen, false, qr, kr, v, g, dorev, nullptr, nullptr, nullptr, nullptr,
+                                  nullptr, nullptr, desc->gn_eps, stream, nullptr, nullptr, false, true, nullptr,
+                                  nullptr, 0, nullptr, false, dout, dg) != hipSuccess)
       return RET_ERR_HIP;
     dov = nullptr;
   } else {

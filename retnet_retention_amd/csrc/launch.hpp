@@ -50,12 +50,18 @@ size_t chunkwise_sched_bytes(const Shape& s, int chunk);
 // `before`/`after` (may be null) are recorded around the main kernel.
 // keep_err: the control block's reset leaves its error word (word 1) as it
 // is, for the second and later launches of one call.
+// gb_dout, gb_dg (both or neither; batch form, with g and out_rev, without
+// q_rev or out_rot): the backward's recomputed forward, which
+// stores dg (the gate's gradient) and, in o at reversed positions, dO (the
+// gradient reaching the retention output through the gate and GroupNorm)
+// instead of the forward's output.
 hipError_t launch_retention_fwd(const Shape& s, int chunk, bool chunked, const void* q, const void* k, const void* v,
                                 const void* g, void* o, const float* state_in, float* state_out, void* snap,
                                 float* chain, int* ctrl, const float2* rot, float eps, hipStream_t stream,
                                 hipEvent_t before = nullptr, hipEvent_t after = nullptr, bool q_rev = false,
                                 bool out_rev = false, const float2* out_rot = nullptr, const int* cu = nullptr,
-                                int total = 0, void* sched = nullptr, bool keep_err = false);
+                                int total = 0, void* sched = nullptr, bool keep_err = false,
+                                const void* gb_dout = nullptr, void* gb_dg = nullptr);
 
 // Up to three parallel-form products of shape s with no state in one grid
 // (q_rev, out_rev, out_rot as above; no rotation of q on load): the
@@ -94,13 +100,8 @@ hipError_t launch_chunkwise_products(const Shape& s, int chunk, int n, const Chu
 // *dst = *src on the device, in stream order (one int).
 hipError_t launch_copy_word(const int* src, int* dst, hipStream_t stream);
 
-// Backward passes of the parallel form (all tensors [batch][seqlen][heads][d]
-// of the descriptor's dtype): the gradient through the swish gate and the
-// per-head GroupNorm (o: the retention output before GroupNorm; `dov_rev`,
-// may be null, also receives dO in reversed token order) and a copy with
-// each sequence's token order reversed.
-hipError_t launch_gate_norm_bwd(const Shape& s, const void* o, const void* g, const void* dout, void* dov, void* dg,
-                                float eps, hipStream_t stream, void* dov_rev = nullptr);
+// Backward pass (tensors [batch][seqlen][heads][d] of the descriptor's
+// dtype): a copy with each sequence's token order reversed.
 hipError_t launch_reverse_tokens(const Shape& s, const void* src, void* dst, hipStream_t stream);
 // States [batch][heads][d][d] fp32: dst = scale[h] * src (transposed per
 // matrix when asked); scale: HOST array [heads].

@@ -158,6 +158,10 @@ struct FwdParams {
   // out_rot's angles of the stored position (null: as computed)
   int q_rev, out_rev;
   const float2* out_rot;
+  // the recomputed forward of the backward (GBW instantiations): dout, and
+  // the gate's gradient dg ([batch][seqlen][heads][d], input dtype)
+  const void* gb_dout;
+  void* gb_dg;
   // packed sequences of different lengths (chunkwise form only): sequence b
   // holds rows cu[b] .. cu[b+1]-1 of `total`, seqlen bounds every length;
   // null: batch sequences of seqlen tokens each
@@ -256,7 +260,12 @@ __device__ __forceinline__ int seq_rows(const FwdParams& p, int b, int64_t& tok0
 // reversed and/or turned back (the backward's products: the parallel kernel,
 // and a second chunkwise instantiation launched only for them); the forward
 // chunkwise kernel carries none of that code.
-template <typename T, int D, bool FAST, bool CROSS, bool XF = false>
+// GBW (with XF): the backward's recomputed forward. In place of the forward
+// epilogue it forms the gradient through the swish gate and the GroupNorm
+// (from the gate g, the caller's dout and the recomputed output, still in
+// registers): dg, stored in token order, and dO, stored at each sequence's
+// reversed token positions.
+template <typename T, int D, bool FAST, bool CROSS, bool XF = false, bool GBW = false>
 __device__ __forceinline__ void out_role(const FwdParams& p, int bh, int ci, int qb, bool chunked, char* l0, char* l1,
                                          char* l2, char* l3) {
   using C = OutTile<T, D, FAST>;
@@ -564,6 +573,76 @@ __device__ __forceinline__ void out_role(const FwdParams& p, int bh, int ci, int
       scale = f * rsqrtf(f * f * (sum_pair32(s2) * (1.0f / D)) + p.eps);
     }
     const float shift = -mean * scale;  // normalized value: o scale + shift
+    if constexpr (GBW) {
+      // With y the normalized row (y = (o - mean) / sigma, sigma =
+      // sqrt(var + eps); here y = o' scale + shift) and s = sigmoid(g):
+      //   dg = dout y s (1 + g (1 - s)),  dy = dout g s,
+      //   dO = (dy - mean(dy) - y mean(dy y)) / sigma.
+      // Whole rows pass through the wave's LDS area, PR rows at a time, so
+      // that every access holds complete rows: LPR2 lanes per row, 16
+      // bytes each, and the two row means reduce across those lanes before
+      // the same access forms dO.
+      constexpr int CPL = 16 / (int)sizeof(T);
+      constexpr int EROW2 = D * 4 + 16;
+      constexpr int PR = (32 * SG::EROW) / EROW2 < 32 ? (32 * SG::EROW) / EROW2 : 32;
+      constexpr int LPR2 = D / CPL, RPA2 = 64 / LPR2;
+      static_assert(PR % RPA2 == 0 && 32 % PR == 0 && PR * EROW2 <= 32 * SG::EROW, "whole rows per pass");
+      const float rsr = scale / f;  // 1 / sigma of this lane's row (f > 0 by the fast path's span rule)
+      const T* DO = reinterpret_cast<const T*>(p.gb_dout) + head0;
+      T* DG = reinterpret_cast<T*>(p.gb_dg) + head0;
+      static_for<32 / PR>([&](auto p_c) __attribute__((always_inline)) {
+        constexpr int P0 = decltype(p_c)::value * PR;  // first row of the pass within the tile
+        if (n >= P0 && n < P0 + PR) {
+#pragma unroll
+          for (int t = 0; t < C::NT; ++t)
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+              *reinterpret_cast<f32x4*>(stg + (n - P0) * EROW2 + (32 * t + 8 * a + 4 * hh) * 4) =
+                  f32x4{__builtin_fmaf(oacc[r][t][4 * a], scale, shift),
+                        __builtin_fmaf(oacc[r][t][4 * a + 1], scale, shift),
+                        __builtin_fmaf(oacc[r][t][4 * a + 2], scale, shift),
+                        __builtin_fmaf(oacc[r][t][4 * a + 3], scale, shift)};
+        }
+#pragma unroll
+        for (int k = 0; k < PR / RPA2; ++k) {
+          const int rr = k * RPA2 + lane / LPR2, col = (lane % LPR2) * CPL;
+          const int orow = qw0 + 32 * r + P0 + rr;
+          const int grow = min(orow, cend - 1);  // rows past the chunk load a clamped row and store nothing
+          const float rs = __shfl(rsr, P0 + rr, 64);
+          float y[CPL], gv[CPL], dv[CPL];
+#pragma unroll
+          for (int e = 0; e < CPL; e += 4) {
+            const f32x4 x = *reinterpret_cast<const f32x4*>(stg + rr * EROW2 + (col + e) * 4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) y[e + i] = x[i];
+          }
+          load16f(G + (int64_t)grow * tstride + col, gv);
+          load16f(DO + (int64_t)grow * tstride + col, dv);
+          float dg[CPL], s1 = 0.f, s2 = 0.f;
+#pragma unroll
+          for (int e = 0; e < CPL; ++e) {
+            const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * gv[e]));
+            dg[e] = dv[e] * y[e] * (sg * __builtin_fmaf(gv[e], 1.0f - sg, 1.0f));
+            dv[e] = dv[e] * gv[e] * sg;  // dy
+            s1 += dv[e];
+            s2 = __builtin_fmaf(dv[e], y[e], s2);
+          }
+#pragma unroll
+          for (int w = 1; w < LPR2; w *= 2) {
+            s1 += __shfl_xor(s1, w, 64);
+            s2 += __shfl_xor(s2, w, 64);
+          }
+          const float m1 = s1 * (1.0f / D), m2 = s2 * (1.0f / D);
+#pragma unroll
+          for (int e = 0; e < CPL; ++e) dv[e] = (dv[e] - m1 - y[e] * m2) * rs;
+          if (orow < cend) {
+            store16f(DG + (int64_t)orow * tstride + col, dg);
+            store16f(O + (int64_t)(p.seqlen - 1 - orow) * tstride + col, dv);
+          }
+        }
+      });
+      continue;
+    }
     // The rows of this tile: gate loads and output stores as buffer
     // accesses from a wave-uniform base (the tile's first row) and a 32-bit
     // lane offset. The forward's stores go through a descriptor whose size
@@ -924,7 +1003,7 @@ __device__ __forceinline__ void state_role(const FwdParams& p, int bh, int ci, i
 // ---------------------------------------------------------------------------
 // XF: the instantiation for the backward's products (reversed query reads,
 // transforming stores); the forward's carries none of that code.
-template <typename T, int D, bool FAST, bool XF = false>
+template <typename T, int D, bool FAST, bool XF = false, bool GBW = false>
 __global__ __launch_bounds__(kWaves<T> * 64, 1) void retention_parallel_kernel(FwdParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the kernel's signature
   __shared__ __attribute__((aligned(1024))) char l0[Stage<T, D>::BYTES];
@@ -948,7 +1027,7 @@ __global__ __launch_bounds__(kWaves<T> * 64, 1) void retention_parallel_kernel(F
     bh = bid % groups;
     qb = p.qblocks - 1 - bid / groups;
   }
-  out_role<T, D, FAST, false, XF>(p, bh, 0, qb, false, l0, l1, l2, l3);
+  out_role<T, D, FAST, false, XF, GBW>(p, bh, 0, qb, false, l0, l1, l2, l3);
 #endif
 }
 
@@ -1001,7 +1080,7 @@ __global__ __launch_bounds__(kWaves<T> * 64, 1) void retention_parallel_multi_ke
 // number of waiting workgroups can fill the chip: in chunk 0 with a
 // carried-in state, whose output workgroups wait for the state parts to
 // publish R_{-1}, the state parts come first.
-template <typename T, int D, bool FAST, bool XF = false>
+template <typename T, int D, bool FAST, bool XF = false, bool GBW = false>
 __global__ __launch_bounds__(kWaves<T> * 64, 1) void retention_chunkwise_kernel(FwdParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the kernel's signature
   __shared__ __attribute__((aligned(1024))) char l0[Stage<T, D>::BYTES];
@@ -1055,9 +1134,9 @@ __global__ __launch_bounds__(kWaves<T> * 64, 1) void retention_chunkwise_kernel(
   if (qb < 0)
     state_role<T, D>(p, bh, ci, state_first ? role : role - 1, l0, l1, l2, l3);
   else if (ci > 0 || p.has_state0)
-    out_role<T, D, FAST, true, XF>(p, bh, ci, qb, true, l0, l1, l2, l3);
+    out_role<T, D, FAST, true, XF, GBW>(p, bh, ci, qb, true, l0, l1, l2, l3);
   else
-    out_role<T, D, FAST, false, XF>(p, bh, ci, qb, true, l0, l1, l2, l3);
+    out_role<T, D, FAST, false, XF, GBW>(p, bh, ci, qb, true, l0, l1, l2, l3);
 #endif
 }
 
@@ -1241,7 +1320,10 @@ static hipError_t launch_fwd_impl(const Shape& s, int chunk, FwdParams p, bool c
     const int64_t blocks = (int64_t)bhs * p.qblocks;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     if (before && hipEventRecord(before, stream) != hipSuccess) return hipErrorInvalidValue;
-    if (p.q_rev || p.out_rev || p.out_rot)
+    if (p.gb_dout)
+      hipLaunchKernelGGL((retention_parallel_kernel<T, D, FAST, true, true>), dim3((unsigned)blocks),
+                         dim3(64 * C::WAVES), 0, stream, p);
+    else if (p.q_rev || p.out_rev || p.out_rot)
       hipLaunchKernelGGL((retention_parallel_kernel<T, D, FAST, true>), dim3((unsigned)blocks), dim3(64 * C::WAVES), 0,
                          stream, p);
     else
@@ -1265,7 +1347,10 @@ static hipError_t launch_fwd_impl(const Shape& s, int chunk, FwdParams p, bool c
                        const_cast<int4*>(p.sched), roles, classes);
   }
   if (before && hipEventRecord(before, stream) != hipSuccess) return hipErrorInvalidValue;
-  if (p.q_rev || p.out_rev || p.out_rot)
+  if (p.gb_dout)
+    hipLaunchKernelGGL((retention_chunkwise_kernel<T, D, FAST, true, true>), dim3((unsigned)blocks),
+                       dim3(64 * C::WAVES), 0, stream, p);
+  else if (p.q_rev || p.out_rev || p.out_rot)
     hipLaunchKernelGGL((retention_chunkwise_kernel<T, D, FAST, true>), dim3((unsigned)blocks), dim3(64 * C::WAVES), 0,
                        stream, p);
   else
@@ -1320,6 +1405,8 @@ static FwdParams make_params(const Shape& s, int chunk, const void* q, const voi
   p.q_rev = q_rev;
   p.out_rev = out_rev;
   p.out_rot = out_rot;
+  p.gb_dout = nullptr;
+  p.gb_dg = nullptr;
   p.q = q;
   p.k = k;
   p.v = v;
@@ -1348,12 +1435,20 @@ hipError_t launch_retention_fwd(const Shape& s, int chunk, bool chunked, const v
                                 const void* g, void* o, const float* state_in, float* state_out, void* snap,
                                 float* chain, int* ctrl, const float2* rot, float eps, hipStream_t stream,
                                 hipEvent_t before, hipEvent_t after, bool q_rev, bool out_rev,
-                                const float2* out_rot, const int* cu, int total, void* sched, bool keep_err) {
+                                const float2* out_rot, const int* cu, int total, void* sched, bool keep_err,
+                                const void* gb_dout, void* gb_dg) {
   if (rot && q_rev) return hipErrorInvalidValue;  // q's angles are those of its own positions
+  // the recomputed forward of the backward: gate, dout and dg given, dO
+  // stored reversed, nothing else transformed, batch form
+  if ((gb_dout != nullptr) != (gb_dg != nullptr) ||
+      (gb_dout && (!g || !out_rev || q_rev || out_rot || cu)))
+    return hipErrorInvalidValue;
   // packed sequences: chunkwise form, forward only, with a schedule buffer
   if (cu && (!chunked || q_rev || out_rev || out_rot || !sched)) return hipErrorInvalidValue;
   FwdParams p = make_params(s, chunk, q, k, v, g, o, state_in, state_out, snap, chain, ctrl, rot, eps, q_rev, out_rev,
                             out_rot, cu, total, sched);
+  p.gb_dout = gb_dout;
+  p.gb_dg = gb_dg;
   if (s.dtype == 1) {
     switch (s.d) {
       case 64: return launch_fwd_t<bf16, 64>(s, chunk, p, chunked, stream, before, after, keep_err);
