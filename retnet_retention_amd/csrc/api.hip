@@ -148,17 +148,17 @@ size_t snap_bytes(const ret_desc_t* d, int32_t chunk) {
 
 // Backward of the parallel form. Workspace slots, each one tensor
 // [batch][seqlen][heads][d] rounded up to 256 bytes: the angle table and the
-// rotated q', k' and reversed q' with rotation, else only the reversed q;
-// then the reversed dO (with a gate, written by the recomputed forward's
-// epilogue).
+// rotated q', k' and reversed q' with rotation (none without: the products
+// read q reversed); with a gate the reversed dO, written by the recomputed
+// forward's epilogue (none without: the products read dout reversed).
 size_t bwd_tensor_bytes(const ret_desc_t* d) {
   return align_up((size_t)d->batch * d->seqlen * d->heads * d->dk * elem_size(d->dtype));
 }
 size_t bwd_table_bytes(const ret_desc_t* d) {
   return d->rotary_base == 0.0 ? 0 : align_up((size_t)d->seqlen * (d->dk / 2) * sizeof(float2));
 }
-size_t bwd_bytes(const ret_desc_t* d, bool /*gate*/) {
-  const int slots = (d->rotary_base == 0.0 ? 1 : 3) + 1;
+size_t bwd_bytes(const ret_desc_t* d, bool gate) {
+  const int slots = (d->rotary_base == 0.0 ? 0 : 3) + (gate ? 1 : 0);
   return bwd_table_bytes(d) + slots * bwd_tensor_bytes(d);
 }
 
@@ -359,10 +359,9 @@ ret_status_t chunkwise_bwd_impl(const ret_desc_t* desc, int32_t chunk, const voi
     table = tab;
     qr = qs;
     kr = ks;
-  } else {
-    qrev = slot();
-    if (ret::launch_reverse_tokens(s, q, qrev, stream) != hipSuccess) return RET_ERR_HIP;
   }
+  // without rotation the products read q in reversed order where they need
+  // it reversed (no copy)
   // dO and its reversed copy
   const void* dov = dout;
   void* dorev = nullptr;
@@ -377,17 +376,20 @@ ret_status_t chunkwise_bwd_impl(const ret_desc_t* desc, int32_t chunk, const voi
                                   false, dout, dg) != hipSuccess)
       return RET_ERR_HIP;
     dov = nullptr;  // the dq product reads the reversed copy back in order
-  } else {
-    dorev = slot();
-    if (ret::launch_reverse_tokens(s, dout, dorev, stream) != hipSuccess) return RET_ERR_HIP;
   }
+  // without a gate the products read dout in reversed order where they need
+  // it reversed (no copy)
+  const void* qr_rev = qrev ? qrev : q;      // reversed q': the rotation pass's copy, or q read reversed
+  const void* do_rev = dorev ? dorev : dout;  // reversed dO: the recompute's copy, or dout read reversed
+  const bool rq = qrev == nullptr, rdo = dorev == nullptr;
   // the parallel backward's three products, each run as the chunkwise form
   // (the same function), storing straight into the caller's tensors, in one
   // launch
   const ret::ChunkProduct prods[kBwdProducts] = {
-      {dov ? dov : dorev, v, kr, dq, s0t, nullptr, snap_of(0), chain_of(0), dov == nullptr, false, table},
-      {v, dorev, qrev, dk, xs, zs, snap_of(1), chain_of(1), true, true, table},
-      {kr, qrev, dorev, dv, ys, nullptr, snap_of(2), chain_of(2), true, true, nullptr},
+      {dov ? dov : dorev, v, kr, dq, s0t, nullptr, snap_of(0), chain_of(0), dov == nullptr, false, table, false,
+       false},
+      {v, do_rev, qr_rev, dk, xs, zs, snap_of(1), chain_of(1), true, true, table, rdo, rq},
+      {kr, qr_rev, do_rev, dv, ys, nullptr, snap_of(2), chain_of(2), true, true, nullptr, rq, rdo},
   };
   const bool keep = !first;  // a recomputed forward before them cleared the error word
   if (ret::launch_chunkwise_products(s, c, kBwdProducts, prods, ctrl, (int64_t)(cb / sizeof(int)), desc->gn_eps,
@@ -478,8 +480,8 @@ ret_status_t retention_parallel_bwd(const ret_desc_t* desc, const void* q, const
   }
   if ((st = check_eps(desc, g)) != RET_OK) return st;
   const size_t need = bwd_bytes(desc, g != nullptr);
-  if (!workspace || workspace_bytes < need) return RET_ERR_WORKSPACE;
-  if (!aligned16(workspace)) return RET_ERR_ALIGN;
+  if (need > 0 && (!workspace || workspace_bytes < need)) return RET_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(workspace)) return RET_ERR_ALIGN;
   if (overlaps(workspace, need, q, n) || overlaps(workspace, need, k, n) || overlaps(workspace, need, v, n) ||
       overlaps(workspace, need, g, n) || overlaps(workspace, need, dout, n) || overlaps(workspace, need, dq, n) ||
       overlaps(workspace, need, dk, n) || overlaps(workspace, need, dv, n) || overlaps(workspace, need, dg, n))
@@ -510,10 +512,9 @@ ret_status_t retention_parallel_bwd(const ret_desc_t* desc, const void* q, const
     table = tab;
     qr = qs;
     kr = ks;
-  } else {
-    qrev = slot();
-    if (ret::launch_reverse_tokens(s, q, qrev, stream) != hipSuccess) return RET_ERR_HIP;
   }
+  // without rotation the products read q in reversed order where they need
+  // it reversed (no copy)
   // dO, the gradient of the retention output before the epilogue (through
   // the gate and GroupNorm, from the recomputed raw output, or dout itself),
   // and its reversed copy
@@ -530,10 +531,12 @@ ret_status_t retention_parallel_bwd(const ret_desc_t* desc, const void* q, const
                                   nullptr, 0, nullptr, false, dout, dg) != hipSuccess)
       return RET_ERR_HIP;
     dov = nullptr;
-  } else {
-    dorev = slot();
-    if (ret::launch_reverse_tokens(s, dout, dorev, stream) != hipSuccess) return RET_ERR_HIP;
   }
+  // without a gate the products read dout in reversed order where they need
+  // it reversed (no copy)
+  const void* qr_rev = qrev ? qrev : q;
+  const void* do_rev = dorev ? dorev : dout;
+  const bool rq = qrev == nullptr, rdo = dorev == nullptr;
   // Three forward products, each storing its gradient straight into the
   // caller's tensor (turned back by the rotation where it applies), in one
   // grid:
@@ -543,9 +546,9 @@ ret_status_t retention_parallel_bwd(const ret_desc_t* desc, const void* q, const
   //        stored reversed);
   //   dv = rev P(rev K', rev Q', rev dO).
   const ret::ParallelProduct prods[3] = {
-      {dov ? dov : dorev, v, kr, dq, dov == nullptr, false, table},
-      {v, dorev, qrev, dk, true, true, table},
-      {kr, qrev, dorev, dv, true, true, nullptr},
+      {dov ? dov : dorev, v, kr, dq, dov == nullptr, false, table, false, false},
+      {v, do_rev, qr_rev, dk, true, true, table, rdo, rq},
+      {kr, qr_rev, do_rev, dv, true, true, nullptr, rq, rdo},
   };
   if (ret::launch_parallel_products(s, 3, prods, desc->gn_eps, stream) != hipSuccess) return RET_ERR_HIP;
   return RET_OK;

@@ -3,29 +3,17 @@
 // training form). Every matrix product of the gradient is again a causal
 // retention product, which the forward kernels compute; the gradient through
 // the swish gate and the per-head GroupNorm is formed in the epilogue of the
-// recomputed forward. These kernels do the rest:
-//   * reverse_tokens_kernel: a copy with the token order of every sequence
-//     reversed (the products with the transposed decay mask run on reversed
-//     sequences, where that mask is causal again), for inputs that no other
-//     pass already writes reversed;
+// recomputed forward. The products with the transposed decay mask run on
+// reversed sequences, where that mask is causal again: the retention
+// kernels read their reversed operands in reversed order (or take the copy
+// the rotation pass writes), turn their stored rows back by the rotation's
+// angles and store them at reversed positions. What is left here:
 //   * state_map_kernel: per-head scaled (and transposed) copies of carried
 //     states.
-// The rotation's gradient (each pair turned back by its angle) and the
-// reversal of the products' outputs happen in the retention kernels' stores.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace ret {
-
-// dst[b][n] = src[b][seqlen - 1 - n], 16 bytes per thread
-__global__ __launch_bounds__(256) void reverse_tokens_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
-                                                             int64_t vecs, int64_t per_tok, int seqlen) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= vecs) return;
-  const int64_t tok = i / per_tok, c = i % per_tok;  // tok = b * seqlen + n
-  const int64_t b = tok / seqlen, n = tok % seqlen;
-  dst[(b * seqlen + (seqlen - 1 - n)) * per_tok + c] = src[i];
-}
 
 // Per (sequence, head) D x D fp32 states: dst = scale_h * src, or its
 // transpose; the scale per head comes from the host.
@@ -66,13 +54,5 @@ hipError_t launch_state_map(const Shape& s, const float* src, float* dst, bool t
   return hipGetLastError();
 }
 
-hipError_t launch_reverse_tokens(const Shape& s, const void* src, void* dst, hipStream_t stream) {
-  const int64_t per_tok = (int64_t)s.heads * s.d * (s.dtype == 1 ? 2 : 4) / 16;
-  const int64_t vecs = (int64_t)s.batch * s.seqlen * per_tok;
-  const unsigned blocks = (unsigned)((vecs + 255) / 256);
-  hipLaunchKernelGGL(reverse_tokens_kernel, dim3(blocks), dim3(256), 0, stream, (const uint4*)src, (uint4*)dst, vecs,
-                     per_tok, s.seqlen);
-  return hipGetLastError();
-}
 
 }  // namespace ret

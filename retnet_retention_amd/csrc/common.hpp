@@ -528,6 +528,41 @@ struct TileLoads {
   __device__ __forceinline__ void init(int64_t gstride, int lane) {
     off = (uint32_t)((lane_row(lane) * (int)gstride + lane_chunk(lane) * EPC) * (int)sizeof(T));
   }
+  // For the reversed loads below: a load's rows run downwards in g.
+  __device__ __forceinline__ void init_rev(int64_t gstride, int lane) {
+    off = (uint32_t)(((TL::RPI - 1 - lane_row(lane)) * (int)gstride + lane_chunk(lane) * EPC) * (int)sizeof(T));
+  }
+  // Reversed token order (after init_rev): tile row r holds row
+  // len - 1 - (row0 + r) of g, for rows row0 .. row0 + ROWS - 1 all below len
+  // (the lowest row of g read, len - row0 - ROWS, is wave-uniform: the
+  // descriptor's base; load n starts NINST - 1 - n loads above it).
+  __device__ __forceinline__ void issue_rev(char* lds, const T* g, int64_t gstride, int len, int row0,
+                                            int wave) const {
+    const __amdgpu_buffer_rsrc_t rs = scalar_rsrc(g + (int64_t)(len - row0 - TL::NINST * TL::RPI) * gstride);
+    const uint32_t step = (uint32_t)(TL::RPI * gstride * (int64_t)sizeof(T));
+#pragma unroll
+    for (int m = 0; m < PER; ++m) {
+      const int n = wave + m * NW;
+      if (TL::NINST % NW != 0 && m == PER - 1 && n >= TL::NINST) break;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + n * TL::LSTRIDE), 16, off,
+                                               (TL::NINST - 1 - n) * step, 0, 0);
+    }
+  }
+  // The same with every row past rmax (rmax >= row0, below len) replaced by
+  // row rmax: tile row r holds row len - 1 - min(row0 + r, rmax).
+  __device__ __forceinline__ void issue_clamped_rev(char* lds, const T* g, int64_t gstride, int len, int row0,
+                                                    int rmax, int wave) const {
+    const __amdgpu_buffer_rsrc_t rs = scalar_rsrc(g + (int64_t)(len - 1 - rmax) * gstride);
+    const int lane = threadIdx.x & 63, lr = lane_row(lane), lc = lane_chunk(lane);
+#pragma unroll
+    for (int m = 0; m < PER; ++m) {
+      const int n = wave + m * NW;
+      if (TL::NINST % NW != 0 && m == PER - 1 && n >= TL::NINST) break;
+      const int r = min(n * TL::RPI + lr, rmax - row0);  // row relative to row0
+      const uint32_t o = (uint32_t)(((rmax - row0 - r) * (int)gstride + lc * EPC) * (int)sizeof(T));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + n * TL::LSTRIDE), 16, o, 0, 0, 0);
+    }
+  }
   // rows row0 .. row0 + ROWS - 1 of g, all in range (g + row0 gstride is
   // wave-uniform)
   __device__ __forceinline__ void issue(char* lds, const T* g, int64_t gstride, int row0, int wave) const {

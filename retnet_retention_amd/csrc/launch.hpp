@@ -73,6 +73,7 @@ struct ParallelProduct {
   void* o;
   bool q_rev, out_rev;
   const float2* out_rot;
+  bool k_rev, v_rev;  // read k / v with each sequence's token order reversed
 };
 hipError_t launch_parallel_products(const Shape& s, int n, const ParallelProduct* products, float eps,
                                     hipStream_t stream);
@@ -93,6 +94,7 @@ struct ChunkProduct {
   float* chain;
   bool q_rev, out_rev;
   const float2* out_rot;
+  bool k_rev, v_rev;  // read k / v with each sequence's token order reversed
 };
 hipError_t launch_chunkwise_products(const Shape& s, int chunk, int n, const ChunkProduct* products, int* ctrl,
                                      int64_t ctrl_stride, float eps, hipStream_t stream, bool keep_err);
@@ -100,9 +102,6 @@ hipError_t launch_chunkwise_products(const Shape& s, int chunk, int n, const Chu
 // *dst = *src on the device, in stream order (one int).
 hipError_t launch_copy_word(const int* src, int* dst, hipStream_t stream);
 
-// Backward pass (tensors [batch][seqlen][heads][d] of the descriptor's
-// dtype): a copy with each sequence's token order reversed.
-hipError_t launch_reverse_tokens(const Shape& s, const void* src, void* dst, hipStream_t stream);
 // States [batch][heads][d][d] fp32: dst = scale[h] * src (transposed per
 // matrix when asked); scale: HOST array [heads].
 hipError_t launch_state_map(const Shape& s, const float* src, float* dst, bool transpose, const float* scale,

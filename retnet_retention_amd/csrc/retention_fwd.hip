@@ -162,6 +162,10 @@ struct FwdParams {
   // the gate's gradient dg ([batch][seqlen][heads][d], input dtype)
   const void* gb_dout;
   void* gb_dg;
+  // (backward instantiations) read k, v with each sequence's token order
+  // reversed: the reversed copies that two gradient products take as keys
+  // or values, read from the forward-order tensor instead of copied
+  int k_rev, v_rev;
   // packed sequences of different lengths (chunkwise form only): sequence b
   // holds rows cu[b] .. cu[b+1]-1 of `total`, seqlen bounds every length;
   // null: batch sequences of seqlen tokens each
@@ -265,7 +269,9 @@ __device__ __forceinline__ int seq_rows(const FwdParams& p, int b, int64_t& tok0
 // (from the gate g, the caller's dout and the recomputed output, still in
 // registers): dg, stored in token order, and dO, stored at each sequence's
 // reversed token positions.
-template <typename T, int D, bool FAST, bool CROSS, bool XF = false, bool GBW = false>
+// KVR (with XF): k and/or v may be read in reversed token order (p.k_rev,
+// p.v_rev).
+template <typename T, int D, bool FAST, bool CROSS, bool XF = false, bool GBW = false, bool KVR = false>
 __device__ __forceinline__ void out_role(const FwdParams& p, int bh, int ci, int qb, bool chunked, char* l0, char* l1,
                                          char* l2, char* l3) {
   using C = OutTile<T, D, FAST>;
@@ -301,10 +307,31 @@ __device__ __forceinline__ void out_role(const FwdParams& p, int bh, int ci, int
 
   TileLoads<T, typename C::KT, C::WAVES> kload;
   TileLoads<T, typename C::VT, C::WAVES> vload;
-  kload.init(tstride, lane);
-  vload.init(tstride, lane);
+  const bool krev = KVR && p.k_rev, vrev = KVR && p.v_rev;  // uniform
+  if (krev)
+    kload.init_rev(tstride, lane);
+  else
+    kload.init(tstride, lane);
+  if (vrev)
+    vload.init_rev(tstride, lane);
+  else
+    vload.init(tstride, lane);
   auto issue_kv = [&](int j, char* kbuf, char* vbuf) __attribute__((always_inline)) {
     const int kb0 = c0 + j * C::BN;
+    if constexpr (KVR) {
+      if (kb0 + C::BN <= cend) {
+        if (krev) kload.issue_rev(kbuf, K, tstride, len, kb0, wave);
+        else kload.issue(kbuf, K, tstride, kb0, wave);
+        if (vrev) vload.issue_rev(vbuf, V, tstride, len, kb0, wave);
+        else vload.issue(vbuf, V, tstride, kb0, wave);
+      } else {
+        if (krev) kload.issue_clamped_rev(kbuf, K, tstride, len, kb0, cend - 1, wave);
+        else kload.issue_clamped(kbuf, K, tstride, kb0, cend - 1, wave);
+        if (vrev) vload.issue_clamped_rev(vbuf, V, tstride, len, kb0, cend - 1, wave);
+        else vload.issue_clamped(vbuf, V, tstride, kb0, cend - 1, wave);
+      }
+      return;
+    }
     if (kb0 + C::BN <= cend) {
       kload.issue(kbuf, K, tstride, kb0, wave);
       vload.issue(vbuf, V, tstride, kb0, wave);
@@ -737,7 +764,7 @@ __device__ __forceinline__ void scale_frag(f32x8& f, const float* z, const bool*
 // and then publishes its snapshot R_i^T for the next chunk's output
 // workgroups. Wave (wr, wc) owns row tiles wr MTW .. +MTW-1 and dv tiles
 // wc NTW .. +NTW-1.
-template <typename T, int D>
+template <typename T, int D, bool KVR = false>
 __device__ __forceinline__ void state_role(const FwdParams& p, int bh, int ci, int part, char* l0, char* l1,
                                            char* l2, char* l3) {
   using SC = StTile<T, D>;
@@ -829,16 +856,38 @@ __device__ __forceinline__ void state_role(const FwdParams& p, int bh, int ci, i
 
   TileLoads<T, typename SC::KT, SC::NW> kload;
   TileLoads<T, typename SC::VT, SC::NW> vload;
-  kload.init(tstride, lane);
-  vload.init(tstride, lane);
+  const bool krev = KVR && p.k_rev, vrev = KVR && p.v_rev;  // uniform
+  if (krev)
+    kload.init_rev(tstride, lane);
+  else
+    kload.init(tstride, lane);
+  if (vrev)
+    vload.init_rev(tstride, lane);
+  else
+    vload.init(tstride, lane);
   auto issue_kv = [&](int j, char* buf) __attribute__((always_inline)) {  // K^T then V tile
     const int kb0 = c0 + j * SC::BK;
+    char* vbuf = buf + SC::KT::BYTES;
+    if constexpr (KVR) {
+      if (kb0 + SC::BK <= cend) {
+        if (krev) kload.issue_rev(buf, K, tstride, len, kb0, wave);
+        else kload.issue(buf, K, tstride, kb0, wave);
+        if (vrev) vload.issue_rev(vbuf, V, tstride, len, kb0, wave);
+        else vload.issue(vbuf, V, tstride, kb0, wave);
+      } else {
+        if (krev) kload.issue_clamped_rev(buf, K, tstride, len, kb0, cend - 1, wave);
+        else kload.issue_clamped(buf, K, tstride, kb0, cend - 1, wave);
+        if (vrev) vload.issue_clamped_rev(vbuf, V, tstride, len, kb0, cend - 1, wave);
+        else vload.issue_clamped(vbuf, V, tstride, kb0, cend - 1, wave);
+      }
+      return;
+    }
     if (kb0 + SC::BK <= cend) {
       kload.issue(buf, K, tstride, kb0, wave);
-      vload.issue(buf + SC::KT::BYTES, V, tstride, kb0, wave);
+      vload.issue(vbuf, V, tstride, kb0, wave);
     } else {
       kload.issue_clamped(buf, K, tstride, kb0, cend - 1, wave);
-      vload.issue_clamped(buf + SC::KT::BYTES, V, tstride, kb0, cend - 1, wave);
+      vload.issue_clamped(vbuf, V, tstride, kb0, cend - 1, wave);
     }
   };
   // zeta_k = g^(cend-1-k); fragment element j is key k0 + kj(j) with
@@ -1042,7 +1091,7 @@ struct MultiParams {
   int nprod;
 };
 
-template <typename T, int D, bool FAST>
+template <typename T, int D, bool FAST, bool KVR>
 __global__ __launch_bounds__(kWaves<T> * 64, 1) void retention_parallel_multi_kernel(MultiParams mp) {
 #if defined(__HIP_DEVICE_COMPILE__)
   __shared__ __attribute__((aligned(1024))) char l0[Stage<T, D>::BYTES];
@@ -1066,7 +1115,7 @@ __global__ __launch_bounds__(kWaves<T> * 64, 1) void retention_parallel_multi_ke
     bh = r % groups;
   }
   prod = uniform_i(prod);
-  out_role<T, D, FAST, false, true>(mp.p[prod], uniform_i(bh), 0, uniform_i(qb), false, l0, l1, l2, l3);
+  out_role<T, D, FAST, false, true, false, KVR>(mp.p[prod], uniform_i(bh), 0, uniform_i(qb), false, l0, l1, l2, l3);
 #endif
 }
 
@@ -1082,6 +1131,7 @@ __global__ __launch_bounds__(kWaves<T> * 64, 1) void retention_parallel_multi_ke
 // publish R_{-1}, the state parts come first.
 template <typename T, int D, bool FAST, bool XF = false, bool GBW = false>
 __global__ __launch_bounds__(kWaves<T> * 64, 1) void retention_chunkwise_kernel(FwdParams p) {
+  constexpr bool KVR = false;
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the kernel's signature
   __shared__ __attribute__((aligned(1024))) char l0[Stage<T, D>::BYTES];
   __shared__ __attribute__((aligned(1024))) char l1[Stage<T, D>::BYTES];
@@ -1132,11 +1182,11 @@ __global__ __launch_bounds__(kWaves<T> * 64, 1) void retention_chunkwise_kernel(
   const int qb = state_first ? (role < SPLIT ? -1 : p.qblocks - 1 - (role - SPLIT))
                              : (role == 0 ? p.qblocks - 1 : role <= SPLIT ? -1 : p.qblocks - 1 - (role - SPLIT));
   if (qb < 0)
-    state_role<T, D>(p, bh, ci, state_first ? role : role - 1, l0, l1, l2, l3);
+    state_role<T, D, KVR>(p, bh, ci, state_first ? role : role - 1, l0, l1, l2, l3);
   else if (ci > 0 || p.has_state0)
-    out_role<T, D, FAST, true, XF, GBW>(p, bh, ci, qb, true, l0, l1, l2, l3);
+    out_role<T, D, FAST, true, XF, GBW, KVR>(p, bh, ci, qb, true, l0, l1, l2, l3);
   else
-    out_role<T, D, FAST, false, XF, GBW>(p, bh, ci, qb, true, l0, l1, l2, l3);
+    out_role<T, D, FAST, false, XF, GBW, KVR>(p, bh, ci, qb, true, l0, l1, l2, l3);
 #endif
 }
 
@@ -1147,7 +1197,7 @@ __global__ __launch_bounds__(kWaves<T> * 64, 1) void retention_chunkwise_kernel(
 // together instead of each launch ending on its own. Each product has its
 // own ready flags, chain and snapshots; the tickets, the count and the error
 // word are those of the first product's control block.
-template <typename T, int D, bool FAST>
+template <typename T, int D, bool FAST, bool KVR>
 __global__ __launch_bounds__(kWaves<T> * 64, 1) void retention_chunkwise_multi_kernel(MultiParams mp) {
 #if defined(__HIP_DEVICE_COMPILE__)
   __shared__ __attribute__((aligned(1024))) char l0[Stage<T, D>::BYTES];
@@ -1186,17 +1236,17 @@ __global__ __launch_bounds__(kWaves<T> * 64, 1) void retention_chunkwise_multi_k
   ci = uniform_i(ci);
   bh = uniform_i(bh);
   role = uniform_i(role);
-  constexpr bool XF = true;
+  constexpr bool XF = true, GBW = false;
   const FwdParams& p = mp.p[uniform_i(prod)];
   const bool state_first = ci == 0 && p.has_state0;
   const int qb = state_first ? (role < SPLIT ? -1 : p.qblocks - 1 - (role - SPLIT))
                              : (role == 0 ? p.qblocks - 1 : role <= SPLIT ? -1 : p.qblocks - 1 - (role - SPLIT));
   if (qb < 0)
-    state_role<T, D>(p, bh, ci, state_first ? role : role - 1, l0, l1, l2, l3);
+    state_role<T, D, KVR>(p, bh, ci, state_first ? role : role - 1, l0, l1, l2, l3);
   else if (ci > 0 || p.has_state0)
-    out_role<T, D, FAST, true, XF>(p, bh, ci, qb, true, l0, l1, l2, l3);
+    out_role<T, D, FAST, true, XF, GBW, KVR>(p, bh, ci, qb, true, l0, l1, l2, l3);
   else
-    out_role<T, D, FAST, false, XF>(p, bh, ci, qb, true, l0, l1, l2, l3);
+    out_role<T, D, FAST, false, XF, GBW, KVR>(p, bh, ci, qb, true, l0, l1, l2, l3);
 #endif
 }
 
@@ -1407,6 +1457,8 @@ static FwdParams make_params(const Shape& s, int chunk, const void* q, const voi
   p.out_rot = out_rot;
   p.gb_dout = nullptr;
   p.gb_dg = nullptr;
+  p.k_rev = 0;
+  p.v_rev = 0;
   p.q = q;
   p.k = k;
   p.v = v;
@@ -1473,8 +1525,14 @@ static hipError_t launch_multi_impl(const Shape& s, MultiParams& mp, hipStream_t
   const int64_t blocks = (int64_t)s.batch * s.heads * qblocks * mp.nprod;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((retention_parallel_multi_kernel<T, D, FAST>), dim3((unsigned)blocks), dim3(64 * C::WAVES), 0,
-                     stream, mp);
+  bool kvr = false;
+  for (int i = 0; i < mp.nprod; ++i) kvr = kvr || mp.p[i].k_rev || mp.p[i].v_rev;
+  if (kvr)
+    hipLaunchKernelGGL((retention_parallel_multi_kernel<T, D, FAST, true>), dim3((unsigned)blocks),
+                       dim3(64 * C::WAVES), 0, stream, mp);
+  else
+    hipLaunchKernelGGL((retention_parallel_multi_kernel<T, D, FAST, false>), dim3((unsigned)blocks),
+                       dim3(64 * C::WAVES), 0, stream, mp);
   return hipGetLastError();
 }
 
@@ -1508,8 +1566,14 @@ static hipError_t launch_cmulti_impl(const Shape& s, int chunk, MultiParams& mp,
   const int64_t blocks = (int64_t)mp.nprod * nchunks * bhs * roles;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   if (blocks == 0) return hipGetLastError();
-  hipLaunchKernelGGL((retention_chunkwise_multi_kernel<T, D, FAST>), dim3((unsigned)blocks), dim3(64 * C::WAVES), 0,
-                     stream, mp);
+  bool kvr = false;
+  for (int i = 0; i < mp.nprod; ++i) kvr = kvr || mp.p[i].k_rev || mp.p[i].v_rev;
+  if (kvr)
+    hipLaunchKernelGGL((retention_chunkwise_multi_kernel<T, D, FAST, true>), dim3((unsigned)blocks),
+                       dim3(64 * C::WAVES), 0, stream, mp);
+  else
+    hipLaunchKernelGGL((retention_chunkwise_multi_kernel<T, D, FAST, false>), dim3((unsigned)blocks),
+                       dim3(64 * C::WAVES), 0, stream, mp);
   return hipGetLastError();
 }
 
@@ -1531,6 +1595,8 @@ hipError_t launch_chunkwise_products(const Shape& s, int chunk, int n, const Chu
     const ChunkProduct& x = pr[i < n ? i : 0];
     mp.p[i] = make_params(s, chunk, x.q, x.k, x.v, nullptr, x.o, x.state_in, x.state_out, x.snap, x.chain, ctrl,
                           nullptr, eps, x.q_rev, x.out_rev, x.out_rot, nullptr, 0, nullptr);
+    mp.p[i].k_rev = x.k_rev;
+    mp.p[i].v_rev = x.v_rev;
   }
   if (s.dtype == 1) {
     switch (s.d) {
@@ -1557,6 +1623,8 @@ hipError_t launch_parallel_products(const Shape& s, int n, const ParallelProduct
     const ParallelProduct& x = pr[i < n ? i : 0];
     mp.p[i] = make_params(s, s.seqlen, x.q, x.k, x.v, nullptr, x.o, nullptr, nullptr, nullptr, nullptr, nullptr,
                           nullptr, eps, x.q_rev, x.out_rev, x.out_rot, nullptr, 0, nullptr);
+    mp.p[i].k_rev = x.k_rev;
+    mp.p[i].v_rev = x.v_rev;
   }
   if (s.dtype == 1) {
     switch (s.d) {

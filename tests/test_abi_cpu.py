@@ -161,9 +161,9 @@ def test_backward_validates_before_any_device_call(L):
     ws_plain = L.retention_parallel_bwd_workspace_bytes(ctypes.byref(d), 0)
     up = lambda x: (x + 255) // 256 * 256
     tensor = up(1 * 8 * 2 * 64 * 2)
-    # no rotation: the reversed q and the reversed dO (with a gate written by
-    # the recomputed forward, which keeps no raw output)
-    assert ws_plain == 2 * tensor and ws_gate == 2 * tensor
+    # no rotation: the products read q (and, without a gate, dout) reversed;
+    # with a gate the recomputed forward writes the reversed dO
+    assert ws_plain == 0 and ws_gate == tensor
     p = [ALIGNED * i for i in range(1, 11)]
     bwd = L.retention_parallel_bwd
     # g and dg: both or neither
@@ -173,8 +173,8 @@ def test_backward_validates_before_any_device_call(L):
                None) == 5
     # an output overlapping an input
     assert bwd(ctypes.byref(d), p[0], p[1], p[2], None, p[4], p[0], p[6], p[7], None, p[9], ws_plain, None) == 8
-    # workspace too small
-    assert bwd(ctypes.byref(d), p[0], p[1], p[2], None, p[4], p[5], p[6], p[7], None, p[9], ws_plain - 1,
+    # workspace too small (with a gate: the reversed dO)
+    assert bwd(ctypes.byref(d), p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7], p[8], p[9], ws_gate - 1,
                None) == 6
 
 
