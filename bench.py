@@ -122,14 +122,27 @@ def chunkwise_bytes(batch, seqlen, heads, dk, dv, elem=2, gate=True, state_out=T
 
 
 # ---------------------------------------------------------------------------
-def time_calls(fn, steps, warmup):
+# Every leg but the headline also warms until this much wall time of its own
+# calls has passed: the GPU's clocks settle only after tens of milliseconds of
+# sustained load, and a few warm-up calls of a short leg are far less.
+SETTLE_MS = 150.0
+
+
+def time_calls(fn, steps, warmup, settle_ms=0.0):
     """Average device time per call over `steps` back-to-back calls (events on
-    torch's current stream, which is the stream the library launches on)."""
+    torch's current stream, which is the stream the library launches on),
+    after `warmup` calls and then, with settle_ms, more calls until that much
+    wall time has passed."""
     import torch
 
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
+    t_settle = time.perf_counter()
+    while (time.perf_counter() - t_settle) * 1e3 < settle_ms:
+        for _ in range(4):
+            fn()
+        torch.cuda.synchronize()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     start.record()
@@ -167,11 +180,12 @@ def chunkwise_inputs(name):
     return w, [t.torch("cuda:0") for t in w.inputs()]
 
 
-def bench_chunkwise(steps, warmup, name="retention_7b_8k", cold_reps=0, prepared=None):
+def bench_chunkwise(steps, warmup, name="retention_7b_8k", cold_reps=0, prepared=None, settle_ms=0.0):
     """Chunkwise calls on one workload: per-call time (reset + kernel) and the
     kernel's own event time per call; with cold_reps, also the kernel after
     a 512 MiB write that evicts L2 and the Infinity Cache. prepared: the
-    result of chunkwise_inputs(name), drawn earlier."""
+    result of chunkwise_inputs(name), drawn earlier. settle_ms: as for
+    time_calls (the headline leg takes exactly its `warmup` calls)."""
     import torch
 
     import retnet_retention_amd as rr
@@ -190,7 +204,7 @@ def bench_chunkwise(steps, warmup, name="retention_7b_8k", cold_reps=0, prepared
     # the step rate: `steps` plain back-to-back calls (reset + kernel)
     for _ in range(warmup):
         step()
-    ms, wall = time_calls(step, steps, 0)
+    ms, wall = time_calls(step, steps, 0, settle_ms=settle_ms)
     # then as many calls that each also record a pair of events around the
     # chunkwise kernel itself (after the control-block reset): the roofline's
     # duration (the event records add a little gap between calls, so these
@@ -250,7 +264,7 @@ def bench_parallel(steps, warmup):
     def step():
         rr.parallel_fwd(q, k, v, g, rotary_base=w.rotary_base, out=out)
 
-    ms, _ = time_calls(step, steps, warmup)
+    ms, _ = time_calls(step, steps, warmup, settle_ms=SETTLE_MS)
     flops = parallel_flops(w.batch, w.seqlen, w.heads, w.dk, w.dv)
     return {"workload": w, "ms": ms, "tflops": flops / (ms * 1e-3) / 1e12}
 
@@ -273,7 +287,7 @@ def bench_parallel_bwd(steps, warmup):
     def step():
         rr.parallel_bwd(q, k, v, dout, g, rotary_base=w.rotary_base, workspace=ws)
 
-    ms, _ = time_calls(step, steps, warmup)
+    ms, _ = time_calls(step, steps, warmup, settle_ms=SETTLE_MS)
     flops = 3 * parallel_flops(w.batch, w.seqlen, w.heads, w.dk, w.dv)
     return {"workload": w, "ms": ms, "flops": flops, "tflops": flops / (ms * 1e-3) / 1e12}
 
@@ -302,7 +316,7 @@ def bench_chunkwise_bwd(steps, warmup):
     def step():
         rr.chunkwise_bwd(q, k, v, dout, g, chunk=w.chunk, workspace=ws)
 
-    ms, _ = time_calls(step, steps, warmup)
+    ms, _ = time_calls(step, steps, warmup, settle_ms=SETTLE_MS)
     rr.check_chunkwise(ws)
     flops = 3 * chunkwise_flops(w.batch, w.seqlen, w.heads, w.dk, w.dv, w.chunk)
     return {"workload": w, "ms": ms, "flops": flops, "tflops": flops / (ms * 1e-3) / 1e12}
@@ -319,7 +333,8 @@ def bench_score_map(steps, warmup):
     w = get("retention_3b")
     q, k, _, _ = (t.torch("cuda:0") for t in w.inputs())
     ws = torch.empty(w.seqlen * w.dk // 2 * 8 + 256, dtype=torch.uint8, device="cuda:0")
-    ms, _ = time_calls(lambda: rr.score_map(q, k, rotary_base=w.rotary_base, workspace=ws), steps, warmup)
+    ms, _ = time_calls(lambda: rr.score_map(q, k, rotary_base=w.rotary_base, workspace=ws), steps, warmup,
+                       settle_ms=SETTLE_MS)
     nbytes = k.numel() * k.element_size() + w.batch * w.seqlen * 4
     return {"workload": w, "us": ms * 1e3, "gbps": nbytes / (ms * 1e-3) / 1e9}
 
@@ -374,7 +389,7 @@ def bench_decode(n_steps=256, warmup=16, batches=None, graph=True):
             it[0] += 1
             rr.recurrent_step(q, k, v, state, g, pos=w.seqlen + it[0], out=out)
 
-        ms, _ = time_calls(step, n_steps, warmup)
+        ms, _ = time_calls(step, n_steps, warmup, settle_ms=SETTLE_MS)
         nbytes = step_bytes(bsz, w.heads, w.dk, w.dv)
         results[bsz] = {"us_per_step": ms * 1e3, "tokens_per_s": bsz / (ms * 1e-3),
                         "gbps": nbytes / (ms * 1e-3) / 1e9}
@@ -465,12 +480,13 @@ def bench_varlen(steps, warmup):
     ws = torch.empty(B.lib().retention_chunkwise_varlen_workspace_bytes(ctypes.byref(desc), chunk),
                      dtype=torch.uint8, device="cuda:0")
     ms_var, _ = time_calls(lambda: rr.chunkwise_varlen_fwd(q, k, v, cu, maxlen, g, chunk=chunk, state_out=st, out=out,
-                                                           workspace=ws), steps, warmup)
+                                                           workspace=ws), steps, warmup, settle_ms=SETTLE_MS)
     rr.check_chunkwise(ws)
     shp = (2, tot // 2, h, d)
     st2 = torch.empty((2, h, d, d), device="cuda:0")
     ms_fix, _ = time_calls(lambda: rr.chunkwise_fwd(q.view(shp), k.view(shp), v.view(shp), g.view(shp), chunk=chunk,
-                                                    state_out=st2, out=out.view(shp), workspace=ws), steps, warmup)
+                                                    state_out=st2, out=out.view(shp), workspace=ws), steps, warmup,
+                         settle_ms=SETTLE_MS)
     rr.check_chunkwise(ws)
     flops_var = sum(chunkwise_flops(1, n, h, d, d, chunk) for n in VARLEN_LENS)
     flops_fix = chunkwise_flops(2, tot // 2, h, d, d, chunk)
@@ -946,7 +962,8 @@ def main():
         others = {}
         if not args.no_other_chunkwise:
             for oname in ("retention_200m", "retention_3b"):
-                o = bench_chunkwise(max(args.steps // 2, 3), max(args.warmup // 4, 3), name=oname)
+                o = bench_chunkwise(max(args.steps // 2, 3), max(args.warmup // 4, 3), name=oname,
+                                    settle_ms=SETTLE_MS)
                 ow = o["workload"]
                 print(f"chunkwise {oname}: {o['ms']:.3f} ms/step, {o['tflops']:.1f} TFLOP/s; kernel alone "
                       f"{o['kernel_ms'] * 1e3:.1f} us, {o['kernel_tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
