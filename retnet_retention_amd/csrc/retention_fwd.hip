@@ -630,41 +630,60 @@ __device__ __forceinline__ void out_role(const FwdParams& p, int bh, int ci, int
                         __builtin_fmaf(oacc[r][t][4 * a + 2], scale, shift),
                         __builtin_fmaf(oacc[r][t][4 * a + 3], scale, shift)};
         }
+        // the pass's gate and dout values, KG accesses at a time, all in
+        // flight before the first is used (64 registers for bf16)
+        constexpr int NK = PR / RPA2, KG = sizeof(T) == 2 ? NK : (NK < 4 ? NK : 4);
+        static_assert(NK % KG == 0, "whole groups");
+        const int grow0 = min(qw0 + 32 * r + P0, cend - 1);
+        const __amdgpu_buffer_rsrc_t grs = scalar_rsrc(G + (int64_t)grow0 * tstride);
+        const __amdgpu_buffer_rsrc_t drs = scalar_rsrc(DO + (int64_t)grow0 * tstride);
 #pragma unroll
-        for (int k = 0; k < PR / RPA2; ++k) {
-          const int rr = k * RPA2 + lane / LPR2, col = (lane % LPR2) * CPL;
-          const int orow = qw0 + 32 * r + P0 + rr;
-          const int grow = min(orow, cend - 1);  // rows past the chunk load a clamped row and store nothing
-          const float rs = __shfl(rsr, P0 + rr, 64);
-          float y[CPL], gv[CPL], dv[CPL];
+        for (int k0 = 0; k0 < NK; k0 += KG) {
+          u32x4b graw[KG], draw[KG];
 #pragma unroll
-          for (int e = 0; e < CPL; e += 4) {
-            const f32x4 x = *reinterpret_cast<const f32x4*>(stg + rr * EROW2 + (col + e) * 4);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) y[e + i] = x[i];
-          }
-          load16f(G + (int64_t)grow * tstride + col, gv);
-          load16f(DO + (int64_t)grow * tstride + col, dv);
-          float dg[CPL], s1 = 0.f, s2 = 0.f;
-#pragma unroll
-          for (int e = 0; e < CPL; ++e) {
-            const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * gv[e]));
-            dg[e] = dv[e] * y[e] * (sg * __builtin_fmaf(gv[e], 1.0f - sg, 1.0f));
-            dv[e] = dv[e] * gv[e] * sg;  // dy
-            s1 += dv[e];
-            s2 = __builtin_fmaf(dv[e], y[e], s2);
+          for (int kk = 0; kk < KG; ++kk) {
+            const int orow = qw0 + 32 * r + P0 + (k0 + kk) * RPA2 + lane / LPR2;
+            const int grow = min(orow, cend - 1);  // rows past the chunk load a clamped row and store nothing
+            const uint32_t off = (uint32_t)(((grow - grow0) * tstride + (lane % LPR2) * CPL) * (int)sizeof(T));
+            graw[kk] = __builtin_amdgcn_raw_buffer_load_b128(grs, off, 0, 0);
+            draw[kk] = __builtin_amdgcn_raw_buffer_load_b128(drs, off, 0, 0);
           }
 #pragma unroll
-          for (int w = 1; w < LPR2; w *= 2) {
-            s1 += __shfl_xor(s1, w, 64);
-            s2 += __shfl_xor(s2, w, 64);
-          }
-          const float m1 = s1 * (1.0f / D), m2 = s2 * (1.0f / D);
+          for (int kk = 0; kk < KG; ++kk) {
+            const int k = k0 + kk;
+            const int rr = k * RPA2 + lane / LPR2, col = (lane % LPR2) * CPL;
+            const int orow = qw0 + 32 * r + P0 + rr;
+            const float rs = __shfl(rsr, P0 + rr, 64);
+            float y[CPL], gv[CPL], dv[CPL];
 #pragma unroll
-          for (int e = 0; e < CPL; ++e) dv[e] = (dv[e] - m1 - y[e] * m2) * rs;
-          if (orow < cend) {
-            store16f(DG + (int64_t)orow * tstride + col, dg);
-            store16f(O + (int64_t)(p.seqlen - 1 - orow) * tstride + col, dv);
+            for (int e = 0; e < CPL; e += 4) {
+              const f32x4 x = *reinterpret_cast<const f32x4*>(stg + rr * EROW2 + (col + e) * 4);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) y[e + i] = x[i];
+            }
+            load16f_raw(graw[kk], gv, (T*)nullptr);
+            load16f_raw(draw[kk], dv, (T*)nullptr);
+            float dg[CPL], s1 = 0.f, s2 = 0.f;
+#pragma unroll
+            for (int e = 0; e < CPL; ++e) {
+              const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * gv[e]));
+              dg[e] = dv[e] * y[e] * (sg * __builtin_fmaf(gv[e], 1.0f - sg, 1.0f));
+              dv[e] = dv[e] * gv[e] * sg;  // dy
+              s1 += dv[e];
+              s2 = __builtin_fmaf(dv[e], y[e], s2);
+            }
+#pragma unroll
+            for (int w = 1; w < LPR2; w *= 2) {
+              s1 += __shfl_xor(s1, w, 64);
+              s2 += __shfl_xor(s2, w, 64);
+            }
+            const float m1 = s1 * (1.0f / D), m2 = s2 * (1.0f / D);
+#pragma unroll
+            for (int e = 0; e < CPL; ++e) dv[e] = (dv[e] - m1 - y[e] * m2) * rs;
+            if (orow < cend) {
+              store16f(DG + (int64_t)orow * tstride + col, dg);
+              store16f(O + (int64_t)(p.seqlen - 1 - orow) * tstride + col, dv);
+            }
           }
         }
       });
