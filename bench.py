@@ -869,7 +869,7 @@ def main():
     ap.add_argument("--profile-out", default=os.path.join(ROOT, "profiles"))
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+        print(f"bench.py measures one GPU only: the library has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
         sys.exit(2)
     if args.profile:
