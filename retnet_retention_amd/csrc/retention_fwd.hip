@@ -86,7 +86,14 @@ struct OutTile {
 // what they are worth).
 constexpr double kFastSpanLog2 = 64.0;
 
-template <typename T, int D>
+// chunkwise grids of at most this many workgroups (one and a half per CU)
+// split each chunk's state over two workgroups (bf16, d = 256): measured on
+// 384 workgroups (-3%) and against it on 480 (+11%), where the extra state
+// workgroups no longer fit beside the others
+constexpr int64_t kSmallGrid = 384;
+
+// SPL: state workgroups per chunk (the default, or two for a small grid)
+template <typename T, int D, int SPL = (kWaves<T> < 8 && D > 128 ? D / 128 : 1)>
 struct StTile {
   // State workgroups per chunk: one (eight waves), or one per 128 dk rows of
   // R (four waves, D = 256). Fewer rows per workgroup shorten the serial
@@ -96,7 +103,7 @@ struct StTile {
   // holding MTW x NTW tiles in fp32 registers; waves past the tiles (D = 64)
   // stay idle.
   static constexpr int NW = kWaves<T>;
-  static constexpr int SPLIT = NW < 8 && D > 128 ? D / 128 : 1;
+  static constexpr int SPLIT = SPL;
   static constexpr int ROWS = D / SPLIT;        // dk rows per workgroup
   static constexpr int BK = 32 / (int)sizeof(T) * 2;  // keys per block: 32 (bf16), 16 (fp32)
   static constexpr int MTA = ROWS / 32, NTA = D / 32;   // tiles of the workgroup
@@ -271,7 +278,9 @@ __device__ __forceinline__ int seq_rows(const FwdParams& p, int b, int64_t& tok0
 // reversed token positions.
 // KVR (with XF): k and/or v may be read in reversed token order (p.k_rev,
 // p.v_rev).
-template <typename T, int D, bool FAST, bool CROSS, bool XF = false, bool GBW = false, bool KVR = false>
+// SPL: the state workgroups per chunk whose snapshots the cross term waits for.
+template <typename T, int D, bool FAST, bool CROSS, bool XF = false, bool GBW = false, bool KVR = false,
+          int SPL = StTile<T, D>::SPLIT>
 __device__ __forceinline__ void out_role(const FwdParams& p, int bh, int ci, int qb, bool chunked, char* l0, char* l1,
                                          char* l2, char* l3) {
   using C = OutTile<T, D, FAST>;
@@ -347,7 +356,7 @@ __device__ __forceinline__ void out_role(const FwdParams& p, int bh, int ci, int
     if (sl == 0) {
       const int* flags = p.ctrl + p.fbase + kCtrlHead + (bh * (p.nchunks + 1) + ci) * kFlagsPerChunk + kMaxSplit;
 #pragma unroll
-      for (int q = 0; q < StTile<T, D>::SPLIT; ++q) wait_flag(flags + q, p.ctrl + 1);
+      for (int q = 0; q < SPL; ++q) wait_flag(flags + q, p.ctrl + 1);
     }
     async_flat<T, C::RT_BYTES, C::WAVES, kCoherent>(buf, R + (int64_t)sl * C::RS * D, wave, lane);
   };
@@ -783,10 +792,10 @@ __device__ __forceinline__ void scale_frag(f32x8& f, const float* z, const bool*
 // and then publishes its snapshot R_i^T for the next chunk's output
 // workgroups. Wave (wr, wc) owns row tiles wr MTW .. +MTW-1 and dv tiles
 // wc NTW .. +NTW-1.
-template <typename T, int D, bool KVR = false>
+template <typename T, int D, bool KVR = false, int SPL = StTile<T, D>::SPLIT>
 __device__ __forceinline__ void state_role(const FwdParams& p, int bh, int ci, int part, char* l0, char* l1,
                                            char* l2, char* l3) {
-  using SC = StTile<T, D>;
+  using SC = StTile<T, D, SPL>;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, hh = lane >> 5;
@@ -1148,7 +1157,7 @@ __global__ __launch_bounds__(kWaves<T> * 64, 1) void retention_parallel_multi_ke
 // number of waiting workgroups can fill the chip: in chunk 0 with a
 // carried-in state, whose output workgroups wait for the state parts to
 // publish R_{-1}, the state parts come first.
-template <typename T, int D, bool FAST, bool XF = false, bool GBW = false>
+template <typename T, int D, bool FAST, bool XF = false, bool GBW = false, int SPL = StTile<T, D>::SPLIT>
 __global__ __launch_bounds__(kWaves<T> * 64, 1) void retention_chunkwise_kernel(FwdParams p) {
   constexpr bool KVR = false;
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the kernel's signature
@@ -1157,7 +1166,7 @@ __global__ __launch_bounds__(kWaves<T> * 64, 1) void retention_chunkwise_kernel(
   __shared__ __attribute__((aligned(1024))) char l2[Stage<T, D>::BYTES];
   __shared__ __attribute__((aligned(1024))) char l3[Stage<T, D>::BYTES];
   __shared__ int s_ticket;
-  constexpr int SPLIT = StTile<T, D>::SPLIT;
+  constexpr int SPLIT = SPL;
   const int bhs = p.batch * p.heads;
   const int roles = SPLIT + p.qblocks;  // workgroups per (sequence, head, chunk)
   // class of this workgroup: blockIdx mod 8, which is also the XCD it runs on
@@ -1201,11 +1210,11 @@ __global__ __launch_bounds__(kWaves<T> * 64, 1) void retention_chunkwise_kernel(
   const int qb = state_first ? (role < SPLIT ? -1 : p.qblocks - 1 - (role - SPLIT))
                              : (role == 0 ? p.qblocks - 1 : role <= SPLIT ? -1 : p.qblocks - 1 - (role - SPLIT));
   if (qb < 0)
-    state_role<T, D, KVR>(p, bh, ci, state_first ? role : role - 1, l0, l1, l2, l3);
+    state_role<T, D, KVR, SPL>(p, bh, ci, state_first ? role : role - 1, l0, l1, l2, l3);
   else if (ci > 0 || p.has_state0)
-    out_role<T, D, FAST, true, XF, GBW, KVR>(p, bh, ci, qb, true, l0, l1, l2, l3);
+    out_role<T, D, FAST, true, XF, GBW, KVR, SPL>(p, bh, ci, qb, true, l0, l1, l2, l3);
   else
-    out_role<T, D, FAST, false, XF, GBW, KVR>(p, bh, ci, qb, true, l0, l1, l2, l3);
+    out_role<T, D, FAST, false, XF, GBW, KVR, SPL>(p, bh, ci, qb, true, l0, l1, l2, l3);
 #endif
 }
 
@@ -1406,7 +1415,16 @@ static hipError_t launch_fwd_impl(const Shape& s, int chunk, FwdParams p, bool c
   hipLaunchKernelGGL(reset_ctrl_kernel, dim3((unsigned)((nctrl + 255) / 256 < 1024 ? (nctrl + 255) / 256 : 1024)),
                      dim3(256), 0, stream, p.ctrl, (int)nctrl, keep_err ? 1 : 0);
   p.xcd_order = bhs % 8 == 0;
-  const int roles = StTile<T, D>::SPLIT + p.qblocks;
+  // A grid of few workgroups per CU is not filled by the chunks'
+  // independent work: the state chain (one link per chunk) sets its length.
+  // There (bf16, d = 256, batch form) each chunk's state splits over two
+  // workgroups of 128 rows, which halves a link's products, combine and
+  // publish.
+  constexpr int SPL1 = StTile<T, D>::SPLIT;
+  constexpr bool CAN2 = sizeof(T) == 2 && D == 256 && SPL1 == 1;
+  const bool two = CAN2 && !p.cu && !p.q_rev && !p.out_rev && !p.out_rot && !p.gb_dout &&
+                   (int64_t)p.nchunks * bhs * (SPL1 + p.qblocks) <= kSmallGrid;
+  const int roles = (two ? 2 : SPL1) + p.qblocks;
   const int64_t blocks = (int64_t)p.nchunks * bhs * roles;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   if (p.cu) {
@@ -1422,6 +1440,9 @@ static hipError_t launch_fwd_impl(const Shape& s, int chunk, FwdParams p, bool c
   else if (p.q_rev || p.out_rev || p.out_rot)
     hipLaunchKernelGGL((retention_chunkwise_kernel<T, D, FAST, true>), dim3((unsigned)blocks), dim3(64 * C::WAVES), 0,
                        stream, p);
+  else if (CAN2 && two)
+    hipLaunchKernelGGL((retention_chunkwise_kernel<T, D, FAST, false, false, CAN2 ? 2 : SPL1>), dim3((unsigned)blocks),
+                       dim3(64 * C::WAVES), 0, stream, p);
   else
     hipLaunchKernelGGL((retention_chunkwise_kernel<T, D, FAST>), dim3((unsigned)blocks), dim3(64 * C::WAVES), 0,
                        stream, p);

@@ -250,9 +250,11 @@ def test_chunkwise_handoff_completes(b, h):
     torch.cuda.synchronize()
     ctrl = ws[:64].view(torch.int32).cpu()
     nchunks = -(-n // chunk)
-    # one state workgroup (bf16 runs eight waves per workgroup) and one output
-    # workgroup (the whole 128-row chunk) per (sequence, head, chunk)
-    total = nchunks * b * h * (1 + 1)
+    # one output workgroup (the whole 128-row chunk) and, this grid being
+    # small (at most 384 workgroups with one state workgroup per chunk), two
+    # state workgroups of 128 rows each per (sequence, head, chunk)
+    assert nchunks * b * h * (1 + 1) <= 384
+    total = nchunks * b * h * (2 + 1)
     assert int(ctrl[0]) == total
     assert int(ctrl[1]) == 0
     if (b * h) % 8 == 0:
