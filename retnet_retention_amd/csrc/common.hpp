@@ -668,6 +668,21 @@ __device__ __forceinline__ float sum16(float x) {
   return x;
 }
 
+// Sum over each group of N consecutive lanes (N = 2 .. 64, a power of two),
+// in every lane of the group: the butterflies of sum16 up to N, then lane
+// exchanges across 16-lane rows.
+template <int N>
+__device__ __forceinline__ float sum_lanes(float x) {
+  static_assert(N >= 2 && N <= 64 && (N & (N - 1)) == 0, "power-of-two lane group");
+  x += dpp<0xB1>(x);
+  if constexpr (N >= 4) x += dpp<0x4E>(x);
+  if constexpr (N >= 8) x += dpp<0x141>(x);
+  if constexpr (N >= 16) x += dpp<0x140>(x);
+  if constexpr (N >= 32) x += __shfl_xor(x, 16, 64);
+  if constexpr (N >= 64) x += __shfl_xor(x, 32, 64);
+  return x;
+}
+
 // Sum of the two lanes l and l ^ 32.
 __device__ __forceinline__ float sum_pair32(float x) { return x + __shfl_xor(x, 32, 64); }
 

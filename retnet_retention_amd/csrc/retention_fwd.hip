@@ -681,11 +681,8 @@ __device__ __forceinline__ void out_role(const FwdParams& p, int bh, int ci, int
               s1 += dv[e];
               s2 = __builtin_fmaf(dv[e], y[e], s2);
             }
-#pragma unroll
-            for (int w = 1; w < LPR2; w *= 2) {
-              s1 += __shfl_xor(s1, w, 64);
-              s2 += __shfl_xor(s2, w, 64);
-            }
+            s1 = sum_lanes<LPR2>(s1);
+            s2 = sum_lanes<LPR2>(s2);
             const float m1 = s1 * (1.0f / D), m2 = s2 * (1.0f / D);
 #pragma unroll
             for (int e = 0; e < CPL; ++e) dv[e] = (dv[e] - m1 - y[e] * m2) * rs;
