@@ -215,7 +215,7 @@ ret_status_t retention_recurrent_step_positions(const ret_desc_t *desc, const vo
  * stored in the input dtype; products accumulate in fp32.
  *
  * Workspace: at least retention_parallel_bwd_workspace_bytes(desc, g != NULL)
- * bytes, never NULL. */
+ * bytes (0 without rotation and gate: workspace may then be NULL). */
 size_t retention_parallel_bwd_workspace_bytes(const ret_desc_t *desc, int32_t has_gate);
 ret_status_t retention_parallel_bwd(const ret_desc_t *desc, const void *q, const void *k, const void *v,
                                     const void *g, const void *dout, void *dq, void *dk, void *dv, void *dg,
