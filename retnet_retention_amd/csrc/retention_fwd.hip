@@ -31,8 +31,10 @@
 // done: the waits always end. Every wait is also
 // bounded; on expiry it sets an error word in the control block and goes on.
 // The backward's products use separate instantiations (XF) that can read q
-// in reversed token order and store their output reversed and turned back by
-// the rotation; the forward instantiations carry none of that code.
+// (and, with KVR, k and v) in reversed token order and store their output
+// reversed and turned back by the rotation; GBW forms the gradient through
+// the gate and GroupNorm in the recomputed forward's epilogue; the forward
+// instantiations carry none of that code.
 #include <type_traits>
 
 #include "common.hpp"
@@ -268,9 +270,9 @@ __device__ __forceinline__ int seq_rows(const FwdParams& p, int b, int64_t& tok0
 // CROSS: the chunk has a previous state R_{i-1} (chunkwise form, chunk > 0
 // or an initial state); the parallel form and chunk 0 without one have none.
 // XF: the instantiations that may read q reversed and store their output
-// reversed and/or turned back (the backward's products: the parallel kernel,
-// and a second chunkwise instantiation launched only for them); the forward
-// chunkwise kernel carries none of that code.
+// reversed and/or turned back (the backward's products: one launch of the
+// parallel or chunkwise multi-product kernel, and the recomputed forward);
+// the forward kernels carry none of that code.
 // GBW (with XF): the backward's recomputed forward. In place of the forward
 // epilogue it forms the gradient through the swish gate and the GroupNorm
 // (from the gate g, the caller's dout and the recomputed output, still in
@@ -1075,8 +1077,9 @@ __device__ __forceinline__ void state_role(const FwdParams& p, int bh, int ci, i
 // ---------------------------------------------------------------------------
 // Kernels.
 // ---------------------------------------------------------------------------
-// XF: the instantiation for the backward's products (reversed query reads,
-// transforming stores); the forward's carries none of that code.
+// XF: the instantiation with reversed query reads and transforming stores;
+// GBW: the backward's recomputed forward (gradient through the gate and
+// GroupNorm in the epilogue). The forward's carries none of that code.
 template <typename T, int D, bool FAST, bool XF = false, bool GBW = false>
 __global__ __launch_bounds__(kWaves<T> * 64, 1) void retention_parallel_kernel(FwdParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the kernel's signature
@@ -1106,8 +1109,8 @@ __global__ __launch_bounds__(kWaves<T> * 64, 1) void retention_parallel_kernel(F
 }
 
 // Several parallel-form products of one shape in one grid (the backward's
-// three gradient products, which share no inputs' roles but none waits for
-// another): dealt out longest query block first across all of them, so that
+// three gradient products, none of which reads another's output): dealt
+// out longest query block first across all of them, so that
 // the long blocks of every product start at once and the short blocks of all
 // fill the end, instead of each launch ending on its own long blocks.
 constexpr int kMaxProducts = 3;
