@@ -166,15 +166,15 @@ size_t bwd_bytes(const ret_desc_t* d, bool gate) {
 // Backward of the chunkwise form: the chunkwise kernel's own workspace for
 // each of the three gradient products, which run in one launch (three
 // control blocks, then three state chains, then three sets of per-chunk
-// states; the recomputed forward uses the first of each), the parallel
-// backward's table and tensor slots, then with a carried state up to three
-// fp32 states (S0^T; the dS terms for the reversed products; their final
+// states; the recomputed forward uses the first chain and the third set),
+// the parallel backward's table and tensor slots, then with a carried state
+// three fp32 states (S0^T; dS^T / g for the reversed dk product; its final
 // state).
 constexpr int kBwdProducts = 3;
 size_t state_bytes(const ret_desc_t* d) { return align_up((size_t)d->batch * d->heads * d->dk * d->dv * 4); }
 size_t cbwd_bytes(const ret_desc_t* d, int32_t chunk, bool gate, bool states) {
   return kBwdProducts * (ctrl_bytes(d, chunk) + chain_bytes(d) + snap_bytes(d, chunk)) + bwd_bytes(d, gate) +
-         (states ? 4 * state_bytes(d) : 0);
+         (states ? 3 * state_bytes(d) : 0);
 }
 
 // Chunkwise forward: every check that does not involve the workspace.
@@ -318,27 +318,29 @@ ret_status_t chunkwise_bwd_impl(const ret_desc_t* desc, int32_t chunk, const voi
   // The call's first chunkwise launch clears the control block's error word,
   // the later one keeps it, so the word reports an error of either.
   bool first = true;
-  // states of the three products (per head g): S0^T for dq; dS^T / g and
-  // dS / g for the reversed ones (their g^(m'+1) then makes g^(N-1-m)); the
-  // reversed dK product's final state Z gives dS0 = g Z^T
+  // Initial states of the products (per head g): S0^T for dq, dS^T / g for
+  // the reversed dk product (its g^(m'+1) then makes g^(N-1-m)); the reversed
+  // dv product's is dS / g, the transpose, and so are all its states: the dk
+  // product's state workgroups write its snapshots too. In the same way the
+  // dq product's states are the recomputed forward's transposed (with a gate,
+  // which recomputes it). The dk product's final state Z gives dS0 = g Z^T.
   float ones[ret::kMaxHeadsHost], inv[ret::kMaxHeadsHost], gam[ret::kMaxHeadsHost];
   for (int h = 0; h < desc->heads; ++h) {
     ones[h] = 1.f;
     inv[h] = (float)(1.0 / head_gamma(desc, h));
     gam[h] = (float)head_gamma(desc, h);
   }
-  float *s0t = nullptr, *xs = nullptr, *ys = nullptr, *zs = nullptr;
+  float *s0t = nullptr, *xs = nullptr, *zs = nullptr;
   if (state_in) {
-    s0t = state_slot(0);
-    zs = state_slot(3);
-    if (ret::launch_state_map(s, state_in, s0t, true, ones, stream) != hipSuccess) return RET_ERR_HIP;
+    zs = state_slot(2);
+    if (!g) {
+      s0t = state_slot(0);
+      if (ret::launch_state_map(s, state_in, s0t, true, ones, stream) != hipSuccess) return RET_ERR_HIP;
+    }
   }
   if (d_state_out) {
     xs = state_slot(1);
-    ys = state_slot(2);
-    if (ret::launch_state_map(s, d_state_out, xs, true, inv, stream) != hipSuccess ||
-        ret::launch_state_map(s, d_state_out, ys, false, inv, stream) != hipSuccess)
-      return RET_ERR_HIP;
+    if (ret::launch_state_map(s, d_state_out, xs, true, inv, stream) != hipSuccess) return RET_ERR_HIP;
   }
   // q', k' and the reversed q'
   const float2* table = nullptr;
@@ -367,13 +369,15 @@ ret_status_t chunkwise_bwd_impl(const ret_desc_t* desc, int32_t chunk, const voi
   void* dorev = nullptr;
   if (g) {
     // the recomputed forward forms dg and dO (stored reversed) in its
-    // epilogue, from the gate, dout and its output in registers; it clears
-    // the error word, the products' launch keeps it
+    // epilogue, from the gate, dout and its output in registers, and writes
+    // the dq product's snapshots beside its own (in the third product's
+    // area, which that launch then refills); it clears the error word, the
+    // products' launch keeps it
     dorev = slot();
     first = false;
-    if (ret::launch_retention_fwd(s, c, true, qr, kr, v, g, dorev, state_in, nullptr, snap, chain, ctrl, nullptr,
-                                  desc->gn_eps, stream, nullptr, nullptr, false, true, nullptr, nullptr, 0, nullptr,
-                                  false, dout, dg) != hipSuccess)
+    if (ret::launch_retention_fwd(s, c, true, qr, kr, v, g, dorev, state_in, nullptr, snap_of(2), chain, ctrl,
+                                  nullptr, desc->gn_eps, stream, nullptr, nullptr, false, true, nullptr, nullptr, 0,
+                                  nullptr, false, dout, dg, snap) != hipSuccess)
       return RET_ERR_HIP;
     dov = nullptr;  // the dq product reads the reversed copy back in order
   }
@@ -385,12 +389,21 @@ ret_status_t chunkwise_bwd_impl(const ret_desc_t* desc, int32_t chunk, const voi
   // the parallel backward's three products, each run as the chunkwise form
   // (the same function), storing straight into the caller's tensors, in one
   // launch
-  const ret::ChunkProduct prods[kBwdProducts] = {
+  ret::ChunkProduct prods[kBwdProducts] = {
       {dov ? dov : dorev, v, kr, dq, s0t, nullptr, snap_of(0), chain_of(0), dov == nullptr, false, table, false,
        false},
       {v, do_rev, qr_rev, dk, xs, zs, snap_of(1), chain_of(1), true, true, table, rdo, rq},
-      {kr, qr_rev, do_rev, dv, ys, nullptr, snap_of(2), chain_of(2), true, true, nullptr, rq, rdo},
+      {kr, qr_rev, do_rev, dv, nullptr, nullptr, snap_of(2), nullptr, true, true, nullptr, rq, rdo},
   };
+  if (g) {  // the dq product's snapshots are the recompute's
+    prods[0].state_wgs = false;
+    prods[0].snap_ready = true;
+    prods[0].cross0 = state_in != nullptr;
+    prods[0].chain = nullptr;
+  }
+  prods[1].xprod = 2;  // the dk product's state workgroups write the dv product's snapshots
+  prods[2].state_wgs = false;
+  prods[2].cross0 = d_state_out != nullptr;
   const bool keep = !first;  // a recomputed forward before them cleared the error word
   if (ret::launch_chunkwise_products(s, c, kBwdProducts, prods, ctrl, (int64_t)(cb / sizeof(int)), desc->gn_eps,
                                      stream, keep) != hipSuccess)

@@ -54,14 +54,17 @@ size_t chunkwise_sched_bytes(const Shape& s, int chunk);
 // q_rev or out_rot): the backward's recomputed forward, which
 // stores dg (the gate's gradient) and, in o at reversed positions, dO (the
 // gradient reaching the retention output through the gate and GroupNorm)
-// instead of the forward's output.
+// instead of the forward's output. xsnap (chunkwise, with gb_dout; may be
+// null): per-chunk states of the same layout as snap that also receive the
+// transpose of each R_{i-1}, the snapshots of a later product whose state
+// is that transpose (the dq gradient product's).
 hipError_t launch_retention_fwd(const Shape& s, int chunk, bool chunked, const void* q, const void* k, const void* v,
                                 const void* g, void* o, const float* state_in, float* state_out, void* snap,
                                 float* chain, int* ctrl, const float2* rot, float eps, hipStream_t stream,
                                 hipEvent_t before = nullptr, hipEvent_t after = nullptr, bool q_rev = false,
                                 bool out_rev = false, const float2* out_rot = nullptr, const int* cu = nullptr,
                                 int total = 0, void* sched = nullptr, bool keep_err = false,
-                                const void* gb_dout = nullptr, void* gb_dg = nullptr);
+                                const void* gb_dout = nullptr, void* gb_dg = nullptr, void* xsnap = nullptr);
 
 // Up to three parallel-form products of shape s with no state in one grid
 // (q_rev, out_rev, out_rot as above; no rotation of q on load): the
@@ -83,6 +86,12 @@ hipError_t launch_parallel_products(const Shape& s, int n, const ParallelProduct
 // and control block, the blocks ctrl_stride ints apart from `ctrl` on (each
 // at least chunkwise_ctrl_bytes() / 4 ints); the first block's error word
 // reports every product's errors. keep_err as for launch_retention_fwd.
+// A product whose state is the transpose of an earlier one's needs no state
+// workgroups of its own (state_wgs false): either the earlier product of the
+// launch names it as xprod, and its state workgroups write this product's
+// snapshots too and raise its flags, or an earlier launch wrote them all
+// (snap_ready). Such a product has no chain and no state_out; cross0 says
+// whether its chunk 0 has a previous state (a snapshot of R_{-1}).
 struct ChunkProduct {
   const void* q;
   const void* k;
@@ -95,6 +104,10 @@ struct ChunkProduct {
   bool q_rev, out_rev;
   const float2* out_rot;
   bool k_rev, v_rev;  // read k / v with each sequence's token order reversed
+  bool state_wgs = true;
+  bool snap_ready = false;
+  bool cross0 = false;
+  int xprod = -1;
 };
 hipError_t launch_chunkwise_products(const Shape& s, int chunk, int n, const ChunkProduct* products, int* ctrl,
                                      int64_t ctrl_stride, float eps, hipStream_t stream, bool keep_err);

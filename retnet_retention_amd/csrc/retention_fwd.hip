@@ -175,6 +175,17 @@ struct FwdParams {
   // reversed: the reversed copies that two gradient products take as keys
   // or values, read from the forward-order tensor instead of copied
   int k_rev, v_rev;
+  // (the chunkwise multi-product kernel) state workgroups per chunk of this
+  // product: the state role's split, or 0 for a product whose snapshots
+  // another product's state workgroups write (raising this product's flags),
+  // or an earlier launch wrote (snap_ready: nothing to wait for)
+  int sroles, snap_ready;
+  // (instantiations with the partner snapshot) the snapshots of a partner
+  // product whose state is the transpose of this one, written by this
+  // product's state workgroups beside their own (null: none), and the ints
+  // from ctrl to the partner's ready flags (-1: raise none)
+  void* xsnap;
+  int xfbase;
   // packed sequences of different lengths (chunkwise form only): sequence b
   // holds rows cu[b] .. cu[b+1]-1 of `total`, seqlen bounds every length;
   // null: batch sequences of seqlen tokens each
@@ -355,7 +366,7 @@ __device__ __forceinline__ void out_role(const FwdParams& p, int bh, int ci, int
   // R^T slice s ([dv][RS dk columns]) into an LDS stage; waits (once) for
   // the snapshot of R_{i-1} to be published
   auto issue_slice = [&](int sl, char* buf) __attribute__((always_inline)) {
-    if (sl == 0) {
+    if (sl == 0 && !(XF && p.snap_ready)) {
       const int* flags = p.ctrl + p.fbase + kCtrlHead + (bh * (p.nchunks + 1) + ci) * kFlagsPerChunk + kMaxSplit;
 #pragma unroll
       for (int q = 0; q < SPL; ++q) wait_flag(flags + q, p.ctrl + 1);
@@ -791,7 +802,12 @@ __device__ __forceinline__ void scale_frag(f32x8& f, const float* z, const bool*
 // and then publishes its snapshot R_i^T for the next chunk's output
 // workgroups. Wave (wr, wc) owns row tiles wr MTW .. +MTW-1 and dv tiles
 // wc NTW .. +NTW-1.
-template <typename T, int D, bool KVR = false, int SPL = StTile<T, D>::SPLIT>
+// XS: the instantiations that may also write a partner product's snapshots
+// (p.xsnap), the backward's: the state of the dv gradient product is the
+// transpose of the dk product's, and that of the dq product the transpose
+// of the recomputed forward's (same decays, same chunks, transposed initial
+// states), so one state workgroup serves both.
+template <typename T, int D, bool KVR = false, int SPL = StTile<T, D>::SPLIT, bool XS = false>
 __device__ __forceinline__ void state_role(const FwdParams& p, int bh, int ci, int part, char* l0, char* l1,
                                            char* l2, char* l3) {
   using SC = StTile<T, D, SPL>;
@@ -852,6 +868,60 @@ __device__ __forceinline__ void state_role(const FwdParams& p, int bh, int ci, i
                           f32x4{acc[mt][nt][4 * a], acc[mt][nt][4 * a + 1], acc[mt][nt][4 * a + 2], acc[mt][nt][4 * a + 3]});
         }
   };
+  // The partner's snapshot (XS, p.xsnap set). Its state R' is R^T, so the
+  // snapshot it reads, R'^T in the fragment order above, is R itself: the 8
+  // elements of the fragment slot of lane (n, h) at step S, tile t are
+  // R[32 t + n][16 S + 8 h .. +7], 8 consecutive dv of one dk row. The
+  // workgroup's rows of R pass through LDS as T, row-major, each row padded
+  // by 16 bytes (the 16-byte reads of one instruction, 32 rows, then hit
+  // distinct banks), 32-row tiles TPA to an array; each lane then reads and
+  // stores whole slots, a wave 1 KiB of contiguous snapshot per store.
+  constexpr int XROWB = D * (int)sizeof(T) + 16;
+  constexpr int XTILEB = 32 * XROWB;
+  constexpr int XTPA = Stage<T, D>::BYTES / XTILEB;
+  static_assert(!XS || SC::MTA <= 4 * XTPA, "the workgroup's rows of R fit the four arrays");
+  auto xs_tile = [&](int tl) __attribute__((always_inline)) {
+    const int ai = tl / XTPA;  // uniform
+    char* a = ai == 0 ? l0 : ai == 1 ? l1 : ai == 2 ? l2 : l3;
+    return a + (tl % XTPA) * XTILEB;
+  };
+  auto xs_stage = [&](const f32x16 (&acc)[SC::MTW][SC::NTW]) __attribute__((always_inline)) {
+    if (!active) return;
+#pragma unroll
+    for (int mt = 0; mt < SC::MTW; ++mt) {
+      char* tile = xs_tile(mt0 + mt);
+#pragma unroll
+      for (int nt = 0; nt < SC::NTW; ++nt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          *reinterpret_cast<T*>(tile + (8 * (i / 4) + 4 * hh + i % 4) * XROWB + (dvw + 32 * nt + n) * (int)sizeof(T)) =
+              (T)acc[mt][nt][i];
+    }
+  };
+  // after a barrier that follows xs_stage: the slots of this workgroup's rows
+  // (tiles t = dk0/32 + tl) into the partner snapshot sn
+  auto xs_store = [&](T* sn) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t rs = scalar_rsrc(sn);
+    constexpr int NS = D / 16;                 // steps S per tile
+    constexpr int EL = 16 / (int)sizeof(T);    // elements per 16 bytes
+#pragma unroll 2
+    for (int x = wave; x < SC::MTA * NS; x += SC::NW) {
+      const int tl = x / NS, S = x % NS;  // uniform
+      const int t = dk0 / 32 + tl;
+      const char* src = xs_tile(tl) + n * XROWB + (16 * S + 8 * hh) * (int)sizeof(T);
+      const int soff = (S / (OT::RS / 16)) * OT::RS * D + ((S % (OT::RS / 16)) * OT::NT + t) * 64 * 8;
+#pragma unroll
+      for (int c = 0; c < 8 / EL; ++c)
+        __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4*>(src + 16 * c), rs,
+                                               (uint32_t)(lane * 8 * (int)sizeof(T) + 16 * c),
+                                               (uint32_t)(soff * (int)sizeof(T)), kSc1);
+    }
+  };
+  auto xflag_of = [&](int j) __attribute__((always_inline)) {
+    return p.ctrl + p.xfbase + kCtrlHead + (bh * (p.nchunks + 1) + j) * kFlagsPerChunk + kMaxSplit + part;
+  };
+  const bool xs = XS && p.xsnap != nullptr;  // uniform
+
   // R_i accumulates from g^b R_{i-1}: for chunk 0 with an initial state that
   // term is added here (R_{-1} = state_in, also published for the output
   // workgroups of chunk 0); for later chunks after the keys, from the chain
@@ -867,6 +937,7 @@ __device__ __forceinline__ void state_role(const FwdParams& p, int bh, int ci, i
         for (int i = 0; i < 16; ++i)
           racc[mt][nt][i] = S0[(int64_t)(dk_of(mt, i / 4) + i % 4) * D + dvw + 32 * nt + n];
     write_snapshot(reinterpret_cast<T*>(p.snap) + (int64_t)bh * p.nchunks * D * D, racc);
+    if (xs) xs_stage(racc);
 #pragma unroll
     for (int mt = 0; mt < SC::MTW; ++mt)
 #pragma unroll
@@ -879,7 +950,17 @@ __device__ __forceinline__ void state_role(const FwdParams& p, int bh, int ci, i
 #pragma unroll
       for (int nt = 0; nt < SC::NTW; ++nt) racc[mt][nt] = zero16();
   }
-  if (ci == 0 && p.state_in) release_flag(flag_of(0, 1));
+  if (ci == 0 && p.state_in) {
+    if (xs) {
+      __syncthreads();  // the staged rows of R_{-1}
+      xs_store(reinterpret_cast<T*>(p.xsnap) + (int64_t)bh * p.nchunks * D * D);
+    }
+    // every wave's snapshot stores (and its LDS reads, before the key blocks
+    // refill the arrays) are done: both snapshots' flags
+    release_flag(flag_of(0, 1));
+    if (xs && p.xfbase >= 0 && threadIdx.x == 0)
+      __hip_atomic_store(xflag_of(0), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 
   TileLoads<T, typename SC::KT, SC::NW> kload;
   TileLoads<T, typename SC::VT, SC::NW> vload;
@@ -1062,7 +1143,12 @@ __device__ __forceinline__ void state_role(const FwdParams& p, int bh, int ci, i
     }
     release_flag(flag_of(ci + 1, 0));
     if (active) write_snapshot(snap_next, racc);
-    release_flag(flag_of(ci + 1, 1));
+    if (xs) xs_stage(racc);  // the key blocks' reads of the arrays ended before the release's barrier
+    release_flag(flag_of(ci + 1, 1));  // its barrier also covers the staged rows
+    if (xs) {
+      xs_store(reinterpret_cast<T*>(p.xsnap) + ((int64_t)bh * p.nchunks + ci + 1) * D * D);
+      if (p.xfbase >= 0) release_flag(xflag_of(ci + 1));
+    }
   } else if (p.state_out && active) {
     float* SO = p.state_out + (int64_t)bh * D * D;
 #pragma unroll
@@ -1210,7 +1296,7 @@ __global__ __launch_bounds__(kWaves<T> * 64, 1) void retention_chunkwise_kernel(
   const int qb = state_first ? (role < SPLIT ? -1 : p.qblocks - 1 - (role - SPLIT))
                              : (role == 0 ? p.qblocks - 1 : role <= SPLIT ? -1 : p.qblocks - 1 - (role - SPLIT));
   if (qb < 0)
-    state_role<T, D, KVR, SPL>(p, bh, ci, state_first ? role : role - 1, l0, l1, l2, l3);
+    state_role<T, D, KVR, SPL, GBW>(p, bh, ci, state_first ? role : role - 1, l0, l1, l2, l3);
   else if (ci > 0 || p.has_state0)
     out_role<T, D, FAST, true, XF, GBW, KVR, SPL>(p, bh, ci, qb, true, l0, l1, l2, l3);
   else
@@ -1220,11 +1306,13 @@ __global__ __launch_bounds__(kWaves<T> * 64, 1) void retention_chunkwise_kernel(
 
 // Several chunkwise products of one shape in one grid (the backward's three
 // gradient products): one ticket sequence for all of them, chunk-major with
-// the products interleaved inside each chunk, so every wait is still for an
-// earlier ticket of the same product, and the products' last chunks end
-// together instead of each launch ending on its own. Each product has its
-// own ready flags, chain and snapshots; the tickets, the count and the error
-// word are those of the first product's control block.
+// the products in order inside each chunk, so every wait is still for an
+// earlier ticket (of the same product, or of an earlier product that writes
+// this one's snapshots), and the products' last chunks end together instead
+// of each launch ending on its own. Each product has its own ready flags,
+// chain and snapshots; the tickets, the count and the error word are those
+// of the first product's control block. A product with sroles = 0 has no
+// state workgroups: its chunks hold only output blocks, longest first.
 template <typename T, int D, bool FAST, bool KVR>
 __global__ __launch_bounds__(kWaves<T> * 64, 1) void retention_chunkwise_multi_kernel(MultiParams mp) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -1237,7 +1325,6 @@ __global__ __launch_bounds__(kWaves<T> * 64, 1) void retention_chunkwise_multi_k
   const FwdParams& p0 = mp.p[0];
   const int nprod = mp.nprod;
   const int bhs = p0.batch * p0.heads;
-  const int roles = SPLIT + p0.qblocks;
   const int cls = p0.xcd_order ? (int)(blockIdx.x & 7) : 0;
   if (threadIdx.x == 0) {
     atomicAdd(p0.ctrl, 1);
@@ -1245,32 +1332,45 @@ __global__ __launch_bounds__(kWaves<T> * 64, 1) void retention_chunkwise_multi_k
   }
   __syncthreads();
   const int t = __builtin_amdgcn_readfirstlane(s_ticket);
-  int ci, bh, role, prod;
-  if (p0.xcd_order) {
-    const int nbl = bhs / 8, per = nbl * roles;
-    ci = t / (nprod * per);
-    const int r = t % (nprod * per);
-    prod = r / per;
-    role = (r % per) / nbl;
-    bh = ((r % per) % nbl) * 8 + cls;
-  } else {
-    const int per = bhs * roles;
-    ci = t / (nprod * per);
-    const int r = t % (nprod * per);
-    prod = r / per;
-    bh = (r % per) / roles;
-    role = (r % per) % roles;
+  // the pairs a ticket sequence serves, and each product's items per chunk
+  const int nbl = p0.xcd_order ? bhs / 8 : bhs;
+  int per[kMaxProducts], all = 0;
+#pragma unroll
+  for (int i = 0; i < kMaxProducts; ++i) {
+    per[i] = i < nprod ? nbl * (mp.p[i].sroles + p0.qblocks) : 0;
+    all += per[i];
   }
-  ci = uniform_i(ci);
+  const int ci = uniform_i(t / all);
+  int r = t % all, prod = 0;
+  if (r >= per[0]) {
+    r -= per[0];
+    prod = 1;
+    if (r >= per[1]) {
+      r -= per[1];
+      prod = 2;
+    }
+  }
+  prod = uniform_i(prod);
+  const FwdParams& p = mp.p[prod];
+  const int roles = p.sroles + p.qblocks;
+  int bh, role;
+  if (p0.xcd_order) {
+    role = r / nbl;
+    bh = (r % nbl) * 8 + cls;
+  } else {
+    bh = r / roles;
+    role = r % roles;
+  }
   bh = uniform_i(bh);
   role = uniform_i(role);
   constexpr bool XF = true, GBW = false;
-  const FwdParams& p = mp.p[uniform_i(prod)];
+  const int sr = p.sroles;
   const bool state_first = ci == 0 && p.has_state0;
-  const int qb = state_first ? (role < SPLIT ? -1 : p.qblocks - 1 - (role - SPLIT))
-                             : (role == 0 ? p.qblocks - 1 : role <= SPLIT ? -1 : p.qblocks - 1 - (role - SPLIT));
+  const int qb = sr == 0        ? p.qblocks - 1 - role
+                 : state_first ? (role < sr ? -1 : p.qblocks - 1 - (role - sr))
+                               : (role == 0 ? p.qblocks - 1 : role <= sr ? -1 : p.qblocks - 1 - (role - sr));
   if (qb < 0)
-    state_role<T, D, KVR>(p, bh, ci, state_first ? role : role - 1, l0, l1, l2, l3);
+    state_role<T, D, KVR, SPLIT, true>(p, bh, ci, state_first ? role : role - 1, l0, l1, l2, l3);
   else if (ci > 0 || p.has_state0)
     out_role<T, D, FAST, true, XF, GBW, KVR>(p, bh, ci, qb, true, l0, l1, l2, l3);
   else
@@ -1499,6 +1599,10 @@ static FwdParams make_params(const Shape& s, int chunk, const void* q, const voi
   p.gb_dg = nullptr;
   p.k_rev = 0;
   p.v_rev = 0;
+  p.sroles = 0;
+  p.snap_ready = 0;
+  p.xsnap = nullptr;
+  p.xfbase = -1;
   p.q = q;
   p.k = k;
   p.v = v;
@@ -1528,12 +1632,13 @@ hipError_t launch_retention_fwd(const Shape& s, int chunk, bool chunked, const v
                                 float* chain, int* ctrl, const float2* rot, float eps, hipStream_t stream,
                                 hipEvent_t before, hipEvent_t after, bool q_rev, bool out_rev,
                                 const float2* out_rot, const int* cu, int total, void* sched, bool keep_err,
-                                const void* gb_dout, void* gb_dg) {
+                                const void* gb_dout, void* gb_dg, void* xsnap) {
   if (rot && q_rev) return hipErrorInvalidValue;  // q's angles are those of its own positions
   // the recomputed forward of the backward: gate, dout and dg given, dO
-  // stored reversed, nothing else transformed, batch form
+  // stored reversed, nothing else transformed, batch form; the partner
+  // snapshots only there
   if ((gb_dout != nullptr) != (gb_dg != nullptr) ||
-      (gb_dout && (!g || !out_rev || q_rev || out_rot || cu)))
+      (gb_dout && (!g || !out_rev || q_rev || out_rot || cu)) || (xsnap && (!gb_dout || !chunked)))
     return hipErrorInvalidValue;
   // packed sequences: chunkwise form, forward only, with a schedule buffer
   if (cu && (!chunked || q_rev || out_rev || out_rot || !sched)) return hipErrorInvalidValue;
@@ -1541,6 +1646,7 @@ hipError_t launch_retention_fwd(const Shape& s, int chunk, bool chunked, const v
                             out_rot, cu, total, sched);
   p.gb_dout = gb_dout;
   p.gb_dg = gb_dg;
+  p.xsnap = xsnap;  // no flags: the later launch reads these snapshots as ready
   if (s.dtype == 1) {
     switch (s.d) {
       case 64: return launch_fwd_t<bf16, 64>(s, chunk, p, chunked, stream, before, after, keep_err);
@@ -1596,14 +1702,18 @@ static hipError_t launch_cmulti_impl(const Shape& s, int chunk, MultiParams& mp,
   hipLaunchKernelGGL(reset_ctrl_kernel, dim3((unsigned)((all + 255) / 256 < 1024 ? (all + 255) / 256 : 1024)),
                      dim3(256), 0, stream, ctrl0, (int)all, keep_err ? 1 : 0);
   const int qblocks = (chunk + C::BM - 1) / C::BM;
+  int64_t roles = 0;  // workgroups per (sequence, head, chunk) over the products
   for (int i = 0; i < mp.nprod; ++i) {
     mp.p[i].qblocks = qblocks;
     mp.p[i].xcd_order = bhs % 8 == 0;
     mp.p[i].ctrl = ctrl0;
     mp.p[i].fbase = (int)(stride * i);
+    // sroles arrives as 1 (state workgroups) or 0, xfbase as the partner's index
+    mp.p[i].sroles = mp.p[i].sroles ? StTile<T, D>::SPLIT : 0;
+    if (mp.p[i].xfbase >= 0) mp.p[i].xfbase = (int)(stride * mp.p[i].xfbase);
+    roles += mp.p[i].sroles + qblocks;
   }
-  const int roles = StTile<T, D>::SPLIT + qblocks;
-  const int64_t blocks = (int64_t)mp.nprod * nchunks * bhs * roles;
+  const int64_t blocks = (int64_t)nchunks * bhs * roles;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   if (blocks == 0) return hipGetLastError();
   bool kvr = false;
@@ -1629,6 +1739,21 @@ static hipError_t launch_cmulti_t(const Shape& s, int chunk, MultiParams& mp, in
 hipError_t launch_chunkwise_products(const Shape& s, int chunk, int n, const ChunkProduct* pr, int* ctrl,
                                      int64_t ctrl_stride, float eps, hipStream_t stream, bool keep_err) {
   if (n < 1 || n > kMaxProducts || chunk < 1 || !ctrl) return hipErrorInvalidValue;
+  // Products without state workgroups: snapshots from an earlier launch, or
+  // from exactly one earlier product of this one (every wait then stays on
+  // an earlier ticket); no chain, no final state.
+  int writer[kMaxProducts] = {-1, -1, -1};
+  for (int i = 0; i < n; ++i) {
+    const int x = pr[i].xprod;
+    if (x < 0) continue;
+    if (x <= i || x >= n || !pr[i].state_wgs || pr[x].state_wgs || pr[x].snap_ready || writer[x] >= 0)
+      return hipErrorInvalidValue;
+    writer[x] = i;
+  }
+  for (int i = 0; i < n; ++i)
+    if (pr[i].state_wgs ? pr[i].snap_ready
+                        : pr[i].state_out || pr[i].state_in || pr[i].snap_ready == (writer[i] >= 0))
+      return hipErrorInvalidValue;
   MultiParams mp;
   mp.nprod = n;
   for (int i = 0; i < kMaxProducts; ++i) {
@@ -1637,6 +1762,11 @@ hipError_t launch_chunkwise_products(const Shape& s, int chunk, int n, const Chu
                           nullptr, eps, x.q_rev, x.out_rev, x.out_rot, nullptr, 0, nullptr);
     mp.p[i].k_rev = x.k_rev;
     mp.p[i].v_rev = x.v_rev;
+    mp.p[i].has_state0 = x.state_in != nullptr || x.cross0;
+    mp.p[i].sroles = x.state_wgs ? 1 : 0;  // the state split is set per instantiation
+    mp.p[i].snap_ready = x.snap_ready;
+    mp.p[i].xsnap = x.xprod >= 0 ? pr[x.xprod].snap : nullptr;
+    mp.p[i].xfbase = x.xprod;  // the partner's index until its flags' offset is known
   }
   if (s.dtype == 1) {
     switch (s.d) {

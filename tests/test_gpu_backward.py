@@ -134,6 +134,10 @@ STATE_CASES = [
     (1, 130, 3, 128, 512, "bf16", False, False, True, False),
     (1, 200, 2, 64, 7, "bf16", True, False, False, True),
     (1, 150, 2, 128, 64, "f32", True, True, True, True),
+    # two state workgroups per chunk (fp32, d = 256), each writing its rows
+    # of the partner product's snapshots
+    (1, 100, 2, 256, 32, "f32", True, False, True, True),
+    (1, 200, 2, 64, 64, "bf16", False, True, False, True),
 ]
 
 
