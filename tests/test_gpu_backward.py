@@ -172,3 +172,30 @@ def test_chunkwise_backward_with_state(b, n, h, d, chunk, dtype, gate, rot, s_in
             assert got[i] is None
             continue
         assert_close(to64(got[i]), r, dtype, name)
+
+
+def test_chunkwise_backward_repeatable_on_one_workspace():
+    """Calls on one workspace return bit-identical gradients, with and without
+    a carried state, whatever the workspace held before (it is filled with
+    random bytes between calls): each call clears its control blocks, and the
+    snapshots one product's state workgroups write for another are complete
+    before that product reads them."""
+    import torch
+
+    b, n, h, d, chunk = 2, 2048, 8, 256, 256
+    _announce(form="chunkwise backward, repeated on one workspace", b=b, n=n, h=h, d=d, chunk=chunk)
+    ts = draw(501, [((b, n, h, d), 1 / 16)] * 3 + [((b, n, h, d), 1 / 8), ((b, n, h, d), 1 / 16)], "bf16")
+    q, k, v, dout, g = (t.torch(DEV) for t in ts)
+    rng = np.random.default_rng(17)
+    s0 = torch.from_numpy((rng.standard_normal((b, h, d, d)) * 0.05).astype(np.float32)).to(DEV)
+    dso = torch.from_numpy((rng.standard_normal((b, h, d, d)) * 0.05).astype(np.float32)).to(DEV)
+    ws = torch.empty(256 << 20, dtype=torch.uint8, device=DEV)
+    for kw in ({}, {"state_in": s0, "d_state_out": dso}):
+        runs = []
+        for _ in range(3):
+            ws.random_(0, 256)
+            runs.append([x.clone() for x in rr.chunkwise_bwd(q, k, v, dout, g, chunk=chunk, workspace=ws, check=True,
+                                                             **kw)])
+        for other in runs[1:]:
+            for x, y in zip(runs[0], other):
+                assert torch.equal(x, y)
