@@ -25,8 +25,10 @@ double head_gamma(const ret_desc_t* d, int h) { return d->gamma ? d->gamma[h] : 
 ret_status_t check_desc(const ret_desc_t* d) {
   if (!d) return RET_ERR_NULL;
   if (d->batch < 1 || d->seqlen < 1 || d->heads < 1 || d->heads > ret::kMaxHeadsHost) return RET_ERR_SHAPE;
-  // every launch grid is bounded by batch * heads * seqlen workgroups
-  if ((int64_t)d->batch * d->heads * d->seqlen > INT32_MAX) return RET_ERR_SHAPE;
+  // every launch grid is bounded by batch * heads * seqlen workgroups; the
+  // product is formed in two steps so that it cannot overflow int64 itself
+  const int64_t bh = (int64_t)d->batch * d->heads;
+  if (bh > INT32_MAX || bh * d->seqlen > INT32_MAX) return RET_ERR_SHAPE;
   // kernels address within one sequence with 32-bit element offsets
   if ((int64_t)d->seqlen * d->heads * (d->dk > d->dv ? d->dk : d->dv) >= INT32_MAX) return RET_ERR_SHAPE;
   if (d->dtype != RET_F32 && d->dtype != RET_BF16) return RET_ERR_UNSUPPORTED;
@@ -419,7 +421,12 @@ extern "C" {
 int32_t retention_abi_version(void) { return 1; }
 
 const char* retention_status_string(ret_status_t s) {
-  switch (s) {
+  // a C caller may pass any int: read it as one (a C++ load of an enum
+  // outside its enumerators' range is undefined)
+  static_assert(sizeof(ret_status_t) == sizeof(int32_t), "ret_status_t is a 32-bit int in the C ABI");
+  int32_t code;
+  std::memcpy(&code, &s, sizeof(code));
+  switch (code) {
     case RET_OK: return "ok";
     case RET_ERR_NULL: return "a required pointer is NULL";
     case RET_ERR_SHAPE: return "batch, seqlen, heads or chunk out of range";

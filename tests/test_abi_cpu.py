@@ -95,6 +95,9 @@ def test_workspace_sizes(L):
     (dict(gammas=[0.9, 0.0, 0.5, 0.5]), 4), (dict(gammas=[0.9, 1.5, 0.5, 0.5]), 4),
     (dict(gammas=[0.9, float("nan"), 0.5, 0.5]), 4), (dict(rotary_base=-1.0), 9),
     (dict(rotary_base=float("inf")), 9),
+    # batch * heads * seqlen past int64 in one product: rejected, not wrapped
+    (dict(batch=2**31 - 1, seqlen=2**31 - 1, heads=16), 2),
+    (dict(batch=2**31 - 1, heads=128), 2),
 ])
 def test_descriptor_validation(L, kw, status):
     d, _ = _desc(**kw)
