@@ -445,8 +445,15 @@ __device__ __forceinline__ void out_role(const FwdParams& p, int bh, int ci, int
       constexpr int t = decltype(t_c)::value, kh = t / U, u = t % U;
       if constexpr (t + 2 < C::KH * U) ring[(t + 2) % 3] = load(std::integral_constant<int, t + 2>{});
       if constexpr (u < C::KS) {
+        // The score products run at raised wave priority, the decay below at
+        // the normal one: after each block's barrier the two waves of a SIMD
+        // start in step, and this lets one wave's products issue while the
+        // other does its decay's vector work (measured: 3B parallel -1.1 to
+        // -1.4%, 7B/8k chunkwise -0.5%).
+        if constexpr (u == 0) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int r = 0; r < QT; ++r) st[r] = mma32(ring[t % 3], qf[r][u], u == 0 ? zero16() : st[r]);
+        if constexpr (u == C::KS - 1) __builtin_amdgcn_s_setprio(0);
         if constexpr (u == C::KS - 1) {
           // decay g^(q-k) and causal mask; element i is key kb0 + 32 kh + k_i
           const int kk0 = kb0 + 32 * kh;
@@ -461,11 +468,12 @@ __device__ __forceinline__ void out_role(const FwdParams& p, int bh, int ci, int
                 st[r][i] *= (i / 4 == 0 ? sb : sb * g8[i / 4]);
               }
               if (diag) {
+                // key kk0 + 4 hh + o_i follows the row when o_i > dq: one
+                // compare with a constant per score
+                const int dq = qrow - kk0 - 4 * hh;
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                  const int key = kk0 + 8 * (i / 4) + 4 * hh + (i % 4);
-                  if (qrow < key) st[r][i] = 0.f;
-                }
+                for (int i = 0; i < 16; ++i)
+                  if (8 * (i / 4) + (i % 4) > dq) st[r][i] = 0.f;
               }
             } else {
 #pragma unroll
