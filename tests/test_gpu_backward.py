@@ -174,6 +174,42 @@ def test_chunkwise_backward_with_state(b, n, h, d, chunk, dtype, gate, rot, s_in
         assert_close(to64(got[i]), r, dtype, name)
 
 
+GENERIC_GAMMAS = [1.0, 0.25, 2.0 ** -40, 0.999]
+
+
+@pytest.mark.parametrize("chunk,s_in", [(512, True), (64, False)])
+def test_chunkwise_backward_generic_decays(chunk, s_in):
+    """Decays 0.25 and 2^-40 give |log2 g| x chunk > 64, so the three gradient
+    products and the recomputed forward run the generic instantiations (an
+    exact decay factor per score and the rescaled cross term), with the gate,
+    a carried state and the state-out gradient; checked head by head against
+    the fp64 oracle."""
+    import torch
+
+    b, n, h, d = 1, 700, 4, 256
+    _announce(form="chunkwise backward, generic decays", chunk=chunk, state_in=s_in, gammas=GENERIC_GAMMAS)
+    ts = draw(907 + chunk, [((b, n, h, d), 1 / 16)] * 3 + [((b, n, h, d), 1 / 8), ((b, n, h, d), 1 / 16)], "bf16")
+    q, k, v, dout, g = ts
+    rng = np.random.default_rng(31 + chunk)
+    s0 = (rng.standard_normal((b, h, d, d)) * 0.05).astype(np.float32) if s_in else None
+    dso = (rng.standard_normal((b, h, d, d)) * 0.05).astype(np.float32)
+    t = lambda a: None if a is None else torch.from_numpy(a).to(DEV)
+    got = rr.chunkwise_bwd(q.torch(DEV), k.torch(DEV), v.torch(DEV), dout.torch(DEV), g.torch(DEV), chunk=chunk,
+                           state_in=t(s0), d_state_out=t(dso), gammas=GENERIC_GAMMAS, check=True)
+    ref = oracle.chunkwise_state_grad(q.f64, k.f64, v.f64, dout.f64, g=g.f64,
+                                      state_in=None if s0 is None else s0.astype(np.float64),
+                                      d_state_out=dso.astype(np.float64), gammas=GENERIC_GAMMAS)
+    for name, x, r in zip(("dq", "dk", "dv", "dg", "d_state_in"), got, ref):
+        if r is None:
+            assert x is None
+            continue
+        x = to64(x)
+        assert_close(x, r, "bf16", name)
+        if x.ndim == 4 and name != "d_state_in":
+            for hd in range(h):
+                assert_close(x[:, :, hd:hd + 1], r[:, :, hd:hd + 1], "bf16", f"{name} head {hd}")
+
+
 def test_chunkwise_backward_repeatable_on_one_workspace():
     """Calls on one workspace return bit-identical gradients, with and without
     a carried state, whatever the workspace held before (it is filled with
