@@ -118,13 +118,15 @@ bool rotate_inputs(const ret_desc_t* d, const void*& k, const float2** table, vo
   char* ws = static_cast<char*>(workspace);
   float2* tab = reinterpret_cast<float2*>(ws);
   char* kr = ws + align_up((size_t)d->seqlen * (d->dk / 2) * sizeof(float2));
-  if (ret::launch_rotary_table(tab, d->seqlen, d->dk, d->rotary_base, d->pos_offset, stream) != hipSuccess)
+  if (cu) {
+    if (ret::launch_rotary_table(tab, d->seqlen, d->dk, d->rotary_base, d->pos_offset, stream) != hipSuccess ||
+        ret::launch_rotate_keys_packed(k, kr, tab, cu, d->batch, total, d->seqlen, d->heads, d->dk, d->dtype,
+                                       stream) != hipSuccess)
+      return false;
+  } else if (ret::launch_rotate_keys_table(k, kr, tab, d->batch, d->seqlen, d->heads, d->dk, d->dtype,
+                                           d->rotary_base, d->pos_offset, stream) != hipSuccess) {
     return false;
-  const hipError_t e =
-      cu ? ret::launch_rotate_keys_packed(k, kr, tab, cu, d->batch, total, d->seqlen, d->heads, d->dk, d->dtype,
-                                          stream)
-         : ret::launch_rotate_keys(k, kr, tab, d->batch, d->seqlen, d->heads, d->dk, d->dtype, stream);
-  if (e != hipSuccess) return false;
+  }
   k = kr;
   *table = tab;
   return true;
@@ -353,10 +355,8 @@ ret_status_t chunkwise_bwd_impl(const ret_desc_t* desc, int32_t chunk, const voi
     void* qs = slot();
     void* ks = slot();
     qrev = slot();
-    if (ret::launch_rotary_table(tab, desc->seqlen, desc->dk, desc->rotary_base, desc->pos_offset, stream) !=
-            hipSuccess ||
-        ret::launch_rotate_keys(q, qs, tab, desc->batch, desc->seqlen, desc->heads, desc->dk, desc->dtype, stream,
-                                qrev) != hipSuccess ||
+    if (ret::launch_rotate_keys_table(q, qs, tab, desc->batch, desc->seqlen, desc->heads, desc->dk, desc->dtype,
+                                      desc->rotary_base, desc->pos_offset, stream, qrev) != hipSuccess ||
         ret::launch_rotate_keys(k, ks, tab, desc->batch, desc->seqlen, desc->heads, desc->dk, desc->dtype,
                                 stream) != hipSuccess)
       return RET_ERR_HIP;
@@ -522,10 +522,8 @@ ret_status_t retention_parallel_bwd(const ret_desc_t* desc, const void* q, const
     void* qs = slot();
     void* ks = slot();
     qrev = slot();
-    if (ret::launch_rotary_table(tab, desc->seqlen, desc->dk, desc->rotary_base, desc->pos_offset, stream) !=
-            hipSuccess ||
-        ret::launch_rotate_keys(q, qs, tab, desc->batch, desc->seqlen, desc->heads, desc->dk, desc->dtype, stream,
-                                qrev) != hipSuccess ||
+    if (ret::launch_rotate_keys_table(q, qs, tab, desc->batch, desc->seqlen, desc->heads, desc->dk, desc->dtype,
+                                      desc->rotary_base, desc->pos_offset, stream, qrev) != hipSuccess ||
         ret::launch_rotate_keys(k, ks, tab, desc->batch, desc->seqlen, desc->heads, desc->dk, desc->dtype,
                                 stream) != hipSuccess)
       return RET_ERR_HIP;

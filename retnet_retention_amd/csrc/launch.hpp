@@ -30,6 +30,10 @@ hipError_t launch_rotate_keys(const void* k, void* kr, const float2* table, int 
 // The same rotation for packed sequences: sequence b holds rows cu[b] ..
 // cu[b+1]-1 of `total` (clamped as the chunkwise kernel clamps them), token n
 // of a sequence turns by the table's row n; at most maxlen tokens each.
+// the table and the rotation of k (and its reversed copy) in one launch
+hipError_t launch_rotate_keys_table(const void* k, void* kr, float2* table, int batch, int seqlen, int heads, int d,
+                                    int dtype, double base, int64_t pos_offset, hipStream_t stream,
+                                    void* krev = nullptr);
 hipError_t launch_rotate_keys_packed(const void* k, void* kr, const float2* table, const int* cu, int batch,
                                      int total, int maxlen, int heads, int d, int dtype, hipStream_t stream);
 

@@ -1,6 +1,6 @@
 // Position rotation of queries and keys, the xPos-like encoding of
 // "Retentive Network: A Successor to Transformer..." (Elamur summary,
-// Summary). Two passes:
+// Summary). Two passes, or both in one launch (rotate_keys_table_kernel):
 //   * a table [n][j] = (cos, sin) of (pos_offset + n) * base^(-2j/d), the
 //     angle formed and reduced in fp64 and rounded to fp32 once, so a
 //     position of several thousand radians keeps full fp32 accuracy;
@@ -64,6 +64,64 @@ __global__ __launch_bounds__(256) void rotate_keys_kernel(const T* __restrict__ 
     const int h = (int)(vec % heads);
     store8(krev + ((b * seqlen + (seqlen - 1 - n)) * heads + h) * d + c8 * 8, y);
   }
+}
+
+// The table and the pass above in one launch: each block takes
+// kFusedPositions consecutive positions, forms their table rows first (the
+// same fp64 formula as rotary_table_kernel, so the same bits), writes them
+// for the retention kernels' query rotation and keeps them in LDS, then turns
+// every (sequence, head) row at those positions. A position's rows of one
+// sequence are contiguous (heads x d elements), so consecutive threads take
+// consecutive 16-byte chunks.
+constexpr int kFusedPositions = 2;
+template <typename T>
+__global__ __launch_bounds__(256) void rotate_keys_table_kernel(const T* __restrict__ k, T* __restrict__ kr,
+                                                                 T* __restrict__ krev, float2* __restrict__ table,
+                                                                 int batch, int seqlen, int heads, int d,
+                                                                 double base, int64_t pos_offset) {
+  __shared__ __attribute__((aligned(16))) float2 cs[kFusedPositions][128];
+  const int n0 = (int)blockIdx.x * kFusedPositions;
+  const int half = d / 2;
+  for (int i = threadIdx.x; i < kFusedPositions * half; i += 256) {
+    const int p = i / half, j = i % half, n = n0 + p;
+    if (n >= seqlen) continue;
+    const double theta = pow(base, -2.0 * j / d);
+    const double phi = (double)(pos_offset + n) * theta;
+    double sn, c;
+    sincos(phi, &sn, &c);
+    const float2 v = make_float2((float)c, (float)sn);
+    cs[p][j] = v;
+    table[(int64_t)n * half + j] = v;
+  }
+  __syncthreads();
+  const int cpr = d / 8;  // chunks per head vector
+  const int per_seq = heads * cpr;
+  const int per_pos = batch * per_seq;
+  for (int i = threadIdx.x; i < kFusedPositions * per_pos; i += 256) {
+    const int p = i / per_pos, r = i % per_pos, n = n0 + p;
+    if (n >= seqlen) continue;
+    const int b = r / per_seq, hc = r % per_seq, c8 = hc % cpr;
+    const int64_t row = (int64_t)b * seqlen + n;
+    const int64_t off = row * heads * d + (int64_t)hc * 8;
+    const CS4 t = ld_cs4(&cs[p][4 * c8]);
+    F8 y = unpack8(ld_raw8(k + off));
+    rotate4(y, t);
+    if (kr) store8(kr + off, y);
+    if (krev) store8(krev + ((int64_t)b * seqlen + (seqlen - 1 - n)) * heads * d + (int64_t)hc * 8, y);
+  }
+}
+
+hipError_t launch_rotate_keys_table(const void* k, void* kr, float2* table, int batch, int seqlen, int heads, int d,
+                                    int dtype, double base, int64_t pos_offset, hipStream_t stream, void* krev) {
+  if (d / 2 > 128) return hipErrorInvalidValue;
+  const unsigned blocks = (unsigned)((seqlen + kFusedPositions - 1) / kFusedPositions);
+  if (dtype == 1)
+    hipLaunchKernelGGL(rotate_keys_table_kernel<bf16>, dim3(blocks), dim3(256), 0, stream, (const bf16*)k,
+                       (bf16*)kr, (bf16*)krev, table, batch, seqlen, heads, d, base, pos_offset);
+  else
+    hipLaunchKernelGGL(rotate_keys_table_kernel<float>, dim3(blocks), dim3(256), 0, stream, (const float*)k,
+                       (float*)kr, (float*)krev, table, batch, seqlen, heads, d, base, pos_offset);
+  return hipGetLastError();
 }
 
 // Packed sequences: blocks of one sequence each (per_seq blocks per

@@ -15,6 +15,10 @@ hipError_t launch_rotary_table(float2*, int, int, double, int64_t, hipStream_t) 
 hipError_t launch_rotate_keys(const void*, void*, const float2*, int, int, int, int, int, hipStream_t, void*) {
   reached("rotate_keys");
 }
+hipError_t launch_rotate_keys_table(const void*, void*, float2*, int, int, int, int, int, double, int64_t, hipStream_t,
+                                    void*) {
+  reached("rotate_keys_table");
+}
 hipError_t launch_rotate_keys_packed(const void*, void*, const float2*, const int*, int, int, int, int, int, int,
                                      hipStream_t) {
   reached("rotate_keys_packed");
