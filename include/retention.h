@@ -187,7 +187,7 @@ ret_status_t retention_recurrent_step(const ret_desc_t *desc, const void *q, con
 
 /* The same step with one rotation position per sequence, for serving a
  * batch whose sequences sit at different lengths ("Key points", first item:
- * decoding latency barely changes with batch size or input length; "Summary":
+ * decode latency stays nearly flat as the batch or the input grows; "Summary":
  * the positions are encoded like xPos, i.e. by each token's own position):
  * `positions` is a
  * DEVICE array of `batch` int64 positions, 8-byte aligned, each in
