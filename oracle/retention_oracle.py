@@ -67,8 +67,8 @@ def default_gammas(heads):
 
 
 def rotate(x, rotary_base, pos_offset=0):
-    """Position rotation of queries and keys, [SUM] Summary ("positions are
-    encoded in a manner similar to xPos").
+    """Position rotation of queries and keys, [SUM] Summary (the pages say the
+    position encoding follows xPos, without a formula).
 
     Reading taken (the pages give no formula): the rotary scheme of the RoFormer
     reference that xPos builds on. Adjacent pairs (x_{2j}, x_{2j+1}) turn by the
@@ -143,8 +143,8 @@ def recurrent(q, k, v, gammas, state_in=None):
 
 
 def chunkwise(q, k, v, gammas, chunk, state_in=None):
-    """Chunkwise recurrent form, [SUM] Summary ("computes in parallel within a
-    chunk and passes the recurrent state between chunks") and [RMB]
+    """Chunkwise recurrent form, [SUM] Summary (parallel work inside each
+    chunk, a recurrent state carried from one chunk to the next) and [RMB]
     "representations". For chunk i of length b (the last one may be short):
         O_i = (Q_i K_i^T (.) D) V_i + (Q_i R_{i-1}) (.) xi
         R_i = K_i^T (V_i (.) zeta) + g^b R_{i-1}
